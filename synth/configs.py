@@ -1,0 +1,67 @@
+"""Workload shapes of the folded tensor+sequence parallel (TSP) layer shard.
+
+The 7B dense shape and the 16K-128K context range are the pages' own
+experimental setting ("Folding Tensor and Sequence Parallelism for
+Memory-Efficient Transformer Training & Inference", section 4, Results).
+The remaining sizes (the tiny fp32 case, fold degree 8, the ranks run) fix a
+concrete single-rank workload for each of those settings.
+"""
+from dataclasses import dataclass, field, replace
+from typing import Tuple
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    hidden: int          # h
+    n_heads: int         # H
+    head_dim: int        # d = h / H
+    ffn: int             # F, SwiGLU inner width
+    seq: int             # S, total sequence length
+    fold: int            # D, fold degree = number of ranks on the TSP axis
+    ranks: Tuple[int, ...] = (0,)   # which ranks' shares this workload runs
+    layers: int = 1
+    dtype: str = "bf16"  # "bf16" or "f32": storage type of every tensor
+    eps: float = 1e-5
+    seed: int = 0
+    w_std: float = 0.02  # weights ~ N(0, w_std^2)
+    x_std: float = 1.0   # activations ~ N(0, x_std^2)
+    gamma: str = "ones"  # RMSNorm gain: "ones" or "normal" (1 + N(0, 0.1^2))
+
+    @property
+    def chunk(self) -> int:      # C = S / (2D)
+        return self.seq // (2 * self.fold)
+
+    @property
+    def local_tokens(self) -> int:  # T = S / D
+        return self.seq // self.fold
+
+    @property
+    def heads_per_shard(self) -> int:
+        return self.n_heads // self.fold
+
+    @property
+    def ffn_per_shard(self) -> int:
+        return self.ffn // self.fold
+
+    def with_(self, **kw) -> "LayerConfig":
+        return replace(self, **kw)
+
+
+CONFIGS = {
+    # Tiny fp32 layer; rank 1 of 4 holds zigzag chunks 1 and 6 (32 tokens each).
+    "tiny_fp32": LayerConfig("tiny_fp32", 64, 4, 16, 172, 256, 4, (1,), 1, "f32"),
+    # 7B-shape bf16 layer shard, 16K context, fold 8, rank 3.
+    "7b_s16k": LayerConfig("7b_s16k", 4096, 32, 128, 11008, 16384, 8, (3,)),
+    # Same shape at 64K context: 8192 local tokens in two chunks of 4096.
+    "7b_s64k": LayerConfig("7b_s64k", 4096, 32, 128, 11008, 65536, 8, (3,)),
+    # Attention-dominated 128K context; the first and last rank both run.
+    "7b_s128k": LayerConfig("7b_s128k", 4096, 32, 128, 11008, 131072, 8, (0, 7)),
+    # Every rank of a 4-layer stack at fold 4, run one after another.
+    "7b_fold4_s32k_4layer": LayerConfig("7b_fold4_s32k_4layer", 4096, 32, 128, 11008,
+                                        32768, 4, (0, 1, 2, 3), 4),
+}
+
+
+def get_config(name: str) -> LayerConfig:
+    return CONFIGS[name]
