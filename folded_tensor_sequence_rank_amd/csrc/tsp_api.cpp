@@ -1,0 +1,535 @@
+// C ABI of one TSP rank's layer share (declared in include/tsp.h): argument
+// validation, workspace carving and the double-buffered shard stream.
+//
+// Shard stream.  The TSP schedules (section 2 of "Folding Tensor and Sequence
+// Parallelism for Memory-Efficient Transformer Training & Inference") move
+// weight shards between ranks: a broadcast per attention iteration, a ring
+// step per MLP shard, and an all-gather of K/V along the sequence; the
+// transfers are pipelined behind the GEMMs.  Here the other ranks' shards are
+// device buffers, and the transfer becomes a copy into one of two workspace
+// slots on a side stream.  Events hand each slot over:
+//   copy stream:    wait free[s] (slot s released by iteration i-2) -> copy -> record ready[s]
+//   compute stream: wait ready[s] -> GEMM / attention / GEMM -> record free[s]
+// so the copy of iteration i+1 runs while iteration i computes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+#include <string>
+
+#include "tsp.h"
+#include "tsp_kernels.h"
+
+using namespace tsp;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                       \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail(TSP_E_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, \
+                  __LINE__);                                                                \
+  } while (0)
+
+struct Dims {
+  int64_t h, H, d, F, D, r, S, C, T, Hd, hs, Fs;
+  size_t es;
+  Dtype dt;
+  float eps;
+  uint32_t flags;
+};
+
+int check_dims(const tsp_dims* p, Dims* o) {
+  if (!p) return fail(TSP_E_INVAL, "dims is NULL");
+  if (p->dtype != TSP_BF16 && p->dtype != TSP_F32)
+    return fail(TSP_E_DTYPE, "dtype %d is neither TSP_BF16 nor TSP_F32", p->dtype);
+  if (p->fold <= 0 || p->rank < 0 || p->rank >= p->fold)
+    return fail(TSP_E_INVAL, "rank %d outside [0, fold=%d)", p->rank, p->fold);
+  if (p->seq < 0 || p->hidden <= 0 || p->n_heads <= 0 || p->head_dim <= 0 || p->ffn <= 0)
+    return fail(TSP_E_INVAL, "sizes must be positive (seq may be 0)");
+  if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return fail(TSP_E_INVAL, "eps must be finite >= 0");
+  if ((int64_t)p->n_heads * p->head_dim != p->hidden)
+    return fail(TSP_E_SHAPE, "hidden %d != n_heads %d * head_dim %d", p->hidden, p->n_heads,
+                p->head_dim);
+  if (p->head_dim != 16 && p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128)
+    return fail(TSP_E_SHAPE, "head_dim %d not in {16, 32, 64, 128}", p->head_dim);
+  if (p->n_heads % p->fold) return fail(TSP_E_SHAPE, "n_heads %d %% fold %d != 0", p->n_heads, p->fold);
+  if (p->ffn % p->fold) return fail(TSP_E_SHAPE, "ffn %d %% fold %d != 0", p->ffn, p->fold);
+  if (p->seq % (2 * (int64_t)p->fold))
+    return fail(TSP_E_SHAPE, "seq %lld is not a multiple of 2*fold", (long long)p->seq);
+  if (p->seq % 8) return fail(TSP_E_SHAPE, "seq %lld is not a multiple of 8", (long long)p->seq);
+  if (p->hidden % 8) return fail(TSP_E_SHAPE, "hidden %d is not a multiple of 8", p->hidden);
+  o->h = p->hidden;
+  o->H = p->n_heads;
+  o->d = p->head_dim;
+  o->F = p->ffn;
+  o->D = p->fold;
+  o->r = p->rank;
+  o->S = p->seq;
+  o->C = p->seq / (2 * p->fold);
+  o->T = 2 * o->C;
+  o->Hd = o->H / o->D;
+  o->hs = o->h / o->D;
+  o->Fs = o->F / o->D;
+  o->dt = p->dtype == TSP_BF16 ? BF16 : F32;
+  o->es = p->dtype == TSP_BF16 ? 2 : 4;
+  o->eps = p->eps;
+  o->flags = p->flags;
+  return TSP_OK;
+}
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace regions.  Offsets are from the workspace base.
+struct AttnWs {
+  size_t xn, y, q, o, slotw[2], slotkv[2], op, ml, end;
+};
+struct MlpWs {
+  size_t xn, y, gg, slotw[2], end;
+};
+
+size_t attn_shard_elems(const Dims& d) { return 4 * (size_t)d.hs * d.h; }
+size_t mlp_shard_elems(const Dims& d) { return 3 * (size_t)d.Fs * d.h; }
+size_t kv_block_elems(const Dims& d) { return 2 * (size_t)d.Hd * d.S * d.d; }
+
+AttnPlan plan_of(const Dims& d) { return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)d.Hd); }
+
+AttnWs attn_ws(const Dims& d, size_t base) {
+  AttnWs w;
+  size_t o = base;
+  const size_t act = al((size_t)d.T * d.h * d.es);
+  w.xn = o; o += act;
+  w.y = o; o += al((size_t)d.T * d.h * 4);
+  w.q = o; o += al((size_t)d.T * d.hs * d.es);
+  w.o = o; o += al((size_t)d.T * d.hs * d.es);
+  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(attn_shard_elems(d) * d.es); }
+  for (int s = 0; s < 2; s++) { w.slotkv[s] = o; o += al(kv_block_elems(d) * d.es); }
+  const AttnPlan p = plan_of(d);
+  const size_t nslot = p.split ? (size_t)d.Hd * p.nqt * p.maxseg * 128 : 0;
+  w.op = o; o += al(nslot * d.d * 4);
+  w.ml = o; o += al(nslot * 2 * 4);
+  w.end = o;
+  return w;
+}
+
+MlpWs mlp_ws(const Dims& d, size_t base) {
+  MlpWs w;
+  size_t o = base;
+  w.xn = o; o += al((size_t)d.T * d.h * d.es);
+  w.y = o; o += al((size_t)d.T * d.h * 4);
+  w.gg = o; o += al((size_t)d.T * d.Fs * d.es);
+  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(mlp_shard_elems(d) * d.es); }
+  w.end = o;
+  return w;
+}
+
+size_t kv_ws_bytes(const Dims& d) { return al((size_t)d.T * d.h * d.es); }
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Events for the slot hand-offs, created once per host thread and device.
+struct Events {
+  hipEvent_t start, join, readyA[2], freeA[2], readyM[2], freeM[2];
+};
+constexpr int kMaxDev = 64;
+thread_local Events* g_ev[kMaxDev] = {};
+
+int get_events(Events** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDev) return fail(TSP_E_HIP, "device index %d unsupported", dev);
+  if (!g_ev[dev]) {
+    Events* e = new Events;
+    hipEvent_t* all[] = {&e->start,     &e->join,      &e->readyA[0], &e->readyA[1], &e->freeA[0],
+                         &e->freeA[1],  &e->readyM[0], &e->readyM[1], &e->freeM[0],  &e->freeM[1]};
+    for (hipEvent_t* p : all) HIP_TRY(hipEventCreateWithFlags(p, hipEventDisableTiming));
+    g_ev[dev] = e;
+  }
+  *out = g_ev[dev];
+  return TSP_OK;
+}
+
+// One call's streams: `cs` carries the copies (== s when not overlapping).
+struct Ctx {
+  const Dims* d;
+  char* ws;
+  hipStream_t s, cs;
+  bool side;
+  Events* ev;
+};
+
+int begin(Ctx& c, hipStream_t s, hipStream_t cs, uint32_t flags) {
+  c.s = s;
+  c.side = cs != nullptr && cs != s && !(flags & TSP_F_NO_OVERLAP);
+  c.cs = c.side ? cs : s;
+  int rc = get_events(&c.ev);
+  if (rc) return rc;
+  if (c.side) {
+    // Copies must not start before earlier work on the compute stream (which
+    // produced the inputs or still reads this workspace) is done.
+    HIP_TRY(hipEventRecord(c.ev->start, c.s));
+    HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->start, 0));
+  }
+  return TSP_OK;
+}
+
+int finish(Ctx& c) {
+  if (c.side) {
+    HIP_TRY(hipEventRecord(c.ev->join, c.cs));
+    HIP_TRY(hipStreamWaitEvent(c.s, c.ev->join, 0));
+  }
+  return TSP_OK;
+}
+
+// Debug modes on the copy stream before a slot is refilled.
+int debug_before_fill(Ctx& c, void* slot, size_t bytes) {
+  if (c.d->flags & TSP_F_DELAY_COPY) HIP_TRY(launch_spin(20000 /* 200 us */, c.cs));
+  if (c.d->flags & TSP_F_POISON_SLOTS)
+    HIP_TRY(launch_fill32(slot, c.d->dt == BF16 ? 0x7FC07FC0u : 0x7FC00000u, bytes, c.cs));
+  return TSP_OK;
+}
+
+// Rows of the gathered K/V that rank r needs from the others: its causal
+// window is [0, (2D-r)C), minus its own chunks r and 2D-1-r.
+int copy_remote_kv(Ctx& c, const char* kv_block, char* slot) {
+  const Dims& d = *c.d;
+  const size_t es = d.es;
+  const int64_t ranges[2][2] = {{0, d.r * d.C}, {(d.r + 1) * d.C, (2 * d.D - 1 - d.r) * d.C}};
+  const char* srcK = kv_block;
+  const char* srcV = kv_block + (size_t)d.Hd * d.S * d.d * es;
+  char* dstK = slot;
+  char* dstV = slot + (size_t)d.Hd * d.S * d.d * es;
+  for (auto& rg : ranges) {
+    const int64_t a = rg[0], n = rg[1] - rg[0];
+    if (n <= 0) continue;
+    const size_t kp = (size_t)d.S * d.d * es;  // one head's K plane
+    HIP_TRY(hipMemcpy2DAsync(dstK + a * d.d * es, kp, srcK + a * d.d * es, kp, n * d.d * es,
+                             d.Hd, hipMemcpyDeviceToDevice, c.cs));
+    const size_t vp = (size_t)d.S * es;  // one V^T row
+    HIP_TRY(hipMemcpy2DAsync(dstV + a * es, vp, srcV + a * es, vp, n * es, d.Hd * d.d,
+                             hipMemcpyDeviceToDevice, c.cs));
+  }
+  return TSP_OK;
+}
+
+GemmArgs gemm_base() {
+  GemmArgs g;
+  memset(&g, 0, sizeof g);
+  return g;
+}
+
+// QKV projection of this rank's tokens with packed shard w (rows [col0, 3hs)
+// of its first block), scattered to Q (if col0 == 0) and to K/V at the
+// tokens' global positions.
+int qkv_gemm(Ctx& c, const void* xn, const char* w, int col0, void* q, char* kvslot) {
+  const Dims& d = *c.d;
+  GemmArgs g = gemm_base();
+  g.A = xn;
+  g.lda = d.h;
+  g.B = w + (size_t)col0 * d.h * d.es;
+  g.ldb = d.h;
+  g.M = (int)d.T;
+  g.N = (int)(3 * d.hs - col0);
+  g.K = (int)d.h;
+  g.Q = q;
+  g.Kd = kvslot;
+  g.Vt = kvslot + (size_t)d.Hd * d.S * d.d * d.es;
+  g.hs = (int)d.hs;
+  g.hd = (int)d.d;
+  g.col0 = col0;
+  g.S = d.S;
+  g.T = d.T;
+  g.chunk = d.C;
+  g.rank = (int)d.r;
+  g.fold = (int)d.D;
+  HIP_TRY(launch_gemm(d.dt, EPI_QKV, g, c.s));
+  return TSP_OK;
+}
+
+// y (+)= a . w^T, or on the last shard out = resid + y + a . w^T.
+int acc_gemm(Ctx& c, const void* a, int64_t K, const char* w, float* y, bool first, bool last,
+             const void* resid, void* out) {
+  const Dims& d = *c.d;
+  GemmArgs g = gemm_base();
+  g.A = a;
+  g.lda = K;
+  g.B = w;
+  g.ldb = K;
+  g.M = (int)d.T;
+  g.N = (int)d.h;
+  g.K = (int)K;
+  g.Y = y;
+  g.ldy = d.h;
+  g.beta = first ? 0 : 1;
+  if (last) {
+    g.R = resid;
+    g.ldr = d.h;
+    g.C = out;
+    g.ldc = d.h;
+    HIP_TRY(launch_gemm(d.dt, EPI_RESID, g, c.s));
+  } else {
+    HIP_TRY(launch_gemm(d.dt, EPI_ACC, g, c.s));
+  }
+  return TSP_OK;
+}
+
+int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void* const* w_attn,
+              const void* kv, void* x1) {
+  const Dims& d = *c.d;
+  char* ws = c.ws;
+  const size_t wbytes = attn_shard_elems(d) * d.es;
+  const size_t kvbytes = kv_block_elems(d) * d.es;
+  const AttnPlan plan = plan_of(d);
+  HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws + L.xn, d.T, (int)d.h, d.eps, c.s));
+  for (int64_t j = 0; j < d.D; j++) {  // broadcast iteration j: shard of rank j
+    const int s = (int)(j & 1);
+    char* slotw = ws + L.slotw[s];
+    char* slotkv = ws + L.slotkv[s];
+    // ---- copy stream: receive shard j and the other ranks' K_j/V_j rows
+    if (c.side && j >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeA[s], 0));
+    int rc = debug_before_fill(c, slotw, wbytes);
+    if (rc) return rc;
+    if (c.d->flags & TSP_F_POISON_SLOTS)
+      HIP_TRY(launch_fill32(slotkv, d.dt == BF16 ? 0x7FC07FC0u : 0x7FC00000u, kvbytes, c.cs));
+    if (j != d.r) HIP_TRY(hipMemcpyAsync(slotw, w_attn[j], wbytes, hipMemcpyDeviceToDevice, c.cs));
+    rc = copy_remote_kv(c, (const char*)kv + (size_t)j * kvbytes, slotkv);
+    if (rc) return rc;
+    if (c.side) {
+      HIP_TRY(hipEventRecord(c.ev->readyA[s], c.cs));
+      HIP_TRY(hipStreamWaitEvent(c.s, c.ev->readyA[s], 0));
+    }
+    // ---- compute stream
+    const char* w = j == d.r ? (const char*)w_attn[d.r] : slotw;
+    rc = qkv_gemm(c, ws + L.xn, w, 0, ws + L.q, slotkv);
+    if (rc) return rc;
+    AttnArgs a;
+    memset(&a, 0, sizeof a);
+    a.Q = ws + L.q;
+    a.K = slotkv;
+    a.Vt = slotkv + (size_t)d.Hd * d.S * d.d * d.es;
+    a.O = ws + L.o;
+    a.Op = (float*)(ws + L.op);
+    a.ML = (float*)(ws + L.ml);
+    a.T = d.T;
+    a.S = d.S;
+    a.chunk = d.C;
+    a.ldo = (int)d.hs;
+    a.rank = (int)d.r;
+    a.fold = (int)d.D;
+    a.Hd = (int)d.Hd;
+    a.nqt = plan.nqt;
+    a.lseg = plan.lseg;
+    a.maxseg = plan.maxseg;
+    a.nitems = plan.nitems;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
+    HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, c.s));
+    rc = acc_gemm(c, ws + L.o, d.hs, w + (size_t)3 * d.hs * d.h * d.es, (float*)(ws + L.y), j == 0,
+                  j == d.D - 1, x, x1);
+    if (rc) return rc;
+    if (c.side) HIP_TRY(hipEventRecord(c.ev->freeA[s], c.s));
+  }
+  return TSP_OK;
+}
+
+int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void* const* w_mlp,
+             void* out) {
+  const Dims& d = *c.d;
+  char* ws = c.ws;
+  const size_t wbytes = mlp_shard_elems(d) * d.es;
+  HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.T, (int)d.h, d.eps, c.s));
+  for (int64_t t = 0; t < d.D; t++) {  // ring step t: shard (r + t) mod D
+    const int64_t j = (d.r + t) % d.D;
+    const int s = (int)(t & 1);
+    const char* w = (const char*)w_mlp[d.r];
+    if (t > 0) {
+      char* slotw = ws + L.slotw[s];
+      if (c.side && t >= 3) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeM[s], 0));
+      int rc = debug_before_fill(c, slotw, wbytes);
+      if (rc) return rc;
+      HIP_TRY(hipMemcpyAsync(slotw, w_mlp[j], wbytes, hipMemcpyDeviceToDevice, c.cs));
+      if (c.side) {
+        HIP_TRY(hipEventRecord(c.ev->readyM[s], c.cs));
+        HIP_TRY(hipStreamWaitEvent(c.s, c.ev->readyM[s], 0));
+      }
+      w = slotw;
+    }
+    GemmArgs g = gemm_base();
+    g.A = ws + L.xn;
+    g.lda = d.h;
+    g.B = w;
+    g.B3 = w + (size_t)d.Fs * d.h * d.es;
+    g.ldb = d.h;
+    g.M = (int)d.T;
+    g.N = (int)d.Fs;
+    g.K = (int)d.h;
+    g.C = ws + L.gg;
+    g.ldc = d.Fs;
+    HIP_TRY(launch_gemm(d.dt, EPI_SWIGLU, g, c.s));
+    int rc = acc_gemm(c, ws + L.gg, d.Fs, w + (size_t)2 * d.Fs * d.h * d.es, (float*)(ws + L.y),
+                      t == 0, t == d.D - 1, x1, out);
+    if (rc) return rc;
+    if (c.side && t > 0) HIP_TRY(hipEventRecord(c.ev->freeM[s], c.s));
+  }
+  return TSP_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (!p) return fail(TSP_E_INVAL, "a required pointer is NULL");
+    if (!aligned(p)) return fail(TSP_E_ALIGN, "pointer %p is not 16-byte aligned", p);
+  }
+  return TSP_OK;
+}
+
+int check_shards(const void* const* w, int64_t D, const char* what) {
+  if (!w) return fail(TSP_E_INVAL, "%s pointer array is NULL", what);
+  for (int64_t j = 0; j < D; j++) {
+    if (!w[j]) return fail(TSP_E_INVAL, "%s[%lld] is NULL", what, (long long)j);
+    if (!aligned(w[j])) return fail(TSP_E_ALIGN, "%s[%lld] is not 16-byte aligned", what, (long long)j);
+  }
+  return TSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tsp_workspace_bytes(const tsp_dims* dims, int which) {
+  Dims d;
+  if (check_dims(dims, &d)) return 0;
+  switch (which) {
+    case TSP_WS_ATTN: return attn_ws(d, 0).end;
+    case TSP_WS_MLP: return mlp_ws(d, 0).end;
+    case TSP_WS_LAYER: {
+      const size_t x1 = al((size_t)d.T * d.h * d.es);
+      const AttnWs a = attn_ws(d, x1);
+      return mlp_ws(d, a.end).end;
+    }
+    case TSP_WS_KV: return kv_ws_bytes(d);
+    default: return 0;
+  }
+}
+
+const char* tsp_strerror(int status) {
+  switch (status) {
+    case TSP_OK: return "success";
+    case TSP_E_INVAL: return "invalid argument";
+    case TSP_E_SHAPE: return "unsupported shape";
+    case TSP_E_ALIGN: return "pointer not 16-byte aligned";
+    case TSP_E_WORKSPACE: return "workspace too small";
+    case TSP_E_DTYPE: return "unsupported dtype";
+    case TSP_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* tsp_last_error(void) { return g_err.c_str(); }
+
+int tsp_zigzag_positions(int64_t seq, int32_t fold, int32_t rank, int64_t* out) {
+  if (fold <= 0 || rank < 0 || rank >= fold || seq < 0 || (!out && seq > 0))
+    return fail(TSP_E_INVAL, "bad zigzag arguments");
+  if (seq % (2 * (int64_t)fold)) return fail(TSP_E_SHAPE, "seq is not a multiple of 2*fold");
+  const int64_t C = seq / (2 * fold);
+  for (int64_t i = 0; i < C; i++) {
+    out[i] = rank * C + i;
+    out[C + i] = (int64_t)(2 * fold - 1 - rank) * C + i;
+  }
+  return TSP_OK;
+}
+
+int tsp_attn_shard(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,
+                   const void* kv, void* x1, void* ws, size_t ws_bytes, void* stream,
+                   void* copy_stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if ((rc = check_ptrs({x, g1, kv, x1, ws})) || (rc = check_shards(w_attn, d.D, "w_attn"))) return rc;
+  const AttnWs L = attn_ws(d, 0);
+  if (ws_bytes < L.end)
+    return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.end);
+  Ctx c{&d, (char*)ws};
+  if ((rc = begin(c, (hipStream_t)stream, (hipStream_t)copy_stream, d.flags))) return rc;
+  if ((rc = attn_body(c, L, x, g1, w_attn, kv, x1))) return rc;
+  return finish(c);
+}
+
+int tsp_mlp_shard(const tsp_dims* dims, const void* x1, const void* g2, const void* const* w_mlp,
+                  void* out, void* ws, size_t ws_bytes, void* stream, void* copy_stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if ((rc = check_ptrs({x1, g2, out, ws})) || (rc = check_shards(w_mlp, d.D, "w_mlp"))) return rc;
+  const MlpWs L = mlp_ws(d, 0);
+  if (ws_bytes < L.end)
+    return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.end);
+  Ctx c{&d, (char*)ws};
+  if ((rc = begin(c, (hipStream_t)stream, (hipStream_t)copy_stream, d.flags))) return rc;
+  if ((rc = mlp_body(c, L, x1, g2, w_mlp, out))) return rc;
+  return finish(c);
+}
+
+int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,
+                    const void* kv, const void* g2, const void* const* w_mlp, void* out, void* ws,
+                    size_t ws_bytes, void* stream, void* copy_stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if ((rc = check_ptrs({x, g1, kv, g2, out, ws})) || (rc = check_shards(w_attn, d.D, "w_attn")) ||
+      (rc = check_shards(w_mlp, d.D, "w_mlp")))
+    return rc;
+  const size_t x1off = 0;
+  const AttnWs A = attn_ws(d, al((size_t)d.T * d.h * d.es));
+  const MlpWs M = mlp_ws(d, A.end);
+  if (ws_bytes < M.end) return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, M.end);
+  Ctx c{&d, (char*)ws};
+  if ((rc = begin(c, (hipStream_t)stream, (hipStream_t)copy_stream, d.flags))) return rc;
+  void* x1 = (char*)ws + x1off;
+  if ((rc = attn_body(c, A, x, g1, w_attn, kv, x1))) return rc;
+  if ((rc = mlp_body(c, M, x1, g2, w_mlp, out))) return rc;
+  return finish(c);
+}
+
+int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,
+                 void* kv, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if ((rc = check_ptrs({x, g1, kv, ws})) || (rc = check_shards(w_attn, d.D, "w_attn"))) return rc;
+  if (ws_bytes < kv_ws_bytes(d))
+    return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, kv_ws_bytes(d));
+  Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr};
+  HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws, d.T, (int)d.h, d.eps, c.s));
+  const size_t kvbytes = kv_block_elems(d) * d.es;
+  for (int64_t j = 0; j < d.D; j++) {
+    rc = qkv_gemm(c, ws, (const char*)w_attn[j], (int)d.hs, nullptr, (char*)kv + (size_t)j * kvbytes);
+    if (rc) return rc;
+  }
+  return TSP_OK;
+}
+
+}  // extern "C"

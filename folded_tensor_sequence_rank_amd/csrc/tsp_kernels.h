@@ -1,0 +1,76 @@
+// Internal launch interface between the C ABI (tsp_api.cpp) and the gfx950
+// kernels (tsp_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsp {
+
+enum Dtype { BF16 = 0, F32 = 1 };
+
+// Epilogues of the projection GEMM C = A . B^T (A [M][K], B [N][K]).
+enum Epi {
+  EPI_ACC = 1,    // Y = (beta ? Y : 0) + acc            (fp32 accumulator, in place)
+  EPI_RESID = 2,  // C = R + (beta ? Y : 0) + acc         (residual add, output dtype)
+  EPI_QKV = 3,    // scatter columns to Q / K / Vt at zigzag positions
+  EPI_SWIGLU = 4  // C = silu(A.B1^T) * (A.B3^T)           (two B operands)
+};
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const void* B3;  // second B operand (EPI_SWIGLU)
+  int64_t lda, ldb;
+  int M, N, K;
+  void* C;
+  int64_t ldc;
+  float* Y;
+  int64_t ldy;
+  int beta;
+  const void* R;
+  int64_t ldr;
+  // EPI_QKV: column c (after adding col0) is part c / hs (0 Q, 1 K, 2 V),
+  // head (c % hs) / hd, dim c % hd.  Q is [heads][T][hd]; K is
+  // [heads][S][hd]; Vt is [heads][hd][S]; local row m sits at global
+  // position zigzag(m).
+  void* Q;
+  void* Kd;
+  void* Vt;
+  int hs, hd, col0;
+  int64_t S, T;
+  int64_t chunk;
+  int rank, fold;
+};
+
+struct AttnArgs {
+  const void* Q;   // [Hd][T][HD]
+  const void* K;   // [Hd][S][HD]
+  const void* Vt;  // [Hd][HD][S]
+  void* O;         // [T][ldo]; head t writes columns [t*HD, (t+1)*HD)
+  float* Op;       // partial outputs of split items [Hd][nqt][maxseg][128][HD]
+  float* ML;       // partial (max, sum) [Hd][nqt][maxseg][128][2]
+  int64_t T, S, chunk;
+  int ldo, rank, fold, Hd;
+  int nqt, lseg, maxseg, nitems;
+  float scale_log2;  // log2(e) / sqrt(HD)
+};
+
+// Attention work plan for one head group (a deterministic function of the dims).
+struct AttnPlan {
+  int nqt;     // query tiles of 128 local rows
+  int lseg;    // keys per split item (multiple of 64)
+  int maxseg;  // largest number of splits of one query tile
+  int nitems;  // work items per head
+  bool split;  // any query tile has more than one split
+};
+AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int Hd);
+
+hipError_t launch_rmsnorm(Dtype dt, const void* x, const void* g, void* y, int64_t rows, int h,
+                          float eps, hipStream_t s);
+hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_attention(Dtype dt, int head_dim, const AttnArgs& a, const AttnPlan& p,
+                            hipStream_t s);
+hipError_t launch_fill32(void* p, uint32_t pattern, size_t bytes, hipStream_t s);
+hipError_t launch_spin(uint64_t ticks, hipStream_t s);
+
+}  // namespace tsp

@@ -1,0 +1,804 @@
+// gfx950 kernels of one TSP rank's layer share: RMSNorm, the projection GEMM
+// (bf16 / fp32 MFMA, fused epilogues) and zigzag-aware causal flash attention.
+//
+// Method: "Folding Tensor and Sequence Parallelism for Memory-Efficient
+// Transformer Training & Inference", section 2 (local projections of the
+// rank's own tokens with each weight shard, flash attention of the local
+// queries against the all-gathered K/V, zigzag partitioning, local
+// accumulation of partial outputs).  The attention kernel follows the
+// published FlashAttention method (tiles of K/V streamed through on-chip
+// memory, running max and running sum of the softmax, one rescale per tile).
+//
+// MFMA conventions relied on (32x32 output block, v_mfma_f32_32x32x16_bf16 and
+// v_mfma_f32_32x32x2_f32): lane l supplies row l%32 of A and column l%32 of B,
+// lanes 0-31 and 32-63 cover the two halves of the k range with the same
+// assignment for A and B; the result element (row, col) lives in lane
+// col + 32*((row/4)%2), register 4*(row/8) + row%4.
+#include "tsp_kernels.h"
+
+#include <math.h>
+
+namespace tsp {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct MF;
+template <>
+struct MF<bf16> {
+  static constexpr int KSTEP = 16;  // k per instruction
+  static constexpr int E = 8;       // operand elements per lane
+  typedef bf16x8 frag;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct MF<float> {
+  static constexpr int KSTEP = 2;
+  static constexpr int E = 1;
+  typedef float frag;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ inline float to_f(bf16 v) { return (float)v; }
+__device__ inline float to_f(float v) { return v; }
+template <typename T>
+__device__ inline T from_f(float v);
+template <>
+__device__ inline bf16 from_f<bf16>(float v) { return (bf16)v; }
+template <>
+__device__ inline float from_f<float>(float v) { return v; }
+
+template <typename T>
+union Chunk {  // one 16-byte vector
+  u32x4 raw;
+  T e[16 / sizeof(T)];
+};
+
+// Zigzag layout: local row i < C is global position r*C + i, row C + i is
+// (2D-1-r)*C + i (section 2, attention layers: zigzag partitioning).
+__device__ __host__ inline int64_t zig(int64_t row, int64_t C, int rank, int fold) {
+  return row < C ? rank * C + row : (int64_t)(2 * fold - 1 - rank) * C + (row - C);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, fp32 math, one wave per row.
+// HBM-bound: reads the row once for the sum of squares and once more (from
+// cache) for the scaled write.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const T* __restrict__ x,
+                                                      const T* __restrict__ g,
+                                                      T* __restrict__ y, int64_t rows, int h,
+                                                      float eps) {
+  constexpr int V = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* xr = x + row * h;
+  T* yr = y + row * h;
+  const bool vec = (h % V) == 0;
+  float ss = 0.f;
+  if (vec) {
+    for (int c = lane; c < h / V; c += 64) {
+      Chunk<T> v;
+      v.raw = *(const u32x4*)(xr + (int64_t)c * V);
+#pragma unroll
+      for (int i = 0; i < V; i++) {
+        const float f = to_f(v.e[i]);
+        ss += f * f;
+      }
+    }
+  } else {
+    for (int i = lane; i < h; i += 64) {
+      const float f = to_f(xr[i]);
+      ss += f * f;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o; o >>= 1) ss += __shfl_xor(ss, o);
+  const float rs = 1.0f / sqrtf(ss / (float)h + eps);
+  if (vec) {
+    for (int c = lane; c < h / V; c += 64) {
+      Chunk<T> v, w, out;
+      v.raw = *(const u32x4*)(xr + (int64_t)c * V);
+      w.raw = *(const u32x4*)(g + (int64_t)c * V);
+#pragma unroll
+      for (int i = 0; i < V; i++) out.e[i] = from_f<T>(to_f(v.e[i]) * rs * to_f(w.e[i]));
+      *(u32x4*)(yr + (int64_t)c * V) = out.raw;
+    }
+  } else {
+    for (int i = lane; i < h; i += 64) yr[i] = from_f<T>(to_f(xr[i]) * rs * to_f(g[i]));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Projection GEMM: acc = A . B^T, A [M][K] (lda), B [N][K] (ldb), both
+// K-contiguous.  256 threads = 2x2 waves; each wave owns (BM/2) x (BN/2) of
+// the tile as 32x32 MFMA blocks.  K is staged through LDS in 128-byte rows
+// (64 bf16 / 32 fp32), double-buffered, with the next tile's global loads in
+// flight in registers during the current tile's MFMAs.  LDS rows are
+// XOR-swizzled in 16-byte chunks so the 32 rows one fragment read touches
+// spread over the banks.
+// ---------------------------------------------------------------------------
+template <typename T, bool VEC>
+__device__ inline u32x4 load_chunk(const T* base, bool rowok, int64_t row, int64_t ld, int k,
+                                   int K) {
+  constexpr int V = 16 / sizeof(T);
+  Chunk<T> r;
+  r.raw = u32x4{0u, 0u, 0u, 0u};
+  if (!rowok) return r.raw;
+  const T* p = base + row * ld + k;
+  if (VEC) {
+    if (k < K) r.raw = *(const u32x4*)p;
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; e++) r.e[e] = (k + e < K) ? p[e] : from_f<T>(0.f);
+  }
+  return r.raw;
+}
+
+template <typename T, int BM, int BN, int EPI, bool VEC>
+__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
+  typedef MF<T> M_;
+  typedef typename M_::frag frag;
+  constexpr bool DUAL = (EPI == EPI_SWIGLU);
+  constexpr int ES = sizeof(T);
+  constexpr int BK = 128 / ES;  // elements per 128-byte LDS row
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int NBR = DUAL ? 2 * BN : BN;  // B rows staged per tile
+  constexpr int AC = BM * 8 / 256;         // 16-byte chunks per thread
+  constexpr int BC = NBR * 8 / 256;
+  constexpr int STAGE = (BM + NBR) * 128;
+  constexpr int NB3 = DUAL ? NB : 1;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Tiles are handed out so that each XCD (workgroups b with equal b % 8)
+  // works on a contiguous range of tiles and shares operands in its L2.
+  const int ntn = (g.N + BN - 1) / BN;
+  const int nt = gridDim.x;
+  const int bid = blockIdx.x;
+  const int per = nt >> 3;
+  const int t = bid < per * 8 ? (bid & 7) * per + (bid >> 3) : bid;
+  const int m0 = (t / ntn) * BM, n0 = (t % ntn) * BN;
+
+  const T* A = (const T*)g.A;
+  const T* B = (const T*)g.B;
+  const T* B3 = (const T*)g.B3;
+  u32x4 ra[AC], rb[BC];
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AC; i++) {
+      const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+      const int gm = m0 + row;
+      ra[i] = load_chunk<T, VEC>(A, gm < g.M, gm, g.lda, k0 + c * (16 / ES), g.K);
+    }
+#pragma unroll
+    for (int i = 0; i < BC; i++) {
+      const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+      const T* src = B;
+      int rr = row;
+      if (DUAL && row >= BN) {
+        src = B3;
+        rr = row - BN;
+      }
+      const int gn = n0 + rr;
+      rb[i] = load_chunk<T, VEC>(src, gn < g.N, gn, g.ldb, k0 + c * (16 / ES), g.K);
+    }
+  };
+  auto sstore = [&](int buf) {
+    char* sA = smem + buf * STAGE;
+    char* sB = sA + BM * 128;
+#pragma unroll
+    for (int i = 0; i < AC; i++) {
+      const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+      *(u32x4*)(sA + row * 128 + ((c ^ (row & 7)) << 4)) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BC; i++) {
+      const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+      *(u32x4*)(sB + row * 128 + ((c ^ (row & 7)) << 4)) = rb[i];
+    }
+  };
+
+  f32x16 acc[MB][NB];
+  f32x16 acc3[DUAL ? MB : 1][NB3];
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+      acc[i][j] = f32x16{0};
+      if (DUAL) acc3[i][j] = f32x16{0};
+    }
+
+  auto compute = [&](int buf) {
+    const char* sA = smem + buf * STAGE;
+    const char* sB = sA + BM * 128;
+#pragma unroll
+    for (int ks = 0; ks < BK / M_::KSTEP; ks++) {
+      const int byte = (ks * M_::KSTEP + lg * M_::E) * ES;
+      const int c = byte >> 4, w = byte & 15;
+      frag af[MB], bfr[NB], bf3[NB3];
+#pragma unroll
+      for (int i = 0; i < MB; i++) {
+        const int row = wm * WM + i * 32 + lr;
+        af[i] = *(const frag*)(sA + row * 128 + ((c ^ (row & 7)) << 4) + w);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; j++) {
+        const int row = wn * WN + j * 32 + lr;
+        bfr[j] = *(const frag*)(sB + row * 128 + ((c ^ (row & 7)) << 4) + w);
+        if (DUAL) {
+          const int r3 = BN + row;
+          bf3[j] = *(const frag*)(sB + r3 * 128 + ((c ^ (r3 & 7)) << 4) + w);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+          acc[i][j] = M_::mma(af[i], bfr[j], acc[i][j]);
+          if (DUAL) acc3[i][j] = M_::mma(af[i], bf3[j], acc3[i][j]);
+        }
+    }
+  };
+
+  const int nk = (g.K + BK - 1) / BK;
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt++) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload((kt + 1) * BK);
+      compute(cur);
+      if (kt + 1 < nk) sstore(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue straight from the accumulators: lane (lr, lg) of block (i, j)
+  // holds column n0 + wn*WN + 32j + lr and rows 8(r/4) + 4lg + r%4.
+#pragma unroll
+  for (int j = 0; j < NB; j++) {
+    const int n = n0 + wn * WN + j * 32 + lr;
+    if (n >= g.N) continue;
+    // Column-dependent part of the destination address.
+    T* cbase = nullptr;
+    int64_t rstride = 0;
+    int part = 0;
+    if constexpr (EPI == EPI_QKV) {
+      const int c = n + g.col0;
+      part = c / g.hs;
+      const int rem = c - part * g.hs;
+      const int head = rem / g.hd;
+      const int e = rem - head * g.hd;
+      if (part == 0) {
+        cbase = (T*)g.Q + (int64_t)head * g.T * g.hd + e;
+        rstride = g.hd;
+      } else if (part == 1) {
+        cbase = (T*)g.Kd + (int64_t)head * g.S * g.hd + e;
+        rstride = g.hd;
+      } else {
+        cbase = (T*)g.Vt + ((int64_t)head * g.hd + e) * g.S;
+        rstride = 1;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        if (m >= g.M) continue;
+        const float v = acc[i][j][r];
+        if constexpr (EPI == EPI_ACC) {
+          float* y = g.Y + (int64_t)m * g.ldy + n;
+          *y = g.beta ? *y + v : v;
+        } else if constexpr (EPI == EPI_RESID) {
+          float s = to_f(((const T*)g.R)[(int64_t)m * g.ldr + n]) + v;
+          if (g.beta) s += g.Y[(int64_t)m * g.ldy + n];
+          ((T*)g.C)[(int64_t)m * g.ldc + n] = from_f<T>(s);
+        } else if constexpr (EPI == EPI_SWIGLU) {
+          const float v3 = acc3[i][j < NB3 ? j : 0][r];
+          const float sg = v / (1.0f + fast_exp2(-v * 1.4426950408889634f));
+          ((T*)g.C)[(int64_t)m * g.ldc + n] = from_f<T>(sg * v3);
+        } else if constexpr (EPI == EPI_QKV) {
+          const int64_t at = part == 0 ? (int64_t)m : zig(m, g.chunk, g.rank, g.fold);
+          cbase[at * rstride] = from_f<T>(v);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Zigzag-aware causal flash attention of the local queries of one head group
+// against the gathered K/V.
+//
+// A work item is (head, query tile of 128 local rows, key segment).  Each of
+// the 4 waves owns 32 queries.  K/V tiles of 64 keys are staged in LDS
+// (double-buffered, loads of the next tile in flight during the current
+// tile's math).  Per tile a wave computes S^T = K . Q^T (lane <-> query,
+// registers <-> keys), applies the causal mask only where the tile reaches
+// past the wave's smallest query position, updates the running max / sum,
+// and accumulates O^T += V^T . P^T with P kept in registers.  K rows are fed
+// to the first product in an order that swaps bits 2 and 3 of the row index,
+// which makes each lane hold 8 consecutive keys per 16-key step of P, so the
+// matching V^T operand is one 16-byte LDS read.
+//
+// Keys a tile loads at or beyond the work item's last query position + 1 are
+// zero-filled (they are masked anyway), so rows the rank never receives are
+// never read.  Query tiles whose key range exceeds the segment length are
+// split into several items; their partial (max, sum, unnormalised O) are
+// merged by attn_combine_kernel.  Items are ordered heaviest first, and
+// head = item % Hd keeps one head on each XCD when Hd divides 8.
+// ---------------------------------------------------------------------------
+__device__ inline int kappa(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ inline bool decode_item(const AttnArgs& a, int item, int& qt, int& seg, int& nseg,
+                                   int64_t& kend) {
+  for (qt = a.nqt - 1; qt >= 0; --qt) {
+    const int64_t last = min(a.T, (int64_t)qt * 128 + 128) - 1;
+    kend = zig(last, a.chunk, a.rank, a.fold) + 1;
+    nseg = (int)((kend + a.lseg - 1) / a.lseg);
+    if (item < nseg) {
+      seg = item;
+      return true;
+    }
+    item -= nseg;
+  }
+  return false;
+}
+
+template <typename T, int HD>
+__global__ void __launch_bounds__(256, 2) attn_kernel(AttnArgs a) {
+  typedef MF<T> M_;
+  typedef typename M_::frag frag;
+  constexpr int ES = sizeof(T);
+  constexpr int BKV = 64;
+  constexpr int KROWB = HD * ES, KCH = KROWB / 16;
+  constexpr int VROWB = BKV * ES, VCH = VROWB / 16;
+  constexpr int KT_BYTES = BKV * KROWB;
+  constexpr int STAGE = KT_BYTES + HD * VROWB;
+  constexpr int KCHUNKS = BKV * KCH, VCHUNKS = HD * VCH;
+  constexpr int KC = (KCHUNKS + 255) / 256, VC = (VCHUNKS + 255) / 256;
+  constexpr int QK = HD / M_::KSTEP;  // k-steps over the head dim
+  constexpr int DB = (HD + 31) / 32;  // 32-row blocks of O^T
+  constexpr int PK = BKV / M_::KSTEP; // k-steps over the keys of a tile
+  constexpr int V = 16 / ES;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int head = blockIdx.x % a.Hd;
+  int qt, seg, nseg;
+  int64_t kend;
+  if (!decode_item(a, blockIdx.x / a.Hd, qt, seg, nseg, kend)) return;
+
+  const int64_t kbeg = (int64_t)seg * a.lseg;
+  const int64_t kfin = min(kend, kbeg + a.lseg);
+  const int64_t row0 = (int64_t)qt * 128 + wave * 32;
+  const int64_t row = row0 + lr;
+  const bool qok = row < a.T;
+  const int64_t qpos = qok ? zig(row, a.chunk, a.rank, a.fold) : -1;
+  const bool wok = row0 < a.T;
+  const bool wfull = row0 + 31 < a.T;
+  const int64_t kend_w = wok ? zig(min(a.T, row0 + 32) - 1, a.chunk, a.rank, a.fold) + 1 : 0;
+  const int64_t qmin_w = wok ? zig(row0, a.chunk, a.rank, a.fold) : 0;
+
+  const T* Qh = (const T*)a.Q + (int64_t)head * a.T * HD;
+  const T* Kh = (const T*)a.K + (int64_t)head * a.S * HD;
+  const T* Vh = (const T*)a.Vt + (int64_t)head * HD * a.S;
+
+  frag qf[QK];
+#pragma unroll
+  for (int ks = 0; ks < QK; ks++) {
+    const int e0 = ks * M_::KSTEP + lg * M_::E;
+    if (qok)
+      qf[ks] = *(const frag*)(Qh + row * HD + e0);
+    else
+      qf[ks] = frag{0};
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; d++) o[d] = f32x16{0};
+  float m = -INFINITY, l = 0.f;
+
+  u32x4 rk[KC], rv[VC];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < KC; i++) {
+      const int id = tid + 256 * i;
+      rk[i] = u32x4{0u, 0u, 0u, 0u};
+      if (KCHUNKS % 256 == 0 || id < KCHUNKS) {
+        const int r = id / KCH, c = id % KCH;
+        const int64_t key = k0 + r;
+        if (key < kend) rk[i] = *(const u32x4*)(Kh + key * HD + c * V);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VC; i++) {
+      const int id = tid + 256 * i;
+      rv[i] = u32x4{0u, 0u, 0u, 0u};
+      if (VCHUNKS % 256 == 0 || id < VCHUNKS) {
+        const int r = id / VCH, c = id % VCH;
+        const int64_t key = k0 + c * V;
+        const T* p = Vh + (int64_t)r * a.S + key;
+        if (key + V <= kend) {
+          rv[i] = *(const u32x4*)p;
+        } else if (key < kend) {
+          Chunk<T> t;
+#pragma unroll
+          for (int e = 0; e < V; e++) t.e[e] = (key + e < kend) ? p[e] : from_f<T>(0.f);
+          rv[i] = t.raw;
+        }
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    char* sK = smem + buf * STAGE;
+    char* sV = sK + KT_BYTES;
+#pragma unroll
+    for (int i = 0; i < KC; i++) {
+      const int id = tid + 256 * i;
+      if (KCHUNKS % 256 == 0 || id < KCHUNKS) {
+        const int r = id / KCH, c = id % KCH;
+        *(u32x4*)(sK + r * KROWB + ((c ^ (r & (KCH - 1))) << 4)) = rk[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VC; i++) {
+      const int id = tid + 256 * i;
+      if (VCHUNKS % 256 == 0 || id < VCHUNKS) {
+        const int r = id / VCH, c = id % VCH;
+        *(u32x4*)(sV + r * VROWB + ((c ^ (r & (VCH - 1))) << 4)) = rv[i];
+      }
+    }
+  };
+
+  auto compute = [&](int buf, int64_t k0) {
+    const char* sK = smem + buf * STAGE;
+    const char* sV = sK + KT_BYTES;
+    f32x16 s[2];
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      s[b] = f32x16{0};
+      const int krow = 32 * b + kappa(lr);
+#pragma unroll
+      for (int ks = 0; ks < QK; ks++) {
+        const int byte = (ks * M_::KSTEP + lg * M_::E) * ES;
+        const int c = byte >> 4, w = byte & 15;
+        const frag kf = *(const frag*)(sK + krow * KROWB + ((c ^ (krow & (KCH - 1))) << 4) + w);
+        s[b] = M_::mma(kf, qf[ks], s[b]);
+      }
+    }
+    // Scale to log2 units, mask, running max.  Register i of block b holds
+    // key k0 + 32b + 16(i/8) + 8*lg + i%8.
+    const bool mask = !wfull || (k0 + BKV - 1 > qmin_w);
+    float mt = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        float v = s[b][i] * a.scale_log2;
+        if (mask) {
+          const int64_t key = k0 + 32 * b + 16 * (i >> 3) + 8 * lg + (i & 7);
+          if (key > qpos) v = -INFINITY;
+        }
+        s[b][i] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = fast_exp2(m - mu);
+    float ls = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const float p = fast_exp2(s[b][i] - mu);
+        s[b][i] = p;
+        ls += p;
+      }
+    l = l * alpha + ls;
+    m = mn;
+#pragma unroll
+    for (int d = 0; d < DB; d++) o[d] *= alpha;
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int st = 0; st < PK; st++) {
+      frag pf;
+      int kk;  // first key (within the tile) this lane supplies at step st
+      if constexpr (M_::E == 8) {
+        const int b = st >> 1, i0 = (st & 1) * 8;
+#pragma unroll
+        for (int t = 0; t < 8; t++) pf[t] = (bf16)s[b][i0 + t];
+        kk = 16 * st + 8 * lg;
+      } else {
+        const int b = st >> 4, i = st & 15;
+        pf = s[b][i];
+        kk = 32 * b + 16 * (i >> 3) + 8 * lg + (i & 7);
+      }
+      const int byte = kk * ES;
+      const int c = byte >> 4, w = byte & 15;
+#pragma unroll
+      for (int d = 0; d < DB; d++) {
+        const int drow = 32 * d + lr;
+        frag vf;
+        if (HD % 32 == 0 || drow < HD)
+          vf = *(const frag*)(sV + drow * VROWB + ((c ^ (drow & (VCH - 1))) << 4) + w);
+        else
+          vf = frag{0};
+        o[d] = M_::mma(vf, pf, o[d]);
+      }
+    }
+  };
+
+  const int ntiles = (int)((kfin - kbeg + BKV - 1) / BKV);
+  if (ntiles > 0) {
+    gload(kbeg);
+    sstore(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t++) {
+      const int64_t k0 = kbeg + (int64_t)t * BKV;
+      if (t + 1 < ntiles) gload(k0 + BKV);
+      if (k0 < kend_w) compute(t & 1, k0);
+      if (t + 1 < ntiles) sstore((t + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  const float lt = l + __shfl_xor(l, 32);
+  if (nseg == 1) {
+    if (qok) {
+      const float inv = 1.0f / lt;
+      T* orow = (T*)a.O + row * a.ldo + head * HD;
+#pragma unroll
+      for (int d = 0; d < DB; d++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int d0 = 32 * d + 8 * q + 4 * lg;
+          if (HD % 32 == 0 || d0 < HD) {
+            Chunk<T> c4;  // only the first 4 elements are used
+#pragma unroll
+            for (int t = 0; t < 4; t++) c4.e[t] = from_f<T>(o[d][4 * q + t] * inv);
+            if constexpr (ES == 2) {
+              *(u32x2*)(orow + d0) = u32x2{c4.raw[0], c4.raw[1]};
+            } else {
+              *(u32x4*)(orow + d0) = c4.raw;
+            }
+          }
+        }
+    }
+  } else {
+    const int64_t slot = (((int64_t)head * a.nqt + qt) * a.maxseg + seg) * 128 + wave * 32 + lr;
+    float* op = a.Op + slot * HD;
+#pragma unroll
+    for (int d = 0; d < DB; d++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int d0 = 32 * d + 8 * q + 4 * lg;
+        if (HD % 32 == 0 || d0 < HD)
+          *(float4*)(op + d0) =
+              make_float4(o[d][4 * q], o[d][4 * q + 1], o[d][4 * q + 2], o[d][4 * q + 3]);
+      }
+    if (lg == 0) {
+      a.ML[2 * slot] = m;
+      a.ML[2 * slot + 1] = lt;
+    }
+  }
+}
+
+// Merge the partial results of split query tiles:
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+template <typename T, int HD>
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
+  constexpr int DQ = HD / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rid = gid / DQ;
+  const int dq = (int)(gid % DQ);
+  const int64_t head = rid / a.T, row = rid % a.T;
+  if (head >= a.Hd) return;
+  const int qt = (int)(row / 128);
+  const int64_t kend = zig(min(a.T, (int64_t)qt * 128 + 128) - 1, a.chunk, a.rank, a.fold) + 1;
+  const int nseg = (int)((kend + a.lseg - 1) / a.lseg);
+  if (nseg == 1) return;
+  const int64_t base = ((head * a.nqt + qt) * a.maxseg) * 128 + (row % 128);
+  float mx = -INFINITY;
+  for (int s = 0; s < nseg; s++) mx = fmaxf(mx, a.ML[2 * (base + s * 128)]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nseg; s++) {
+    const int64_t slot = base + s * 128;
+    const float w = fast_exp2(a.ML[2 * slot] - mx);
+    L += w * a.ML[2 * slot + 1];
+    const float4 v = *(const float4*)(a.Op + slot * HD + 4 * dq);
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float inv = 1.0f / L;
+  T* out = (T*)a.O + row * a.ldo + head * HD + 4 * dq;
+  out[0] = from_f<T>(acc.x * inv);
+  out[1] = from_f<T>(acc.y * inv);
+  out[2] = from_f<T>(acc.z * inv);
+  out[3] = from_f<T>(acc.w * inv);
+}
+
+// ---------------------------------------------------------------------------
+// Small helpers for the shard stream's debug modes.
+// ---------------------------------------------------------------------------
+__global__ void fill32_kernel(uint32_t* p, uint32_t pat, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = pat;
+}
+
+__global__ void spin_kernel(uint64_t ticks) {
+  if (threadIdx.x == 0) {
+    const uint64_t t0 = wall_clock64();
+    while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int Hd) {
+  AttnPlan p{};
+  p.nqt = (int)((T + 127) / 128);
+  if (T <= 0) return p;
+  int64_t tiles = 0, kmax = 0;
+  for (int qt = 0; qt < p.nqt; qt++) {
+    const int64_t kend = zig(std::min(T, (int64_t)qt * 128 + 128) - 1, chunk, rank, fold) + 1;
+    tiles += (kend + 63) / 64;
+    kmax = std::max(kmax, kend);
+  }
+  // About 1024 work items fill 256 CUs two workgroups deep, twice over.
+  const int64_t target = 1024;
+  int64_t lseg;
+  if ((int64_t)p.nqt * Hd >= target) {
+    lseg = (kmax + 63) / 64 * 64;
+  } else {
+    const int64_t per_item = (tiles * Hd + target - 1) / target;
+    lseg = std::max<int64_t>(16, per_item) * 64;
+  }
+  p.lseg = (int)lseg;
+  p.maxseg = 1;
+  p.nitems = 0;
+  for (int qt = 0; qt < p.nqt; qt++) {
+    const int64_t kend = zig(std::min(T, (int64_t)qt * 128 + 128) - 1, chunk, rank, fold) + 1;
+    const int ns = (int)((kend + lseg - 1) / lseg);
+    p.maxseg = std::max(p.maxseg, ns);
+    p.nitems += ns;
+  }
+  p.split = p.maxseg > 1;
+  return p;
+}
+
+hipError_t launch_rmsnorm(Dtype dt, const void* x, const void* g, void* y, int64_t rows, int h,
+                          float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (dt == BF16)
+    rmsnorm_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)g, (bf16*)y, rows, h, eps);
+  else
+    rmsnorm_kernel<float><<<grid, 256, 0, s>>>((const float*)x, (const float*)g, (float*)y, rows, h,
+                                               eps);
+  return hipGetLastError();
+}
+
+template <typename T, int BM, int BN, int EPI>
+static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
+  const int nt = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  if (vec)
+    gemm_kernel<T, BM, BN, EPI, true><<<nt, 256, 0, s>>>(a);
+  else
+    gemm_kernel<T, BM, BN, EPI, false><<<nt, 256, 0, s>>>(a);
+}
+
+template <int EPI>
+static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
+  const bool big = a.M >= 1024 && a.N >= 512;
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (big)
+      gemm_go<bf16, 256, 128, EPI>(a, vec, s);
+    else
+      gemm_go<bf16, 128, 64, EPI>(a, vec, s);
+  } else {
+    if (big)
+      gemm_go<bf16, 256, 256, EPI>(a, vec, s);
+    else
+      gemm_go<bf16, 128, 128, EPI>(a, vec, s);
+  }
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  const int V = dt == BF16 ? 8 : 4;
+  const bool vec = a.K % V == 0 && a.lda % V == 0 && a.ldb % V == 0 && aligned16(a.A) &&
+                   aligned16(a.B) && (a.B3 == nullptr || aligned16(a.B3));
+  if (dt == BF16) {
+    switch (epi) {
+      case EPI_ACC: gemm_bf16<EPI_ACC>(a, vec, s); break;
+      case EPI_RESID: gemm_bf16<EPI_RESID>(a, vec, s); break;
+      case EPI_QKV: gemm_bf16<EPI_QKV>(a, vec, s); break;
+      case EPI_SWIGLU: gemm_bf16<EPI_SWIGLU>(a, vec, s); break;
+    }
+  } else {
+    switch (epi) {
+      case EPI_ACC: gemm_go<float, 64, 64, EPI_ACC>(a, vec, s); break;
+      case EPI_RESID: gemm_go<float, 64, 64, EPI_RESID>(a, vec, s); break;
+      case EPI_QKV: gemm_go<float, 64, 64, EPI_QKV>(a, vec, s); break;
+      case EPI_SWIGLU: gemm_go<float, 64, 64, EPI_SWIGLU>(a, vec, s); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int HD>
+static void attn_go(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
+  attn_kernel<T, HD><<<p.nitems * a.Hd, 256, 0, s>>>(a);
+  if (p.split) {
+    const int64_t n = (int64_t)a.Hd * a.T * (HD / 4);
+    attn_combine_kernel<T, HD><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+  }
+}
+
+hipError_t launch_attention(Dtype dt, int hd, const AttnArgs& a, const AttnPlan& p,
+                            hipStream_t s) {
+  if (a.T <= 0 || p.nitems <= 0) return hipSuccess;
+  if (dt == BF16) {
+    switch (hd) {
+      case 16: attn_go<bf16, 16>(a, p, s); break;
+      case 32: attn_go<bf16, 32>(a, p, s); break;
+      case 64: attn_go<bf16, 64>(a, p, s); break;
+      case 128: attn_go<bf16, 128>(a, p, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (hd) {
+      case 16: attn_go<float, 16>(a, p, s); break;
+      case 32: attn_go<float, 32>(a, p, s); break;
+      case 64: attn_go<float, 64>(a, p, s); break;
+      case 128: attn_go<float, 128>(a, p, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill32(void* p, uint32_t pattern, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+  fill32_kernel<<<grid, 256, 0, s>>>((uint32_t*)p, pattern, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_spin(uint64_t ticks, hipStream_t s) {
+  spin_kernel<<<1, 64, 0, s>>>(ticks);
+  return hipGetLastError();
+}
+
+}  // namespace tsp

@@ -1,0 +1,197 @@
+"""Thin ctypes binding of libtsp.so (C ABI in include/tsp.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+PyTorch supplies device memory and streams.  The helpers at the bottom put
+weights into the packed shard layout the ABI defines (tensor slicing and
+transposes on the device) and size the gathered K/V buffer.
+
+If libtsp.so is missing this module raises on first use; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtsp.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "tsp.h")
+
+TSP_BF16, TSP_F32 = 0, 1
+TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV = 1, 2, 3, 4
+TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP = 1, 2, 4
+STATUS = {0: "TSP_OK", -1: "TSP_E_INVAL", -2: "TSP_E_SHAPE", -3: "TSP_E_ALIGN",
+          -4: "TSP_E_WORKSPACE", -5: "TSP_E_DTYPE", -6: "TSP_E_HIP"}
+
+
+class TspError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class TspDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("fold", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("seq", ctypes.c_int64), ("eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_pp = ctypes.POINTER(ctypes.c_void_p)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtsp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m folded_tensor_sequence_rank_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        D = ctypes.POINTER(TspDims)
+        L.tsp_workspace_bytes.argtypes = [D, ctypes.c_int]
+        L.tsp_workspace_bytes.restype = _sz
+        L.tsp_strerror.argtypes = [ctypes.c_int]
+        L.tsp_strerror.restype = ctypes.c_char_p
+        L.tsp_last_error.argtypes = []
+        L.tsp_last_error.restype = ctypes.c_char_p
+        L.tsp_zigzag_positions.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(ctypes.c_int64)]
+        L.tsp_attn_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _sz, _vp, _vp]
+        L.tsp_mlp_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
+        L.tsp_layer_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
+        L.tsp_kv_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp]
+        for f in ("tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
+                  "tsp_zigzag_positions"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> List[str]:
+    """Function names declared in include/tsp.h."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsp_[a-z_]+)\s*\(", src)))
+
+
+def make_dims(cfg, rank: int, flags: int = 0, seq: Optional[int] = None) -> TspDims:
+    """TspDims from any object with hidden, n_heads, head_dim, ffn, fold, seq,
+    eps and dtype ("bf16" or "f32") attributes."""
+    return TspDims(cfg.hidden, cfg.n_heads, cfg.head_dim, cfg.ffn, cfg.fold, rank,
+                   cfg.seq if seq is None else seq, cfg.eps,
+                   TSP_BF16 if cfg.dtype == "bf16" else TSP_F32, flags)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise TspError(rc, lib().tsp_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ptrs(ts: Sequence) -> ctypes.Array:
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def workspace_bytes(dims: TspDims, which: int) -> int:
+    return int(lib().tsp_workspace_bytes(ctypes.byref(dims), which))
+
+
+def zigzag_positions(seq: int, fold: int, rank: int) -> np.ndarray:
+    out = np.zeros(max(seq // fold, 1), np.int64)
+    _check(lib().tsp_zigzag_positions(seq, fold, rank,
+                                      out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+    return out[: seq // fold]
+
+
+def tsp_attn_shard(dims, x, g1, w_attn, kv, x1, ws, stream=None, copy_stream=None):
+    _check(lib().tsp_attn_shard(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
+                                _ptr(x1), _ptr(ws), _nbytes(ws), _stream(stream),
+                                None if copy_stream is None else _stream(copy_stream)))
+
+
+def tsp_mlp_shard(dims, x1, g2, w_mlp, out, ws, stream=None, copy_stream=None):
+    _check(lib().tsp_mlp_shard(ctypes.byref(dims), _ptr(x1), _ptr(g2), _ptrs(w_mlp), _ptr(out),
+                               _ptr(ws), _nbytes(ws), _stream(stream),
+                               None if copy_stream is None else _stream(copy_stream)))
+
+
+def tsp_layer_shard(dims, x, g1, w_attn, kv, g2, w_mlp, out, ws, stream=None, copy_stream=None):
+    _check(lib().tsp_layer_shard(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
+                                 _ptr(g2), _ptrs(w_mlp), _ptr(out), _ptr(ws), _nbytes(ws),
+                                 _stream(stream),
+                                 None if copy_stream is None else _stream(copy_stream)))
+
+
+def tsp_kv_shard(dims, x, g1, w_attn, kv, ws, stream=None):
+    _check(lib().tsp_kv_shard(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
+                              _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# Layout helpers (device tensors in, device tensors out)
+# ----------------------------------------------------------------------------
+
+def pack_attn_shards(wq, wk, wv, wo, fold: int):
+    """Packed attention shards from math-layout [h, h] weights (Q = n @ wq):
+    per shard j the output-major blocks of W_Q, W_K, W_V columns of head
+    group j, then the output-major block of W_O's rows of that group."""
+    import torch
+    h = wq.shape[0]
+    hs = h // fold
+    out = []
+    for j in range(fold):
+        c = slice(j * hs, (j + 1) * hs)
+        out.append(torch.cat([wq[:, c].t().reshape(-1), wk[:, c].t().reshape(-1),
+                              wv[:, c].t().reshape(-1), wo[c, :].t().reshape(-1)]).contiguous())
+    return out
+
+
+def pack_mlp_shards(w1, w3, w2, fold: int):
+    """Packed MLP shards from math-layout weights (w1, w3 [h, F]; w2 [F, h])."""
+    import torch
+    F = w1.shape[1]
+    fs = F // fold
+    out = []
+    for j in range(fold):
+        c = slice(j * fs, (j + 1) * fs)
+        out.append(torch.cat([w1[:, c].t().reshape(-1), w3[:, c].t().reshape(-1),
+                              w2[c, :].t().reshape(-1)]).contiguous())
+    return out
+
+
+def kv_elems(cfg) -> int:
+    """Elements of the gathered K/V buffer: D blocks of 2 * (H/D) * S * d."""
+    return 2 * cfg.n_heads * cfg.seq * cfg.head_dim

@@ -1,0 +1,196 @@
+/*
+ * tsp.h - C ABI of one rank's share of a folded tensor+sequence parallel
+ * (TSP) transformer layer, on one AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: "Folding Tensor and Sequence Parallelism for
+ * Memory-Efficient Transformer Training & Inference" (gist.science summary),
+ * section 2 "Metodologia: TSP", main design components.  TSP folds tensor and
+ * sequence parallelism onto ONE device axis of D ranks: each rank keeps 1/D
+ * of the parameters and 1/D of the tokens.  Attention weight shards are
+ * broadcast one per iteration, K/V are all-gathered along the sequence before
+ * flash attention, zigzag partitioning balances causal work, and gated-MLP
+ * weight shards circulate on a ring while each rank sums its partial outputs
+ * locally (no all-reduce).
+ *
+ * This library computes rank r's share on one GPU.  The other ranks' weight
+ * shards and the all-gathered K/V are ordinary device buffers; the library
+ * streams them through two workspace slots with copies on a side stream that
+ * overlap the compute, in place of the broadcast / all-gather / ring
+ * transfers between GPUs.
+ *
+ * ---------------------------------------------------------------------------
+ * Notation: h hidden, H heads, d = h/H head dim, F FFN width, S sequence
+ * length, D fold degree, r rank.  C = S/(2D) zigzag chunk, T = S/D = 2C local
+ * tokens, Hd = H/D heads per shard, hs = h/D = Hd*d, Fs = F/D.
+ * b = element size (2 for bf16, 4 for fp32).
+ *
+ * Layer (pre-norm): x1 = x + Attn(RMSNorm(x; g1)) W_O,
+ *                   out = x1 + (silu(n2 W1) * (n2 W3)) W2, n2 = RMSNorm(x1; g2).
+ * RMSNorm(x; g) = x / sqrt(mean(x^2) + eps) * g.  Attention is causal
+ * (key position <= query position), scale 1/sqrt(d), every head has its own
+ * K/V, no bias or positional encoding.
+ *
+ * Zigzag layout (section 2, attention layers): the sequence is cut into 2D
+ * chunks of C tokens; rank r holds chunk r then chunk 2D-1-r.  Local row
+ * i < C is global position r*C + i; local row C + i is (2D-1-r)*C + i.
+ *
+ * Weight shards (section 2: attention shards pack W_Q, W_K, W_V, W_O; the MLP
+ * shards are W1, W3, W2).  Shard j covers heads [j*Hd, (j+1)*Hd) and FFN
+ * columns [j*Fs, (j+1)*Fs).  Every matrix block is stored "output-major"
+ * (each row is one output feature, its input features contiguous), so a
+ * projection y = a W reads block row n as column n of W:
+ *   attention shard j, 4*hs*h elements, contiguous:
+ *     [0,    hs) rows x h cols : row n = column j*hs + n of W_Q
+ *     [hs, 2hs)  rows x h cols : row n = column j*hs + n of W_K
+ *     [2hs,3hs)  rows x h cols : row n = column j*hs + n of W_V
+ *     then h rows x hs cols    : row n, col k = W_O[j*hs + k][n]
+ *   MLP shard j, 3*Fs*h elements, contiguous:
+ *     Fs rows x h cols : row n = column j*Fs + n of W1 (gate, through silu)
+ *     Fs rows x h cols : row n = column j*Fs + n of W3 (linear branch)
+ *     h rows x Fs cols : row n, col k = W2[j*Fs + k][n]
+ *
+ * Gathered K/V (the all-gather's result), D blocks of 2*Hd*S*d elements;
+ * block j = [K_j | Vt_j]:
+ *     K_j  [Hd][S][d] : K_j[t][p][e]  = K of head j*Hd+t, position p, dim e
+ *     Vt_j [Hd][d][S] : Vt_j[t][e][p] = V of head j*Hd+t, position p, dim e
+ * V is stored transposed so that the P.V contraction reads keys contiguously.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every entry point
+ *   - Device pointers are plain device addresses; host pointer arrays
+ *     (w_attn, w_mlp: D entries) are read during the call only.  The caller
+ *     owns every buffer; the library allocates no device memory per call.
+ *   - All tensors of one call share dims->dtype; accumulation is fp32.
+ *     bf16 intermediates: normalised activations, Q/K/V, attention
+ *     probabilities, per-shard attention output and the SwiGLU product.
+ *   - Device pointers must be 16-byte aligned, tensors contiguous.
+ *   - Outputs must not alias inputs or the workspace.
+ *   - Streams are hipStream_t passed as void*; NULL means the null stream.
+ *     Calls are asynchronous: all work is enqueued on `stream`; side-stream
+ *     copies go to `copy_stream` (if NULL or equal to `stream`, copies run
+ *     in order on `stream`) and that stream is joined back into `stream`
+ *     before the call returns.  No host synchronisation.
+ *   - Return 0 (TSP_OK) on success.  Argument errors return a negative code
+ *     BEFORE anything is enqueued.  TSP_E_HIP reports a failed launch or
+ *     copy; tsp_last_error() gives the detail (thread-local).
+ *   - Calls that share a workspace must not overlap in time.
+ *   - An empty sequence (S == 0) is valid and enqueues nothing.
+ */
+#ifndef TSP_H
+#define TSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { TSP_BF16 = 0, TSP_F32 = 1 };
+
+enum {
+  TSP_OK = 0,
+  TSP_E_INVAL = -1,     /* null pointer, rank outside [0, D), negative size */
+  TSP_E_SHAPE = -2,     /* h != H*d, H % D, F % D, S % 2D, S % 8, unsupported d */
+  TSP_E_ALIGN = -3,     /* a device pointer is not 16-byte aligned */
+  TSP_E_WORKSPACE = -4, /* ws_bytes < tsp_workspace_bytes(...) */
+  TSP_E_DTYPE = -5,     /* dtype is neither TSP_BF16 nor TSP_F32 */
+  TSP_E_HIP = -6        /* a HIP launch or copy failed */
+};
+
+/* Workspace kinds for tsp_workspace_bytes. */
+enum { TSP_WS_ATTN = 1, TSP_WS_MLP = 2, TSP_WS_LAYER = 3, TSP_WS_KV = 4 };
+
+/* Debug flags (tsp_dims.flags).  Results must be identical with or without
+ * them; they exist to expose missing stream hand-offs in tests. */
+enum {
+  TSP_F_DELAY_COPY = 1u,   /* a bounded spin kernel runs on the copy stream before each copy */
+  TSP_F_POISON_SLOTS = 2u, /* each slot is filled with NaN before it is refilled */
+  TSP_F_NO_OVERLAP = 4u    /* run the copies in order on the compute stream */
+};
+
+typedef struct tsp_dims {
+  int32_t hidden;   /* h */
+  int32_t n_heads;  /* H */
+  int32_t head_dim; /* d; supported: 16, 32, 64, 128 */
+  int32_t ffn;      /* F */
+  int32_t fold;     /* D, ranks on the TSP axis */
+  int32_t rank;     /* r in [0, D) */
+  int64_t seq;      /* S, total sequence length */
+  float eps;        /* RMSNorm epsilon (inside the square root) */
+  int32_t dtype;    /* TSP_BF16 or TSP_F32 */
+  uint32_t flags;   /* TSP_F_* */
+} tsp_dims;
+
+/* Bytes of workspace an entry point needs for these dims (0 on bad dims). */
+size_t tsp_workspace_bytes(const tsp_dims* dims, int which);
+
+/* Static description of a status code. */
+const char* tsp_strerror(int status);
+
+/* Detail of the last error returned on this host thread ("" if none). */
+const char* tsp_last_error(void);
+
+/* Host helper: writes the T = S/D global positions of rank r's local rows
+ * (zigzag layout above) into out[0..T).  Returns TSP_E_SHAPE if S % 2D. */
+int tsp_zigzag_positions(int64_t seq, int32_t fold, int32_t rank, int64_t* out);
+
+/*
+ * Attention half of rank r's layer share: x1 = x + Attn(RMSNorm(x; g1)) W_O.
+ * Section 2, attention layers: for broadcast iteration j = 0..D-1 the packed
+ * shard j is used (w_attn[r] is read in place, the others are copied into a
+ * workspace slot on the side stream), the rank projects its own tokens to
+ * Q_j/K_j/V_j, the other ranks' K_j/V_j rows the rank's causal window needs
+ * (positions < (2D-r)*C) are copied from `kv` next to its own, zigzag-aware
+ * causal flash attention runs over the full gathered K/V, and the partial
+ * O-projection of head group j is accumulated locally in fp32.
+ *   x      [T][h]   local rows in zigzag order
+ *   g1     [h]      RMSNorm gain
+ *   w_attn D device pointers to packed attention shards (layout above)
+ *   kv     gathered K/V (layout above); only other ranks' rows are read
+ *   x1     [T][h]   output
+ *   ws     workspace of at least tsp_workspace_bytes(dims, TSP_WS_ATTN) bytes
+ */
+int tsp_attn_shard(const tsp_dims* dims, const void* x, const void* g1,
+                   const void* const* w_attn, const void* kv, void* x1,
+                   void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/*
+ * MLP half: out = x1 + sum_j (silu(n2 W1_j) * (n2 W3_j)) W2_j, n2 = RMSNorm(x1; g2).
+ * Section 2, gated MLP layers: ring step t = 0..D-1 uses shard (r + t) mod D
+ * (own shard first, read in place; the others are copied into a workspace
+ * slot on the side stream); the partial outputs are summed locally in fp32,
+ * so no all-reduce is needed.
+ *   x1    [T][h], g2 [h], w_mlp D device pointers to packed MLP shards,
+ *   out   [T][h], ws >= tsp_workspace_bytes(dims, TSP_WS_MLP).
+ */
+int tsp_mlp_shard(const tsp_dims* dims, const void* x1, const void* g2,
+                  const void* const* w_mlp, void* out,
+                  void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/*
+ * Whole layer share: tsp_attn_shard then tsp_mlp_shard, with x1 kept in the
+ * workspace and the first MLP shard copies issued while attention runs.
+ *   ws >= tsp_workspace_bytes(dims, TSP_WS_LAYER).
+ */
+int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1,
+                    const void* const* w_attn, const void* kv, const void* g2,
+                    const void* const* w_mlp, void* out,
+                    void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/*
+ * Rank r's contribution to the K/V all-gather (section 2, attention layers:
+ * the all-gather rebuilds full-length K/V along the sequence): writes K and
+ * V of rank r's local tokens, for every head, at their global positions into
+ * `kv` (layout above).  Rows of other ranks are left untouched.
+ *   x [T][h], g1 [h], w_attn D device pointers, ws >= tsp_workspace_bytes(dims, TSP_WS_KV).
+ */
+int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1,
+                 const void* const* w_attn, void* kv,
+                 void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSP_H */

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/tsp.h declares, sizes workspaces, and rejects bad arguments with the
+documented status before touching a GPU."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle.tsp_oracle as O
+import synth
+from folded_tensor_sequence_rank_amd import tsp
+
+C3 = synth.get_config("7b_s64k")
+TINY = synth.get_config("tiny_fp32")
+
+
+def test_exports_every_declared_symbol():
+    L = tsp.lib()
+    syms = tsp.header_symbols()
+    assert {"tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
+            "tsp_workspace_bytes", "tsp_strerror", "tsp_last_error",
+            "tsp_zigzag_positions"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_strerror():
+    L = tsp.lib()
+    for code, name in tsp.STATUS.items():
+        assert L.tsp_strerror(code).decode()
+    assert L.tsp_strerror(12345).decode() == "unknown status"
+
+
+def test_zigzag_helper_matches_statement_and_oracle():
+    # The tiny workload's rank 1 of 4 holds chunks 1 and 6 of 32 tokens.
+    p = tsp.zigzag_positions(256, 4, 1)
+    assert np.array_equal(p, np.r_[32:64, 192:224])
+    for S, D in [(16, 1), (64, 2), (1024, 8), (96, 3)]:
+        for r in range(D):
+            assert np.array_equal(tsp.zigzag_positions(S, D, r), O.zigzag_positions(S, D, r))
+    with pytest.raises(tsp.TspError) as e:
+        tsp.zigzag_positions(100, 8, 0)
+    assert e.value.name == "TSP_E_SHAPE"
+
+
+def test_workspace_sizes():
+    d = tsp.make_dims(C3, 3)
+    a = tsp.workspace_bytes(d, tsp.TSP_WS_ATTN)
+    m = tsp.workspace_bytes(d, tsp.TSP_WS_MLP)
+    l = tsp.workspace_bytes(d, tsp.TSP_WS_LAYER)
+    k = tsp.workspace_bytes(d, tsp.TSP_WS_KV)
+    T, h = 8192, 4096
+    assert a > 2 * 2 * 4 * 65536 * 128 * 2      # two K/V slots of one head group
+    assert l >= a + m + T * h * 2                 # x1 kept between the halves
+    assert k >= T * h * 2
+    assert l < 2 << 30                            # about 1 GB at the 64K workload
+    bad = tsp.make_dims(C3.with_(fold=3), 0)
+    assert tsp.workspace_bytes(bad, tsp.TSP_WS_ATTN) == 0
+    assert tsp.workspace_bytes(d, 99) == 0
+
+
+def _call_attn(dims, x=16, g=16, w=None, kv=16, out=16, ws=16, ws_bytes=1 << 40):
+    """Call tsp_attn_shard with fake (never dereferenced) addresses."""
+    L = tsp.lib()
+    D = dims.fold if dims.fold > 0 else 1
+    arr = (ctypes.c_void_p * D)(*([w if w is not None else 4096] * D))
+    return L.tsp_attn_shard(ctypes.byref(dims), x, g, arr, kv, out, ws, ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("case,field,value,status", [
+    ("rank_high", "rank", 8, "TSP_E_INVAL"),
+    ("rank_neg", "rank", -1, "TSP_E_INVAL"),
+    ("fold_zero", "fold", 0, "TSP_E_INVAL"),
+    ("dtype", "dtype", 7, "TSP_E_DTYPE"),
+    ("h_ne_Hd", "hidden", 4000, "TSP_E_SHAPE"),
+    ("head_dim", "head_dim", 96, "TSP_E_SHAPE"),
+    ("seq_2D", "seq", 65536 + 8, "TSP_E_SHAPE"),
+    ("ffn_D", "ffn", 11001, "TSP_E_SHAPE"),
+])
+def test_bad_dims(case, field, value, status):
+    d = tsp.make_dims(C3, 3)
+    if field == "head_dim":
+        d.head_dim, d.n_heads = 96, 4096 // 96  # keeps nothing consistent on purpose
+    else:
+        setattr(d, field, value)
+    rc = _call_attn(d)
+    assert tsp.STATUS[rc] == status, (rc, tsp.lib().tsp_last_error())
+
+
+def test_bad_pointers_and_workspace():
+    d = tsp.make_dims(C3, 3)
+    assert tsp.STATUS[_call_attn(d, x=0)] == "TSP_E_INVAL"
+    assert tsp.STATUS[_call_attn(d, w=0)] == "TSP_E_INVAL"
+    assert tsp.STATUS[_call_attn(d, kv=24)] == "TSP_E_ALIGN"
+    assert tsp.STATUS[_call_attn(d, w=4100)] == "TSP_E_ALIGN"
+    assert tsp.STATUS[_call_attn(d, ws_bytes=1000)] == "TSP_E_WORKSPACE"
+    assert "workspace" in tsp.lib().tsp_last_error().decode()
+    # null host pointer array
+    rc = tsp.lib().tsp_attn_shard(ctypes.byref(d), 16, 16, None, 16, 16, 16, 1 << 40, None, None)
+    assert tsp.STATUS[rc] == "TSP_E_INVAL"
+
+
+def test_empty_sequence_is_a_no_op():
+    d = tsp.make_dims(C3, 3, seq=0)
+    assert _call_attn(d, x=0, kv=0, out=0, ws=0, ws_bytes=0) == 0
+    L = tsp.lib()
+    arr = (ctypes.c_void_p * 8)()
+    assert L.tsp_mlp_shard(ctypes.byref(d), None, None, arr, None, None, 0, None, None) == 0
+    assert L.tsp_kv_shard(ctypes.byref(d), None, None, arr, None, None, 0, None) == 0
+
+
+def test_dims_struct_layout():
+    assert ctypes.sizeof(tsp.TspDims) == 48
+    assert tsp.TspDims.seq.offset == 24 and tsp.TspDims.flags.offset == 40
+
+
+def test_product_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(tsp, "_lib", None)
+    monkeypatch.setattr(tsp, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        tsp.lib()

@@ -1,0 +1,202 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: relative Frobenius error <= 1e-2 for bf16 workloads and <= 1e-4 for
+fp32, on the whole output and on each block's delta (x1 - x, out - x1), so
+the residual cannot hide an error.  The oracle runs in float64 on the very
+values the GPU receives.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.tsp_oracle as O
+import synth
+from gpu_harness import (LayerDev, RankRun, f64, fill_kv, layer_dev, new_kv, rel_fro, say,
+                         to_dev, tol)
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.get_config("tiny_fp32")
+
+
+def _cfg(**kw):
+    base = dict(name="case", hidden=256, n_heads=2, head_dim=128, ffn=688, seq=1600, fold=4,
+                ranks=(0,), layers=1, dtype="bf16")
+    base.update(kw)
+    return synth.LayerConfig(**base)
+
+
+# Small workloads that together cover several tiles and ragged tails in every
+# dimension, each head size, fold 1/2/4/8, fp32 and bf16, a random RMSNorm
+# gain, and chunk lengths that are not multiples of the 128-row query tile.
+SMALL = {
+    "tiny_fp32": TINY,
+    "tiny_bf16": TINY.with_(dtype="bf16"),
+    "bf16_d128_ragged": _cfg(hidden=512, n_heads=4),              # C=200, F/D=172
+    "bf16_d128_ragged_lowres": _cfg(hidden=512, n_heads=4, x_std=0.02),
+    "bf16_d64_lowres_gamma": _cfg(hidden=256, n_heads=4, head_dim=64, ffn=1024, seq=2048, fold=4,
+                                  x_std=0.02, gamma="normal"),
+    "tiny_bf16_lowres": TINY.with_(dtype="bf16", x_std=0.02),
+    "bf16_d64_fold2": _cfg(hidden=256, n_heads=4, head_dim=64, ffn=512, seq=1024, fold=2),
+    "bf16_d32_fold8_gamma": _cfg(hidden=256, n_heads=8, head_dim=32, ffn=704, seq=1024, fold=8,
+                                 gamma="normal"),
+    "bf16_d16_fold1": _cfg(hidden=64, n_heads=4, head_dim=16, ffn=176, seq=200, fold=1),
+    "bf16_c20": _cfg(hidden=128, n_heads=4, head_dim=32, ffn=344, seq=160, fold=4),
+    "f32_d64": _cfg(hidden=128, n_heads=2, head_dim=64, ffn=344, seq=512, fold=2, dtype="f32"),
+    "f32_d128_fold4": _cfg(hidden=512, n_heads=4, head_dim=128, ffn=1376, seq=1024, fold=4,
+                           dtype="f32", gamma="normal"),
+}
+
+
+def _setup(cfg, layer=0):
+    w = synth.gen_weights(cfg, layer)
+    x_full = synth.gen_x_rows(cfg, 0, cfg.seq, layer)
+    L = layer_dev(cfg, w)
+    pos = [O.zigzag_positions(cfg.seq, cfg.fold, r) for r in range(cfg.fold)]
+    from folded_tensor_sequence_rank_amd import tsp
+    for r in range(cfg.fold):  # the library's zigzag agrees with the oracle's
+        assert np.array_equal(tsp.zigzag_positions(cfg.seq, cfg.fold, r), pos[r])
+    xs = [to_dev(x_full[p], cfg) for p in pos]
+    return w, x_full, L, xs, pos
+
+
+def _round(cfg, a):
+    """The oracle value as the output dtype would store it."""
+    a = np.asarray(a, np.float64)
+    r = synth.bf16_round(a.astype(np.float32)) if cfg.dtype == "bf16" else a.astype(np.float32)
+    return r.astype(np.float64)
+
+
+def _check(cfg, name, got, want, base=None, want_base=None):
+    """Whole output: rel Frobenius <= tol.  Block delta (got - base versus
+    want - want_base): its error, beyond the output's own storage rounding,
+    must be <= tol of the delta's norm.  The rounding term is what storing
+    the oracle's exact result in the output dtype costs; without it a bf16
+    residual stream (|x| ~ 1) would swamp a small block delta."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    e = rel_fro(got, want)
+    msg = f"{name}: rel {e:.3e}"
+    ok = bool(e <= tol(cfg))
+    if base is not None:
+        dref = want - want_base
+        err = np.linalg.norm((got - base) - dref)
+        rnd = np.linalg.norm(want - _round(cfg, want))
+        if want_base is not base:
+            rnd += np.linalg.norm(want_base - _round(cfg, want_base))
+        bound = tol(cfg) * np.linalg.norm(dref) + 1.25 * rnd
+        msg += (f", delta err {err / max(np.linalg.norm(dref), 1e-300):.3e} of |delta| "
+                f"(bound {bound / max(np.linalg.norm(dref), 1e-300):.3e}, "
+                f"storage rounding {rnd / max(np.linalg.norm(dref), 1e-300):.3e})")
+        ok = ok and bool(err <= bound)
+    say("   ", msg)
+    assert ok, msg
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_all_ranks(case):
+    cfg = SMALL[case]
+    say(f"[gpu] small parity {case}: h={cfg.hidden} H={cfg.n_heads} d={cfg.head_dim} "
+        f"F={cfg.ffn} S={cfg.seq} D={cfg.fold} {cfg.dtype}")
+    w, x_full, L, xs, pos = _setup(cfg)
+    x1_ref = O.attention_block_rows(x_full, w, cfg.n_heads, cfg.eps, np.arange(cfg.seq))
+    out_ref = O.mlp_block(x1_ref, w, cfg.eps)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    parts = []
+    for r in range(cfg.fold):
+        run = RankRun(cfg, r)
+        x1 = run.attn(xs[r], L, kv)
+        out = run.mlp(x1, L)
+        lay = run.layer(xs[r], L, kv)
+        torch.cuda.synchronize()
+        xr = x_full[pos[r]].astype(np.float64)
+        _check(cfg, f"rank {r} x1", f64(x1), x1_ref[pos[r]], xr, xr)
+        _check(cfg, f"rank {r} out", f64(out), out_ref[pos[r]], f64(x1), x1_ref[pos[r]])
+        assert torch.equal(lay, out), "layer call differs from attention + MLP calls"
+        parts.append(f64(lay))
+    # brute force over the fold: un-zigzagged shares rebuild the unsharded layer
+    full = O.unzigzag(parts, cfg.seq, cfg.fold)
+    _check(cfg, "all ranks un-zigzagged", full, out_ref)
+
+
+def test_split_attention_items():
+    """A shape whose query tiles are split over several key segments and
+    merged afterwards."""
+    cfg = _cfg(hidden=512, n_heads=4, head_dim=128, ffn=1024, seq=8192, fold=2)
+    say("[gpu] split-segment attention parity, S=8192 D=2")
+    w, x_full, L, xs, pos = _setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    for r in range(cfg.fold):
+        x1 = RankRun(cfg, r).attn(xs[r], L, kv)
+        torch.cuda.synchronize()
+        ref = O.attention_block_rows(x_full, w, cfg.n_heads, cfg.eps, pos[r])
+        xr = x_full[pos[r]].astype(np.float64)
+        _check(cfg, f"rank {r} x1", f64(x1), ref, xr, xr)
+
+
+def test_own_kv_rows_not_read():
+    """The rank's own rows in the gathered K/V stay NaN: it must use the rows
+    it projects itself."""
+    cfg = SMALL["bf16_d128_ragged"]
+    say("[gpu] own K/V rows are computed, not read")
+    w, x_full, L, xs, pos = _setup(cfg)
+    r = 2
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv, skip=r)
+    out = RankRun(cfg, r).layer(xs[r], L, kv)
+    torch.cuda.synchronize()
+    ref = O.layer_rows(x_full, w, cfg.n_heads, cfg.eps, pos[r])
+    _check(cfg, "rank 2 out", f64(out), ref)
+
+
+@pytest.mark.parametrize("flags", ["delay_poison", "no_overlap", "null_copy_stream"])
+def test_stream_handoff_bitwise(flags):
+    """Delaying the copy stream and poisoning slots with NaN before each
+    refill must not change a single bit; neither must running the copies in
+    order on the compute stream.  Repeated runs are bitwise reproducible."""
+    from folded_tensor_sequence_rank_amd import tsp
+    cfg = SMALL["bf16_d32_fold8_gamma"]
+    say(f"[gpu] stream hand-off, mode {flags}")
+    w, x_full, L, xs, pos = _setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    r = 5
+    base = RankRun(cfg, r).layer(xs[r], L, kv)
+    again = RankRun(cfg, r).layer(xs[r], L, kv)
+    if flags == "delay_poison":
+        run = RankRun(cfg, r, flags=tsp.TSP_F_DELAY_COPY | tsp.TSP_F_POISON_SLOTS)
+    elif flags == "no_overlap":
+        run = RankRun(cfg, r, flags=tsp.TSP_F_NO_OVERLAP)
+    else:
+        run = RankRun(cfg, r, copy_stream=False)
+    other = run.layer(xs[r], L, kv)
+    other2 = run.layer(xs[r], L, kv)
+    torch.cuda.synchronize()
+    assert torch.equal(base, again)
+    assert torch.equal(base, other)
+    assert torch.equal(base, other2)
+    assert torch.isfinite(other).all()
+
+
+def test_7b_s16k_rank3_full():
+    """The 7B shape at 16K context, fold 8, rank 3: every output row against
+    the oracle."""
+    cfg = synth.get_config("7b_s16k")
+    r = cfg.ranks[0]
+    say(f"[gpu] 7B shape S={cfg.seq} D={cfg.fold} rank {r}: full rank parity")
+    w, x_full, L, xs, pos = _setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv, skip=r)
+    run = RankRun(cfg, r)
+    x1 = run.attn(xs[r], L, kv)
+    out = run.mlp(x1, L)
+    torch.cuda.synchronize()
+    say("    GPU done; oracle running")
+    x1_ref = O.attention_block_rows(x_full, w, cfg.n_heads, cfg.eps, pos[r])
+    out_ref = O.mlp_block(x1_ref, w, cfg.eps)
+    xr = x_full[pos[r]].astype(np.float64)
+    _check(cfg, "x1", f64(x1), x1_ref, xr, xr)
+    _check(cfg, "out", f64(out), out_ref, f64(x1), x1_ref)
