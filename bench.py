@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Throughput of one rank's TSP layer share on one MI355X.
+
+A step is one tsp_layer_shard call: RMSNorm, D attention shards (QKV
+projection, zigzag causal flash attention against the gathered K/V, O
+projection accumulated in place), RMSNorm, D MLP shards (W1/W3 with SwiGLU,
+W2 accumulated in place), residuals, with the other ranks' shards and K/V
+rows streamed through the side-stream slots.  Inputs are resident in HBM
+before the timed region; the other ranks' K/V rows (the all-gather's
+payload) are produced beforehand with tsp_kv_shard and are not timed.
+
+Default workload: the 7B shape (h 4096, 32 heads x 128, SwiGLU 11008) at
+S = 65536, fold D = 8, rank 3 (8192 local tokens in two zigzag chunks).
+
+Prints one JSON line.  value = algorithmic TFLOP/s of the layer share:
+F = 8 T h^2 + 6 T h F + 4 h P, P = causal (query, key) pairs of the rank.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for p in (ROOT, os.path.join(ROOT, "tests")):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+METRIC = "TFLOP/s and tokens/s per TSP layer shard (7B shape), % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "folded_tensor_sequence_rank_amd", "csrc", "tsp_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="7b_s64k")
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=32,
+                    help="local rows of the rank's second chunk the oracle computes")
+    ap.add_argument("--no-profile", action="store_true")
+    return ap.parse_args()
+
+
+def flops_per_launch(cfg, r):
+    """Algorithmic FLOPs of one launch of each kernel class."""
+    import oracle.tsp_oracle as O  # closed-form pair count only
+    T, h, D = cfg.local_tokens, cfg.hidden, cfg.fold
+    hs, Fs = h // D, cfg.ffn // D
+    pairs = O.causal_pairs(cfg.seq, D, r)  # per head
+    return {"qkv": 2 * T * 3 * hs * h, "attn": 4 * hs * pairs, "oproj": 2 * T * hs * h,
+            "w13": 2 * T * 2 * Fs * h, "w2": 2 * T * Fs * h}
+
+
+def bytes_per_launch(cfg):
+    es = 2 if cfg.dtype == "bf16" else 4
+    T, h = cfg.local_tokens, cfg.hidden
+    return {"rmsnorm": 2 * T * h * es + h * es}
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None once the kernel source has changed since the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, r, rows):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle.tsp_oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=os.cpu_count())
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    pos = O.zigzag_positions(cfg.seq, cfg.fold, r)[cfg.chunk: cfg.chunk + rows]
+    pmax = int(pos.max()) + 1
+    x = synth.gen_x_rows(cfg, 0, pmax)
+    w = synth.gen_weights(cfg)
+    t0 = time.perf_counter()
+    O.layer_rows(x, w, cfg.n_heads, cfg.eps, pos)
+    dt = time.perf_counter() - t0
+    h, F = cfg.hidden, cfg.ffn
+    executed = (2 * rows * h * h + 2 * 2 * pmax * h * h + 4 * h * int(np.sum(pos + 1))
+                + 2 * rows * h * h + 6 * rows * h * F)
+    return {"value": executed / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": (f"{cfg.name}, rank {r}: fp64 numpy oracle layer_rows for the first {rows} "
+                       f"local rows of the second zigzag chunk (positions {int(pos[0])}.."
+                       f"{int(pos[-1])}), including the K/V projection of all {pmax} positions "
+                       f"they attend to; value = FLOPs the oracle executed / wall time")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the layer: the TSP path here runs on a "
+              "single MI355X (one rank at its real shape); multi-GPU runs are not part of it.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import oracle.tsp_oracle as O
+    import synth
+    from folded_tensor_sequence_rank_amd import tsp
+    from gpu_harness import RankRun, fill_kv, layer_dev, new_kv, to_dev
+
+    cfg = synth.get_config(args.workload)
+    r = cfg.ranks[0] if args.rank is None else args.rank
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    w = synth.gen_weights(cfg)
+    L = layer_dev(cfg, w)
+    del w
+    xs = []
+    for q in range(cfg.fold):
+        xs.append(to_dev(synth.gen_rows(cfg, tsp.zigzag_positions(cfg.seq, cfg.fold, q)), cfg))
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv, skip=r)
+    x = xs[r]
+    for q in range(cfg.fold):
+        if q != r:
+            xs[q] = None
+    out = torch.empty_like(x)
+    run = RankRun(cfg, r)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    for _ in range(args.warmup):
+        run.layer(x, L, kv, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run.layer(x, L, kv, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out).all(), "non-finite output"
+
+    T = cfg.local_tokens
+    f_alg = O.flops_rank(cfg.hidden, cfg.ffn, cfg.seq, cfg.fold, r)
+    tflops = f_alg / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    kernels, roofline = {}, None
+    if not args.no_profile:
+        prun = RankRun(cfg, r, flags=tsp.TSP_F_PROFILE)
+        prun.layer(x, L, kv, out)
+        torch.cuda.synchronize()
+        tsp.tsp_profile_read(reset=True)
+        for _ in range(args.steps):
+            prun.layer(x, L, kv, out)
+        torch.cuda.synchronize()
+        prof = tsp.tsp_profile_read(reset=True)
+        fl = flops_per_launch(cfg, r)
+        by = bytes_per_launch(cfg)
+        for k, (tot, n) in prof.items():
+            if n == 0:
+                continue
+            avg = tot / n
+            ent = {"ms_avg": round(avg, 5), "launches_per_step": n / args.steps,
+                   "ms_per_step": round(tot / args.steps, 4)}
+            if k in fl:
+                ent["tflops"] = round(fl[k] / (avg * 1e-3) / 1e12, 1)
+            if k in by:
+                ent["gbs"] = round(by[k] / (avg * 1e-3) / 1e9, 1)
+            kernels[k] = ent
+        dom = max((k for k in kernels if k in fl), key=lambda k: kernels[k]["ms_per_step"])
+        ach = fl[dom] / (kernels[dom]["ms_avg"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                    "flops_per_launch": fl[dom], "traffic": traffic_for(dom)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, r, args.cpu_rows)
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "hidden": cfg.hidden, "heads": cfg.n_heads,
+                   "head_dim": cfg.head_dim, "ffn": cfg.ffn, "seq": cfg.seq, "fold": cfg.fold,
+                   "rank": r, "local_tokens": T, "parallelism": "tsp-rank-share"},
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "frac_of_peak": round(tflops / peak, 4),
+        "flops_per_step": f_alg,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

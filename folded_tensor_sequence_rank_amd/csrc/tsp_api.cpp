@@ -20,6 +20,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <string>
+#include <vector>
 
 #include "tsp.h"
 #include "tsp_kernels.h"
@@ -173,10 +174,51 @@ struct Ctx {
   hipStream_t s, cs;
   bool side;
   Events* ev;
+  bool prof;
 };
+
+// Per-kernel timing (TSP_F_PROFILE): timing-enabled events bracket each
+// launch on the compute stream; tsp_profile_read resolves them later.
+struct ProfState {
+  struct Pending {
+    int k;
+    hipEvent_t a, b;
+  };
+  std::vector<hipEvent_t> pool;
+  std::vector<Pending> pending;
+  double ms[TSP_K_COUNT] = {};
+  int64_t n[TSP_K_COUNT] = {};
+};
+thread_local ProfState g_prof;
+
+hipError_t prof_event(hipEvent_t* e) {
+  if (!g_prof.pool.empty()) {
+    *e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(e);
+}
+
+// Runs `stmt` (which launches one kernel class on c.s) between two events.
+#define TIMED(c, k, stmt)                                              \
+  do {                                                                 \
+    hipEvent_t ev0_ = nullptr, ev1_ = nullptr;                         \
+    if ((c).prof) {                                                    \
+      HIP_TRY(prof_event(&ev0_));                                      \
+      HIP_TRY(prof_event(&ev1_));                                      \
+      HIP_TRY(hipEventRecord(ev0_, (c).s));                            \
+    }                                                                  \
+    stmt;                                                              \
+    if ((c).prof) {                                                    \
+      HIP_TRY(hipEventRecord(ev1_, (c).s));                            \
+      g_prof.pending.push_back({(k), ev0_, ev1_});                     \
+    }                                                                  \
+  } while (0)
 
 int begin(Ctx& c, hipStream_t s, hipStream_t cs, uint32_t flags) {
   c.s = s;
+  c.prof = (flags & TSP_F_PROFILE) != 0;
   c.side = cs != nullptr && cs != s && !(flags & TSP_F_NO_OVERLAP);
   c.cs = c.side ? cs : s;
   int rc = get_events(&c.ev);
@@ -297,7 +339,7 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
   const size_t wbytes = attn_shard_elems(d) * d.es;
   const size_t kvbytes = kv_block_elems(d) * d.es;
   const AttnPlan plan = plan_of(d);
-  HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws + L.xn, d.T, (int)d.h, d.eps, c.s));
+  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws + L.xn, d.T, (int)d.h, d.eps, c.s)));
   for (int64_t j = 0; j < d.D; j++) {  // broadcast iteration j: shard of rank j
     const int s = (int)(j & 1);
     char* slotw = ws + L.slotw[s];
@@ -317,7 +359,7 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     }
     // ---- compute stream
     const char* w = j == d.r ? (const char*)w_attn[d.r] : slotw;
-    rc = qkv_gemm(c, ws + L.xn, w, 0, ws + L.q, slotkv);
+    TIMED(c, TSP_K_QKV, rc = qkv_gemm(c, ws + L.xn, w, 0, ws + L.q, slotkv));
     if (rc) return rc;
     AttnArgs a;
     memset(&a, 0, sizeof a);
@@ -339,9 +381,11 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     a.maxseg = plan.maxseg;
     a.nitems = plan.nitems;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
-    HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, c.s));
-    rc = acc_gemm(c, ws + L.o, d.hs, w + (size_t)3 * d.hs * d.h * d.es, (float*)(ws + L.y), j == 0,
-                  j == d.D - 1, x, x1);
+    TIMED(c, TSP_K_ATTN, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 0, c.s)));
+    if (plan.split) TIMED(c, TSP_K_MERGE, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 1, c.s)));
+    TIMED(c, TSP_K_OPROJ,
+          rc = acc_gemm(c, ws + L.o, d.hs, w + (size_t)3 * d.hs * d.h * d.es, (float*)(ws + L.y),
+                        j == 0, j == d.D - 1, x, x1));
     if (rc) return rc;
     if (c.side) HIP_TRY(hipEventRecord(c.ev->freeA[s], c.s));
   }
@@ -353,7 +397,7 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
   const Dims& d = *c.d;
   char* ws = c.ws;
   const size_t wbytes = mlp_shard_elems(d) * d.es;
-  HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.T, (int)d.h, d.eps, c.s));
+  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.T, (int)d.h, d.eps, c.s)));
   for (int64_t t = 0; t < d.D; t++) {  // ring step t: shard (r + t) mod D
     const int64_t j = (d.r + t) % d.D;
     const int s = (int)(t & 1);
@@ -381,9 +425,11 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
     g.K = (int)d.h;
     g.C = ws + L.gg;
     g.ldc = d.Fs;
-    HIP_TRY(launch_gemm(d.dt, EPI_SWIGLU, g, c.s));
-    int rc = acc_gemm(c, ws + L.gg, d.Fs, w + (size_t)2 * d.Fs * d.h * d.es, (float*)(ws + L.y),
-                      t == 0, t == d.D - 1, x1, out);
+    TIMED(c, TSP_K_W13, HIP_TRY(launch_gemm(d.dt, EPI_SWIGLU, g, c.s)));
+    int rc = 0;
+    TIMED(c, TSP_K_W2,
+          rc = acc_gemm(c, ws + L.gg, d.Fs, w + (size_t)2 * d.Fs * d.h * d.es, (float*)(ws + L.y),
+                        t == 0, t == d.D - 1, x1, out));
     if (rc) return rc;
     if (c.side && t > 0) HIP_TRY(hipEventRecord(c.ev->freeM[s], c.s));
   }
@@ -522,12 +568,38 @@ int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1, const void
   if ((rc = check_ptrs({x, g1, kv, ws})) || (rc = check_shards(w_attn, d.D, "w_attn"))) return rc;
   if (ws_bytes < kv_ws_bytes(d))
     return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, kv_ws_bytes(d));
-  Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr};
-  HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws, d.T, (int)d.h, d.eps, c.s));
+  Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr,
+        (d.flags & TSP_F_PROFILE) != 0};
+  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws, d.T, (int)d.h, d.eps, c.s)));
   const size_t kvbytes = kv_block_elems(d) * d.es;
   for (int64_t j = 0; j < d.D; j++) {
-    rc = qkv_gemm(c, ws, (const char*)w_attn[j], (int)d.hs, nullptr, (char*)kv + (size_t)j * kvbytes);
+    TIMED(c, TSP_K_QKV,
+          rc = qkv_gemm(c, ws, (const char*)w_attn[j], (int)d.hs, nullptr,
+                        (char*)kv + (size_t)j * kvbytes));
     if (rc) return rc;
+  }
+  return TSP_OK;
+}
+
+int tsp_profile_read(double* ms, int64_t* n, int reset) {
+  g_err.clear();
+  for (auto& p : g_prof.pending) {
+    float t = 0.f;
+    HIP_TRY(hipEventSynchronize(p.b));
+    HIP_TRY(hipEventElapsedTime(&t, p.a, p.b));
+    g_prof.ms[p.k] += t;
+    g_prof.n[p.k] += 1;
+    g_prof.pool.push_back(p.a);
+    g_prof.pool.push_back(p.b);
+  }
+  g_prof.pending.clear();
+  for (int k = 0; k < TSP_K_COUNT; k++) {
+    if (ms) ms[k] = g_prof.ms[k];
+    if (n) n[k] = g_prof.n[k];
+    if (reset) {
+      g_prof.ms[k] = 0;
+      g_prof.n[k] = 0;
+    }
   }
   return TSP_OK;
 }

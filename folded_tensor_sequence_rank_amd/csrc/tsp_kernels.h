@@ -68,8 +68,10 @@ AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int 
 hipError_t launch_rmsnorm(Dtype dt, const void* x, const void* g, void* y, int64_t rows, int h,
                           float eps, hipStream_t s);
 hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s);
+// part 0: the attention kernel; part 1: the merge of split items (no-op
+// when the plan has no split).
 hipError_t launch_attention(Dtype dt, int head_dim, const AttnArgs& a, const AttnPlan& p,
-                            hipStream_t s);
+                            int part, hipStream_t s);
 hipError_t launch_fill32(void* p, uint32_t pattern, size_t bytes, hipStream_t s);
 hipError_t launch_spin(uint64_t ticks, hipStream_t s);
 

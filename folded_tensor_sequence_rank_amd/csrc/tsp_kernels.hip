@@ -757,31 +757,32 @@ hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
 }
 
 template <typename T, int HD>
-static void attn_go(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  attn_kernel<T, HD><<<p.nitems * a.Hd, 256, 0, s>>>(a);
-  if (p.split) {
+static void attn_go(const AttnArgs& a, const AttnPlan& p, int part, hipStream_t s) {
+  if (part == 0) {
+    attn_kernel<T, HD><<<p.nitems * a.Hd, 256, 0, s>>>(a);
+  } else if (p.split) {
     const int64_t n = (int64_t)a.Hd * a.T * (HD / 4);
     attn_combine_kernel<T, HD><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
   }
 }
 
-hipError_t launch_attention(Dtype dt, int hd, const AttnArgs& a, const AttnPlan& p,
+hipError_t launch_attention(Dtype dt, int hd, const AttnArgs& a, const AttnPlan& p, int part,
                             hipStream_t s) {
   if (a.T <= 0 || p.nitems <= 0) return hipSuccess;
   if (dt == BF16) {
     switch (hd) {
-      case 16: attn_go<bf16, 16>(a, p, s); break;
-      case 32: attn_go<bf16, 32>(a, p, s); break;
-      case 64: attn_go<bf16, 64>(a, p, s); break;
-      case 128: attn_go<bf16, 128>(a, p, s); break;
+      case 16: attn_go<bf16, 16>(a, p, part, s); break;
+      case 32: attn_go<bf16, 32>(a, p, part, s); break;
+      case 64: attn_go<bf16, 64>(a, p, part, s); break;
+      case 128: attn_go<bf16, 128>(a, p, part, s); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (hd) {
-      case 16: attn_go<float, 16>(a, p, s); break;
-      case 32: attn_go<float, 32>(a, p, s); break;
-      case 64: attn_go<float, 64>(a, p, s); break;
-      case 128: attn_go<float, 128>(a, p, s); break;
+      case 16: attn_go<float, 16>(a, p, part, s); break;
+      case 32: attn_go<float, 32>(a, p, part, s); break;
+      case 64: attn_go<float, 64>(a, p, part, s); break;
+      case 128: attn_go<float, 128>(a, p, part, s); break;
       default: return hipErrorInvalidValue;
     }
   }

@@ -23,7 +23,8 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "tsp.h")
 
 TSP_BF16, TSP_F32 = 0, 1
 TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV = 1, 2, 3, 4
-TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP = 1, 2, 4
+TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP, TSP_F_PROFILE = 1, 2, 4, 8
+KERNELS = ["rmsnorm", "qkv", "attn", "merge", "oproj", "w13", "w2"]  # TSP_K_* order
 STATUS = {0: "TSP_OK", -1: "TSP_E_INVAL", -2: "TSP_E_SHAPE", -3: "TSP_E_ALIGN",
           -4: "TSP_E_WORKSPACE", -5: "TSP_E_DTYPE", -6: "TSP_E_HIP"}
 
@@ -70,8 +71,10 @@ def lib() -> ctypes.CDLL:
         L.tsp_mlp_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_layer_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_kv_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp]
+        L.tsp_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         for f in ("tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
-                  "tsp_zigzag_positions"):
+                  "tsp_zigzag_positions", "tsp_profile_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -158,6 +161,15 @@ def tsp_layer_shard(dims, x, g1, w_attn, kv, g2, w_mlp, out, ws, stream=None, co
 def tsp_kv_shard(dims, x, g1, w_attn, kv, ws, stream=None):
     _check(lib().tsp_kv_shard(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
                               _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def tsp_profile_read(reset: bool = True) -> dict:
+    """Per-kernel-class totals of calls made with TSP_F_PROFILE:
+    {name: (total_ms, launches)}."""
+    ms = (ctypes.c_double * len(KERNELS))()
+    n = (ctypes.c_int64 * len(KERNELS))()
+    _check(lib().tsp_profile_read(ms, n, 1 if reset else 0))
+    return {k: (ms[i], n[i]) for i, k in enumerate(KERNELS)}
 
 
 # ----------------------------------------------------------------------------

@@ -106,7 +106,20 @@ enum { TSP_WS_ATTN = 1, TSP_WS_MLP = 2, TSP_WS_LAYER = 3, TSP_WS_KV = 4 };
 enum {
   TSP_F_DELAY_COPY = 1u,   /* a bounded spin kernel runs on the copy stream before each copy */
   TSP_F_POISON_SLOTS = 2u, /* each slot is filled with NaN before it is refilled */
-  TSP_F_NO_OVERLAP = 4u    /* run the copies in order on the compute stream */
+  TSP_F_NO_OVERLAP = 4u,   /* run the copies in order on the compute stream */
+  TSP_F_PROFILE = 8u       /* time each kernel launch with HIP events (tsp_profile_read) */
+};
+
+/* Kernel classes reported by tsp_profile_read. */
+enum {
+  TSP_K_RMSNORM = 0, /* RMSNorm of the rank's tokens */
+  TSP_K_QKV = 1,     /* QKV projection of one attention shard (+ K/V scatter) */
+  TSP_K_ATTN = 2,    /* zigzag causal flash attention of one head group */
+  TSP_K_MERGE = 3,   /* merge of split attention work items */
+  TSP_K_OPROJ = 4,   /* O projection of one shard, accumulated in fp32 */
+  TSP_K_W13 = 5,     /* W1/W3 projection of one MLP shard with the SwiGLU product */
+  TSP_K_W2 = 6,      /* W2 projection of one MLP shard, accumulated in fp32 */
+  TSP_K_COUNT = 7
 };
 
 typedef struct tsp_dims {
@@ -188,6 +201,19 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1,
 int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1,
                  const void* const* w_attn, void* kv,
                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Per-kernel timing of calls made with TSP_F_PROFILE: every kernel the
+ * library launches on the compute stream is bracketed by two HIP events on
+ * that stream.  tsp_profile_read waits for the recorded events, adds their
+ * elapsed times into per-class totals and writes, for each class k in
+ * [0, TSP_K_COUNT), the total milliseconds ms[k] and the launch count n[k]
+ * since the last reset (either pointer may be NULL).  reset != 0 clears the
+ * totals afterwards.  State is per host thread; events of one thread must
+ * all belong to the device current at the read.  The timing events cost a
+ * few microseconds per launch, so calls timed this way are slightly slower.
+ */
+int tsp_profile_read(double* ms, int64_t* n, int reset);
 
 #ifdef __cplusplus
 }
