@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=32,
                     help="local rows of the rank's second chunk the oracle computes")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first copy a buffer of this many MiB three times (a kernel of known "
+                         "traffic for scaling HBM counters)")
     return ap.parse_args()
 
 
@@ -130,6 +133,14 @@ def main():
     cfg = synth.get_config(args.workload)
     r = cfg.ranks[0] if args.rank is None else args.rank
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_setup = time.perf_counter()
     w = synth.gen_weights(cfg)
     L = layer_dev(cfg, w)

@@ -38,6 +38,13 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    # Every kernel the host code launches must have its launch stub defined
+    # (a stub the host pass failed to emit would only show up at load time).
+    nm = subprocess.run(["nm", tmp], capture_output=True, text=True).stdout
+    missing = [l.split()[-1] for l in nm.splitlines()
+               if l.split()[:1] == ["U"] and "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("undefined kernel launch stubs: " + ", ".join(missing[:5]))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

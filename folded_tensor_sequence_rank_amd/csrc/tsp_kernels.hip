@@ -125,10 +125,21 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* __restrict__ x,
 // Projection GEMM: acc = A . B^T, A [M][K] (lda), B [N][K] (ldb), both
 // K-contiguous.  256 threads = 2x2 waves; each wave owns (BM/2) x (BN/2) of
 // the tile as 32x32 MFMA blocks.  K is staged through LDS in 128-byte rows
-// (64 bf16 / 32 fp32), double-buffered, with the next tile's global loads in
-// flight in registers during the current tile's MFMAs.  LDS rows are
-// XOR-swizzled in 16-byte chunks so the 32 rows one fragment read touches
-// spread over the banks.
+// (64 bf16 / 32 fp32), double-buffered.  LDS rows are XOR-swizzled in
+// 16-byte chunks so the 32 rows one fragment read touches spread over the
+// banks.
+//
+// Vector path (K, lda, ldb multiples of 16 bytes): tiles go straight from
+// global memory to LDS with buffer loads (no staging registers); rows past M
+// or N and chunks past K read as zero through the buffer's range check.  One
+// barrier per K step: after it every wave's loads of this step have landed
+// and every wave has finished reading the other buffer, which the next
+// step's loads then refill while this step's MFMAs run.  Scalar path (odd
+// sizes): element-wise guarded loads through registers.
+//
+// The MFMA takes B's fragment as its first operand, so a lane of the 32x32
+// result holds one output row m and, per group of four registers, four
+// consecutive columns n: the epilogues use 4-wide loads and stores.
 // ---------------------------------------------------------------------------
 template <typename T, bool VEC>
 __device__ inline u32x4 load_chunk(const T* base, bool rowok, int64_t row, int64_t ld, int k,
@@ -147,13 +158,76 @@ __device__ inline u32x4 load_chunk(const T* base, bool rowok, int64_t row, int64
   return r.raw;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Buffer resources and buffer->LDS loads exist only in the device pass; the
+// host pass (which emits the launch stubs) sees inert placeholders.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t brsrc;
+#else
+typedef const void* brsrc;
+#endif
+
+__device__ inline brsrc make_rsrc(const void* p, uint64_t bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)n, 0x00020000);
+#else
+  return p;
+#endif
+}
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16*lane
+// (lds must be the same for every lane of the wave).
+__device__ inline void buffer_to_lds16(brsrc r, void* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past any range: reads 0
+
+template <typename T>
+__device__ inline void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    Chunk<T> v;
+    v.e[0] = from_f<T>(a);
+    v.e[1] = from_f<T>(b);
+    v.e[2] = from_f<T>(c);
+    v.e[3] = from_f<T>(d);
+    *(u32x2*)p = u32x2{v.raw[0], v.raw[1]};
+  } else {
+    *(float4*)p = make_float4(a, b, c, d);
+  }
+}
+
+template <typename T>
+__device__ inline void load4(const T* p, float* o) {
+  if constexpr (sizeof(T) == 2) {
+    Chunk<T> v;
+    const u32x2 r = *(const u32x2*)p;
+    v.raw[0] = r[0];
+    v.raw[1] = r[1];
+#pragma unroll
+    for (int t = 0; t < 4; t++) o[t] = to_f(v.e[t]);
+  } else {
+    const float4 r = *(const float4*)p;
+    o[0] = r.x;
+    o[1] = r.y;
+    o[2] = r.z;
+    o[3] = r.w;
+  }
+}
+
 template <typename T, int BM, int BN, int EPI, bool VEC>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   typedef MF<T> M_;
   typedef typename M_::frag frag;
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   constexpr int ES = sizeof(T);
+  constexpr int V = 16 / ES;
   constexpr int BK = 128 / ES;  // elements per 128-byte LDS row
+  constexpr int KS = BK / M_::KSTEP;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int NBR = DUAL ? 2 * BN : BN;  // B rows staged per tile
@@ -161,7 +235,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   constexpr int BC = NBR * 8 / 256;
   constexpr int STAGE = (BM + NBR) * 128;
   constexpr int NB3 = DUAL ? NB : 1;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 || BN == 192 || BN == 96, "tile");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -180,42 +254,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   const T* A = (const T*)g.A;
   const T* B = (const T*)g.B;
   const T* B3 = (const T*)g.B3;
-  u32x4 ra[AC], rb[BC];
-
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < AC; i++) {
-      const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-      const int gm = m0 + row;
-      ra[i] = load_chunk<T, VEC>(A, gm < g.M, gm, g.lda, k0 + c * (16 / ES), g.K);
-    }
-#pragma unroll
-    for (int i = 0; i < BC; i++) {
-      const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-      const T* src = B;
-      int rr = row;
-      if (DUAL && row >= BN) {
-        src = B3;
-        rr = row - BN;
-      }
-      const int gn = n0 + rr;
-      rb[i] = load_chunk<T, VEC>(src, gn < g.N, gn, g.ldb, k0 + c * (16 / ES), g.K);
-    }
-  };
-  auto sstore = [&](int buf) {
-    char* sA = smem + buf * STAGE;
-    char* sB = sA + BM * 128;
-#pragma unroll
-    for (int i = 0; i < AC; i++) {
-      const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-      *(u32x4*)(sA + row * 128 + ((c ^ (row & 7)) << 4)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BC; i++) {
-      const int id = tid + 256 * i, row = id >> 3, c = id & 7;
-      *(u32x4*)(sB + row * 128 + ((c ^ (row & 7)) << 4)) = rb[i];
-    }
-  };
+  const int nk = (g.K + BK - 1) / BK;
 
   f32x16 acc[MB][NB];
   f32x16 acc3[DUAL ? MB : 1][NB3];
@@ -230,99 +269,283 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   auto compute = [&](int buf) {
     const char* sA = smem + buf * STAGE;
     const char* sB = sA + BM * 128;
-#pragma unroll
-    for (int ks = 0; ks < BK / M_::KSTEP; ks++) {
+    frag af[2][MB], bfr[2][NB], bf3[2][NB3];
+    auto fetch = [&](int ks, int set) {
       const int byte = (ks * M_::KSTEP + lg * M_::E) * ES;
       const int c = byte >> 4, w = byte & 15;
-      frag af[MB], bfr[NB], bf3[NB3];
 #pragma unroll
       for (int i = 0; i < MB; i++) {
         const int row = wm * WM + i * 32 + lr;
-        af[i] = *(const frag*)(sA + row * 128 + ((c ^ (row & 7)) << 4) + w);
+        af[set][i] = *(const frag*)(sA + row * 128 + ((c ^ (row & 7)) << 4) + w);
       }
 #pragma unroll
       for (int j = 0; j < NB; j++) {
         const int row = wn * WN + j * 32 + lr;
-        bfr[j] = *(const frag*)(sB + row * 128 + ((c ^ (row & 7)) << 4) + w);
+        bfr[set][j] = *(const frag*)(sB + row * 128 + ((c ^ (row & 7)) << 4) + w);
         if (DUAL) {
           const int r3 = BN + row;
-          bf3[j] = *(const frag*)(sB + r3 * 128 + ((c ^ (r3 & 7)) << 4) + w);
+          bf3[set][j] = *(const frag*)(sB + r3 * 128 + ((c ^ (r3 & 7)) << 4) + w);
         }
       }
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) fetch(ks + 1, cur ^ 1);
 #pragma unroll
       for (int i = 0; i < MB; i++)
 #pragma unroll
         for (int j = 0; j < NB; j++) {
-          acc[i][j] = M_::mma(af[i], bfr[j], acc[i][j]);
-          if (DUAL) acc3[i][j] = M_::mma(af[i], bf3[j], acc3[i][j]);
+          acc[i][j] = M_::mma(bfr[cur][j], af[cur][i], acc[i][j]);
+          if (DUAL) acc3[i][j] = M_::mma(bf3[cur][j], af[cur][i], acc3[i][j]);
         }
+      // Interleave the next step's fragment reads with this step's MFMAs so
+      // LDS latency hides behind the matrix pipe.
+      if (ks + 1 < KS) {
+        constexpr int NR = MB + NB + NB3 * (DUAL ? 1 : 0);
+        constexpr int NM = MB * NB * (DUAL ? 2 : 1);
+        constexpr int PER = NM / NR > 0 ? NM / NR : 1;
+#pragma unroll
+        for (int q = 0; q < NR; q++) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
+        }
+      }
     }
   };
 
-  const int nk = (g.K + BK - 1) / BK;
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
+  if constexpr (VEC) {
+    // Direct global -> LDS.  Load round i of A covers tile rows [32i, 32i+32);
+    // wave w writes rows 32i + 8w .. +8 (1 KB), lane l the 16 bytes at
+    // physical chunk l%8 of row 32i + 8w + l/8, i.e. logical chunk
+    // (l%8) ^ (row%8).
+    const brsrc rA = make_rsrc(A, (uint64_t)g.M * g.lda * ES);
+    const brsrc rB = make_rsrc(B, (uint64_t)g.N * g.ldb * ES);
+    const brsrc rB3 = make_rsrc(DUAL ? B3 : B, (uint64_t)g.N * g.ldb * ES);
+    const int lrow = 8 * wave + (lane >> 3);
+    const int lc = (lane & 7) ^ (lrow & 7);  // logical chunk (row%8 == lrow%8)
+    uint32_t offA[AC], offB[BC];
+#pragma unroll
+    for (int i = 0; i < AC; i++) {
+      const int gm = m0 + 32 * i + lrow;
+      offA[i] = gm < g.M ? (uint32_t)(((int64_t)gm * g.lda + lc * V) * ES) : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < BC; i++) {
+      const int rr = 32 * i + lrow;
+      const int gn = n0 + (DUAL && rr >= BN ? rr - BN : rr);
+      offB[i] = gn < g.N ? (uint32_t)(((int64_t)gn * g.ldb + lc * V) * ES) : kOOB;
+    }
+    auto issue = [&](int kt, int buf) {
+      const int k0 = kt * BK;
+      const bool kok = k0 + lc * V < g.K;
+      char* sA = smem + buf * STAGE;
+      char* sB = sA + BM * 128;
+#pragma unroll
+      for (int i = 0; i < AC; i++)
+        buffer_to_lds16(rA, sA + i * 4096 + wave * 1024, kok ? offA[i] : kOOB, k0 * ES);
+#pragma unroll
+      for (int i = 0; i < BC; i++) {
+        const bool second = DUAL && 32 * i >= BN;
+        buffer_to_lds16(second ? rB3 : rB, sB + i * 4096 + wave * 1024, kok ? offB[i] : kOOB,
+                        k0 * ES);
+      }
+    };
+    if (nk > 0) issue(0, 0);
     for (int kt = 0; kt < nk; kt++) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * BK);
-      compute(cur);
-      if (kt + 1 < nk) sstore(cur ^ 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+      compute(kt & 1);
+    }
+  } else {
+    u32x4 ra[AC], rb[BC];
+    auto gload = [&](int k0) {
+#pragma unroll
+      for (int i = 0; i < AC; i++) {
+        const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+        const int gm = m0 + row;
+        ra[i] = load_chunk<T, false>(A, gm < g.M, gm, g.lda, k0 + c * V, g.K);
+      }
+#pragma unroll
+      for (int i = 0; i < BC; i++) {
+        const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+        const T* src = B;
+        int rr = row;
+        if (DUAL && row >= BN) {
+          src = B3;
+          rr = row - BN;
+        }
+        const int gn = n0 + rr;
+        rb[i] = load_chunk<T, false>(src, gn < g.N, gn, g.ldb, k0 + c * V, g.K);
+      }
+    };
+    auto sstore = [&](int buf) {
+      char* sA = smem + buf * STAGE;
+      char* sB = sA + BM * 128;
+#pragma unroll
+      for (int i = 0; i < AC; i++) {
+        const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+        *(u32x4*)(sA + row * 128 + ((c ^ (row & 7)) << 4)) = ra[i];
+      }
+#pragma unroll
+      for (int i = 0; i < BC; i++) {
+        const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+        *(u32x4*)(sB + row * 128 + ((c ^ (row & 7)) << 4)) = rb[i];
+      }
+    };
+    if (nk > 0) {
+      gload(0);
+      sstore(0);
+      __syncthreads();
+      for (int kt = 0; kt < nk; kt++) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+        compute(cur);
+        if (kt + 1 < nk) sstore(cur ^ 1);
+        __syncthreads();
+      }
     }
   }
 
-  // Epilogue straight from the accumulators: lane (lr, lg) of block (i, j)
-  // holds column n0 + wn*WN + 32j + lr and rows 8(r/4) + 4lg + r%4.
+  // Epilogue straight from the accumulators: in block (i, j) the lane holds
+  // row m = m0 + wm*WM + 32i + lr and, for q = 0..3, the four columns
+  // n0 + wn*WN + 32j + 8q + 4lg + {0,1,2,3} in registers 4q..4q+3.
+  float* __restrict__ Y = g.Y;
+  const T* __restrict__ R = (const T*)g.R;
+  T* __restrict__ C = (T*)g.C;
 #pragma unroll
-  for (int j = 0; j < NB; j++) {
-    const int n = n0 + wn * WN + j * 32 + lr;
-    if (n >= g.N) continue;
-    // Column-dependent part of the destination address.
-    T* cbase = nullptr;
-    int64_t rstride = 0;
-    int part = 0;
-    if constexpr (EPI == EPI_QKV) {
-      const int c = n + g.col0;
-      part = c / g.hs;
-      const int rem = c - part * g.hs;
-      const int head = rem / g.hd;
-      const int e = rem - head * g.hd;
-      if (part == 0) {
-        cbase = (T*)g.Q + (int64_t)head * g.T * g.hd + e;
-        rstride = g.hd;
-      } else if (part == 1) {
-        cbase = (T*)g.Kd + (int64_t)head * g.S * g.hd + e;
-        rstride = g.hd;
-      } else {
-        cbase = (T*)g.Vt + ((int64_t)head * g.hd + e) * g.S;
-        rstride = 1;
-      }
-    }
+  for (int i = 0; i < MB; i++) {
+    const int m = m0 + wm * WM + i * 32 + lr;
+    if (m >= g.M) continue;
+    int64_t pos = m;
+    if constexpr (EPI == EPI_QKV) pos = zig(m, g.chunk, g.rank, g.fold);
 #pragma unroll
-    for (int i = 0; i < MB; i++)
+    for (int j = 0; j < NB; j++) {
+      float v[16], w[16];
+      bool ok[4], full[4];
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        if (m >= g.M) continue;
-        const float v = acc[i][j][r];
-        if constexpr (EPI == EPI_ACC) {
-          float* y = g.Y + (int64_t)m * g.ldy + n;
-          *y = g.beta ? *y + v : v;
-        } else if constexpr (EPI == EPI_RESID) {
-          float s = to_f(((const T*)g.R)[(int64_t)m * g.ldr + n]) + v;
-          if (g.beta) s += g.Y[(int64_t)m * g.ldy + n];
-          ((T*)g.C)[(int64_t)m * g.ldc + n] = from_f<T>(s);
-        } else if constexpr (EPI == EPI_SWIGLU) {
-          const float v3 = acc3[i][j < NB3 ? j : 0][r];
-          const float sg = v / (1.0f + fast_exp2(-v * 1.4426950408889634f));
-          ((T*)g.C)[(int64_t)m * g.ldc + n] = from_f<T>(sg * v3);
-        } else if constexpr (EPI == EPI_QKV) {
-          const int64_t at = part == 0 ? (int64_t)m : zig(m, g.chunk, g.rank, g.fold);
-          cbase[at * rstride] = from_f<T>(v);
+      for (int q = 0; q < 4; q++) {
+        const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+        ok[q] = n < g.N;
+        full[q] = n + 3 < g.N;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          v[4 * q + e] = acc[i][j][4 * q + e];
+          w[4 * q + e] = 0.f;
         }
       }
+      if constexpr (EPI == EPI_ACC || EPI == EPI_RESID) {
+        const bool vy = (g.ldy & 3) == 0;
+        if (g.beta) {  // gather the accumulator first, then add
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+            const float* py = Y + (int64_t)m * g.ldy + n;
+            if (full[q] && vy) {
+              const float4 y = *(const float4*)py;
+              w[4 * q] = y.x;
+              w[4 * q + 1] = y.y;
+              w[4 * q + 2] = y.z;
+              w[4 * q + 3] = y.w;
+            } else if (ok[q]) {
+#pragma unroll
+              for (int e = 0; e < 4; e++)
+                if (n + e < g.N) w[4 * q + e] = py[e];
+            }
+          }
+        }
+        if constexpr (EPI == EPI_RESID) {
+          const bool vr = (g.ldr & 3) == 0 && (g.ldc & 3) == 0;
+          float rr[16];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+            const T* pr = R + (int64_t)m * g.ldr + n;
+            if (full[q] && vr) {
+              load4<T>(pr, rr + 4 * q);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; e++) rr[4 * q + e] = (ok[q] && n + e < g.N) ? to_f(pr[e]) : 0.f;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+            float s[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) s[e] = rr[4 * q + e] + w[4 * q + e] + v[4 * q + e];
+            T* pc = C + (int64_t)m * g.ldc + n;
+            if (full[q] && vr) {
+              store4<T>(pc, s[0], s[1], s[2], s[3]);
+            } else if (ok[q]) {
+#pragma unroll
+              for (int e = 0; e < 4; e++)
+                if (n + e < g.N) pc[e] = from_f<T>(s[e]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+            float* py = Y + (int64_t)m * g.ldy + n;
+            if (full[q] && vy) {
+              *(float4*)py = make_float4(w[4 * q] + v[4 * q], w[4 * q + 1] + v[4 * q + 1],
+                                         w[4 * q + 2] + v[4 * q + 2], w[4 * q + 3] + v[4 * q + 3]);
+            } else if (ok[q]) {
+#pragma unroll
+              for (int e = 0; e < 4; e++)
+                if (n + e < g.N) py[e] = w[4 * q + e] + v[4 * q + e];
+            }
+          }
+        }
+      } else if constexpr (EPI == EPI_SWIGLU) {
+        const bool vc = (g.ldc & 3) == 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+          float s[4];
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const float a = v[4 * q + e];
+            const float b = acc3[i][j < NB3 ? j : 0][4 * q + e];
+            s[e] = a / (1.0f + fast_exp2(-a * 1.4426950408889634f)) * b;
+          }
+          T* pc = C + (int64_t)m * g.ldc + n;
+          if (full[q] && vc) {
+            store4<T>(pc, s[0], s[1], s[2], s[3]);
+          } else if (ok[q]) {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              if (n + e < g.N) pc[e] = from_f<T>(s[e]);
+          }
+        }
+      } else if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          if (!ok[q]) continue;
+          const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+          // hs and hd are multiples of 4, so the four columns share part and head.
+          const int c = n + g.col0;
+          const int part = c / g.hs;
+          const int rem = c - part * g.hs;
+          const int head = rem / g.hd;
+          const int e = rem - head * g.hd;
+          if (part == 0) {
+            store4<T>((T*)g.Q + ((int64_t)head * g.T + m) * g.hd + e, v[4 * q], v[4 * q + 1],
+                      v[4 * q + 2], v[4 * q + 3]);
+          } else if (part == 1) {
+            store4<T>((T*)g.Kd + ((int64_t)head * g.S + pos) * g.hd + e, v[4 * q], v[4 * q + 1],
+                      v[4 * q + 2], v[4 * q + 3]);
+          } else {
+            T* pv = (T*)g.Vt + ((int64_t)head * g.hd + e) * g.S + pos;
+#pragma unroll
+            for (int t = 0; t < 4; t++) pv[(int64_t)t * g.S] = from_f<T>(v[4 * q + t]);
+          }
+        }
+      }
+    }
   }
 }
 
@@ -715,19 +938,30 @@ static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
     gemm_kernel<T, BM, BN, EPI, false><<<nt, 256, 0, s>>>(a);
 }
 
+// Tile choice: the shape whose estimated time (rounds of 256 concurrent
+// tiles x tile area / relative efficiency) is smallest.  Larger tiles read
+// fewer LDS bytes per MFMA; 128x128 is for small problems.
 template <int EPI>
 static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
-  const bool big = a.M >= 1024 && a.N >= 512;
+  struct Cand { int bm, bn; double eff; };
+  const Cand single[] = {{256, 256, 1.0}, {256, 192, 0.95}, {128, 128, 0.55}};
+  const Cand dual[] = {{256, 128, 1.0}, {128, 64, 0.5}};
+  const Cand* cs = EPI == EPI_SWIGLU ? dual : single;
+  const int nc = EPI == EPI_SWIGLU ? 2 : 3;
+  int best = 0;
+  double bt = 1e300;
+  for (int c = 0; c < nc; c++) {
+    const int64_t tiles = (int64_t)((a.M + cs[c].bm - 1) / cs[c].bm) * ((a.N + cs[c].bn - 1) / cs[c].bn);
+    const double t = (double)((tiles + 255) / 256) * cs[c].bm * cs[c].bn / cs[c].eff;
+    if (t < bt * 0.999) { bt = t; best = c; }
+  }
   if constexpr (EPI == EPI_SWIGLU) {
-    if (big)
-      gemm_go<bf16, 256, 128, EPI>(a, vec, s);
-    else
-      gemm_go<bf16, 128, 64, EPI>(a, vec, s);
+    if (best == 0) gemm_go<bf16, 256, 128, EPI>(a, vec, s);
+    else gemm_go<bf16, 128, 64, EPI>(a, vec, s);
   } else {
-    if (big)
-      gemm_go<bf16, 256, 256, EPI>(a, vec, s);
-    else
-      gemm_go<bf16, 128, 128, EPI>(a, vec, s);
+    if (best == 0) gemm_go<bf16, 256, 256, EPI>(a, vec, s);
+    else if (best == 1) gemm_go<bf16, 256, 192, EPI>(a, vec, s);
+    else gemm_go<bf16, 128, 128, EPI>(a, vec, s);
   }
 }
 
