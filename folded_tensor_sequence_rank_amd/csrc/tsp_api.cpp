@@ -123,7 +123,7 @@ AttnWs attn_ws(const Dims& d, size_t base) {
   for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(attn_shard_elems(d) * d.es); }
   for (int s = 0; s < 2; s++) { w.slotkv[s] = o; o += al(kv_block_elems(d) * d.es); }
   const AttnPlan p = plan_of(d);
-  const size_t nslot = p.split ? (size_t)d.Hd * p.nqt * p.maxseg * 128 : 0;
+  const size_t nslot = p.split ? (size_t)d.Hd * p.nqt * p.maxseg * p.bq : 0;
   w.op = o; o += al(nslot * d.d * 4);
   w.ml = o; o += al(nslot * 2 * 4);
   w.end = o;

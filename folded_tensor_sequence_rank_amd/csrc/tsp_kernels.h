@@ -57,7 +57,8 @@ struct AttnArgs {
 
 // Attention work plan for one head group (a deterministic function of the dims).
 struct AttnPlan {
-  int nqt;     // query tiles of 128 local rows
+  int bq;      // local query rows per tile
+  int nqt;     // query tiles of bq local rows
   int lseg;    // keys per split item (multiple of 64)
   int maxseg;  // largest number of splits of one query tile
   int nitems;  // work items per head

@@ -18,6 +18,10 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <type_traits>
+#include <vector>
+
 namespace tsp {
 
 typedef __bf16 bf16;
@@ -553,31 +557,44 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 // Zigzag-aware causal flash attention of the local queries of one head group
 // against the gathered K/V.
 //
-// A work item is (head, query tile of 128 local rows, key segment).  Each of
-// the 4 waves owns 32 queries.  K/V tiles of 64 keys are staged in LDS
-// (double-buffered, loads of the next tile in flight during the current
-// tile's math).  Per tile a wave computes S^T = K . Q^T (lane <-> query,
-// registers <-> keys), applies the causal mask only where the tile reaches
-// past the wave's smallest query position, updates the running max / sum,
-// and accumulates O^T += V^T . P^T with P kept in registers.  K rows are fed
-// to the first product in an order that swaps bits 2 and 3 of the row index,
-// which makes each lane hold 8 consecutive keys per 16-key step of P, so the
-// matching V^T operand is one 16-byte LDS read.
+// A work item is (head, query tile of kBQ local rows, key segment).  Each of
+// the 4 waves owns kQB blocks of 32 queries (every K or V^T fragment read
+// from LDS feeds kQB MFMAs); with kQB = 1 two workgroups share a CU, so one
+// wave's softmax overlaps the other's MFMAs.  K/V tiles of 64 keys go
+// straight from global memory into LDS (double-buffered, one barrier per
+// tile); keys at or past the item's last query position + 1 read as zero,
+// so rows the rank never receives are never used.  Per tile a wave computes
+// S^T = K . Q^T (lane <-> query, registers <-> keys), masks only tiles that
+// reach past its smallest query position, and accumulates O^T += V^T . P^T
+// with P kept in registers.  Softmax runs in log2 units with the scale
+// folded into one FMA; the running max used for the exponentials is only
+// raised (rescaling O and the running sum) when a new score exceeds it by
+// more than 2^8, which keeps every exponential <= 2^8 while skipping almost
+// all rescales.  K rows are fed to the first product in an order that swaps
+// bits 2 and 3 of the row index, which makes each lane hold 8 consecutive
+// keys per 16-key step of P, so the matching V^T operand is one 16-byte LDS
+// read.
 //
-// Keys a tile loads at or beyond the work item's last query position + 1 are
-// zero-filled (they are masked anyway), so rows the rank never receives are
-// never read.  Query tiles whose key range exceeds the segment length are
-// split into several items; their partial (max, sum, unnormalised O) are
-// merged by attn_combine_kernel.  Items are ordered heaviest first, and
+// Query tiles whose key range exceeds the segment length are split into
+// several items; their partial (max, sum, unnormalised O) are merged by
+// attn_combine_kernel.  Items are ordered heaviest first, and
 // head = item % Hd keeps one head on each XCD when Hd divides 8.
 // ---------------------------------------------------------------------------
+constexpr int kQB = 1;     // 32-query blocks per wave (two waves share a SIMD)
+constexpr int kBQ = 128 * kQB;  // local query rows per work item (4 waves)
+constexpr int kBKV = 64;   // keys per tile
+
 __device__ inline int kappa(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ __host__ inline int64_t qtile_kend(int64_t T, int qt, int64_t C, int rank, int fold) {
+  const int64_t last = (T < (int64_t)qt * kBQ + kBQ ? T : (int64_t)qt * kBQ + kBQ) - 1;
+  return zig(last, C, rank, fold) + 1;
+}
 
 __device__ inline bool decode_item(const AttnArgs& a, int item, int& qt, int& seg, int& nseg,
                                    int64_t& kend) {
   for (qt = a.nqt - 1; qt >= 0; --qt) {
-    const int64_t last = min(a.T, (int64_t)qt * 128 + 128) - 1;
-    kend = zig(last, a.chunk, a.rank, a.fold) + 1;
+    kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold);
     nseg = (int)((kend + a.lseg - 1) / a.lseg);
     if (item < nseg) {
       seg = item;
@@ -589,21 +606,22 @@ __device__ inline bool decode_item(const AttnArgs& a, int item, int& qt, int& se
 }
 
 template <typename T, int HD>
-__global__ void __launch_bounds__(256, 2) attn_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a) {
   typedef MF<T> M_;
   typedef typename M_::frag frag;
   constexpr int ES = sizeof(T);
-  constexpr int BKV = 64;
-  constexpr int KROWB = HD * ES, KCH = KROWB / 16;
-  constexpr int VROWB = BKV * ES, VCH = VROWB / 16;
-  constexpr int KT_BYTES = BKV * KROWB;
-  constexpr int STAGE = KT_BYTES + HD * VROWB;
-  constexpr int KCHUNKS = BKV * KCH, VCHUNKS = HD * VCH;
-  constexpr int KC = (KCHUNKS + 255) / 256, VC = (VCHUNKS + 255) / 256;
-  constexpr int QK = HD / M_::KSTEP;  // k-steps over the head dim
-  constexpr int DB = (HD + 31) / 32;  // 32-row blocks of O^T
-  constexpr int PK = BKV / M_::KSTEP; // k-steps over the keys of a tile
   constexpr int V = 16 / ES;
+  constexpr int QB = kQB;
+  constexpr int KROWB = HD * ES, KCH = KROWB / 16;
+  constexpr int VROWB = kBKV * ES, VCH = VROWB / 16;
+  constexpr int KT_BYTES = kBKV * KROWB;
+  constexpr int VT_BYTES = HD * VROWB;
+  constexpr int STAGE = KT_BYTES + VT_BYTES;
+  constexpr int KI = KT_BYTES / 1024, VI = VT_BYTES / 1024;  // 1 KB wave loads per tile
+  constexpr int QK = HD / M_::KSTEP;    // k-steps over the head dim
+  constexpr int DB = (HD + 31) / 32;    // 32-row blocks of O^T
+  constexpr int PK = kBKV / M_::KSTEP;  // k-steps over the keys of a tile
+  static_assert(KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0, "tile bytes");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -613,151 +631,201 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArgs a) {
   int64_t kend;
   if (!decode_item(a, blockIdx.x / a.Hd, qt, seg, nseg, kend)) return;
 
-  const int64_t kbeg = (int64_t)seg * a.lseg;
-  const int64_t kfin = min(kend, kbeg + a.lseg);
-  const int64_t row0 = (int64_t)qt * 128 + wave * 32;
-  const int64_t row = row0 + lr;
-  const bool qok = row < a.T;
-  const int64_t qpos = qok ? zig(row, a.chunk, a.rank, a.fold) : -1;
-  const bool wok = row0 < a.T;
-  const bool wfull = row0 + 31 < a.T;
-  const int64_t kend_w = wok ? zig(min(a.T, row0 + 32) - 1, a.chunk, a.rank, a.fold) + 1 : 0;
-  const int64_t qmin_w = wok ? zig(row0, a.chunk, a.rank, a.fold) : 0;
+  // Positions fit in 32 bits (S < 2^31).
+  const int kend32 = (int)kend;
+  const int kbeg = seg * a.lseg;
+  const int kfin = min(kend32, kbeg + a.lseg);
+  const int T32 = (int)a.T;
+  const int row0 = qt * kBQ + wave * 32 * QB;  // this wave's first local row
+  const int C32 = (int)a.chunk;
+  int qpos[QB];
+  bool qok[QB];
+#pragma unroll
+  for (int b = 0; b < QB; b++) {
+    const int row = row0 + 32 * b + lr;
+    qok[b] = row < T32;
+    qpos[b] = qok[b] ? (int)zig(row, C32, a.rank, a.fold) : -1;
+  }
+  const bool wok = row0 < T32;
+  const bool wfull = row0 + 32 * QB - 1 < T32;
+  const int kend_w = wok ? (int)zig(min(T32, row0 + 32 * QB) - 1, C32, a.rank, a.fold) + 1 : 0;
+  const int qmin_w = wok ? (int)zig(row0, C32, a.rank, a.fold) : 0;
 
   const T* Qh = (const T*)a.Q + (int64_t)head * a.T * HD;
   const T* Kh = (const T*)a.K + (int64_t)head * a.S * HD;
   const T* Vh = (const T*)a.Vt + (int64_t)head * HD * a.S;
 
-  frag qf[QK];
+  frag qf[QB][QK];
 #pragma unroll
-  for (int ks = 0; ks < QK; ks++) {
-    const int e0 = ks * M_::KSTEP + lg * M_::E;
-    if (qok)
-      qf[ks] = *(const frag*)(Qh + row * HD + e0);
-    else
-      qf[ks] = frag{0};
+  for (int b = 0; b < QB; b++)
+#pragma unroll
+    for (int ks = 0; ks < QK; ks++) {
+      const int e0 = ks * M_::KSTEP + lg * M_::E;
+      if (qok[b])
+        qf[b][ks] = *(const frag*)(Qh + (row0 + 32 * b + lr) * HD + e0);
+      else
+        qf[b][ks] = frag{0};
+    }
+
+  f32x16 o[QB][DB];
+#pragma unroll
+  for (int b = 0; b < QB; b++)
+#pragma unroll
+    for (int d = 0; d < DB; d++) o[b][d] = f32x16{0};
+  float m[QB], l[QB];
+#pragma unroll
+  for (int b = 0; b < QB; b++) {
+    m[b] = -INFINITY;
+    l[b] = 0.f;
   }
 
-  f32x16 o[DB];
+  // Direct loads.  Wave-load ii of the K tile fills LDS bytes
+  // [ii*1024, ii*1024+1024): lane l writes 16 bytes at physical chunk p of
+  // row r, holding logical chunk p ^ (r % KCH) of key k0 + r.  Likewise for
+  // V^T rows d (64 keys each).
+  const brsrc rK = make_rsrc(Kh, (uint64_t)a.S * HD * ES);
+  const brsrc rV = make_rsrc(Vh, (uint64_t)HD * a.S * ES);
+  constexpr int KJ = (KI + 3) / 4, VJ = (VI + 3) / 4;  // wave loads per tile per wave
+  int krow[KJ], voff[VJ], vkey[VJ];
+  uint32_t koff[KJ];
 #pragma unroll
-  for (int d = 0; d < DB; d++) o[d] = f32x16{0};
-  float m = -INFINITY, l = 0.f;
-
-  u32x4 rk[KC], rv[VC];
-  auto gload = [&](int64_t k0) {
+  for (int j = 0; j < KJ; j++) {
+    const int b = (wave + 4 * j) * 1024 + 16 * lane;
+    const int r = b / KROWB, p = (b % KROWB) >> 4;
+    krow[j] = r;
+    koff[j] = (uint32_t)((r * HD + (p ^ (r & (KCH - 1))) * V) * ES);
+  }
 #pragma unroll
-    for (int i = 0; i < KC; i++) {
-      const int id = tid + 256 * i;
-      rk[i] = u32x4{0u, 0u, 0u, 0u};
-      if (KCHUNKS % 256 == 0 || id < KCHUNKS) {
-        const int r = id / KCH, c = id % KCH;
-        const int64_t key = k0 + r;
-        if (key < kend) rk[i] = *(const u32x4*)(Kh + key * HD + c * V);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VC; i++) {
-      const int id = tid + 256 * i;
-      rv[i] = u32x4{0u, 0u, 0u, 0u};
-      if (VCHUNKS % 256 == 0 || id < VCHUNKS) {
-        const int r = id / VCH, c = id % VCH;
-        const int64_t key = k0 + c * V;
-        const T* p = Vh + (int64_t)r * a.S + key;
-        if (key + V <= kend) {
-          rv[i] = *(const u32x4*)p;
-        } else if (key < kend) {
-          Chunk<T> t;
-#pragma unroll
-          for (int e = 0; e < V; e++) t.e[e] = (key + e < kend) ? p[e] : from_f<T>(0.f);
-          rv[i] = t.raw;
-        }
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int j = 0; j < VJ; j++) {
+    const int b = (wave + 4 * j) * 1024 + 16 * lane;
+    const int d = b / VROWB, p = (b % VROWB) >> 4;
+    const int c = p ^ (d & (VCH - 1));
+    vkey[j] = c * V;
+    voff[j] = (int)(((int64_t)d * a.S + c * V) * ES);
+  }
+  auto issue = [&](int k0, int buf) {
     char* sK = smem + buf * STAGE;
     char* sV = sK + KT_BYTES;
 #pragma unroll
-    for (int i = 0; i < KC; i++) {
-      const int id = tid + 256 * i;
-      if (KCHUNKS % 256 == 0 || id < KCHUNKS) {
-        const int r = id / KCH, c = id % KCH;
-        *(u32x4*)(sK + r * KROWB + ((c ^ (r & (KCH - 1))) << 4)) = rk[i];
-      }
+    for (int j = 0; j < KJ; j++) {
+      if (KI % 4 == 0 || wave + 4 * j < KI)
+        buffer_to_lds16(rK, sK + (wave + 4 * j) * 1024, k0 + krow[j] < kend32 ? koff[j] : kOOB,
+                        (uint32_t)(k0 * HD * ES));
     }
 #pragma unroll
-    for (int i = 0; i < VC; i++) {
-      const int id = tid + 256 * i;
-      if (VCHUNKS % 256 == 0 || id < VCHUNKS) {
-        const int r = id / VCH, c = id % VCH;
-        *(u32x4*)(sV + r * VROWB + ((c ^ (r & (VCH - 1))) << 4)) = rv[i];
-      }
+    for (int j = 0; j < VJ; j++) {
+      if (VI % 4 == 0 || wave + 4 * j < VI)
+        buffer_to_lds16(rV, sV + (wave + 4 * j) * 1024,
+                        k0 + vkey[j] < kend32 ? (uint32_t)voff[j] : kOOB, (uint32_t)(k0 * ES));
+    }
+  };
+  // A V^T chunk that straddles kend was loaded whole: zero its keys >= kend.
+  auto fixup = [&](int k0, int buf) {
+    char* sV = smem + buf * STAGE + KT_BYTES;
+    const int first = kend32 - k0;  // first key to clear, within the tile
+    const int upto = min(kBKV, (first + V - 1) / V * V);
+    for (int i = tid; i < HD * (upto - first); i += 256) {
+      const int d = i / (upto - first), key = first + i % (upto - first);
+      const int byte = key * ES;
+      const int c = byte >> 4, w = byte & 15;
+      *(T*)(sV + d * VROWB + ((c ^ (d & (VCH - 1))) << 4) + w) = from_f<T>(0.f);
     }
   };
 
-  auto compute = [&](int buf, int64_t k0) {
+  const float cs = a.scale_log2;
+  auto compute = [&](int buf, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const char* sK = smem + buf * STAGE;
     const char* sV = sK + KT_BYTES;
-    f32x16 s[2];
+    f32x16 s[QB][2];
 #pragma unroll
-    for (int b = 0; b < 2; b++) {
-      s[b] = f32x16{0};
-      const int krow = 32 * b + kappa(lr);
+    for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+      for (int b = 0; b < QB; b++) s[b][kb] = f32x16{0};
+      const int krow = 32 * kb + kappa(lr);
 #pragma unroll
       for (int ks = 0; ks < QK; ks++) {
         const int byte = (ks * M_::KSTEP + lg * M_::E) * ES;
         const int c = byte >> 4, w = byte & 15;
         const frag kf = *(const frag*)(sK + krow * KROWB + ((c ^ (krow & (KCH - 1))) << 4) + w);
-        s[b] = M_::mma(kf, qf[ks], s[b]);
+#pragma unroll
+        for (int b = 0; b < QB; b++) s[b][kb] = M_::mma(kf, qf[b][ks], s[b][kb]);
       }
     }
-    // Scale to log2 units, mask, running max.  Register i of block b holds
-    // key k0 + 32b + 16(i/8) + 8*lg + i%8.
-    const bool mask = !wfull || (k0 + BKV - 1 > qmin_w);
-    float mt = -INFINITY;
+    // Keep each fragment read one step ahead of the MFMAs that use it.
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+    for (int q = 0; q < 2 * QK; q++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Register i of block kb holds key k0 + 32kb + 16(i/8) + 8lg + i%8.
+    float mt[QB];
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        float v = s[b][i] * a.scale_log2;
-        if (mask) {
-          const int64_t key = k0 + 32 * b + 16 * (i >> 3) + 8 * lg + (i & 7);
-          if (key > qpos) v = -INFINITY;
+    for (int b = 0; b < QB; b++) {
+      float x = -INFINITY;
+      // key - k0 - 8lg = 32kb + 16(i/8) + i%8 must not exceed qpos - k0 - 8lg
+      const int lim = max(-1, min(kBKV, qpos[b] - k0)) - 8 * lg;
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          if (MASK) {
+            if (32 * kb + 16 * (i >> 3) + (i & 7) > lim) s[b][kb][i] = -INFINITY;
+          }
+          x = fmaxf(x, s[b][kb][i]);
         }
-        s[b][i] = v;
-        mt = fmaxf(mt, v);
+      x = fmaxf(x, __shfl_xor(x, 32));
+      mt[b] = x * cs;  // log2 units (scale > 0, so -inf stays -inf)
+    }
+    bool grow = false;
+#pragma unroll
+    for (int b = 0; b < QB; b++) grow |= mt[b] > m[b] + 8.0f;
+    if (__any(grow)) {
+#pragma unroll
+      for (int b = 0; b < QB; b++) {
+        const float mn = fmaxf(m[b], mt[b]);
+        const float alpha = m[b] == -INFINITY ? 0.f : fast_exp2(m[b] - mn);
+        m[b] = mn;
+        l[b] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; d++) o[b][d] *= alpha;
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    const float mu = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - mu);
-    float ls = 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    frag pf[QB][PK];
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+    for (int b = 0; b < QB; b++) {
+      const float nm = m[b] == -INFINITY ? 0.f : -m[b];
+      float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const float p = fast_exp2(s[b][i] - mu);
-        s[b][i] = p;
-        ls += p;
+      for (int st = 0; st < PK; st++) {
+        if constexpr (M_::E == 8) {
+          const int kb = st >> 1, i0 = (st & 1) * 8;
+#pragma unroll
+          for (int t = 0; t < 8; t++) {
+            const float p = fast_exp2(fmaf(s[b][kb][i0 + t], cs, nm));
+            ls += p;
+            pf[b][st][t] = (bf16)p;
+          }
+        } else {
+          const float p = fast_exp2(fmaf(s[b][st >> 4][st & 15], cs, nm));
+          ls += p;
+          pf[b][st] = p;
+        }
       }
-    l = l * alpha + ls;
-    m = mn;
-#pragma unroll
-    for (int d = 0; d < DB; d++) o[d] *= alpha;
+      l[b] += ls;
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T . P^T
 #pragma unroll
     for (int st = 0; st < PK; st++) {
-      frag pf;
       int kk;  // first key (within the tile) this lane supplies at step st
       if constexpr (M_::E == 8) {
-        const int b = st >> 1, i0 = (st & 1) * 8;
-#pragma unroll
-        for (int t = 0; t < 8; t++) pf[t] = (bf16)s[b][i0 + t];
         kk = 16 * st + 8 * lg;
       } else {
-        const int b = st >> 4, i = st & 15;
-        pf = s[b][i];
-        kk = 32 * b + 16 * (i >> 3) + 8 * lg + (i & 7);
+        const int i = st & 15;
+        kk = 32 * (st >> 4) + 16 * (i >> 3) + 8 * lg + (i & 7);
       }
       const int byte = kk * ES;
       const int c = byte >> 4, w = byte & 15;
@@ -769,62 +837,72 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(AttnArgs a) {
           vf = *(const frag*)(sV + drow * VROWB + ((c ^ (drow & (VCH - 1))) << 4) + w);
         else
           vf = frag{0};
-        o[d] = M_::mma(vf, pf, o[d]);
+#pragma unroll
+        for (int b = 0; b < QB; b++) o[b][d] = M_::mma(vf, pf[b][st], o[b][d]);
       }
+    }
+#pragma unroll
+    for (int q = 0; q < PK * DB; q++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 2);
     }
   };
 
-  const int ntiles = (int)((kfin - kbeg + BKV - 1) / BKV);
-  if (ntiles > 0) {
-    gload(kbeg);
-    sstore(0);
+  const int ntiles = (kfin - kbeg + kBKV - 1) / kBKV;
+  if (ntiles > 0) issue(kbeg, 0);
+  for (int t = 0; t < ntiles; t++) {
+    const int k0 = kbeg + t * kBKV;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int t = 0; t < ntiles; t++) {
-      const int64_t k0 = kbeg + (int64_t)t * BKV;
-      if (t + 1 < ntiles) gload(k0 + BKV);
-      if (k0 < kend_w) compute(t & 1, k0);
-      if (t + 1 < ntiles) sstore((t + 1) & 1);
+    if (k0 + kBKV > kend32 && (kend32 % V) != 0) {  // last tile, V^T chunk straddles kend
+      fixup(k0, t & 1);
       __syncthreads();
+    }
+    if (t + 1 < ntiles) issue(k0 + kBKV, (t + 1) & 1);
+    if (k0 < kend_w) {
+      if (!wfull || k0 + kBKV - 1 > qmin_w)
+        compute(t & 1, k0, std::true_type{});
+      else
+        compute(t & 1, k0, std::false_type{});
     }
   }
 
-  const float lt = l + __shfl_xor(l, 32);
-  if (nseg == 1) {
-    if (qok) {
-      const float inv = 1.0f / lt;
-      T* orow = (T*)a.O + row * a.ldo + head * HD;
+#pragma unroll
+  for (int b = 0; b < QB; b++) {
+    const float lt = l[b] + __shfl_xor(l[b], 32);
+    const int64_t row = row0 + 32 * b + lr;
+    (void)kend_w;
+    if (nseg == 1) {
+      if (qok[b]) {
+        const float inv = 1.0f / lt;
+        T* orow = (T*)a.O + row * a.ldo + head * HD;
+#pragma unroll
+        for (int d = 0; d < DB; d++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int d0 = 32 * d + 8 * q + 4 * lg;
+            if (HD % 32 == 0 || d0 < HD)
+              store4<T>(orow + d0, o[b][d][4 * q] * inv, o[b][d][4 * q + 1] * inv,
+                        o[b][d][4 * q + 2] * inv, o[b][d][4 * q + 3] * inv);
+          }
+      }
+    } else {
+      const int64_t slot =
+          (((int64_t)head * a.nqt + qt) * a.maxseg + seg) * kBQ + wave * 32 * QB + 32 * b + lr;
+      float* op = a.Op + slot * HD;
 #pragma unroll
       for (int d = 0; d < DB; d++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
           const int d0 = 32 * d + 8 * q + 4 * lg;
-          if (HD % 32 == 0 || d0 < HD) {
-            Chunk<T> c4;  // only the first 4 elements are used
-#pragma unroll
-            for (int t = 0; t < 4; t++) c4.e[t] = from_f<T>(o[d][4 * q + t] * inv);
-            if constexpr (ES == 2) {
-              *(u32x2*)(orow + d0) = u32x2{c4.raw[0], c4.raw[1]};
-            } else {
-              *(u32x4*)(orow + d0) = c4.raw;
-            }
-          }
+          if (HD % 32 == 0 || d0 < HD)
+            *(float4*)(op + d0) =
+                make_float4(o[b][d][4 * q], o[b][d][4 * q + 1], o[b][d][4 * q + 2], o[b][d][4 * q + 3]);
         }
-    }
-  } else {
-    const int64_t slot = (((int64_t)head * a.nqt + qt) * a.maxseg + seg) * 128 + wave * 32 + lr;
-    float* op = a.Op + slot * HD;
-#pragma unroll
-    for (int d = 0; d < DB; d++)
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int d0 = 32 * d + 8 * q + 4 * lg;
-        if (HD % 32 == 0 || d0 < HD)
-          *(float4*)(op + d0) =
-              make_float4(o[d][4 * q], o[d][4 * q + 1], o[d][4 * q + 2], o[d][4 * q + 3]);
+      if (lg == 0) {
+        a.ML[2 * slot] = m[b];
+        a.ML[2 * slot + 1] = lt;
       }
-    if (lg == 0) {
-      a.ML[2 * slot] = m;
-      a.ML[2 * slot + 1] = lt;
     }
   }
 }
@@ -839,18 +917,19 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int dq = (int)(gid % DQ);
   const int64_t head = rid / a.T, row = rid % a.T;
   if (head >= a.Hd) return;
-  const int qt = (int)(row / 128);
-  const int64_t kend = zig(min(a.T, (int64_t)qt * 128 + 128) - 1, a.chunk, a.rank, a.fold) + 1;
+  const int qt = (int)(row / kBQ);
+  const int64_t kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold);
   const int nseg = (int)((kend + a.lseg - 1) / a.lseg);
   if (nseg == 1) return;
-  const int64_t base = ((head * a.nqt + qt) * a.maxseg) * 128 + (row % 128);
+  const int64_t base = ((head * a.nqt + qt) * a.maxseg) * kBQ + (row % kBQ);
   float mx = -INFINITY;
-  for (int s = 0; s < nseg; s++) mx = fmaxf(mx, a.ML[2 * (base + s * 128)]);
+  for (int s = 0; s < nseg; s++) mx = fmaxf(mx, a.ML[2 * (base + s * kBQ)]);
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < nseg; s++) {
-    const int64_t slot = base + s * 128;
-    const float w = fast_exp2(a.ML[2 * slot] - mx);
+    const int64_t slot = base + s * kBQ;
+    const float ms = a.ML[2 * slot];
+    const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - mx);
     L += w * a.ML[2 * slot + 1];
     const float4 v = *(const float4*)(a.Op + slot * HD + 4 * dq);
     acc.x += w * v.x;
@@ -859,11 +938,8 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
     acc.w += w * v.w;
   }
   const float inv = 1.0f / L;
-  T* out = (T*)a.O + row * a.ldo + head * HD + 4 * dq;
-  out[0] = from_f<T>(acc.x * inv);
-  out[1] = from_f<T>(acc.y * inv);
-  out[2] = from_f<T>(acc.z * inv);
-  out[3] = from_f<T>(acc.w * inv);
+  store4<T>((T*)a.O + row * a.ldo + head * HD + 4 * dq, acc.x * inv, acc.y * inv, acc.z * inv,
+            acc.w * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -885,35 +961,67 @@ __global__ void spin_kernel(uint64_t ticks) {
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
+// Split length for the attention work items: the candidate whose simulated
+// schedule (items dispatched in order onto 256 CUs, each taking the first
+// free one; cost = keys + a fixed per-item overhead + a merge cost per split
+// item) finishes first.  Cached per shape.
 AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int Hd) {
   AttnPlan p{};
-  p.nqt = (int)((T + 127) / 128);
+  p.bq = kBQ;
+  p.nqt = (int)((T + kBQ - 1) / kBQ);
   if (T <= 0) return p;
-  int64_t tiles = 0, kmax = 0;
+  struct Key { int64_t T, S, C; int r, D, Hd; };
+  struct Entry { Key k; AttnPlan p; };
+  static thread_local std::vector<Entry> cache;
+  for (const Entry& e : cache)
+    if (e.k.T == T && e.k.S == S && e.k.C == chunk && e.k.r == rank && e.k.D == fold && e.k.Hd == Hd)
+      return e.p;
+  std::vector<int64_t> kend(p.nqt);
+  int64_t kmax = 0;
   for (int qt = 0; qt < p.nqt; qt++) {
-    const int64_t kend = zig(std::min(T, (int64_t)qt * 128 + 128) - 1, chunk, rank, fold) + 1;
-    tiles += (kend + 63) / 64;
-    kmax = std::max(kmax, kend);
+    kend[qt] = qtile_kend(T, qt, chunk, rank, fold);
+    kmax = std::max(kmax, kend[qt]);
   }
-  // About 1024 work items fill 256 CUs two workgroups deep, twice over.
-  const int64_t target = 1024;
-  int64_t lseg;
-  if ((int64_t)p.nqt * Hd >= target) {
-    lseg = (kmax + 63) / 64 * 64;
-  } else {
-    const int64_t per_item = (tiles * Hd + target - 1) / target;
-    lseg = std::max<int64_t>(16, per_item) * 64;
+  const int64_t kmax64 = (kmax + 63) / 64 * 64;
+  const int kCU = kQB == 1 ? 512 : 256;  // concurrent workgroups
+  const double overhead = 3 * kBKV, merge = 2 * kBKV;  // in key units
+  double best = 1e300;
+  int64_t best_l = kmax64;
+  std::vector<double> cu(kCU);
+  for (int64_t lseg = 1024; ; lseg += 256) {
+    if (lseg > kmax64) lseg = kmax64;
+    std::fill(cu.begin(), cu.end(), 0.0);
+    // dispatch order: query tiles heaviest first, segments in order, heads innermost
+    int64_t items = 0;
+    for (int qt = p.nqt - 1; qt >= 0; --qt) {
+      const int ns = (int)((kend[qt] + lseg - 1) / lseg);
+      for (int sg = 0; sg < ns; sg++) {
+        const double keys = (double)std::min(lseg, kend[qt] - sg * lseg);
+        const double cost = keys + overhead + (ns > 1 ? merge : 0.0);
+        for (int h = 0; h < Hd; h++) {
+          auto it = std::min_element(cu.begin(), cu.end());
+          *it += cost;
+          items++;
+        }
+      }
+    }
+    const double span = *std::max_element(cu.begin(), cu.end());
+    if (span < best * 0.999) {
+      best = span;
+      best_l = lseg;
+    }
+    if (lseg >= kmax64) break;
   }
-  p.lseg = (int)lseg;
+  p.lseg = (int)best_l;
   p.maxseg = 1;
   p.nitems = 0;
   for (int qt = 0; qt < p.nqt; qt++) {
-    const int64_t kend = zig(std::min(T, (int64_t)qt * 128 + 128) - 1, chunk, rank, fold) + 1;
-    const int ns = (int)((kend + lseg - 1) / lseg);
+    const int ns = (int)((kend[qt] + best_l - 1) / best_l);
     p.maxseg = std::max(p.maxseg, ns);
     p.nitems += ns;
   }
   p.split = p.maxseg > 1;
+  cache.push_back({{T, S, chunk, rank, fold, Hd}, p});
   return p;
 }
 
