@@ -582,9 +582,29 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 constexpr int kQB = 1;     // 32-query blocks per wave (two waves share a SIMD)
 constexpr int kBQ = 128 * kQB;  // local query rows per work item (4 waves)
-constexpr int kBKV = 64;   // keys per tile
+constexpr int kBKV = 64;   // keys per tile (largest; the 128-dim bf16 kernel uses 32)
+
+// Keys per K/V tile and LDS stages: 32-key tiles in a 4-deep ring for the
+// 128-dim bf16 kernel (three tiles of loads in flight while one computes,
+// still 64 KB so two workgroups share a CU); 64-key double buffering
+// elsewhere.
+template <typename T, int HD>
+struct AttnTile {
+  static constexpr bool deep = sizeof(T) == 2 && HD == 128;
+  static constexpr int BKV = deep ? 32 : 64;
+  static constexpr int NSTAGE = 2;
+  static constexpr int WAVES = deep ? 3 : 2;  // waves per SIMD the kernel is sized for
+};
 
 __device__ inline int kappa(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// XOR swizzle of the 16-byte chunk c in row r of an LDS tile with `nch`
+// chunks per row: rows of 128 bytes or more use r % nch; 64-byte rows (four
+// share one 256-byte bank sweep) use (r / 4) % 4.
+template <int NCH>
+__device__ inline int swz(int c, int r) {
+  return NCH >= 8 ? c ^ (r & (NCH - 1)) : c ^ ((r >> 2) & (NCH - 1));
+}
 
 __device__ __host__ inline int64_t qtile_kend(int64_t T, int qt, int64_t C, int rank, int fold) {
   const int64_t last = (T < (int64_t)qt * kBQ + kBQ ? T : (int64_t)qt * kBQ + kBQ) - 1;
@@ -606,23 +626,27 @@ __device__ inline bool decode_item(const AttnArgs& a, int item, int& qt, int& se
 }
 
 template <typename T, int HD>
-__global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) attn_kernel(AttnArgs a) {
   typedef MF<T> M_;
   typedef typename M_::frag frag;
   constexpr int ES = sizeof(T);
   constexpr int V = 16 / ES;
   constexpr int QB = kQB;
+  constexpr int BKV = AttnTile<T, HD>::BKV;
+  constexpr int NSTAGE = AttnTile<T, HD>::NSTAGE;
+  constexpr int NKB = BKV / 32;         // 32-key blocks per tile
   constexpr int KROWB = HD * ES, KCH = KROWB / 16;
-  constexpr int VROWB = kBKV * ES, VCH = VROWB / 16;
-  constexpr int KT_BYTES = kBKV * KROWB;
+  constexpr int VROWB = BKV * ES, VCH = VROWB / 16;
+  constexpr int KT_BYTES = BKV * KROWB;
   constexpr int VT_BYTES = HD * VROWB;
   constexpr int STAGE = KT_BYTES + VT_BYTES;
   constexpr int KI = KT_BYTES / 1024, VI = VT_BYTES / 1024;  // 1 KB wave loads per tile
   constexpr int QK = HD / M_::KSTEP;    // k-steps over the head dim
   constexpr int DB = (HD + 31) / 32;    // 32-row blocks of O^T
-  constexpr int PK = kBKV / M_::KSTEP;  // k-steps over the keys of a tile
+  constexpr int PK = BKV / M_::KSTEP;   // k-steps over the keys of a tile
   static_assert(KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0, "tile bytes");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  static_assert(NSTAGE == 2 || (KI % 4 == 0 && VI % 4 == 0), "deep rings need equal loads per wave");
+  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
@@ -693,13 +717,13 @@ __global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a)
     const int b = (wave + 4 * j) * 1024 + 16 * lane;
     const int r = b / KROWB, p = (b % KROWB) >> 4;
     krow[j] = r;
-    koff[j] = (uint32_t)((r * HD + (p ^ (r & (KCH - 1))) * V) * ES);
+    koff[j] = (uint32_t)((r * HD + swz<KCH>(p, r) * V) * ES);
   }
 #pragma unroll
   for (int j = 0; j < VJ; j++) {
     const int b = (wave + 4 * j) * 1024 + 16 * lane;
     const int d = b / VROWB, p = (b % VROWB) >> 4;
-    const int c = p ^ (d & (VCH - 1));
+    const int c = swz<VCH>(p, d);
     vkey[j] = c * V;
     voff[j] = (int)(((int64_t)d * a.S + c * V) * ES);
   }
@@ -723,12 +747,12 @@ __global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a)
   auto fixup = [&](int k0, int buf) {
     char* sV = smem + buf * STAGE + KT_BYTES;
     const int first = kend32 - k0;  // first key to clear, within the tile
-    const int upto = min(kBKV, (first + V - 1) / V * V);
+    const int upto = min(BKV, (first + V - 1) / V * V);
     for (int i = tid; i < HD * (upto - first); i += 256) {
       const int d = i / (upto - first), key = first + i % (upto - first);
       const int byte = key * ES;
       const int c = byte >> 4, w = byte & 15;
-      *(T*)(sV + d * VROWB + ((c ^ (d & (VCH - 1))) << 4) + w) = from_f<T>(0.f);
+      *(T*)(sV + d * VROWB + (swz<VCH>(c, d) << 4) + w) = from_f<T>(0.f);
     }
   };
 
@@ -737,9 +761,9 @@ __global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a)
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* sK = smem + buf * STAGE;
     const char* sV = sK + KT_BYTES;
-    f32x16 s[QB][2];
+    f32x16 s[QB][NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
+    for (int kb = 0; kb < NKB; kb++) {
 #pragma unroll
       for (int b = 0; b < QB; b++) s[b][kb] = f32x16{0};
       const int krow = 32 * kb + kappa(lr);
@@ -747,14 +771,14 @@ __global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a)
       for (int ks = 0; ks < QK; ks++) {
         const int byte = (ks * M_::KSTEP + lg * M_::E) * ES;
         const int c = byte >> 4, w = byte & 15;
-        const frag kf = *(const frag*)(sK + krow * KROWB + ((c ^ (krow & (KCH - 1))) << 4) + w);
+        const frag kf = *(const frag*)(sK + krow * KROWB + (swz<KCH>(c, krow) << 4) + w);
 #pragma unroll
         for (int b = 0; b < QB; b++) s[b][kb] = M_::mma(kf, qf[b][ks], s[b][kb]);
       }
     }
     // Keep each fragment read one step ahead of the MFMAs that use it.
 #pragma unroll
-    for (int q = 0; q < 2 * QK; q++) {
+    for (int q = 0; q < NKB * QK; q++) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);
     }
@@ -765,9 +789,9 @@ __global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a)
     for (int b = 0; b < QB; b++) {
       float x = -INFINITY;
       // key - k0 - 8lg = 32kb + 16(i/8) + i%8 must not exceed qpos - k0 - 8lg
-      const int lim = max(-1, min(kBKV, qpos[b] - k0)) - 8 * lg;
+      const int lim = max(-1, min(BKV, qpos[b] - k0)) - 8 * lg;
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++)
+      for (int kb = 0; kb < NKB; kb++)
 #pragma unroll
         for (int i = 0; i < 16; i++) {
           if (MASK) {
@@ -834,7 +858,7 @@ __global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a)
         const int drow = 32 * d + lr;
         frag vf;
         if (HD % 32 == 0 || drow < HD)
-          vf = *(const frag*)(sV + drow * VROWB + ((c ^ (drow & (VCH - 1))) << 4) + w);
+          vf = *(const frag*)(sV + drow * VROWB + (swz<VCH>(c, drow) << 4) + w);
         else
           vf = frag{0};
 #pragma unroll
@@ -848,22 +872,39 @@ __global__ void __launch_bounds__(256, kQB == 1 ? 2 : 1) attn_kernel(AttnArgs a)
     }
   };
 
-  const int ntiles = (kfin - kbeg + kBKV - 1) / kBKV;
-  if (ntiles > 0) issue(kbeg, 0);
+  const int ntiles = (kfin - kbeg + BKV - 1) / BKV;
+  // Prologue: tiles 0 .. NSTAGE-2 in flight.
+#pragma unroll
+  for (int t = 0; t < NSTAGE - 1; t++)
+    if (t < ntiles) issue(kbeg + t * BKV, t);
   for (int t = 0; t < ntiles; t++) {
-    const int k0 = kbeg + t * kBKV;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int k0 = kbeg + t * BKV;
+    // Wait for this tile's loads: loads retire in order, and each wave has
+    // issued LPT loads for each of the (at most NSTAGE-2) later tiles.
+    if constexpr (NSTAGE == 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      constexpr int LPT = (KI + VI) / 4;
+      const int later = min(NSTAGE - 2, ntiles - 1 - t);
+      static_assert(NSTAGE == 4 && LPT == 4, "wait counts below assume 4 loads per tile");
+      if (later >= 2)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    if (k0 + kBKV > kend32 && (kend32 % V) != 0) {  // last tile, V^T chunk straddles kend
-      fixup(k0, t & 1);
+    if (k0 + BKV > kend32 && (kend32 % V) != 0) {  // last tile, V^T chunk straddles kend
+      fixup(k0, t % NSTAGE);
       __syncthreads();
     }
-    if (t + 1 < ntiles) issue(k0 + kBKV, (t + 1) & 1);
+    if (t + NSTAGE - 1 < ntiles) issue(k0 + (NSTAGE - 1) * BKV, (t + NSTAGE - 1) % NSTAGE);
     if (k0 < kend_w) {
-      if (!wfull || k0 + kBKV - 1 > qmin_w)
-        compute(t & 1, k0, std::true_type{});
+      if (!wfull || k0 + BKV - 1 > qmin_w)
+        compute(t % NSTAGE, k0, std::true_type{});
       else
-        compute(t & 1, k0, std::false_type{});
+        compute(t % NSTAGE, k0, std::false_type{});
     }
   }
 
@@ -983,7 +1024,7 @@ AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int 
     kmax = std::max(kmax, kend[qt]);
   }
   const int64_t kmax64 = (kmax + 63) / 64 * 64;
-  const int kCU = kQB == 1 ? 512 : 256;  // concurrent workgroups
+  const int kCU = kQB == 1 ? 768 : 256;  // concurrent workgroups (up to 3 per CU)
   const double overhead = 3 * kBKV, merge = 2 * kBKV;  // in key units
   double best = 1e300;
   int64_t best_l = kmax64;
