@@ -223,8 +223,8 @@ __device__ inline void load4(const T* p, float* o) {
   }
 }
 
-template <typename T, int BM, int BN, int EPI, bool VEC>
-__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
+template <typename T, int BM, int BN, int EPI, bool VEC, int NW>
+__global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   typedef MF<T> M_;
   typedef typename M_::frag frag;
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
@@ -232,19 +232,23 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
   constexpr int V = 16 / ES;
   constexpr int BK = 128 / ES;  // elements per 128-byte LDS row
   constexpr int KS = BK / M_::KSTEP;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int NT = NW * 64;              // threads
+  constexpr int WGN = NW / 2;              // waves along N (2 along M)
+  constexpr int WM = BM / 2, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int NBR = DUAL ? 2 * BN : BN;  // B rows staged per tile
-  constexpr int AC = BM * 8 / 256;         // 16-byte chunks per thread
-  constexpr int BC = NBR * 8 / 256;
+  constexpr int AC = BM * 8 / NT;          // 16-byte chunks per thread
+  constexpr int BC = NBR * 8 / NT;
+  constexpr int RR = NT / 8;               // tile rows one load round covers
   constexpr int STAGE = (BM + NBR) * 128;
   constexpr int NB3 = DUAL ? NB : 1;
   static_assert(BM % 64 == 0 && BN % 64 == 0 || BN == 192 || BN == 96, "tile");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lr = lane & 31, lg = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // Tiles are handed out so that each XCD (workgroups b with equal b % 8)
   // works on a contiguous range of tiles and shares operands in its L2.
@@ -270,59 +274,63 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       if (DUAL) acc3[i][j] = f32x16{0};
     }
 
-  auto compute = [&](int buf) {
+  frag af[2][MB], bfr[2][NB], bf3[2][NB3];
+  // Fragment reads of k-step ks of LDS buffer buf into register set `set`.
+  auto fetch = [&](int buf, int ks, int set) {
     const char* sA = smem + buf * STAGE;
     const char* sB = sA + BM * 128;
-    frag af[2][MB], bfr[2][NB], bf3[2][NB3];
-    auto fetch = [&](int ks, int set) {
-      const int byte = (ks * M_::KSTEP + lg * M_::E) * ES;
-      const int c = byte >> 4, w = byte & 15;
+    const int byte = (ks * M_::KSTEP + lg * M_::E) * ES;
+    const int c = byte >> 4, w = byte & 15;
 #pragma unroll
-      for (int i = 0; i < MB; i++) {
-        const int row = wm * WM + i * 32 + lr;
-        af[set][i] = *(const frag*)(sA + row * 128 + ((c ^ (row & 7)) << 4) + w);
-      }
+    for (int i = 0; i < MB; i++) {
+      const int row = wm * WM + i * 32 + lr;
+      af[set][i] = *(const frag*)(sA + row * 128 + ((c ^ (row & 7)) << 4) + w);
+    }
 #pragma unroll
-      for (int j = 0; j < NB; j++) {
-        const int row = wn * WN + j * 32 + lr;
-        bfr[set][j] = *(const frag*)(sB + row * 128 + ((c ^ (row & 7)) << 4) + w);
-        if (DUAL) {
-          const int r3 = BN + row;
-          bf3[set][j] = *(const frag*)(sB + r3 * 128 + ((c ^ (r3 & 7)) << 4) + w);
-        }
-      }
-    };
-    fetch(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-      const int cur = ks & 1;
-      if (ks + 1 < KS) fetch(ks + 1, cur ^ 1);
-#pragma unroll
-      for (int i = 0; i < MB; i++)
-#pragma unroll
-        for (int j = 0; j < NB; j++) {
-          acc[i][j] = M_::mma(bfr[cur][j], af[cur][i], acc[i][j]);
-          if (DUAL) acc3[i][j] = M_::mma(bf3[cur][j], af[cur][i], acc3[i][j]);
-        }
-      // Interleave the next step's fragment reads with this step's MFMAs so
-      // LDS latency hides behind the matrix pipe.
-      if (ks + 1 < KS) {
-        constexpr int NR = MB + NB + NB3 * (DUAL ? 1 : 0);
-        constexpr int NM = MB * NB * (DUAL ? 2 : 1);
-        constexpr int PER = NM / NR > 0 ? NM / NR : 1;
-#pragma unroll
-        for (int q = 0; q < NR; q++) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
-        }
+    for (int j = 0; j < NB; j++) {
+      const int row = wn * WN + j * 32 + lr;
+      bfr[set][j] = *(const frag*)(sB + row * 128 + ((c ^ (row & 7)) << 4) + w);
+      if (DUAL) {
+        const int r3 = BN + row;
+        bf3[set][j] = *(const frag*)(sB + r3 * 128 + ((c ^ (r3 & 7)) << 4) + w);
       }
     }
   };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+      for (int j = 0; j < NB; j++) {
+        acc[i][j] = M_::mma(bfr[set][j], af[set][i], acc[i][j]);
+        if (DUAL) acc3[i][j] = M_::mma(bf3[set][j], af[set][i], acc3[i][j]);
+      }
+  };
+  // Interleave the fragment reads just issued with the MFMAs that follow.
+  auto interleave = [&]() {
+    constexpr int NR = MB + NB + NB3 * (DUAL ? 1 : 0);
+    constexpr int NM = MB * NB * (DUAL ? 2 : 1);
+    constexpr int PER = NM / NR > 0 ? NM / NR : 1;
+#pragma unroll
+    for (int q = 0; q < NR; q++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
+    }
+  };
+  // k-steps 0 .. KS-2 of buffer buf (fragments of step 0 already in set 0).
+  auto compute_head = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ks++) {
+      fetch(buf, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+      interleave();
+    }
+  };
+  constexpr int LAST = (KS - 1) & 1;  // register set of the last k-step
 
   if constexpr (VEC) {
-    // Direct global -> LDS.  Load round i of A covers tile rows [32i, 32i+32);
-    // wave w writes rows 32i + 8w .. +8 (1 KB), lane l the 16 bytes at
-    // physical chunk l%8 of row 32i + 8w + l/8, i.e. logical chunk
+    // Direct global -> LDS.  Load round i of A covers tile rows [RR*i, RR*i+RR);
+    // wave w writes rows RR*i + 8w .. +8 (1 KB), lane l the 16 bytes at
+    // physical chunk l%8 of row RR*i + 8w + l/8, i.e. logical chunk
     // (l%8) ^ (row%8).
     const brsrc rA = make_rsrc(A, (uint64_t)g.M * g.lda * ES);
     const brsrc rB = make_rsrc(B, (uint64_t)g.N * g.ldb * ES);
@@ -332,12 +340,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
     uint32_t offA[AC], offB[BC];
 #pragma unroll
     for (int i = 0; i < AC; i++) {
-      const int gm = m0 + 32 * i + lrow;
+      const int gm = m0 + RR * i + lrow;
       offA[i] = gm < g.M ? (uint32_t)(((int64_t)gm * g.lda + lc * V) * ES) : kOOB;
     }
 #pragma unroll
     for (int i = 0; i < BC; i++) {
-      const int rr = 32 * i + lrow;
+      const int rr = RR * i + lrow;
       const int gn = n0 + (DUAL && rr >= BN ? rr - BN : rr);
       offB[i] = gn < g.N ? (uint32_t)(((int64_t)gn * g.ldb + lc * V) * ES) : kOOB;
     }
@@ -348,33 +356,62 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       char* sB = sA + BM * 128;
 #pragma unroll
       for (int i = 0; i < AC; i++)
-        buffer_to_lds16(rA, sA + i * 4096 + wave * 1024, kok ? offA[i] : kOOB, k0 * ES);
+        buffer_to_lds16(rA, sA + i * RR * 128 + wave * 1024, kok ? offA[i] : kOOB, k0 * ES);
 #pragma unroll
       for (int i = 0; i < BC; i++) {
-        const bool second = DUAL && 32 * i >= BN;
-        buffer_to_lds16(second ? rB3 : rB, sB + i * 4096 + wave * 1024, kok ? offB[i] : kOOB,
+        const bool second = DUAL && RR * i >= BN;
+        buffer_to_lds16(second ? rB3 : rB, sB + i * RR * 128 + wave * 1024, kok ? offB[i] : kOOB,
                         k0 * ES);
       }
     };
-    if (nk > 0) issue(0, 0);
-    for (int kt = 0; kt < nk; kt++) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Pipeline: tiles kt and kt+1 are resident or in flight while kt computes.
+    // The barrier sits before the last k-step's MFMAs: every wave has its
+    // fragments of buffer kt in registers (so that buffer may be refilled
+    // with tile kt+2) and tile kt+1 has landed (so its first fragments can
+    // be read while those MFMAs run).
+    if (nk > 0) {
+      issue(0, 0);
+      if (nk > 1) issue(1, 1);
+      if (nk > 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AC + BC) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-      compute(kt & 1);
+      fetch(0, 0, 0);
+      for (int kt = 0; kt < nk; kt++) {
+        const int cur = kt & 1;
+        compute_head(cur);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);  // keep the last step's MFMAs below the barrier
+        if (kt + 2 < nk) issue(kt + 2, cur);
+        if (kt + 1 < nk) fetch(cur ^ 1, 0, LAST ^ 1);
+        mfmas(LAST);
+        interleave();
+        // The next iteration starts from register set 0: move if needed.
+        if constexpr (LAST == 0) {
+#pragma unroll
+          for (int i = 0; i < MB; i++) af[0][i] = af[1][i];
+#pragma unroll
+          for (int j = 0; j < NB; j++) {
+            bfr[0][j] = bfr[1][j];
+            if (DUAL) bf3[0][j] = bf3[1][j];
+          }
+        }
+      }
     }
   } else {
     u32x4 ra[AC], rb[BC];
     auto gload = [&](int k0) {
 #pragma unroll
       for (int i = 0; i < AC; i++) {
-        const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+        const int id = tid + NT * i, row = id >> 3, c = id & 7;
         const int gm = m0 + row;
         ra[i] = load_chunk<T, false>(A, gm < g.M, gm, g.lda, k0 + c * V, g.K);
       }
 #pragma unroll
       for (int i = 0; i < BC; i++) {
-        const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+        const int id = tid + NT * i, row = id >> 3, c = id & 7;
         const T* src = B;
         int rr = row;
         if (DUAL && row >= BN) {
@@ -390,12 +427,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       char* sB = sA + BM * 128;
 #pragma unroll
       for (int i = 0; i < AC; i++) {
-        const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+        const int id = tid + NT * i, row = id >> 3, c = id & 7;
         *(u32x4*)(sA + row * 128 + ((c ^ (row & 7)) << 4)) = ra[i];
       }
 #pragma unroll
       for (int i = 0; i < BC; i++) {
-        const int id = tid + 256 * i, row = id >> 3, c = id & 7;
+        const int id = tid + NT * i, row = id >> 3, c = id & 7;
         *(u32x4*)(sB + row * 128 + ((c ^ (row & 7)) << 4)) = rb[i];
       }
     };
@@ -406,7 +443,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs g) {
       for (int kt = 0; kt < nk; kt++) {
         const int cur = kt & 1;
         if (kt + 1 < nk) gload((kt + 1) * BK);
-        compute(cur);
+        fetch(cur, 0, 0);
+        compute_head(cur);
+        mfmas(LAST);
         if (kt + 1 < nk) sstore(cur ^ 1);
         __syncthreads();
       }
@@ -1078,13 +1117,13 @@ hipError_t launch_rmsnorm(Dtype dt, const void* x, const void* g, void* y, int64
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN, int EPI>
+template <typename T, int BM, int BN, int EPI, int NW = 4>
 static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
   const int nt = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (vec)
-    gemm_kernel<T, BM, BN, EPI, true><<<nt, 256, 0, s>>>(a);
+    gemm_kernel<T, BM, BN, EPI, true, NW><<<nt, NW * 64, 0, s>>>(a);
   else
-    gemm_kernel<T, BM, BN, EPI, false><<<nt, 256, 0, s>>>(a);
+    gemm_kernel<T, BM, BN, EPI, false, NW><<<nt, NW * 64, 0, s>>>(a);
 }
 
 // Tile choice: the shape whose estimated time (rounds of 256 concurrent
@@ -1105,10 +1144,10 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
     if (t < bt * 0.999) { bt = t; best = c; }
   }
   if constexpr (EPI == EPI_SWIGLU) {
-    if (best == 0) gemm_go<bf16, 256, 128, EPI>(a, vec, s);
+    if (best == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
     else gemm_go<bf16, 128, 64, EPI>(a, vec, s);
   } else {
-    if (best == 0) gemm_go<bf16, 256, 256, EPI>(a, vec, s);
+    if (best == 0) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
     else if (best == 1) gemm_go<bf16, 256, 192, EPI>(a, vec, s);
     else gemm_go<bf16, 128, 128, EPI>(a, vec, s);
   }
