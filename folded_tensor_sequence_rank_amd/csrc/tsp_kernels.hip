@@ -223,7 +223,7 @@ __device__ inline void load4(const T* p, float* o) {
   }
 }
 
-template <typename T, int BM, int BN, int EPI, bool VEC, int NW>
+template <typename T, int BM, int BN, int EPI, bool VEC, int NW, int WGM>
 __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   typedef MF<T> M_;
   typedef typename M_::frag frag;
@@ -233,8 +233,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   constexpr int BK = 128 / ES;  // elements per 128-byte LDS row
   constexpr int KS = BK / M_::KSTEP;
   constexpr int NT = NW * 64;              // threads
-  constexpr int WGN = NW / 2;              // waves along N (2 along M)
-  constexpr int WM = BM / 2, WN = BN / WGN;
+  constexpr int WGN = NW / WGM;            // waves along N (WGM along M)
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int NBR = DUAL ? 2 * BN : BN;  // B rows staged per tile
   constexpr int AC = BM * 8 / NT;          // 16-byte chunks per thread
@@ -1117,13 +1117,13 @@ hipError_t launch_rmsnorm(Dtype dt, const void* x, const void* g, void* y, int64
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN, int EPI, int NW = 4>
+template <typename T, int BM, int BN, int EPI, int NW = 4, int WGM = 2>
 static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
   const int nt = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (vec)
-    gemm_kernel<T, BM, BN, EPI, true, NW><<<nt, NW * 64, 0, s>>>(a);
+    gemm_kernel<T, BM, BN, EPI, true, NW, WGM><<<nt, NW * 64, 0, s>>>(a);
   else
-    gemm_kernel<T, BM, BN, EPI, false, NW><<<nt, NW * 64, 0, s>>>(a);
+    gemm_kernel<T, BM, BN, EPI, false, NW, WGM><<<nt, NW * 64, 0, s>>>(a);
 }
 
 // Tile choice: the shape whose estimated time (rounds of 256 concurrent
@@ -1148,7 +1148,7 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
     else gemm_go<bf16, 128, 64, EPI>(a, vec, s);
   } else {
     if (best == 0) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
-    else if (best == 1) gemm_go<bf16, 256, 192, EPI>(a, vec, s);
+    else if (best == 1) gemm_go<bf16, 256, 192, EPI, 8, 4>(a, vec, s);
     else gemm_go<bf16, 128, 128, EPI>(a, vec, s);
   }
 }
