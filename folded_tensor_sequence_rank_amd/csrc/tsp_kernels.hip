@@ -627,12 +627,18 @@ constexpr int kBKV = 64;   // keys per tile (largest; the 128-dim bf16 kernel us
 // 128-dim bf16 kernel (three tiles of loads in flight while one computes,
 // still 64 KB so two workgroups share a CU); 64-key double buffering
 // elsewhere.
+#ifndef TSP_ATTN128_BKV
+#define TSP_ATTN128_BKV 32   // keys per tile of the 128-dim bf16 kernel
+#endif
+#ifndef TSP_ATTN128_WAVES
+#define TSP_ATTN128_WAVES 3  // waves per SIMD the 128-dim bf16 kernel is sized for
+#endif
 template <typename T, int HD>
 struct AttnTile {
   static constexpr bool deep = sizeof(T) == 2 && HD == 128;
-  static constexpr int BKV = deep ? 32 : 64;
+  static constexpr int BKV = deep ? TSP_ATTN128_BKV : 64;
   static constexpr int NSTAGE = 2;
-  static constexpr int WAVES = deep ? 3 : 2;  // waves per SIMD the kernel is sized for
+  static constexpr int WAVES = deep ? TSP_ATTN128_WAVES : 2;  // waves per SIMD
 };
 
 __device__ inline int kappa(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
@@ -1063,7 +1069,7 @@ AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int 
     kmax = std::max(kmax, kend[qt]);
   }
   const int64_t kmax64 = (kmax + 63) / 64 * 64;
-  const int kCU = kQB == 1 ? 768 : 256;  // concurrent workgroups (up to 3 per CU)
+  const int kCU = 256 * (kQB == 1 ? TSP_ATTN128_WAVES : 1);  // concurrent workgroups
   const double overhead = 3 * kBKV, merge = 2 * kBKV;  // in key units
   double best = 1e300;
   int64_t best_l = kmax64;
