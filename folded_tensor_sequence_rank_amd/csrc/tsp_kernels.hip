@@ -656,16 +656,34 @@ __device__ __host__ inline int64_t qtile_kend(int64_t T, int qt, int64_t C, int 
   return zig(last, C, rank, fold) + 1;
 }
 
+// Work items are dispatched segment-major: every query tile's first key
+// segment, then every tile's second, ... (heaviest tiles first within a
+// segment), so the workgroups in flight read the same key range and share it
+// in L2.  Query tile qt has a segment s iff its causal end kend(qt) > s*lseg;
+// kend grows with qt, so those tiles form a suffix [q0(s), nqt).
+__device__ inline int first_tile_past(const AttnArgs& a, int64_t lo) {
+  int l = 0, h = a.nqt;  // smallest qt with kend(qt) > lo
+  while (l < h) {
+    const int mid = (l + h) >> 1;
+    if (qtile_kend(a.T, mid, a.chunk, a.rank, a.fold) > lo)
+      h = mid;
+    else
+      l = mid + 1;
+  }
+  return l;
+}
+
 __device__ inline bool decode_item(const AttnArgs& a, int item, int& qt, int& seg, int& nseg,
                                    int64_t& kend) {
-  for (qt = a.nqt - 1; qt >= 0; --qt) {
-    kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold);
-    nseg = (int)((kend + a.lseg - 1) / a.lseg);
-    if (item < nseg) {
-      seg = item;
+  for (seg = 0; seg < a.maxseg; seg++) {
+    const int cnt = a.nqt - first_tile_past(a, (int64_t)seg * a.lseg);
+    if (item < cnt) {
+      qt = a.nqt - 1 - item;
+      kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold);
+      nseg = (int)((kend + a.lseg - 1) / a.lseg);
       return true;
     }
-    item -= nseg;
+    item -= cnt;
   }
   return false;
 }
@@ -1077,11 +1095,14 @@ AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int 
   for (int64_t lseg = 1024; ; lseg += 256) {
     if (lseg > kmax64) lseg = kmax64;
     std::fill(cu.begin(), cu.end(), 0.0);
-    // dispatch order: query tiles heaviest first, segments in order, heads innermost
+    // dispatch order (as decode_item): segment-major, heaviest query tiles
+    // first within a segment, heads innermost
     int64_t items = 0;
-    for (int qt = p.nqt - 1; qt >= 0; --qt) {
-      const int ns = (int)((kend[qt] + lseg - 1) / lseg);
-      for (int sg = 0; sg < ns; sg++) {
+    const int maxs = (int)((kmax + lseg - 1) / lseg);
+    for (int sg = 0; sg < maxs; sg++) {
+      for (int qt = p.nqt - 1; qt >= 0; --qt) {
+        const int ns = (int)((kend[qt] + lseg - 1) / lseg);
+        if (sg >= ns) continue;
         const double keys = (double)std::min(lseg, kend[qt] - sg * lseg);
         const double cost = keys + overhead + (ns > 1 ? merge : 0.0);
         for (int h = 0; h < Hd; h++) {
