@@ -317,13 +317,18 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
     }
   };
   // k-steps 0 .. KS-2 of buffer buf (fragments of step 0 already in set 0).
+#ifndef TSP_GEMM_SETPRIO
+#define TSP_GEMM_SETPRIO 1  // raise wave priority around the MFMA-heavy k-steps
+#endif
   auto compute_head = [&](int buf) {
+    if (TSP_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks + 1 < KS; ks++) {
       fetch(buf, ks + 1, (ks + 1) & 1);
       mfmas(ks & 1);
       interleave();
     }
+    if (TSP_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
   constexpr int LAST = (KS - 1) & 1;  // register set of the last k-step
 
@@ -628,10 +633,10 @@ constexpr int kBKV = 64;   // keys per tile (largest; the 128-dim bf16 kernel us
 // still 64 KB so two workgroups share a CU); 64-key double buffering
 // elsewhere.
 #ifndef TSP_ATTN128_BKV
-#define TSP_ATTN128_BKV 32   // keys per tile of the 128-dim bf16 kernel
+#define TSP_ATTN128_BKV 64   // keys per tile of the 128-dim bf16 kernel
 #endif
 #ifndef TSP_ATTN128_WAVES
-#define TSP_ATTN128_WAVES 3  // waves per SIMD the 128-dim bf16 kernel is sized for
+#define TSP_ATTN128_WAVES 2  // waves per SIMD the 128-dim bf16 kernel is sized for
 #endif
 template <typename T, int HD>
 struct AttnTile {
@@ -825,6 +830,10 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     const char* sK = smem + buf * STAGE;
     const char* sV = sK + KT_BYTES;
     f32x16 s[QB][NKB];
+#ifndef TSP_ATTN_SETPRIO
+#define TSP_ATTN_SETPRIO 1  // raise wave priority around MFMA blocks
+#endif
+    if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < NKB; kb++) {
 #pragma unroll
@@ -846,6 +855,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
       __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
     // Register i of block kb holds key k0 + 32kb + 16(i/8) + 8lg + i%8.
     float mt[QB];
 #pragma unroll
@@ -905,6 +915,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     }
     __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T . P^T
+    if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < PK; st++) {
       int kk;  // first key (within the tile) this lane supplies at step st
@@ -933,6 +944,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
       __builtin_amdgcn_sched_group_barrier(0x008, QB, 2);
     }
+    if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   const int ntiles = (kfin - kbeg + BKV - 1) / BKV;
@@ -1170,9 +1182,17 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
     const double t = (double)((tiles + 255) / 256) * cs[c].bm * cs[c].bn / cs[c].eff;
     if (t < bt * 0.999) { bt = t; best = c; }
   }
+#ifndef TSP_ACC_SMALLK_TILE
+#define TSP_ACC_SMALLK_TILE 0
+#endif
   if constexpr (EPI == EPI_SWIGLU) {
     if (best == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
     else gemm_go<bf16, 128, 64, EPI>(a, vec, s);
+  } else if ((EPI == EPI_ACC || EPI == EPI_RESID) && TSP_ACC_SMALLK_TILE != 0 && a.K <= 2048 &&
+             best == 0) {
+    // accumulate GEMMs with short K are bound by the fp32 accumulator traffic
+    if (TSP_ACC_SMALLK_TILE == 1) gemm_go<bf16, 128, 128, EPI, 4>(a, vec, s);
+    else gemm_go<bf16, 128, 128, EPI, 8>(a, vec, s);
   } else {
     if (best == 0) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
     else if (best == 1) gemm_go<bf16, 256, 192, EPI, 8, 4>(a, vec, s);
