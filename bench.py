@@ -52,14 +52,16 @@ def parse():
     return ap.parse_args()
 
 
-def flops_per_launch(cfg, r):
-    """Algorithmic FLOPs of one launch of each kernel class."""
+def flops_per_step(cfg, r):
+    """Algorithmic FLOPs of each kernel class in one layer share (all its
+    launches together): D QKV projections and D head-group attentions; the O
+    and W2 projections over all shards (however they are grouped into
+    launches); D W1/W3 projections."""
     import oracle.tsp_oracle as O  # closed-form pair count only
-    T, h, D = cfg.local_tokens, cfg.hidden, cfg.fold
-    hs, Fs = h // D, cfg.ffn // D
+    T, h, D, F = cfg.local_tokens, cfg.hidden, cfg.fold, cfg.ffn
     pairs = O.causal_pairs(cfg.seq, D, r)  # per head
-    return {"qkv": 2 * T * 3 * hs * h, "attn": 4 * hs * pairs, "oproj": 2 * T * hs * h,
-            "w13": 2 * T * 2 * Fs * h, "w2": 2 * T * Fs * h}
+    return {"qkv": 2 * T * 3 * h * h, "attn": 4 * h * pairs, "oproj": 2 * T * h * h,
+            "w13": 2 * T * 2 * F * h, "w2": 2 * T * F * h}
 
 
 def bytes_per_launch(cfg):
@@ -186,15 +188,18 @@ def main():
             prun.layer(x, L, kv, out)
         torch.cuda.synchronize()
         prof = tsp.tsp_profile_read(reset=True)
-        fl = flops_per_launch(cfg, r)
+        fs = flops_per_step(cfg, r)
         by = bytes_per_launch(cfg)
+        fl = {}  # FLOPs per launch of each class
         for k, (tot, n) in prof.items():
             if n == 0:
                 continue
             avg = tot / n
-            ent = {"ms_avg": round(avg, 5), "launches_per_step": n / args.steps,
+            per_step = n / args.steps
+            ent = {"ms_avg": round(avg, 5), "launches_per_step": per_step,
                    "ms_per_step": round(tot / args.steps, 4)}
-            if k in fl:
+            if k in fs:
+                fl[k] = fs[k] / per_step
                 ent["tflops"] = round(fl[k] / (avg * 1e-3) / 1e12, 1)
             if k in by:
                 ent["gbs"] = round(by[k] / (avg * 1e-3) / 1e9, 1)
@@ -203,7 +208,7 @@ def main():
         ach = fl[dom] / (kernels[dom]["ms_avg"] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                    "flops_per_launch": fl[dom], "traffic": traffic_for(dom)}
+                    "flops_per_launch": int(fl[dom]), "traffic": traffic_for(dom)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -100,14 +100,27 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace regions.  Offsets are from the workspace base.
 struct AttnWs {
-  size_t xn, y, q, o, slotw[2], slotkv[2], op, ml, end;
+  size_t xn, y, q, o, slotw[2], slotkv[2], bo[2], op, ml, end;
 };
 struct MlpWs {
-  size_t xn, y, gg, slotw[2], end;
+  size_t xn, y, gg, slotw[2], bw[2], end;
 };
 
 size_t attn_shard_elems(const Dims& d) { return 4 * (size_t)d.hs * d.h; }
 size_t mlp_shard_elems(const Dims& d) { return 3 * (size_t)d.Fs * d.h; }
+
+// Accumulation groups.  The O projections (and W2 projections) of G
+// consecutive shards run as one GEMM with K = G*hs (G*Fs): the shards'
+// attention outputs (SwiGLU products) sit side by side, and each shard's W_O
+// (W2) block is copied next to the others' on the side stream.  That cuts the
+// fp32 accumulator's read-modify-write passes from D to D/G per half layer.
+// G <= D/2, so a rank never holds more than half of W_O or W2 at once.
+#ifndef TSP_ACC_GROUP
+#define TSP_ACC_GROUP 4
+#endif
+int64_t acc_group(const Dims& d) {
+  return std::max<int64_t>(1, std::min<int64_t>(TSP_ACC_GROUP, d.D / 2));
+}
 size_t kv_block_elems(const Dims& d) { return 2 * (size_t)d.Hd * d.S * d.d; }
 
 AttnPlan plan_of(const Dims& d) { return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)d.Hd); }
@@ -118,10 +131,12 @@ AttnWs attn_ws(const Dims& d, size_t base) {
   const size_t act = al((size_t)d.T * d.h * d.es);
   w.xn = o; o += act;
   w.y = o; o += al((size_t)d.T * d.h * 4);
+  const int64_t G = acc_group(d);
   w.q = o; o += al((size_t)d.T * d.hs * d.es);
-  w.o = o; o += al((size_t)d.T * d.hs * d.es);
-  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(attn_shard_elems(d) * d.es); }
+  w.o = o; o += al((size_t)d.T * G * d.hs * d.es);  // [T][G*hs]
+  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(3 * (size_t)d.hs * d.h * d.es); }
   for (int s = 0; s < 2; s++) { w.slotkv[s] = o; o += al(kv_block_elems(d) * d.es); }
+  for (int s = 0; s < 2; s++) { w.bo[s] = o; o += al((size_t)d.h * G * d.hs * d.es); }  // [h][G*hs]
   const AttnPlan p = plan_of(d);
   const size_t nslot = p.split ? (size_t)d.Hd * p.nqt * p.maxseg * p.bq : 0;
   w.op = o; o += al(nslot * d.d * 4);
@@ -133,10 +148,12 @@ AttnWs attn_ws(const Dims& d, size_t base) {
 MlpWs mlp_ws(const Dims& d, size_t base) {
   MlpWs w;
   size_t o = base;
+  const int64_t G = acc_group(d);
   w.xn = o; o += al((size_t)d.T * d.h * d.es);
   w.y = o; o += al((size_t)d.T * d.h * 4);
-  w.gg = o; o += al((size_t)d.T * d.Fs * d.es);
-  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(mlp_shard_elems(d) * d.es); }
+  w.gg = o; o += al((size_t)d.T * G * d.Fs * d.es);  // [T][G*Fs]
+  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(2 * (size_t)d.Fs * d.h * d.es); }
+  for (int s = 0; s < 2; s++) { w.bw[s] = o; o += al((size_t)d.h * G * d.Fs * d.es); }  // [h][G*Fs]
   w.end = o;
   return w;
 }
@@ -147,7 +164,7 @@ bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Events for the slot hand-offs, created once per host thread and device.
 struct Events {
-  hipEvent_t start, join, readyA[2], freeA[2], readyM[2], freeM[2];
+  hipEvent_t start, join, readyA[2], freeA[2], readyM[2], freeM[2], freeO[2], freeW[2];
 };
 constexpr int kMaxDev = 64;
 thread_local Events* g_ev[kMaxDev] = {};
@@ -158,8 +175,10 @@ int get_events(Events** out) {
   if (dev < 0 || dev >= kMaxDev) return fail(TSP_E_HIP, "device index %d unsupported", dev);
   if (!g_ev[dev]) {
     Events* e = new Events;
-    hipEvent_t* all[] = {&e->start,     &e->join,      &e->readyA[0], &e->readyA[1], &e->freeA[0],
-                         &e->freeA[1],  &e->readyM[0], &e->readyM[1], &e->freeM[0],  &e->freeM[1]};
+    hipEvent_t* all[] = {&e->start,    &e->join,     &e->readyA[0], &e->readyA[1],
+                         &e->freeA[0], &e->freeA[1], &e->readyM[0], &e->readyM[1],
+                         &e->freeM[0], &e->freeM[1], &e->freeO[0],  &e->freeO[1],
+                         &e->freeW[0], &e->freeW[1]};
     for (hipEvent_t* p : all) HIP_TRY(hipEventCreateWithFlags(p, hipEventDisableTiming));
     g_ev[dev] = e;
   }
@@ -305,15 +324,16 @@ int qkv_gemm(Ctx& c, const void* xn, const char* w, int col0, void* q, char* kvs
   return TSP_OK;
 }
 
-// y (+)= a . w^T, or on the last shard out = resid + y + a . w^T.
-int acc_gemm(Ctx& c, const void* a, int64_t K, const char* w, float* y, bool first, bool last,
-             const void* resid, void* out) {
+// y (+)= a . w^T, or on the last group out = resid + y + a . w^T.
+// a [T][ld], w [h][ld]; only the first K columns take part.
+int acc_gemm(Ctx& c, const void* a, int64_t K, int64_t ld, const char* w, float* y, bool first,
+             bool last, const void* resid, void* out) {
   const Dims& d = *c.d;
   GemmArgs g = gemm_base();
   g.A = a;
-  g.lda = K;
+  g.lda = ld;
   g.B = w;
-  g.ldb = K;
+  g.ldb = ld;
   g.M = (int)d.T;
   g.N = (int)d.h;
   g.K = (int)K;
@@ -336,21 +356,33 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
               const void* kv, void* x1) {
   const Dims& d = *c.d;
   char* ws = c.ws;
-  const size_t wbytes = attn_shard_elems(d) * d.es;
-  const size_t kvbytes = kv_block_elems(d) * d.es;
+  const size_t es = d.es;
+  const size_t qkvbytes = 3 * (size_t)d.hs * d.h * es;
+  const size_t kvbytes = kv_block_elems(d) * es;
+  const int64_t G = acc_group(d);
   const AttnPlan plan = plan_of(d);
   TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws + L.xn, d.T, (int)d.h, d.eps, c.s)));
   for (int64_t j = 0; j < d.D; j++) {  // broadcast iteration j: shard of rank j
     const int s = (int)(j & 1);
+    const int64_t gi = j / G, gp = j % G;  // accumulation group, position in it
+    const int gb = (int)(gi & 1);
     char* slotw = ws + L.slotw[s];
     char* slotkv = ws + L.slotkv[s];
-    // ---- copy stream: receive shard j and the other ranks' K_j/V_j rows
+    char* bo = ws + L.bo[gb];
+    // ---- copy stream: receive shard j (Q|K|V into the slot, W_O next to
+    // its group's other W_O blocks) and the other ranks' K_j/V_j rows.
     if (c.side && j >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeA[s], 0));
-    int rc = debug_before_fill(c, slotw, wbytes);
+    if (c.side && gp == 0 && gi >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeO[gb], 0));
+    int rc = debug_before_fill(c, slotw, qkvbytes);
     if (rc) return rc;
-    if (c.d->flags & TSP_F_POISON_SLOTS)
-      HIP_TRY(launch_fill32(slotkv, d.dt == BF16 ? 0x7FC07FC0u : 0x7FC00000u, kvbytes, c.cs));
-    if (j != d.r) HIP_TRY(hipMemcpyAsync(slotw, w_attn[j], wbytes, hipMemcpyDeviceToDevice, c.cs));
+    if (c.d->flags & TSP_F_POISON_SLOTS) {
+      const uint32_t nan = d.dt == BF16 ? 0x7FC07FC0u : 0x7FC00000u;
+      HIP_TRY(launch_fill32(slotkv, nan, kvbytes, c.cs));
+      if (gp == 0) HIP_TRY(launch_fill32(bo, nan, (size_t)d.h * G * d.hs * es, c.cs));
+    }
+    if (j != d.r) HIP_TRY(hipMemcpyAsync(slotw, w_attn[j], qkvbytes, hipMemcpyDeviceToDevice, c.cs));
+    HIP_TRY(hipMemcpy2DAsync(bo + gp * d.hs * es, G * d.hs * es, (const char*)w_attn[j] + qkvbytes,
+                             d.hs * es, d.hs * es, d.h, hipMemcpyDeviceToDevice, c.cs));
     rc = copy_remote_kv(c, (const char*)kv + (size_t)j * kvbytes, slotkv);
     if (rc) return rc;
     if (c.side) {
@@ -365,14 +397,14 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     memset(&a, 0, sizeof a);
     a.Q = ws + L.q;
     a.K = slotkv;
-    a.Vt = slotkv + (size_t)d.Hd * d.S * d.d * d.es;
-    a.O = ws + L.o;
+    a.Vt = slotkv + (size_t)d.Hd * d.S * d.d * es;
+    a.O = ws + L.o + gp * d.hs * es;  // this shard's columns of the group's [T][G*hs]
     a.Op = (float*)(ws + L.op);
     a.ML = (float*)(ws + L.ml);
     a.T = d.T;
     a.S = d.S;
     a.chunk = d.C;
-    a.ldo = (int)d.hs;
+    a.ldo = (int)(G * d.hs);
     a.rank = (int)d.r;
     a.fold = (int)d.D;
     a.Hd = (int)d.Hd;
@@ -383,10 +415,13 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
     TIMED(c, TSP_K_ATTN, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 0, c.s)));
     if (plan.split) TIMED(c, TSP_K_MERGE, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 1, c.s)));
-    TIMED(c, TSP_K_OPROJ,
-          rc = acc_gemm(c, ws + L.o, d.hs, w + (size_t)3 * d.hs * d.h * d.es, (float*)(ws + L.y),
-                        j == 0, j == d.D - 1, x, x1));
-    if (rc) return rc;
+    if (gp == G - 1 || j == d.D - 1) {  // group complete: one O projection over its shards
+      TIMED(c, TSP_K_OPROJ,
+            rc = acc_gemm(c, ws + L.o, (gp + 1) * d.hs, G * d.hs, bo, (float*)(ws + L.y), gi == 0,
+                          j == d.D - 1, x, x1));
+      if (rc) return rc;
+      if (c.side) HIP_TRY(hipEventRecord(c.ev->freeO[gb], c.s));
+    }
     if (c.side) HIP_TRY(hipEventRecord(c.ev->freeA[s], c.s));
   }
   return TSP_OK;
@@ -396,42 +431,59 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
              void* out) {
   const Dims& d = *c.d;
   char* ws = c.ws;
-  const size_t wbytes = mlp_shard_elems(d) * d.es;
+  const size_t es = d.es;
+  const size_t w13bytes = 2 * (size_t)d.Fs * d.h * es;
+  const int64_t G = acc_group(d);
   TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.T, (int)d.h, d.eps, c.s)));
   for (int64_t t = 0; t < d.D; t++) {  // ring step t: shard (r + t) mod D
     const int64_t j = (d.r + t) % d.D;
     const int s = (int)(t & 1);
+    const int64_t gi = t / G, gp = t % G;
+    const int gb = (int)(gi & 1);
+    char* bw = ws + L.bw[gb];
     const char* w = (const char*)w_mlp[d.r];
+    // ---- copy stream: W1|W3 of a remote shard into the slot; every shard's
+    // W2 block next to its group's others.
+    if (c.side && t >= 3) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeM[s], 0));
+    if (c.side && gp == 0 && gi >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeW[gb], 0));
     if (t > 0) {
       char* slotw = ws + L.slotw[s];
-      if (c.side && t >= 3) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeM[s], 0));
-      int rc = debug_before_fill(c, slotw, wbytes);
+      int rc = debug_before_fill(c, slotw, w13bytes);
       if (rc) return rc;
-      HIP_TRY(hipMemcpyAsync(slotw, w_mlp[j], wbytes, hipMemcpyDeviceToDevice, c.cs));
-      if (c.side) {
-        HIP_TRY(hipEventRecord(c.ev->readyM[s], c.cs));
-        HIP_TRY(hipStreamWaitEvent(c.s, c.ev->readyM[s], 0));
-      }
+      HIP_TRY(hipMemcpyAsync(slotw, w_mlp[j], w13bytes, hipMemcpyDeviceToDevice, c.cs));
       w = slotw;
     }
+    if ((c.d->flags & TSP_F_POISON_SLOTS) && gp == 0)
+      HIP_TRY(launch_fill32(bw, d.dt == BF16 ? 0x7FC07FC0u : 0x7FC00000u,
+                            (size_t)d.h * G * d.Fs * es, c.cs));
+    HIP_TRY(hipMemcpy2DAsync(bw + gp * d.Fs * es, G * d.Fs * es, (const char*)w_mlp[j] + w13bytes,
+                             d.Fs * es, d.Fs * es, d.h, hipMemcpyDeviceToDevice, c.cs));
+    if (c.side) {
+      HIP_TRY(hipEventRecord(c.ev->readyM[s], c.cs));
+      HIP_TRY(hipStreamWaitEvent(c.s, c.ev->readyM[s], 0));
+    }
+    // ---- compute stream
     GemmArgs g = gemm_base();
     g.A = ws + L.xn;
     g.lda = d.h;
     g.B = w;
-    g.B3 = w + (size_t)d.Fs * d.h * d.es;
+    g.B3 = w + (size_t)d.Fs * d.h * es;
     g.ldb = d.h;
     g.M = (int)d.T;
     g.N = (int)d.Fs;
     g.K = (int)d.h;
-    g.C = ws + L.gg;
-    g.ldc = d.Fs;
+    g.C = ws + L.gg + gp * d.Fs * es;  // this shard's columns of the group's [T][G*Fs]
+    g.ldc = G * d.Fs;
     TIMED(c, TSP_K_W13, HIP_TRY(launch_gemm(d.dt, EPI_SWIGLU, g, c.s)));
     int rc = 0;
-    TIMED(c, TSP_K_W2,
-          rc = acc_gemm(c, ws + L.gg, d.Fs, w + (size_t)2 * d.Fs * d.h * d.es, (float*)(ws + L.y),
-                        t == 0, t == d.D - 1, x1, out));
-    if (rc) return rc;
-    if (c.side && t > 0) HIP_TRY(hipEventRecord(c.ev->freeM[s], c.s));
+    if (gp == G - 1 || t == d.D - 1) {  // group complete: one W2 projection over its shards
+      TIMED(c, TSP_K_W2,
+            rc = acc_gemm(c, ws + L.gg, (gp + 1) * d.Fs, G * d.Fs, bw, (float*)(ws + L.y), gi == 0,
+                          t == d.D - 1, x1, out));
+      if (rc) return rc;
+      if (c.side) HIP_TRY(hipEventRecord(c.ev->freeW[gb], c.s));
+    }
+    if (c.side) HIP_TRY(hipEventRecord(c.ev->freeM[s], c.s));
   }
   return TSP_OK;
 }

@@ -1172,9 +1172,9 @@ template <int EPI>
 static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
   struct Cand { int bm, bn; double eff; };
   const Cand single[] = {{256, 256, 1.0}, {256, 192, 0.95}, {128, 128, 0.55}};
-  const Cand dual[] = {{256, 128, 1.0}, {128, 64, 0.5}};
+  const Cand dual[] = {{256, 128, 1.0}, {128, 64, 0.5}, {128, 192, 0.8}};
   const Cand* cs = EPI == EPI_SWIGLU ? dual : single;
-  const int nc = EPI == EPI_SWIGLU ? 2 : 3;
+  const int nc = 3;
   int best = 0;
   double bt = 1e300;
   for (int c = 0; c < nc; c++) {
@@ -1185,8 +1185,15 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
 #ifndef TSP_ACC_SMALLK_TILE
 #define TSP_ACC_SMALLK_TILE 0
 #endif
+#ifndef TSP_W13_TILE
+#define TSP_W13_TILE 0
+#endif
   if constexpr (EPI == EPI_SWIGLU) {
+    if (TSP_W13_TILE == 1 && best != 1) best = 2;
+    if (TSP_W13_TILE == 2 && best != 1) best = 3;
     if (best == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
+    else if (best == 2) gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
+    else if (best == 3) gemm_go<bf16, 256, 192, EPI, 4, 2>(a, vec, s);
     else gemm_go<bf16, 128, 64, EPI>(a, vec, s);
   } else if ((EPI == EPI_ACC || EPI == EPI_RESID) && TSP_ACC_SMALLK_TILE != 0 && a.K <= 2048 &&
              best == 0) {
