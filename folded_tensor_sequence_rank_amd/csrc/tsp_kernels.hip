@@ -145,6 +145,20 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* __restrict__ x,
 // result holds one output row m and, per group of four registers, four
 // consecutive columns n: the epilogues use 4-wide loads and stores.
 // ---------------------------------------------------------------------------
+// XOR swizzle of the 16-byte chunk c in row r of an LDS tile with NCH chunks
+// per row.  The LDS has 64 banks of 4 bytes (256 bytes per sweep) and serves
+// a 16-byte read for 16 lanes at a time, so 16 consecutive rows read at one
+// logical chunk must land on 16 different 16-byte bank groups: the rows that
+// share a sweep position (r / (16 / NCH) for rows shorter than a sweep) get
+// different XOR terms.
+template <int NCH>
+__device__ __host__ inline int swz(int c, int r) {
+  if constexpr (NCH >= 16)
+    return c ^ (r & 15);
+  else
+    return c ^ ((r / (16 / NCH)) & (NCH - 1));
+}
+
 template <typename T, bool VEC>
 __device__ inline u32x4 load_chunk(const T* base, bool rowok, int64_t row, int64_t ld, int k,
                                    int K) {
@@ -284,15 +298,15 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < MB; i++) {
       const int row = wm * WM + i * 32 + lr;
-      af[set][i] = *(const frag*)(sA + row * 128 + ((c ^ (row & 7)) << 4) + w);
+      af[set][i] = *(const frag*)(sA + row * 128 + (swz<8>(c, row) << 4) + w);
     }
 #pragma unroll
     for (int j = 0; j < NB; j++) {
       const int row = wn * WN + j * 32 + lr;
-      bfr[set][j] = *(const frag*)(sB + row * 128 + ((c ^ (row & 7)) << 4) + w);
+      bfr[set][j] = *(const frag*)(sB + row * 128 + (swz<8>(c, row) << 4) + w);
       if (DUAL) {
         const int r3 = BN + row;
-        bf3[set][j] = *(const frag*)(sB + r3 * 128 + ((c ^ (r3 & 7)) << 4) + w);
+        bf3[set][j] = *(const frag*)(sB + r3 * 128 + (swz<8>(c, r3) << 4) + w);
       }
     }
   };
@@ -341,7 +355,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
     const brsrc rB = make_rsrc(B, (uint64_t)g.N * g.ldb * ES);
     const brsrc rB3 = make_rsrc(DUAL ? B3 : B, (uint64_t)g.N * g.ldb * ES);
     const int lrow = 8 * wave + (lane >> 3);
-    const int lc = (lane & 7) ^ (lrow & 7);  // logical chunk (row%8 == lrow%8)
+    // logical chunk of this lane's physical chunk lane%8 (round offsets RR*i
+    // are multiples of 16 rows, so the swizzle term depends on lrow only)
+    const int lc = swz<8>(lane & 7, lrow);
     uint32_t offA[AC], offB[BC];
 #pragma unroll
     for (int i = 0; i < AC; i++) {
@@ -433,12 +449,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < AC; i++) {
         const int id = tid + NT * i, row = id >> 3, c = id & 7;
-        *(u32x4*)(sA + row * 128 + ((c ^ (row & 7)) << 4)) = ra[i];
+        *(u32x4*)(sA + row * 128 + (swz<8>(c, row) << 4)) = ra[i];
       }
 #pragma unroll
       for (int i = 0; i < BC; i++) {
         const int id = tid + NT * i, row = id >> 3, c = id & 7;
-        *(u32x4*)(sB + row * 128 + ((c ^ (row & 7)) << 4)) = rb[i];
+        *(u32x4*)(sB + row * 128 + (swz<8>(c, row) << 4)) = rb[i];
       }
     };
     if (nk > 0) {
@@ -648,13 +664,7 @@ struct AttnTile {
 
 __device__ inline int kappa(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// XOR swizzle of the 16-byte chunk c in row r of an LDS tile with `nch`
-// chunks per row: rows of 128 bytes or more use r % nch; 64-byte rows (four
-// share one 256-byte bank sweep) use (r / 4) % 4.
-template <int NCH>
-__device__ inline int swz(int c, int r) {
-  return NCH >= 8 ? c ^ (r & (NCH - 1)) : c ^ ((r >> 2) & (NCH - 1));
-}
+
 
 __device__ __host__ inline int64_t qtile_kend(int64_t T, int qt, int64_t C, int rank, int fold) {
   const int64_t last = (T < (int64_t)qt * kBQ + kBQ ? T : (int64_t)qt * kBQ + kBQ) - 1;
