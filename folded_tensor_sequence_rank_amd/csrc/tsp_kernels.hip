@@ -205,6 +205,27 @@ __device__ inline void buffer_to_lds16(brsrc r, void* lds, uint32_t voff, uint32
 
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past any range: reads 0
 
+// Max and sum of a value with the lane 32 positions away, through the
+// cross-half lane swap (no LDS round trip): after the swap the two results
+// hold the lane's own value and its partner's, in an order that depends on
+// the half, so their max or sum is the same in both halves.
+__device__ inline float halves_max(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+#else
+  return x;
+#endif
+}
+__device__ inline float halves_sum(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+#else
+  return x;
+#endif
+}
+
 template <typename T>
 __device__ inline void store4(T* p, float a, float b, float c, float d) {
   if constexpr (sizeof(T) == 2) {
@@ -651,6 +672,12 @@ constexpr int kBKV = 64;   // keys per tile (largest; the 128-dim bf16 kernel us
 #ifndef TSP_ATTN128_BKV
 #define TSP_ATTN128_BKV 64   // keys per tile of the 128-dim bf16 kernel
 #endif
+#ifndef TSP_ATTN_VPRE
+#define TSP_ATTN_VPRE 2      // 16-key steps of V^T fragments read before the softmax
+#endif
+#ifndef TSP_ATTN_PERMLANE
+#define TSP_ATTN_PERMLANE 1  // cross-half max through the lane swap, not LDS
+#endif
 #ifndef TSP_ATTN128_WAVES
 #define TSP_ATTN128_WAVES 2  // waves per SIMD the 128-dim bf16 kernel is sized for
 #endif
@@ -866,11 +893,36 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     }
     __builtin_amdgcn_sched_barrier(0);
     if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    // V^T fragments of the whole tile, read while the products above run
+    // and the softmax below computes (the K fragments' registers are free).
+    auto vfrag = [&](int st, int d) {
+      int kk;  // first key (within the tile) this lane supplies at step st
+      if constexpr (M_::E == 8) {
+        kk = 16 * st + 8 * lg;
+      } else {
+        const int i = st & 15;
+        kk = 32 * (st >> 4) + 16 * (i >> 3) + 8 * lg + (i & 7);
+      }
+      const int byte = kk * ES;
+      const int c = byte >> 4, w = byte & 15;
+      const int drow = 32 * d + lr;
+      if (HD % 32 == 0 || drow < HD)
+        return *(const frag*)(sV + drow * VROWB + (swz<VCH>(c, drow) << 4) + w);
+      return frag{0};
+    };
+    constexpr int NVP = TSP_ATTN_VPRE < PK ? TSP_ATTN_VPRE : PK;  // steps read early
+    frag vpre[NVP > 0 ? NVP : 1][DB];
+#pragma unroll
+    for (int st = 0; st < NVP; st++)
+#pragma unroll
+      for (int d = 0; d < DB; d++) vpre[st][d] = vfrag(st, d);
+    if constexpr (NVP > 0) __builtin_amdgcn_sched_barrier(0);
     // Register i of block kb holds key k0 + 32kb + 16(i/8) + 8lg + i%8.
     float mt[QB];
 #pragma unroll
     for (int b = 0; b < QB; b++) {
-      float x = -INFINITY;
+      // four independent max chains (short dependency paths)
+      float xs[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       // key - k0 - 8lg = 32kb + 16(i/8) + i%8 must not exceed qpos - k0 - 8lg
       const int lim = max(-1, min(BKV, qpos[b] - k0)) - 8 * lg;
 #pragma unroll
@@ -880,9 +932,14 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
           if (MASK) {
             if (32 * kb + 16 * (i >> 3) + (i & 7) > lim) s[b][kb][i] = -INFINITY;
           }
-          x = fmaxf(x, s[b][kb][i]);
+          xs[i & 3] = fmaxf(xs[i & 3], s[b][kb][i]);
         }
+      float x = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+#if TSP_ATTN_PERMLANE
+      x = halves_max(x);
+#else
       x = fmaxf(x, __shfl_xor(x, 32));
+#endif
       mt[b] = x * cs;  // log2 units (scale > 0, so -inf stays -inf)
     }
     bool grow = false;
@@ -904,7 +961,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 #pragma unroll
     for (int b = 0; b < QB; b++) {
       const float nm = m[b] == -INFINITY ? 0.f : -m[b];
-      float ls = 0.f;
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sum chains
 #pragma unroll
       for (int st = 0; st < PK; st++) {
         if constexpr (M_::E == 8) {
@@ -912,47 +969,35 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 #pragma unroll
           for (int t = 0; t < 8; t++) {
             const float p = fast_exp2(fmaf(s[b][kb][i0 + t], cs, nm));
-            ls += p;
+            ls[t & 3] += p;
             pf[b][st][t] = (bf16)p;
           }
         } else {
           const float p = fast_exp2(fmaf(s[b][st >> 4][st & 15], cs, nm));
-          ls += p;
+          ls[st & 3] += p;
           pf[b][st] = p;
         }
       }
-      l[b] += ls;
+      l[b] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
     __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T . P^T
     if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < PK; st++) {
-      int kk;  // first key (within the tile) this lane supplies at step st
-      if constexpr (M_::E == 8) {
-        kk = 16 * st + 8 * lg;
-      } else {
-        const int i = st & 15;
-        kk = 32 * (st >> 4) + 16 * (i >> 3) + 8 * lg + (i & 7);
-      }
-      const int byte = kk * ES;
-      const int c = byte >> 4, w = byte & 15;
 #pragma unroll
       for (int d = 0; d < DB; d++) {
-        const int drow = 32 * d + lr;
-        frag vf;
-        if (HD % 32 == 0 || drow < HD)
-          vf = *(const frag*)(sV + drow * VROWB + (swz<VCH>(c, drow) << 4) + w);
-        else
-          vf = frag{0};
+        const frag vf = st < NVP ? vpre[st < NVP ? st : 0][d] : vfrag(st, d);
 #pragma unroll
         for (int b = 0; b < QB; b++) o[b][d] = M_::mma(vf, pf[b][st], o[b][d]);
       }
     }
+    if constexpr (NVP == 0) {
 #pragma unroll
-    for (int q = 0; q < PK * DB; q++) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 2);
+      for (int q = 0; q < PK * DB; q++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 2);
+      }
     }
     if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
@@ -995,7 +1040,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 
 #pragma unroll
   for (int b = 0; b < QB; b++) {
-    const float lt = l[b] + __shfl_xor(l[b], 32);
+    const float lt = halves_sum(l[b]);
     const int64_t row = row0 + 32 * b + lr;
     (void)kend_w;
     if (nseg == 1) {
