@@ -217,6 +217,16 @@ __device__ inline float halves_max(float x) {
   return x;
 #endif
 }
+// acc + v.x + v.y for a pair of bf16 values, in one instruction.
+__device__ inline float add_pair(bf16 x, bf16 y, float acc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {x, y}, one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
+#else
+  return acc + (float)x + (float)y;
+#endif
+}
 __device__ inline float halves_sum(float x) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -675,6 +685,9 @@ constexpr int kBKV = 64;   // keys per tile (largest; the 128-dim bf16 kernel us
 #ifndef TSP_ATTN_VPRE
 #define TSP_ATTN_VPRE 2      // 16-key steps of V^T fragments read before the softmax
 #endif
+#ifndef TSP_ATTN_ISSUE
+#define TSP_ATTN_ISSUE 0     // where the next tile's loads go: 0 top, 1 after S, 2 split
+#endif
 #ifndef TSP_ATTN_PERMLANE
 #define TSP_ATTN_PERMLANE 1  // cross-half max through the lane swap, not LDS
 #endif
@@ -832,22 +845,24 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     vkey[j] = c * V;
     voff[j] = (int)(((int64_t)d * a.S + c * V) * ES);
   }
-  auto issue = [&](int k0, int buf) {
+  // Loads [lo, hi) of this wave's KJ + VJ loads of a tile (K first).
+  auto issue_part = [&](int k0, int buf, int lo, int hi) {
     char* sK = smem + buf * STAGE;
     char* sV = sK + KT_BYTES;
 #pragma unroll
     for (int j = 0; j < KJ; j++) {
-      if (KI % 4 == 0 || wave + 4 * j < KI)
+      if (j >= lo && j < hi && (KI % 4 == 0 || wave + 4 * j < KI))
         buffer_to_lds16(rK, sK + (wave + 4 * j) * 1024, k0 + krow[j] < kend32 ? koff[j] : kOOB,
                         (uint32_t)(k0 * HD * ES));
     }
 #pragma unroll
     for (int j = 0; j < VJ; j++) {
-      if (VI % 4 == 0 || wave + 4 * j < VI)
+      if (KJ + j >= lo && KJ + j < hi && (VI % 4 == 0 || wave + 4 * j < VI))
         buffer_to_lds16(rV, sV + (wave + 4 * j) * 1024,
                         k0 + vkey[j] < kend32 ? (uint32_t)voff[j] : kOOB, (uint32_t)(k0 * ES));
     }
   };
+  auto issue = [&](int k0, int buf) { issue_part(k0, buf, 0, KJ + VJ); };
   // A V^T chunk that straddles kend was loaded whole: zero its keys >= kend.
   auto fixup = [&](int k0, int buf) {
     char* sV = smem + buf * STAGE + KT_BYTES;
@@ -862,7 +877,11 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   };
 
   const float cs = a.scale_log2;
-  auto compute = [&](int buf, int k0, auto mask_tag) {
+  // The next tile's loads are issued inside compute, spread over its phases
+  // (nk0 < 0: none), so that they do not queue up behind each other at the
+  // top of the tile.
+  constexpr int NL = KJ + VJ;
+  auto compute = [&](int buf, int k0, auto mask_tag, int nk0, int nbuf) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* sK = smem + buf * STAGE;
     const char* sV = sK + KT_BYTES;
@@ -893,6 +912,10 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     }
     __builtin_amdgcn_sched_barrier(0);
     if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    if (TSP_ATTN_ISSUE >= 1 && nk0 >= 0) {
+      issue_part(nk0, nbuf, 0, TSP_ATTN_ISSUE == 1 ? NL : NL / 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // V^T fragments of the whole tile, read while the products above run
     // and the softmax below computes (the K fragments' registers are free).
     auto vfrag = [&](int st, int d) {
@@ -981,6 +1004,10 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
       l[b] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (TSP_ATTN_ISSUE == 2 && nk0 >= 0) {
+      issue_part(nk0, nbuf, NL / 2, NL);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // O^T += V^T . P^T
     if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -1029,12 +1056,15 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
       fixup(k0, t % NSTAGE);
       __syncthreads();
     }
-    if (t + NSTAGE - 1 < ntiles) issue(k0 + (NSTAGE - 1) * BKV, (t + NSTAGE - 1) % NSTAGE);
+    const bool more = t + NSTAGE - 1 < ntiles;
+    const int nk0 = more ? k0 + (NSTAGE - 1) * BKV : -1, nbuf = (t + NSTAGE - 1) % NSTAGE;
+    if (more && (TSP_ATTN_ISSUE == 0 || k0 >= kend_w)) issue(nk0, nbuf);
+    const int cnk0 = TSP_ATTN_ISSUE == 0 ? -1 : nk0;
     if (k0 < kend_w) {
       if (!wfull || k0 + BKV - 1 > qmin_w)
-        compute(t % NSTAGE, k0, std::true_type{});
+        compute(t % NSTAGE, k0, std::true_type{}, cnk0, nbuf);
       else
-        compute(t % NSTAGE, k0, std::false_type{});
+        compute(t % NSTAGE, k0, std::false_type{}, cnk0, nbuf);
     }
   }
 
@@ -1074,6 +1104,362 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
         a.ML[2 * slot] = m[b];
         a.ML[2 * slot + 1] = lt;
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined attention for bf16 with 128-dim heads.  Same work
+// items, tiles, LDS layouts, masking and softmax as attn_kernel (one wave per
+// 32 queries, 64-key tiles, two workgroups per CU), but each wave overlaps
+// its own MFMAs with its softmax instead of alternating between them:
+//   phase A of tile t:  S(t+1) = K(t+1) . Q^T      with the exponentials of
+//                                                  tile t's second 32 keys
+//   phase B of tile t:  O^T += V^T(t) . P^T(t)     with the exponentials of
+//                                                  tile t+1's first 32 keys
+// The row max of S(t+1) is taken between the phases; the lazy rescale of O
+// (same 2^8 rule) is applied after phase B, once tile t's products are in.
+// K runs one tile ahead of V^T, so each has its own pair of LDS buffers:
+// iteration t reads K(t+1) and V^T(t) and loads K(t+2) and V^T(t+1), one
+// barrier per tile as before.
+// ---------------------------------------------------------------------------
+#ifndef TSP_ATTN_PIPE
+#define TSP_ATTN_PIPE 1  // use the pipelined kernel for bf16, head_dim 128
+#endif
+#ifndef TSP_PIPE_MODE
+#define TSP_PIPE_MODE 2  // 2: explicit per-MFMA groups; 1: group barriers
+#endif
+#ifndef TSP_ATTN_DOTSUM
+#define TSP_ATTN_DOTSUM 0  // 1: row sums from bf16 pairs (one instruction per two keys)
+#endif
+#ifndef TSP_PIPE_DIST
+#define TSP_PIPE_DIST 4    // LDS fragment reads kept in flight ahead of the MFMAs
+#endif
+#ifndef TSP_PIPE_VALU
+#define TSP_PIPE_VALU 4  // VALU instructions placed after each MFMA of a phase
+#endif
+
+__global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
+  typedef bf16 T;
+  typedef MF<bf16> M_;
+  typedef bf16x8 frag;
+  static_assert(kQB == 1 && kBQ == 128, "one 32-query block per wave");
+  constexpr int HD = 128, ES = 2, V = 8, BKV = 64;
+  constexpr int KROWB = HD * ES, KCH = KROWB / 16;   // K rows: 256 B
+  constexpr int VROWB = BKV * ES, VCH = VROWB / 16;  // V^T rows: 128 B
+  constexpr int KT = BKV * KROWB, VT = HD * VROWB;   // 16 KB per tile each
+  constexpr int QK = HD / 16, DB = HD / 32, PK = BKV / 16;
+  constexpr int KJ = KT / 4096, VJ = VT / 4096;      // 1 KB loads per wave per tile
+  __shared__ __attribute__((aligned(16))) char smem[2 * KT + 2 * VT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int head = blockIdx.x % a.Hd;
+  int qt, seg, nseg;
+  int64_t kend;
+  if (!decode_item(a, blockIdx.x / a.Hd, qt, seg, nseg, kend)) return;
+  const int kend32 = (int)kend;
+  const int kbeg = seg * a.lseg;
+  const int kfin = min(kend32, kbeg + a.lseg);
+  const int T32 = (int)a.T, C32 = (int)a.chunk;
+  const int row0 = qt * kBQ + wave * 32;
+  const bool qok = row0 + lr < T32;
+  const int qpos = qok ? (int)zig(row0 + lr, C32, a.rank, a.fold) : -1;
+  const bool wok = row0 < T32;
+  const bool wfull = row0 + 31 < T32;
+  const int kend_w = wok ? (int)zig(min(T32, row0 + 32) - 1, C32, a.rank, a.fold) + 1 : 0;
+  const int qmin_w = wok ? (int)zig(row0, C32, a.rank, a.fold) : 0;
+
+  const T* Qh = (const T*)a.Q + (int64_t)head * a.T * HD;
+  const T* Kh = (const T*)a.K + (int64_t)head * a.S * HD;
+  const T* Vh = (const T*)a.Vt + (int64_t)head * HD * a.S;
+  frag qf[QK];
+#pragma unroll
+  for (int ks = 0; ks < QK; ks++)
+    qf[ks] = qok ? *(const frag*)(Qh + (int64_t)(row0 + lr) * HD + ks * 16 + lg * 8) : frag{0};
+
+  // Direct loads, as in attn_kernel.
+  const brsrc rK = make_rsrc(Kh, (uint64_t)a.S * HD * ES);
+  const brsrc rV = make_rsrc(Vh, (uint64_t)HD * a.S * ES);
+  int krow[KJ], vkey[VJ];
+  uint32_t koff[KJ], voff[VJ];
+#pragma unroll
+  for (int j = 0; j < KJ; j++) {
+    const int b = (wave + 4 * j) * 1024 + 16 * lane;
+    const int r = b / KROWB, p = (b % KROWB) >> 4;
+    krow[j] = r;
+    koff[j] = (uint32_t)((r * HD + swz<KCH>(p, r) * V) * ES);
+  }
+#pragma unroll
+  for (int j = 0; j < VJ; j++) {
+    const int b = (wave + 4 * j) * 1024 + 16 * lane;
+    const int d = b / VROWB, p = (b % VROWB) >> 4;
+    const int c = swz<VCH>(p, d);
+    vkey[j] = c * V;
+    voff[j] = (uint32_t)(((int64_t)d * a.S + c * V) * ES);
+  }
+  char* const sK0 = smem;
+  char* const sV0 = smem + 2 * KT;
+  auto issueK = [&](int k0, int buf) {
+#pragma unroll
+    for (int j = 0; j < KJ; j++)
+      buffer_to_lds16(rK, sK0 + buf * KT + (wave + 4 * j) * 1024,
+                      k0 + krow[j] < kend32 ? koff[j] : kOOB, (uint32_t)(k0 * HD * ES));
+  };
+  auto issueV = [&](int k0, int buf) {
+#pragma unroll
+    for (int j = 0; j < VJ; j++)
+      buffer_to_lds16(rV, sV0 + buf * VT + (wave + 4 * j) * 1024,
+                      k0 + vkey[j] < kend32 ? voff[j] : kOOB, (uint32_t)(k0 * ES));
+  };
+  auto fixupV = [&](int k0, int buf) {
+    char* sV = sV0 + buf * VT;
+    const int first = kend32 - k0;
+    const int upto = min(BKV, (first + V - 1) / V * V);
+    for (int i = tid; i < HD * (upto - first); i += 256) {
+      const int d = i / (upto - first), key = first + i % (upto - first);
+      const int byte = key * ES;
+      *(T*)(sV + d * VROWB + (swz<VCH>(byte >> 4, d) << 4) + (byte & 15)) = from_f<T>(0.f);
+    }
+  };
+  // K fragment of 32-key block kb, k-step ks (rows fed in kappa order) and
+  // V^T fragment of d-block d, 16-key step st.
+  auto kfrag = [&](int buf, int kb, int ks) {
+    const int r = 32 * kb + kappa(lr);
+    return *(const frag*)(sK0 + buf * KT + r * KROWB + (swz<KCH>(2 * ks + lg, r) << 4));
+  };
+  auto vfrag = [&](int buf, int st, int d) {
+    const int r = 32 * d + lr;
+    return *(const frag*)(sV0 + buf * VT + r * VROWB + (swz<VCH>(2 * st + lg, r) << 4));
+  };
+
+  const float cs = a.scale_log2;
+  // Register i of block kb holds key k0 + 32kb + 16(i/8) + 8lg + i%8.
+  auto mask_rows = [&](f32x16* s, int k0) {
+    const int lim = max(-1, min(BKV, qpos - k0)) - 8 * lg;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        if (32 * kb + 16 * (i >> 3) + (i & 7) > lim) s[kb][i] = -INFINITY;
+  };
+  auto row_max = [&](const f32x16* s) {
+    float xs[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) xs[i & 3] = fmaxf(xs[i & 3], s[kb][i]);
+    return halves_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]))) * cs;
+  };
+  // P fragments of one 32-key block (16-key steps 2kb, 2kb+1).
+  // One element e of a P fragment and its part of the row sum.  With
+  // TSP_ATTN_DOTSUM the sum takes the bf16 values the V^T product uses, a
+  // pair per instruction once the pair's second element is in.
+  auto pel = [&](float x, float nm, frag& pv, int e, float* ls) {
+    const float p = fast_exp2(fmaf(x, cs, nm));
+    pv[e] = (bf16)p;
+#if TSP_ATTN_DOTSUM
+    if (e & 1) ls[(e >> 1) & 3] = add_pair(pv[e - 1], pv[e], ls[(e >> 1) & 3]);
+#else
+    ls[e & 3] += p;
+#endif
+  };
+  auto exps = [&](const f32x16& sb, float nm, frag& p0, frag& p1, float* ls) {
+#pragma unroll
+    for (int t = 0; t < 8; t++) pel(sb[t], nm, p0, t, ls);
+#pragma unroll
+    for (int t = 0; t < 8; t++) pel(sb[8 + t], nm, p1, t, ls);
+  };
+  // Keeps a phase's softmax results inside the phase: without it the
+  // compiler sinks the exponentials next to their later uses, out of the
+  // MFMA block they are meant to overlap.
+  auto pin = [](frag& p0, frag& p1, float* ls) {
+    asm volatile("" : "+v"(p0), "+v"(p1), "+v"(ls[0]), "+v"(ls[1]), "+v"(ls[2]), "+v"(ls[3]));
+  };
+  auto s_product = [&](int buf, f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+      s[kb] = f32x16{0};
+#pragma unroll
+      for (int ks = 0; ks < QK; ks++) s[kb] = M_::mma(kfrag(buf, kb, ks), qf[ks], s[kb]);
+    }
+  };
+  auto pv_product = [&](int buf, const frag* pf, f32x16* o) {
+#pragma unroll
+    for (int st = 0; st < PK; st++)
+#pragma unroll
+      for (int d = 0; d < DB; d++) o[d] = M_::mma(vfrag(buf, st, d), pf[st], o[d]);
+  };
+  // 16 MFMAs with their 16 fragment reads kept 4 ahead and TSP_PIPE_VALU
+  // VALU (or transcendental) instructions after each MFMA.
+#define TSP_PIPE_SCHED(id)                                        \
+  do {                                                            \
+    _Pragma("unroll") for (int q_ = 0; q_ < 4; q_++)              \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, id);         \
+    _Pragma("unroll") for (int q_ = 0; q_ < 16; q_++) {           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, id);         \
+      if (q_ < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, id); \
+      __builtin_amdgcn_sched_group_barrier(0x402, TSP_PIPE_VALU, id); \
+    }                                                             \
+  } while (0)
+
+  const int ntiles = (kfin - kbeg + BKV - 1) / BKV;
+  const int kw = min(kend_w, kfin);
+  const int ntw = kw > kbeg ? (kw - kbeg + BKV - 1) / BKV : 0;  // tiles this wave computes
+  auto needmask = [&](int k0) { return !wfull || k0 + BKV - 1 > qmin_w; };
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; d++) o[d] = f32x16{0};
+  frag pf[PK];    // P of the tile whose V^T product comes next
+  f32x16 sh;      // that tile's second 32-key block of S (exponentials pending)
+
+  // Prologue: K(0), V^T(0), K(1) in; S(0), its max and first-block P.
+  issueK(kbeg, 0);
+  issueV(kbeg, 0);
+  if (ntiles > 1) issueK(kbeg + BKV, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (ntw > 0) {
+    f32x16 s[2];
+    s_product(0, s);
+    if (needmask(kbeg)) mask_rows(s, kbeg);
+    m = row_max(s);
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    exps(s[0], m == -INFINITY ? 0.f : -m, pf[0], pf[1], ls);
+    l = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    sh = s[1];
+  }
+
+  for (int t = 0; t < ntiles; t++) {
+    const int k0 = kbeg + t * BKV;
+    // K(t+1) and V^T(t) have landed; every wave is done with K(t), V^T(t-1).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (k0 + BKV > kend32 && (kend32 % V) != 0) {  // last tile, V^T chunk straddles kend
+      fixupV(k0, t & 1);
+      __syncthreads();
+    }
+    if (t + 2 < ntiles) issueK(k0 + 2 * BKV, t & 1);
+    if (t + 1 < ntiles) issueV(k0 + BKV, (t + 1) & 1);
+    if (t >= ntw) continue;
+    const float nm = m == -INFINITY ? 0.f : -m;
+    if (t + 1 < ntw) {
+      // phase A
+      f32x16 s[2];
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#if TSP_PIPE_MODE == 2
+      // one group per MFMA: the MFMA, the fragment read four MFMAs ahead
+      // (the last four groups read phase B's first V^T fragments) and one
+      // element of the pending second block's softmax
+      const int kbuf = (t + 1) & 1, vbuf = t & 1;
+      constexpr int PD = TSP_PIPE_DIST;  // fragment reads in flight
+      frag kq[PD], vq[PD];
+#pragma unroll
+      for (int i = 0; i < PD; i++) kq[i] = kfrag(kbuf, i >> 3, i & 7);
+      s[0] = f32x16{0};
+      s[1] = f32x16{0};
+      __builtin_amdgcn_sched_barrier(0);
+      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const frag f = kq[i % PD];
+        if (i + PD < 16)
+          kq[i % PD] = kfrag(kbuf, (i + PD) >> 3, (i + PD) & 7);
+        else
+          vq[i + PD - 16] = vfrag(vbuf, (i + PD - 16) >> 2, (i + PD - 16) & 3);
+        s[i >> 3] = M_::mma(f, qf[i & 7], s[i >> 3]);
+        pel(sh[i], nm, pf[2 + (i >> 3)], i & 7, ls);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pin(pf[2], pf[3], ls);
+#else
+      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      s_product((t + 1) & 1, s);
+      exps(sh, nm, pf[2], pf[3], ls);
+      pin(pf[2], pf[3], ls);
+      TSP_PIPE_SCHED(1);
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      // row max of S(t+1), rescale factor
+      if (needmask(k0 + BKV)) mask_rows(s, k0 + BKV);
+      const float mt = row_max(s);
+      const bool grow = __any(mt > m + 8.0f);
+      const float mn = grow ? fmaxf(m, mt) : m;
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+      const float nm2 = mn == -INFINITY ? 0.f : -mn;
+      __builtin_amdgcn_sched_barrier(0);
+      // phase B
+      frag pn[2];
+      float ls2[4] = {0.f, 0.f, 0.f, 0.f};
+#if TSP_PIPE_MODE == 2
+      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const frag f = vq[i % PD];
+        if (i + PD < 16) vq[i % PD] = vfrag(vbuf, (i + PD) >> 2, (i + PD) & 3);
+        o[i & 3] = M_::mma(f, pf[i >> 2], o[i & 3]);
+        pel(s[0][i], nm2, pn[i >> 3], i & 7, ls2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pin(pn[0], pn[1], ls2);
+#else
+      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      pv_product(t & 1, pf, o);
+      exps(s[0], nm2, pn[0], pn[1], ls2);
+      pin(pn[0], pn[1], ls2);
+      TSP_PIPE_SCHED(2);
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+      if (grow) {
+#pragma unroll
+        for (int d = 0; d < DB; d++) o[d] *= alpha;
+        l *= alpha;
+      }
+      l += (ls2[0] + ls2[1]) + (ls2[2] + ls2[3]);
+      m = mn;
+      pf[0] = pn[0];
+      pf[1] = pn[1];
+      sh = s[1];
+    } else {
+      // this wave's last tile: the rest of its P, then its V^T product
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      exps(sh, nm, pf[2], pf[3], ls);
+      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      pv_product(t & 1, pf, o);
+    }
+  }
+#undef TSP_PIPE_SCHED
+
+  const float lt = halves_sum(l);
+  const int64_t row = row0 + lr;
+  if (nseg == 1) {
+    if (qok) {
+      const float inv = 1.0f / lt;
+      T* orow = (T*)a.O + row * a.ldo + head * HD;
+#pragma unroll
+      for (int d = 0; d < DB; d++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          store4<T>(orow + 32 * d + 8 * q + 4 * lg, o[d][4 * q] * inv, o[d][4 * q + 1] * inv,
+                    o[d][4 * q + 2] * inv, o[d][4 * q + 3] * inv);
+    }
+  } else {
+    const int64_t slot = (((int64_t)head * a.nqt + qt) * a.maxseg + seg) * kBQ + wave * 32 + lr;
+    float* op = a.Op + slot * HD;
+#pragma unroll
+    for (int d = 0; d < DB; d++)
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        *(float4*)(op + 32 * d + 8 * q + 4 * lg) =
+            make_float4(o[d][4 * q], o[d][4 * q + 1], o[d][4 * q + 2], o[d][4 * q + 3]);
+    if (lg == 0) {
+      a.ML[2 * slot] = m;
+      a.ML[2 * slot + 1] = lt;
     }
   }
 }
@@ -1290,7 +1676,10 @@ hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
 template <typename T, int HD>
 static void attn_go(const AttnArgs& a, const AttnPlan& p, int part, hipStream_t s) {
   if (part == 0) {
-    attn_kernel<T, HD><<<p.nitems * a.Hd, 256, 0, s>>>(a);
+    if (TSP_ATTN_PIPE && sizeof(T) == 2 && HD == 128)
+      attn_pipe_kernel<<<p.nitems * a.Hd, 256, 0, s>>>(a);
+    else
+      attn_kernel<T, HD><<<p.nitems * a.Hd, 256, 0, s>>>(a);
   } else if (p.split) {
     const int64_t n = (int64_t)a.Hd * a.T * (HD / 4);
     attn_combine_kernel<T, HD><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
