@@ -267,6 +267,12 @@ int debug_before_fill(Ctx& c, void* slot, size_t bytes) {
   return TSP_OK;
 }
 
+// The attention kernels read the other ranks' rows straight from the
+// gathered K/V when every zigzag chunk boundary falls on a 64-key tile
+// boundary (a tile then comes wholly from the rank's own rows or wholly from
+// the others'); otherwise those rows are first copied next to the rank's own.
+bool kv_in_place(const Dims& d) { return d.C % 64 == 0; }
+
 // Rows of the gathered K/V that rank r needs from the others: its causal
 // window is [0, (2D-r)C), minus its own chunks r and 2D-1-r.
 int copy_remote_kv(Ctx& c, const char* kv_block, char* slot) {
@@ -370,7 +376,9 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     char* slotkv = ws + L.slotkv[s];
     char* bo = ws + L.bo[gb];
     // ---- copy stream: receive shard j (Q|K|V into the slot, W_O next to
-    // its group's other W_O blocks) and the other ranks' K_j/V_j rows.
+    // its group's other W_O blocks); the other ranks' K_j/V_j rows are read
+    // in place from kv, or copied next to the rank's own rows when chunk
+    // boundaries do not fall on attention key tiles.
     if (c.side && j >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeA[s], 0));
     if (c.side && gp == 0 && gi >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeO[gb], 0));
     int rc = debug_before_fill(c, slotw, qkvbytes);
@@ -383,8 +391,11 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     if (j != d.r) HIP_TRY(hipMemcpyAsync(slotw, w_attn[j], qkvbytes, hipMemcpyDeviceToDevice, c.cs));
     HIP_TRY(hipMemcpy2DAsync(bo + gp * d.hs * es, G * d.hs * es, (const char*)w_attn[j] + qkvbytes,
                              d.hs * es, d.hs * es, d.h, hipMemcpyDeviceToDevice, c.cs));
-    rc = copy_remote_kv(c, (const char*)kv + (size_t)j * kvbytes, slotkv);
-    if (rc) return rc;
+    const char* kvj = (const char*)kv + (size_t)j * kvbytes;
+    if (!kv_in_place(d)) {
+      rc = copy_remote_kv(c, kvj, slotkv);
+      if (rc) return rc;
+    }
     if (c.side) {
       HIP_TRY(hipEventRecord(c.ev->readyA[s], c.cs));
       HIP_TRY(hipStreamWaitEvent(c.s, c.ev->readyA[s], 0));
@@ -398,6 +409,10 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     a.Q = ws + L.q;
     a.K = slotkv;
     a.Vt = slotkv + (size_t)d.Hd * d.S * d.d * es;
+    if (kv_in_place(d)) {
+      a.Kg = kvj;
+      a.Vtg = kvj + (size_t)d.Hd * d.S * d.d * es;
+    }
     a.O = ws + L.o + gp * d.hs * es;  // this shard's columns of the group's [T][G*hs]
     a.Op = (float*)(ws + L.op);
     a.ML = (float*)(ws + L.ml);

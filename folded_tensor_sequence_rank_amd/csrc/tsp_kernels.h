@@ -46,6 +46,11 @@ struct AttnArgs {
   const void* Q;   // [Hd][T][HD]
   const void* K;   // [Hd][S][HD]
   const void* Vt;  // [Hd][HD][S]
+  // Other ranks' rows read in place (same layouts as K / Vt), or null when K
+  // and Vt hold every row.  With them, K and Vt are read only in the rank's
+  // own chunks, and chunk boundaries fall on 64-key tile boundaries.
+  const void* Kg;
+  const void* Vtg;
   void* O;         // [T][ldo]; head t writes columns [t*HD, (t+1)*HD)
   float* Op;       // partial outputs of split items [Hd][nqt][maxseg][128][HD]
   float* ML;       // partial (max, sum) [Hd][nqt][maxseg][128][2]

@@ -702,6 +702,23 @@ struct AttnTile {
   static constexpr int WAVES = deep ? TSP_ATTN128_WAVES : 2;  // waves per SIMD
 };
 
+// Does the key tile starting at k0 lie in one of the rank's own chunks
+// (r and 2D-1-r), whose K/V rows come from the rank's own buffer when the
+// other ranks' rows are read in place?
+struct OwnChunks {
+  int lo1, hi1, lo2, hi2;
+  __device__ OwnChunks(const AttnArgs& a) {
+    const int c = (int)a.chunk;
+    lo1 = a.rank * c;
+    hi1 = lo1 + c;
+    lo2 = (2 * a.fold - 1 - a.rank) * c;
+    hi2 = lo2 + c;
+  }
+  __device__ bool operator()(int k0) const {
+    return (k0 >= lo1 && k0 < hi1) || (k0 >= lo2 && k0 < hi2);
+  }
+};
+
 __device__ inline int kappa(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 
@@ -825,8 +842,14 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   // [ii*1024, ii*1024+1024): lane l writes 16 bytes at physical chunk p of
   // row r, holding logical chunk p ^ (r % KCH) of key k0 + r.  Likewise for
   // V^T rows d (64 keys each).
-  const brsrc rK = make_rsrc(Kh, (uint64_t)a.S * HD * ES);
-  const brsrc rV = make_rsrc(Vh, (uint64_t)HD * a.S * ES);
+  const brsrc rK_own = make_rsrc(Kh, (uint64_t)a.S * HD * ES);
+  const brsrc rV_own = make_rsrc(Vh, (uint64_t)HD * a.S * ES);
+  const bool split_src = a.Kg != nullptr;
+  const OwnChunks own_tile(a);
+  const brsrc rKg = make_rsrc(split_src ? (const T*)a.Kg + (int64_t)head * a.S * HD : Kh,
+                              (uint64_t)a.S * HD * ES);
+  const brsrc rVg = make_rsrc(split_src ? (const T*)a.Vtg + (int64_t)head * HD * a.S : Vh,
+                              (uint64_t)HD * a.S * ES);
   constexpr int KJ = (KI + 3) / 4, VJ = (VI + 3) / 4;  // wave loads per tile per wave
   int krow[KJ], voff[VJ], vkey[VJ];
   uint32_t koff[KJ];
@@ -849,6 +872,9 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   auto issue_part = [&](int k0, int buf, int lo, int hi) {
     char* sK = smem + buf * STAGE;
     char* sV = sK + KT_BYTES;
+    const bool mine = !split_src || own_tile(k0);
+    const brsrc rK = mine ? rK_own : rKg;
+    const brsrc rV = mine ? rV_own : rVg;
 #pragma unroll
     for (int j = 0; j < KJ; j++) {
       if (j >= lo && j < hi && (KI % 4 == 0 || wave + 4 * j < KI))
@@ -1179,8 +1205,14 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     qf[ks] = qok ? *(const frag*)(Qh + (int64_t)(row0 + lr) * HD + ks * 16 + lg * 8) : frag{0};
 
   // Direct loads, as in attn_kernel.
-  const brsrc rK = make_rsrc(Kh, (uint64_t)a.S * HD * ES);
-  const brsrc rV = make_rsrc(Vh, (uint64_t)HD * a.S * ES);
+  const brsrc rK_own = make_rsrc(Kh, (uint64_t)a.S * HD * ES);
+  const brsrc rV_own = make_rsrc(Vh, (uint64_t)HD * a.S * ES);
+  const bool split_src = a.Kg != nullptr;
+  const OwnChunks own_tile(a);
+  const brsrc rKg = make_rsrc(split_src ? (const T*)a.Kg + (int64_t)head * a.S * HD : Kh,
+                              (uint64_t)a.S * HD * ES);
+  const brsrc rVg = make_rsrc(split_src ? (const T*)a.Vtg + (int64_t)head * HD * a.S : Vh,
+                              (uint64_t)HD * a.S * ES);
   int krow[KJ], vkey[VJ];
   uint32_t koff[KJ], voff[VJ];
 #pragma unroll
@@ -1201,12 +1233,14 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   char* const sK0 = smem;
   char* const sV0 = smem + 2 * KT;
   auto issueK = [&](int k0, int buf) {
+    const brsrc rK = !split_src || own_tile(k0) ? rK_own : rKg;
 #pragma unroll
     for (int j = 0; j < KJ; j++)
       buffer_to_lds16(rK, sK0 + buf * KT + (wave + 4 * j) * 1024,
                       k0 + krow[j] < kend32 ? koff[j] : kOOB, (uint32_t)(k0 * HD * ES));
   };
   auto issueV = [&](int k0, int buf) {
+    const brsrc rV = !split_src || own_tile(k0) ? rV_own : rVg;
 #pragma unroll
     for (int j = 0; j < VJ; j++)
       buffer_to_lds16(rV, sV0 + buf * VT + (wave + 4 * j) * 1024,

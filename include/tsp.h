@@ -13,10 +13,12 @@
  * locally (no all-reduce).
  *
  * This library computes rank r's share on one GPU.  The other ranks' weight
- * shards and the all-gathered K/V are ordinary device buffers; the library
- * streams them through two workspace slots with copies on a side stream that
- * overlap the compute, in place of the broadcast / all-gather / ring
- * transfers between GPUs.
+ * shards and the all-gathered K/V are ordinary device buffers.  The weight
+ * shards stream through two workspace slots with copies on a side stream that
+ * overlap the compute, in place of the broadcast / ring transfers between
+ * GPUs; the other ranks' K/V rows (the all-gather's payload) are read in
+ * place by the attention kernel when C is a multiple of 64, and otherwise
+ * copied into a slot next to the rank's own rows as well.
  *
  * ---------------------------------------------------------------------------
  * Notation: h hidden, H heads, d = h/H head dim, F FFN width, S sequence
@@ -153,9 +155,10 @@ int tsp_zigzag_positions(int64_t seq, int32_t fold, int32_t rank, int64_t* out);
  * Section 2, attention layers: for broadcast iteration j = 0..D-1 the packed
  * shard j is used (w_attn[r] is read in place, the others are copied into a
  * workspace slot on the side stream), the rank projects its own tokens to
- * Q_j/K_j/V_j, the other ranks' K_j/V_j rows the rank's causal window needs
- * (positions < (2D-r)*C) are copied from `kv` next to its own, zigzag-aware
- * causal flash attention runs over the full gathered K/V, and the partial
+ * Q_j/K_j/V_j, zigzag-aware causal flash attention runs over the gathered
+ * K/V (the rank's own rows from the projection, the other ranks' rows its
+ * causal window needs, positions < (2D-r)*C, from `kv`: read in place when
+ * C % 64 == 0, else first copied next to its own), and the partial
  * O-projection of head group j is accumulated locally in fp32.
  *   x      [T][h]   local rows in zigzag order
  *   g1     [h]      RMSNorm gain

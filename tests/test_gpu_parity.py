@@ -33,6 +33,8 @@ SMALL = {
     "tiny_fp32": TINY,
     "tiny_bf16": TINY.with_(dtype="bf16"),
     "bf16_d128_ragged": _cfg(hidden=512, n_heads=4),              # C=200, F/D=172
+    # C=256: other ranks' K/V rows are read in place (C % 64 == 0)
+    "bf16_d128_inplace": _cfg(hidden=512, n_heads=4, ffn=1376, seq=2048),
     "bf16_d128_ragged_lowres": _cfg(hidden=512, n_heads=4, x_std=0.02),
     "bf16_d64_lowres_gamma": _cfg(hidden=256, n_heads=4, head_dim=64, ffn=1024, seq=2048, fold=4,
                                   x_std=0.02, gamma="normal"),
@@ -137,11 +139,13 @@ def test_split_attention_items():
         _check(cfg, f"rank {r} x1", f64(x1), ref, xr, xr)
 
 
-def test_own_kv_rows_not_read():
+@pytest.mark.parametrize("case", ["bf16_d128_ragged", "bf16_d128_inplace"])
+def test_own_kv_rows_not_read(case):
     """The rank's own rows in the gathered K/V stay NaN: it must use the rows
-    it projects itself."""
-    cfg = SMALL["bf16_d128_ragged"]
-    say("[gpu] own K/V rows are computed, not read")
+    it projects itself (other ranks' rows copied, C=200, or read in place,
+    C=256)."""
+    cfg = SMALL[case]
+    say(f"[gpu] own K/V rows are computed, not read ({case})")
     w, x_full, L, xs, pos = _setup(cfg)
     r = 2
     kv = new_kv(cfg)
