@@ -707,7 +707,7 @@ struct AttnTile {
 // other ranks' rows are read in place?
 struct OwnChunks {
   int lo1, hi1, lo2, hi2;
-  __device__ OwnChunks(const AttnArgs& a) {
+  __device__ __attribute__((always_inline)) OwnChunks(const AttnArgs& a) {
     const int c = (int)a.chunk;
     lo1 = a.rank * c;
     hi1 = lo1 + c;
@@ -733,7 +733,7 @@ __device__ __host__ inline int64_t qtile_kend(int64_t T, int qt, int64_t C, int 
 // segment), so the workgroups in flight read the same key range and share it
 // in L2.  Query tile qt has a segment s iff its causal end kend(qt) > s*lseg;
 // kend grows with qt, so those tiles form a suffix [q0(s), nqt).
-__device__ inline int first_tile_past(const AttnArgs& a, int64_t lo) {
+__device__ __attribute__((always_inline)) inline int first_tile_past(const AttnArgs& a, int64_t lo) {
   int l = 0, h = a.nqt;  // smallest qt with kend(qt) > lo
   while (l < h) {
     const int mid = (l + h) >> 1;
@@ -745,7 +745,7 @@ __device__ inline int first_tile_past(const AttnArgs& a, int64_t lo) {
   return l;
 }
 
-__device__ inline bool decode_item(const AttnArgs& a, int item, int& qt, int& seg, int& nseg,
+__device__ __attribute__((always_inline)) inline bool decode_item(const AttnArgs& a, int item, int& qt, int& seg, int& nseg,
                                    int64_t& kend) {
   for (seg = 0; seg < a.maxseg; seg++) {
     const int cnt = a.nqt - first_tile_past(a, (int64_t)seg * a.lseg);
@@ -842,14 +842,10 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   // [ii*1024, ii*1024+1024): lane l writes 16 bytes at physical chunk p of
   // row r, holding logical chunk p ^ (r % KCH) of key k0 + r.  Likewise for
   // V^T rows d (64 keys each).
-  const brsrc rK_own = make_rsrc(Kh, (uint64_t)a.S * HD * ES);
-  const brsrc rV_own = make_rsrc(Vh, (uint64_t)HD * a.S * ES);
   const bool split_src = a.Kg != nullptr;
   const OwnChunks own_tile(a);
-  const brsrc rKg = make_rsrc(split_src ? (const T*)a.Kg + (int64_t)head * a.S * HD : Kh,
-                              (uint64_t)a.S * HD * ES);
-  const brsrc rVg = make_rsrc(split_src ? (const T*)a.Vtg + (int64_t)head * HD * a.S : Vh,
-                              (uint64_t)HD * a.S * ES);
+  const T* Kgh = split_src ? (const T*)a.Kg + (int64_t)head * a.S * HD : Kh;
+  const T* Vgh = split_src ? (const T*)a.Vtg + (int64_t)head * HD * a.S : Vh;
   constexpr int KJ = (KI + 3) / 4, VJ = (VI + 3) / 4;  // wave loads per tile per wave
   int krow[KJ], voff[VJ], vkey[VJ];
   uint32_t koff[KJ];
@@ -873,8 +869,8 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     char* sK = smem + buf * STAGE;
     char* sV = sK + KT_BYTES;
     const bool mine = !split_src || own_tile(k0);
-    const brsrc rK = mine ? rK_own : rKg;
-    const brsrc rV = mine ? rV_own : rVg;
+    const brsrc rK = make_rsrc(mine ? Kh : Kgh, (uint64_t)a.S * HD * ES);
+    const brsrc rV = make_rsrc(mine ? Vh : Vgh, (uint64_t)HD * a.S * ES);
 #pragma unroll
     for (int j = 0; j < KJ; j++) {
       if (j >= lo && j < hi && (KI % 4 == 0 || wave + 4 * j < KI))
@@ -1152,17 +1148,11 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 #ifndef TSP_ATTN_PIPE
 #define TSP_ATTN_PIPE 1  // use the pipelined kernel for bf16, head_dim 128
 #endif
-#ifndef TSP_PIPE_MODE
-#define TSP_PIPE_MODE 2  // 2: explicit per-MFMA groups; 1: group barriers
-#endif
 #ifndef TSP_ATTN_DOTSUM
 #define TSP_ATTN_DOTSUM 0  // 1: row sums from bf16 pairs (one instruction per two keys)
 #endif
 #ifndef TSP_PIPE_DIST
 #define TSP_PIPE_DIST 4    // LDS fragment reads kept in flight ahead of the MFMAs
-#endif
-#ifndef TSP_PIPE_VALU
-#define TSP_PIPE_VALU 4  // VALU instructions placed after each MFMA of a phase
 #endif
 
 __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
@@ -1205,14 +1195,10 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     qf[ks] = qok ? *(const frag*)(Qh + (int64_t)(row0 + lr) * HD + ks * 16 + lg * 8) : frag{0};
 
   // Direct loads, as in attn_kernel.
-  const brsrc rK_own = make_rsrc(Kh, (uint64_t)a.S * HD * ES);
-  const brsrc rV_own = make_rsrc(Vh, (uint64_t)HD * a.S * ES);
   const bool split_src = a.Kg != nullptr;
   const OwnChunks own_tile(a);
-  const brsrc rKg = make_rsrc(split_src ? (const T*)a.Kg + (int64_t)head * a.S * HD : Kh,
-                              (uint64_t)a.S * HD * ES);
-  const brsrc rVg = make_rsrc(split_src ? (const T*)a.Vtg + (int64_t)head * HD * a.S : Vh,
-                              (uint64_t)HD * a.S * ES);
+  const T* Kgh = split_src ? (const T*)a.Kg + (int64_t)head * a.S * HD : Kh;
+  const T* Vgh = split_src ? (const T*)a.Vtg + (int64_t)head * HD * a.S : Vh;
   int krow[KJ], vkey[VJ];
   uint32_t koff[KJ], voff[VJ];
 #pragma unroll
@@ -1232,19 +1218,32 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   }
   char* const sK0 = smem;
   char* const sV0 = smem + 2 * KT;
+  // Tiles wholly below kend need no per-lane range selects.
   auto issueK = [&](int k0, int buf) {
-    const brsrc rK = !split_src || own_tile(k0) ? rK_own : rKg;
+    const brsrc rK = make_rsrc(!split_src || own_tile(k0) ? Kh : Kgh, (uint64_t)a.S * HD * ES);
+    if (k0 + BKV <= kend32) {
 #pragma unroll
-    for (int j = 0; j < KJ; j++)
-      buffer_to_lds16(rK, sK0 + buf * KT + (wave + 4 * j) * 1024,
-                      k0 + krow[j] < kend32 ? koff[j] : kOOB, (uint32_t)(k0 * HD * ES));
+      for (int j = 0; j < KJ; j++)
+        buffer_to_lds16(rK, sK0 + buf * KT + (wave + 4 * j) * 1024, koff[j], (uint32_t)(k0 * HD * ES));
+    } else {
+#pragma unroll
+      for (int j = 0; j < KJ; j++)
+        buffer_to_lds16(rK, sK0 + buf * KT + (wave + 4 * j) * 1024,
+                        k0 + krow[j] < kend32 ? koff[j] : kOOB, (uint32_t)(k0 * HD * ES));
+    }
   };
   auto issueV = [&](int k0, int buf) {
-    const brsrc rV = !split_src || own_tile(k0) ? rV_own : rVg;
+    const brsrc rV = make_rsrc(!split_src || own_tile(k0) ? Vh : Vgh, (uint64_t)HD * a.S * ES);
+    if (k0 + BKV <= kend32) {
 #pragma unroll
-    for (int j = 0; j < VJ; j++)
-      buffer_to_lds16(rV, sV0 + buf * VT + (wave + 4 * j) * 1024,
-                      k0 + vkey[j] < kend32 ? voff[j] : kOOB, (uint32_t)(k0 * ES));
+      for (int j = 0; j < VJ; j++)
+        buffer_to_lds16(rV, sV0 + buf * VT + (wave + 4 * j) * 1024, voff[j], (uint32_t)(k0 * ES));
+    } else {
+#pragma unroll
+      for (int j = 0; j < VJ; j++)
+        buffer_to_lds16(rV, sV0 + buf * VT + (wave + 4 * j) * 1024,
+                        k0 + vkey[j] < kend32 ? voff[j] : kOOB, (uint32_t)(k0 * ES));
+    }
   };
   auto fixupV = [&](int k0, int buf) {
     char* sV = sV0 + buf * VT;
@@ -1258,13 +1257,21 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   };
   // K fragment of 32-key block kb, k-step ks (rows fed in kappa order) and
   // V^T fragment of d-block d, 16-key step st.
+  // The lane-dependent part of each fragment address is computed once; the
+  // buffer, block and d offsets are compile-time and become the reads'
+  // immediate offsets (the swizzle terms do not depend on them: 32-row blocks
+  // leave r % 16 and (r / 2) % 8 unchanged).
+  int koffl[QK], voffl[PK];
+#pragma unroll
+  for (int ks = 0; ks < QK; ks++)
+    koffl[ks] = kappa(lr) * KROWB + (swz<KCH>(2 * ks + lg, kappa(lr)) << 4);
+#pragma unroll
+  for (int st = 0; st < PK; st++) voffl[st] = lr * VROWB + (swz<VCH>(2 * st + lg, lr) << 4);
   auto kfrag = [&](int buf, int kb, int ks) {
-    const int r = 32 * kb + kappa(lr);
-    return *(const frag*)(sK0 + buf * KT + r * KROWB + (swz<KCH>(2 * ks + lg, r) << 4));
+    return *(const frag*)(sK0 + buf * KT + kb * 32 * KROWB + koffl[ks]);
   };
   auto vfrag = [&](int buf, int st, int d) {
-    const int r = 32 * d + lr;
-    return *(const frag*)(sV0 + buf * VT + r * VROWB + (swz<VCH>(2 * st + lg, r) << 4));
+    return *(const frag*)(sV0 + buf * VT + d * 32 * VROWB + voffl[st]);
   };
 
   const float cs = a.scale_log2;
@@ -1324,18 +1331,6 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
 #pragma unroll
       for (int d = 0; d < DB; d++) o[d] = M_::mma(vfrag(buf, st, d), pf[st], o[d]);
   };
-  // 16 MFMAs with their 16 fragment reads kept 4 ahead and TSP_PIPE_VALU
-  // VALU (or transcendental) instructions after each MFMA.
-#define TSP_PIPE_SCHED(id)                                        \
-  do {                                                            \
-    _Pragma("unroll") for (int q_ = 0; q_ < 4; q_++)              \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, id);         \
-    _Pragma("unroll") for (int q_ = 0; q_ < 16; q_++) {           \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, id);         \
-      if (q_ < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, id); \
-      __builtin_amdgcn_sched_group_barrier(0x402, TSP_PIPE_VALU, id); \
-    }                                                             \
-  } while (0)
 
   const int ntiles = (kfin - kbeg + BKV - 1) / BKV;
   const int kw = min(kend_w, kfin);
@@ -1366,28 +1361,30 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     sh = s[1];
   }
 
+  // Unrolled by two so that the buffer parity P = t & 1 is known in each copy
+  // and the buffer offsets fold into the LDS reads' immediate offsets.
+#pragma unroll 2
   for (int t = 0; t < ntiles; t++) {
+    const int P = t & 1;
     const int k0 = kbeg + t * BKV;
     // K(t+1) and V^T(t) have landed; every wave is done with K(t), V^T(t-1).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (k0 + BKV > kend32 && (kend32 % V) != 0) {  // last tile, V^T chunk straddles kend
-      fixupV(k0, t & 1);
+      fixupV(k0, P);
       __syncthreads();
     }
-    if (t + 2 < ntiles) issueK(k0 + 2 * BKV, t & 1);
-    if (t + 1 < ntiles) issueV(k0 + BKV, (t + 1) & 1);
+    if (t + 2 < ntiles) issueK(k0 + 2 * BKV, P);
+    if (t + 1 < ntiles) issueV(k0 + BKV, 1 - P);
     if (t >= ntw) continue;
     const float nm = m == -INFINITY ? 0.f : -m;
     if (t + 1 < ntw) {
-      // phase A
+      // phase A: one group per MFMA -- the MFMA, the fragment read PD MFMAs
+      // ahead (the last groups read phase B's first V^T fragments) and one
+      // element of the pending second block's softmax
       f32x16 s[2];
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#if TSP_PIPE_MODE == 2
-      // one group per MFMA: the MFMA, the fragment read four MFMAs ahead
-      // (the last four groups read phase B's first V^T fragments) and one
-      // element of the pending second block's softmax
-      const int kbuf = (t + 1) & 1, vbuf = t & 1;
+      const int kbuf = 1 - P, vbuf = P;
       constexpr int PD = TSP_PIPE_DIST;  // fragment reads in flight
       frag kq[PD], vq[PD];
 #pragma unroll
@@ -1408,13 +1405,6 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       pin(pf[2], pf[3], ls);
-#else
-      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-      s_product((t + 1) & 1, s);
-      exps(sh, nm, pf[2], pf[3], ls);
-      pin(pf[2], pf[3], ls);
-      TSP_PIPE_SCHED(1);
-#endif
       __builtin_amdgcn_sched_barrier(0);
       if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
       l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -1426,10 +1416,9 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
       const float nm2 = mn == -INFINITY ? 0.f : -mn;
       __builtin_amdgcn_sched_barrier(0);
-      // phase B
+      // phase B: the V^T(t) products with the first block of S(t+1)'s softmax
       frag pn[2];
       float ls2[4] = {0.f, 0.f, 0.f, 0.f};
-#if TSP_PIPE_MODE == 2
       if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 16; i++) {
@@ -1440,13 +1429,6 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       pin(pn[0], pn[1], ls2);
-#else
-      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-      pv_product(t & 1, pf, o);
-      exps(s[0], nm2, pn[0], pn[1], ls2);
-      pin(pn[0], pn[1], ls2);
-      TSP_PIPE_SCHED(2);
-#endif
       __builtin_amdgcn_sched_barrier(0);
       if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
       if (grow) {
@@ -1464,10 +1446,9 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
       exps(sh, nm, pf[2], pf[3], ls);
       l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      pv_product(t & 1, pf, o);
+      pv_product(P, pf, o);
     }
   }
-#undef TSP_PIPE_SCHED
 
   const float lt = halves_sum(l);
   const int64_t row = row0 + lr;
