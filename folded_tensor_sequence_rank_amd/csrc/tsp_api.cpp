@@ -428,6 +428,9 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     a.maxseg = plan.maxseg;
     a.nitems = plan.nitems;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
+    // Largest block sum of exponentials before the softmax reference is
+    // raised: 2^64 keeps every term far from fp32/bf16 overflow.
+    a.sum_cap = (d.flags & TSP_F_RESCALE_TEST) ? 2.0f : 18446744073709551616.0f;
     TIMED(c, TSP_K_ATTN, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 0, c.s)));
     if (plan.split) TIMED(c, TSP_K_MERGE, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 1, c.s)));
     if (gp == G - 1 || j == d.D - 1) {  // group complete: one O projection over its shards

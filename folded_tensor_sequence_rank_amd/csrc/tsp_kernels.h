@@ -58,6 +58,7 @@ struct AttnArgs {
   int ldo, rank, fold, Hd;
   int nqt, lseg, maxseg, nitems;
   float scale_log2;  // log2(e) / sqrt(HD)
+  float sum_cap;     // largest 32-key block sum of exponentials before the reference max is raised
 };
 
 // Attention work plan for one head group (a deterministic function of the dims).

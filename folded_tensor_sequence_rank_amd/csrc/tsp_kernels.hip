@@ -1148,6 +1148,9 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 #ifndef TSP_ATTN_PIPE
 #define TSP_ATTN_PIPE 1  // use the pipelined kernel for bf16, head_dim 128
 #endif
+#ifndef TSP_ATTN_SUMCHECK
+#define TSP_ATTN_SUMCHECK 1  // lazy softmax reference checked on block sums (no per-tile max)
+#endif
 #ifndef TSP_ATTN_DOTSUM
 #define TSP_ATTN_DOTSUM 0  // 1: row sums from bf16 pairs (one instruction per two keys)
 #endif
@@ -1275,6 +1278,12 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   };
 
   const float cs = a.scale_log2;
+  const float kSumCap = a.sum_cap;
+  // Online softmax state: reference max m (log2 units), row sum l, O^T.
+  float m = -INFINITY, l = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; d++) o[d] = f32x16{0};
   // Register i of block kb holds key k0 + 32kb + 16(i/8) + 8lg + i%8.
   auto mask_rows = [&](f32x16* s, int k0) {
     const int lim = max(-1, min(BKV, qpos - k0)) - 8 * lg;
@@ -1317,6 +1326,27 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   auto pin = [](frag& p0, frag& p1, float* ls) {
     asm volatile("" : "+v"(p0), "+v"(p1), "+v"(ls[0]), "+v"(ls[1]), "+v"(ls[2]), "+v"(ls[3]));
   };
+  // Row max of one 32-key block, in log2 units.
+  auto block_max = [&](const f32x16& sb) {
+    float xs[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int i = 0; i < 16; i++) xs[i & 3] = fmaxf(xs[i & 3], sb[i]);
+    return halves_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]))) * cs;
+  };
+  auto scale_frag = [](frag& pv, float alpha) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) pv[e] = (bf16)((float)pv[e] * alpha);
+  };
+  // Raise the reference max to mn: rescale O, the row sum and the P blocks
+  // already formed (npf of them, in pf) by 2^(m - mn).
+  auto raise_ref = [&](float mn, frag* pv, int npf) {
+    const float alpha = m == -INFINITY ? 1.f : fast_exp2(m - mn);
+#pragma unroll
+    for (int d = 0; d < DB; d++) o[d] *= alpha;
+    l *= alpha;
+    for (int q = 0; q < npf; q++) scale_frag(pv[q], alpha);
+    m = mn;
+  };
   auto s_product = [&](int buf, f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
@@ -1337,10 +1367,6 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   const int ntw = kw > kbeg ? (kw - kbeg + BKV - 1) / BKV : 0;  // tiles this wave computes
   auto needmask = [&](int k0) { return !wfull || k0 + BKV - 1 > qmin_w; };
 
-  float m = -INFINITY, l = 0.f;
-  f32x16 o[DB];
-#pragma unroll
-  for (int d = 0; d < DB; d++) o[d] = f32x16{0};
   frag pf[PK];    // P of the tile whose V^T product comes next
   f32x16 sh;      // that tile's second 32-key block of S (exponentials pending)
 
@@ -1407,6 +1433,28 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       pin(pf[2], pf[3], ls);
       __builtin_amdgcn_sched_barrier(0);
       if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+#if TSP_ATTN_SUMCHECK
+      {
+        // The block's exponentials used the running reference m.  A score
+        // more than 2^64 above it (or a non-finite sum) is caught on the
+        // block sum and repaired here: raise m to the block's max, rescale,
+        // redo the block.
+        float lsa = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        if (__any(!(lsa <= kSumCap))) {
+          raise_ref(fmaxf(m, block_max(sh)), pf, 2);
+          float lr4[4] = {0.f, 0.f, 0.f, 0.f};
+          const float nmr = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+          for (int t8 = 0; t8 < 8; t8++) pel(sh[t8], nmr, pf[2], t8, lr4);
+#pragma unroll
+          for (int t8 = 0; t8 < 8; t8++) pel(sh[8 + t8], nmr, pf[3], t8, lr4);
+          lsa = (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]);
+        }
+        l += lsa;
+      }
+      if (needmask(k0 + BKV)) mask_rows(s, k0 + BKV);
+      const float nm2 = m == -INFINITY ? 0.f : -m;
+#else
       l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       // row max of S(t+1), rescale factor
       if (needmask(k0 + BKV)) mask_rows(s, k0 + BKV);
@@ -1415,6 +1463,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       const float mn = grow ? fmaxf(m, mt) : m;
       const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
       const float nm2 = mn == -INFINITY ? 0.f : -mn;
+#endif
       __builtin_amdgcn_sched_barrier(0);
       // phase B: the V^T(t) products with the first block of S(t+1)'s softmax
       frag pn[2];
@@ -1431,6 +1480,24 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       pin(pn[0], pn[1], ls2);
       __builtin_amdgcn_sched_barrier(0);
       if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+#if TSP_ATTN_SUMCHECK
+      {
+        float lsb = (ls2[0] + ls2[1]) + (ls2[2] + ls2[3]);
+        if (__any(!(lsb <= kSumCap))) {
+          // O already holds tile t's products (formed with the old m);
+          // take the max of both blocks of S(t+1) so its second block passes
+          raise_ref(fmaxf(m, row_max(s)), pf, 0);
+          float lr4[4] = {0.f, 0.f, 0.f, 0.f};
+          const float nmr = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+          for (int t8 = 0; t8 < 8; t8++) pel(s[0][t8], nmr, pn[0], t8, lr4);
+#pragma unroll
+          for (int t8 = 0; t8 < 8; t8++) pel(s[0][8 + t8], nmr, pn[1], t8, lr4);
+          lsb = (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]);
+        }
+        l += lsb;
+      }
+#else
       if (grow) {
 #pragma unroll
         for (int d = 0; d < DB; d++) o[d] *= alpha;
@@ -1438,6 +1505,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       }
       l += (ls2[0] + ls2[1]) + (ls2[2] + ls2[3]);
       m = mn;
+#endif
       pf[0] = pn[0];
       pf[1] = pn[1];
       sh = s[1];
@@ -1445,7 +1513,16 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       // this wave's last tile: the rest of its P, then its V^T product
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
       exps(sh, nm, pf[2], pf[3], ls);
-      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      float lsa = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#if TSP_ATTN_SUMCHECK
+      if (__any(!(lsa <= kSumCap))) {
+        raise_ref(fmaxf(m, block_max(sh)), pf, 2);
+        float lr4[4] = {0.f, 0.f, 0.f, 0.f};
+        exps(sh, m == -INFINITY ? 0.f : -m, pf[2], pf[3], lr4);
+        lsa = (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]);
+      }
+#endif
+      l += lsa;
       pv_product(P, pf, o);
     }
   }
@@ -1647,6 +1724,7 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
   if constexpr (EPI == EPI_SWIGLU) {
     if (TSP_W13_TILE == 1 && best != 1) best = 2;
     if (TSP_W13_TILE == 2 && best != 1) best = 3;
+    if (TSP_W13_TILE == 3) best = 0;
     if (best == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
     else if (best == 2) gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
     else if (best == 3) gemm_go<bf16, 256, 192, EPI, 4, 2>(a, vec, s);

@@ -24,6 +24,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "tsp.h")
 TSP_BF16, TSP_F32 = 0, 1
 TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV = 1, 2, 3, 4
 TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP, TSP_F_PROFILE = 1, 2, 4, 8
+TSP_F_RESCALE_TEST = 16
 KERNELS = ["rmsnorm", "qkv", "attn", "merge", "oproj", "w13", "w2"]  # TSP_K_* order
 STATUS = {0: "TSP_OK", -1: "TSP_E_INVAL", -2: "TSP_E_SHAPE", -3: "TSP_E_ALIGN",
           -4: "TSP_E_WORKSPACE", -5: "TSP_E_DTYPE", -6: "TSP_E_HIP"}

@@ -104,12 +104,17 @@ enum {
 enum { TSP_WS_ATTN = 1, TSP_WS_MLP = 2, TSP_WS_LAYER = 3, TSP_WS_KV = 4 };
 
 /* Debug flags (tsp_dims.flags).  Results must be identical with or without
- * them; they exist to expose missing stream hand-offs in tests. */
+ * the first four; they exist to expose missing stream hand-offs in tests.
+ * TSP_F_RESCALE_TEST changes only the rounding: the bf16 attention with
+ * 128-dim heads keeps a lazy softmax reference max and raises it when a
+ * 32-key block's exponentials sum past 2^64; with this flag the bound is 2,
+ * so the rescale path runs on ordinary inputs. */
 enum {
   TSP_F_DELAY_COPY = 1u,   /* a bounded spin kernel runs on the copy stream before each copy */
   TSP_F_POISON_SLOTS = 2u, /* each slot is filled with NaN before it is refilled */
   TSP_F_NO_OVERLAP = 4u,   /* run the copies in order on the compute stream */
-  TSP_F_PROFILE = 8u       /* time each kernel launch with HIP events (tsp_profile_read) */
+  TSP_F_PROFILE = 8u,      /* time each kernel launch with HIP events (tsp_profile_read) */
+  TSP_F_RESCALE_TEST = 16u /* softmax rescale bound 2 instead of 2^64 (see above) */
 };
 
 /* Kernel classes reported by tsp_profile_read. */

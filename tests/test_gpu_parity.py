@@ -139,6 +139,27 @@ def test_split_attention_items():
         _check(cfg, f"rank {r} x1", f64(x1), ref, xr, xr)
 
 
+@pytest.mark.parametrize("case", ["bf16_d128_ragged", "bf16_d128_inplace", "split"])
+def test_softmax_rescale_path(case):
+    """TSP_F_RESCALE_TEST lowers the bound at which the 128-dim bf16
+    attention raises its lazy softmax reference from 2^64 to 2, so the rescale
+    path (O, row sum and the P block already formed rescaled, the block
+    redone) runs on most tiles; every rank must still match the oracle."""
+    from folded_tensor_sequence_rank_amd import tsp
+    cfg = (SMALL[case] if case != "split" else
+           _cfg(hidden=512, n_heads=4, head_dim=128, ffn=1024, seq=8192, fold=2))
+    say(f"[gpu] softmax rescale path ({case})")
+    w, x_full, L, xs, pos = _setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    for r in range(cfg.fold):
+        x1 = RankRun(cfg, r, flags=tsp.TSP_F_RESCALE_TEST).attn(xs[r], L, kv)
+        torch.cuda.synchronize()
+        ref = O.attention_block_rows(x_full, w, cfg.n_heads, cfg.eps, pos[r])
+        xr = x_full[pos[r]].astype(np.float64)
+        _check(cfg, f"rank {r} x1", f64(x1), ref, xr, xr)
+
+
 @pytest.mark.parametrize("case", ["bf16_d128_ragged", "bf16_d128_inplace"])
 def test_own_kv_rows_not_read(case):
     """The rank's own rows in the gathered K/V stay NaN: it must use the rows
