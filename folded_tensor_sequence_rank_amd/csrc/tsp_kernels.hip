@@ -1221,17 +1221,20 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   }
   char* const sK0 = smem;
   char* const sV0 = smem + 2 * KT;
+  // The wave's 1 KB slice of each tile, as a wave-uniform (scalar) offset so
+  // that the LDS destinations are formed without per-load VALU work.
+  const int wofs = __builtin_amdgcn_readfirstlane(wave * 1024);
   // Tiles wholly below kend need no per-lane range selects.
   auto issueK = [&](int k0, int buf) {
     const brsrc rK = make_rsrc(!split_src || own_tile(k0) ? Kh : Kgh, (uint64_t)a.S * HD * ES);
     if (k0 + BKV <= kend32) {
 #pragma unroll
       for (int j = 0; j < KJ; j++)
-        buffer_to_lds16(rK, sK0 + buf * KT + (wave + 4 * j) * 1024, koff[j], (uint32_t)(k0 * HD * ES));
+        buffer_to_lds16(rK, sK0 + buf * KT + wofs + 4096 * j, koff[j], (uint32_t)(k0 * HD * ES));
     } else {
 #pragma unroll
       for (int j = 0; j < KJ; j++)
-        buffer_to_lds16(rK, sK0 + buf * KT + (wave + 4 * j) * 1024,
+        buffer_to_lds16(rK, sK0 + buf * KT + wofs + 4096 * j,
                         k0 + krow[j] < kend32 ? koff[j] : kOOB, (uint32_t)(k0 * HD * ES));
     }
   };
@@ -1240,11 +1243,11 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     if (k0 + BKV <= kend32) {
 #pragma unroll
       for (int j = 0; j < VJ; j++)
-        buffer_to_lds16(rV, sV0 + buf * VT + (wave + 4 * j) * 1024, voff[j], (uint32_t)(k0 * ES));
+        buffer_to_lds16(rV, sV0 + buf * VT + wofs + 4096 * j, voff[j], (uint32_t)(k0 * ES));
     } else {
 #pragma unroll
       for (int j = 0; j < VJ; j++)
-        buffer_to_lds16(rV, sV0 + buf * VT + (wave + 4 * j) * 1024,
+        buffer_to_lds16(rV, sV0 + buf * VT + wofs + 4096 * j,
                         k0 + vkey[j] < kend32 ? voff[j] : kOOB, (uint32_t)(k0 * ES));
     }
   };
