@@ -1390,9 +1390,6 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     sh = s[1];
   }
 
-  // Unrolled by two so that the buffer parity P = t & 1 is known in each copy
-  // and the buffer offsets fold into the LDS reads' immediate offsets.
-#pragma unroll 2
   for (int t = 0; t < ntiles; t++) {
     const int P = t & 1;
     const int k0 = kbeg + t * BKV;
@@ -1416,8 +1413,10 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       const int kbuf = 1 - P, vbuf = P;
       constexpr int PD = TSP_PIPE_DIST;  // fragment reads in flight
       frag kq[PD], vq[PD];
+      // MFMA i accumulates block i % 2 at k-step i / 2: the two blocks'
+      // chains alternate, so no MFMA waits on the one just before it.
 #pragma unroll
-      for (int i = 0; i < PD; i++) kq[i] = kfrag(kbuf, i >> 3, i & 7);
+      for (int i = 0; i < PD; i++) kq[i] = kfrag(kbuf, i & 1, i >> 1);
       s[0] = f32x16{0};
       s[1] = f32x16{0};
       __builtin_amdgcn_sched_barrier(0);
@@ -1426,10 +1425,10 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       for (int i = 0; i < 16; i++) {
         const frag f = kq[i % PD];
         if (i + PD < 16)
-          kq[i % PD] = kfrag(kbuf, (i + PD) >> 3, (i + PD) & 7);
+          kq[i % PD] = kfrag(kbuf, (i + PD) & 1, (i + PD) >> 1);
         else
           vq[i + PD - 16] = vfrag(vbuf, (i + PD - 16) >> 2, (i + PD - 16) & 3);
-        s[i >> 3] = M_::mma(f, qf[i & 7], s[i >> 3]);
+        s[i & 1] = M_::mma(f, qf[i >> 1], s[i & 1]);
         pel(sh[i], nm, pf[2 + (i >> 3)], i & 7, ls);
         __builtin_amdgcn_sched_barrier(0);
       }
