@@ -350,15 +350,30 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
         if (DUAL) acc3[i][j] = M_::mma(bf3[set][j], af[set][i], acc3[i][j]);
       }
   };
-  // Interleave the fragment reads just issued with the MFMAs that follow.
+  // Interleave the fragment reads of the next k-step with this k-step's
+  // MFMAs (TSP_GEMM_SCHED 2: each read after a group of MFMAs).
+#ifndef TSP_GEMM_SCHED
+#define TSP_GEMM_SCHED 2  // per fragment read: MFMAs first, then the read (1: read first; 3: reads first)
+#endif
   auto interleave = [&]() {
     constexpr int NR = MB + NB + NB3 * (DUAL ? 1 : 0);
     constexpr int NM = MB * NB * (DUAL ? 2 : 1);
     constexpr int PER = NM / NR > 0 ? NM / NR : 1;
+    if constexpr (TSP_GEMM_SCHED == 1) {
 #pragma unroll
-    for (int q = 0; q < NR; q++) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
+      for (int q = 0; q < NR; q++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
+      }
+    } else if constexpr (TSP_GEMM_SCHED == 2) {
+#pragma unroll
+      for (int q = 0; q < NR; q++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // then one DS read
+      }
+    } else if constexpr (TSP_GEMM_SCHED == 3) {
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // all reads first
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
     }
   };
   // k-steps 0 .. KS-2 of buffer buf (fragments of step 0 already in set 0).
@@ -1155,7 +1170,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 #define TSP_ATTN_DOTSUM 0  // 1: row sums from bf16 pairs (one instruction per two keys)
 #endif
 #ifndef TSP_PIPE_DIST
-#define TSP_PIPE_DIST 4    // LDS fragment reads kept in flight ahead of the MFMAs
+#define TSP_PIPE_DIST 3    // LDS fragment reads kept in flight ahead of the MFMAs
 #endif
 
 __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
