@@ -685,15 +685,18 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
 // several items; their partial (max, sum, unnormalised O) are merged by
 // attn_combine_kernel.  Items are ordered heaviest first, and
 // head = item % Hd keeps one head on each XCD when Hd divides 8.
+//
+// attn_kernel serves fp32 and the head dims other than 128; bf16 with
+// 128-dim heads runs the software-pipelined attn_pipe_kernel further down
+// (same items, tiles and layouts).
 // ---------------------------------------------------------------------------
 constexpr int kQB = 1;     // 32-query blocks per wave (two waves share a SIMD)
 constexpr int kBQ = 128 * kQB;  // local query rows per work item (4 waves)
-constexpr int kBKV = 64;   // keys per tile (largest; the 128-dim bf16 kernel uses 32)
+constexpr int kBKV = 64;   // keys per tile
 
-// Keys per K/V tile and LDS stages: 32-key tiles in a 4-deep ring for the
-// 128-dim bf16 kernel (three tiles of loads in flight while one computes,
-// still 64 KB so two workgroups share a CU); 64-key double buffering
-// elsewhere.
+// Keys per K/V tile and LDS stages of attn_kernel: 64-key tiles, double
+// buffered (the 128-dim bf16 instance is only used when the pipelined kernel
+// is switched off).
 #ifndef TSP_ATTN128_BKV
 #define TSP_ATTN128_BKV 64   // keys per tile of the 128-dim bf16 kernel
 #endif
