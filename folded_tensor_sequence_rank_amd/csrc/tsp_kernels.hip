@@ -288,7 +288,17 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   constexpr int STAGE = (BM + NBR) * 128;
   constexpr int NB3 = DUAL ? NB : 1;
   static_assert(BM % 64 == 0 && BN % 64 == 0 || BN == 192 || BN == 96, "tile");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+#ifndef TSP_GEMM_PP
+#define TSP_GEMM_PP 1
+#endif
+  // Ping-pong schedule (below): 8 waves, 16-bit operands, and the split A
+  // buffers plus the three-slot B ring must fit in LDS.  Used for the
+  // 256x256 single-B tiles, where it measured faster than the lockstep loop
+  // (on 256x192 it did not).
+  constexpr int PPLDS = 2 * BM * 128 + 3 * NBR * 128;
+  constexpr bool PP = TSP_GEMM_PP && VEC && NW == 8 && sizeof(T) == 2 && PPLDS <= 160 * 1024 &&
+                      (NBR / 32) % 2 == 0 && BM == 256 && BN == 256 && !DUAL;
+  __shared__ __attribute__((aligned(16))) char smem[PP ? PPLDS : 2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -431,6 +441,130 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
                         k0 * ES);
       }
     };
+    if constexpr (PP) {
+      // Ping-pong schedule.  SIMD s runs waves s (group 0) and s + 4 (group
+      // 1).  Time is cut into phases separated by workgroup barriers; in
+      // each phase one group only issues MFMAs on fragments already in
+      // registers while the other only moves data: its fragment reads of the
+      // next k-tile and its half of the global->LDS loads.  Group 1 runs one
+      // phase behind group 0, so each SIMD has one wave feeding the matrix
+      // core while the other waits on memory:
+      //   group 0: mem(0) | mma(0) | mem(1) | mma(1) | ...
+      //   group 1:   -    | mem(0) | mma(0) | mem(1) | mma(1) ...
+      // Group g reads only rows [g*BM/2, (g+1)*BM/2) of the A tile, kept in
+      // its own double buffer, and the whole B tile, kept in a ring of three.
+      // In mem(kt) group g loads its A half of tile kt+1 and half of the B
+      // rows of tile kt+2; both land before the barrier that ends its mma(kt).
+      // A buffers are rewritten two phases after their last reader, B slots
+      // three phases after theirs (B(kt+2) replaces B(kt-1)).
+#ifndef TSP_PP_AGPR
+#define TSP_PP_AGPR 1
+#endif
+      // Naming an accumulation register here makes the compiler select the
+      // MFMA form whose accumulator lives in AGPRs: the accumulators then
+      // stay out of the VGPR banks that the other wave's LDS reads fill.
+      if (TSP_PP_AGPR) asm volatile("" ::: "a0");
+      const int grp = wave >> 2, w4 = wave & 3;
+      constexpr int AH = BM / 2;                 // A rows per group
+      constexpr int RA2 = AH / 32, RB = NBR / 32, RB2 = RB / 2;
+      static_assert(RB % 2 == 0, "B rows split evenly between the groups");
+      char* const sAg = smem + grp * 2 * AH * 128;   // this group's A buffers
+      char* const sBr = smem + 2 * BM * 128;         // B ring
+      const int lrow4 = 8 * w4 + (lane >> 3);
+      const int lc4 = swz<8>(lane & 7, lrow4);
+      const int mg = m0 + grp * AH;
+      const bool fullA = mg + AH <= g.M, fullB = n0 + BN <= g.N;
+      const uint32_t vA = (uint32_t)(((int64_t)(mg + lrow4) * g.lda + lc4 * V) * ES);
+      const uint32_t vB = (uint32_t)(((int64_t)(n0 + lrow4) * g.ldb + lc4 * V) * ES);
+      auto loadA = [&](int kt) {  // this group's A half of tile kt
+        const int k0 = kt * BK;
+        const bool kok = k0 + lc4 * V < g.K;
+        char* d = sAg + (kt & 1) * AH * 128 + w4 * 1024;
+#pragma unroll
+        for (int i = 0; i < RA2; i++) {
+          const bool ok = kok && (fullA || mg + 32 * i + lrow4 < g.M);
+          buffer_to_lds16(rA, d + i * 4096, ok ? vA : kOOB, (uint32_t)(32 * i * g.lda * ES + k0 * ES));
+        }
+      };
+      auto loadB = [&](int kt, int half) {  // B rows [half*NBR/2, +NBR/2) of tile kt
+        const int k0 = kt * BK;
+        const bool kok = k0 + lc4 * V < g.K;
+        char* d = sBr + (kt % 3) * NBR * 128 + w4 * 1024;
+#pragma unroll
+        for (int q = 0; q < RB2; q++) {
+          const int i = half * RB2 + q;
+          const bool second = DUAL && 32 * i >= BN;
+          const int rr = second ? 32 * i - BN : 32 * i;
+          const bool ok = kok && (fullB || n0 + rr + lrow4 < g.N);
+          buffer_to_lds16(second ? rB3 : rB, d + i * 4096, ok ? vB : kOOB,
+                          (uint32_t)(rr * g.ldb * ES + k0 * ES));
+        }
+      };
+      frag afk[KS][MB], bfk[KS][NB], b3k[KS][NB3];
+      auto fetch_all = [&](int kt) {
+        const char* sA = sAg + (kt & 1) * AH * 128;
+        const char* sB = sBr + (kt % 3) * NBR * 128;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+          const int byte = (ks * M_::KSTEP + lg * M_::E) * ES;
+          const int c = byte >> 4, w = byte & 15;
+#pragma unroll
+          for (int i = 0; i < MB; i++) {
+            const int row = wm * WM + i * 32 + lr - grp * AH;  // row within the group's half
+            afk[ks][i] = *(const frag*)(sA + row * 128 + (swz<8>(c, row) << 4) + w);
+          }
+#pragma unroll
+          for (int j = 0; j < NB; j++) {
+            const int row = wn * WN + j * 32 + lr;
+            bfk[ks][j] = *(const frag*)(sB + row * 128 + (swz<8>(c, row) << 4) + w);
+            if (DUAL) {
+              const int r3 = BN + row;
+              b3k[ks][j] = *(const frag*)(sB + r3 * 128 + (swz<8>(c, r3) << 4) + w);
+            }
+          }
+        }
+      };
+      auto mma_all = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+          for (int i = 0; i < MB; i++)
+#pragma unroll
+            for (int j = 0; j < NB; j++) {
+              acc[i][j] = M_::mma(bfk[ks][j], afk[ks][i], acc[i][j]);
+              if (DUAL) acc3[i][j] = M_::mma(b3k[ks][j], afk[ks][i], acc3[i][j]);
+            }
+      };
+      // A workgroup barrier that the compiler neither moves memory
+      // operations across nor pairs with waits of its own.
+      auto bar = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if (nk > 0) {
+        loadA(0);
+        loadB(0, grp);
+        if (nk > 1) loadB(1, grp);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        bar();
+        if (grp == 1) bar();
+        for (int kt = 0; kt < nk; kt++) {
+          // (Issuing the fragment reads ahead of the loads measured slower.)
+          if (kt + 1 < nk) loadA(kt + 1);
+          if (kt + 2 < nk) loadB(kt + 2, grp);
+          fetch_all(kt);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          bar();
+          if (TSP_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(1);
+          mma_all();
+          if (TSP_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          // group 1's last phase needs no barrier: no wave waits for it
+          if (grp == 0 || kt + 1 < nk) bar();
+        }
+      }
+    } else {
     // Pipeline: tiles kt and kt+1 are resident or in flight while kt computes.
     // The barrier sits before the last k-step's MFMAs: every wave has its
     // fragments of buffer kt in registers (so that buffer may be refilled
@@ -466,6 +600,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
           }
         }
       }
+    }
     }
   } else {
     u32x4 ra[AC], rb[BC];
@@ -525,6 +660,58 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   float* __restrict__ Y = g.Y;
   const T* __restrict__ R = (const T*)g.R;
   T* __restrict__ C = (T*)g.C;
+  if constexpr ((EPI == EPI_ACC || EPI == EPI_RESID) && sizeof(T) == 2) {
+    // Whole tile inside the matrix, 16-byte aligned rows: the accumulator
+    // (and residual) reads of up to four blocks are all issued before the
+    // first wait, then their results are stored.  (The memory counter also
+    // counts stores, so a block-at-a-time loop pays a full read round trip
+    // and a store drain per block.)
+    const bool aligned = (g.ldy & 3) == 0 && (EPI != EPI_RESID || ((g.ldr & 3) == 0 && (g.ldc & 3) == 0));
+    if (m0 + BM <= g.M && n0 + BN <= g.N && aligned) {
+      constexpr int NBLK = MB * NB, HB = NBLK < 4 ? NBLK : 4;
+      const bool beta = g.beta != 0;
+#pragma unroll
+      for (int b0 = 0; b0 < NBLK; b0 += HB) {
+        float4 yv[HB][4];
+        u32x2 rv[HB][4];
+#pragma unroll
+        for (int bb = 0; bb < HB; bb++) {
+          if (b0 + bb >= NBLK) break;
+          const int i = (b0 + bb) / NB, j = (b0 + bb) % NB;
+          const int64_t m = m0 + wm * WM + i * 32 + lr;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+            yv[bb][q] = beta ? *(const float4*)(Y + m * g.ldy + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (EPI == EPI_RESID) rv[bb][q] = *(const u32x2*)(R + m * g.ldr + n);
+          }
+        }
+#pragma unroll
+        for (int bb = 0; bb < HB; bb++) {
+          if (b0 + bb >= NBLK) break;
+          const int i = (b0 + bb) / NB, j = (b0 + bb) % NB;
+          const int64_t m = m0 + wm * WM + i * 32 + lr;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+            float s[4] = {yv[bb][q].x + acc[i][j][4 * q], yv[bb][q].y + acc[i][j][4 * q + 1],
+                          yv[bb][q].z + acc[i][j][4 * q + 2], yv[bb][q].w + acc[i][j][4 * q + 3]};
+            if constexpr (EPI == EPI_RESID) {
+              Chunk<T> r;
+              r.raw[0] = rv[bb][q][0];
+              r.raw[1] = rv[bb][q][1];
+#pragma unroll
+              for (int e = 0; e < 4; e++) s[e] += to_f(r.e[e]);
+              store4<T>(C + m * g.ldc + n, s[0], s[1], s[2], s[3]);
+            } else {
+              *(float4*)(Y + m * g.ldy + n) = make_float4(s[0], s[1], s[2], s[3]);
+            }
+          }
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MB; i++) {
     const int m = m0 + wm * WM + i * 32 + lr;
