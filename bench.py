@@ -87,6 +87,51 @@ def traffic_for(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
+class ClockSampler:
+    """Samples the GPU's current graphics clock (MHz, through amdsmi, as
+    torch.cuda.clock_rate reports it) on a host thread while the timed steps
+    run; None where the query is unavailable."""
+
+    def __init__(self):
+        import threading
+        self.samples = []
+        self.stop = threading.Event()
+        self.th = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import torch
+        try:
+            while not self.stop.is_set():
+                self.samples.append(float(torch.cuda.clock_rate(0)))
+                time.sleep(0.002)
+        except Exception:  # noqa: BLE001 - no clock query on this host
+            pass
+
+    def __enter__(self):
+        self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.th.join(timeout=5)
+
+    def summary(self):
+        v = sorted(x for x in self.samples if x > 0)
+        if not v:
+            return None
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, r, rows):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -111,7 +156,7 @@ def cpu_baseline(cfg, r, rows):
     executed = (2 * rows * h * h + 2 * 2 * pmax * h * h + 4 * h * int(np.sum(pos + 1))
                 + 2 * rows * h * h + 6 * rows * h * F)
     return {"value": executed / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt * reps, 3),
+            "kind": "oracle", "seconds": round(dt * reps, 3), "cpu": cpu_model(),
             "sample": (f"{cfg.name}, rank {r}: fp64 numpy oracle layer_rows for the first {rows} "
                        f"local rows of the second zigzag chunk (positions {int(pos[0])}.."
                        f"{int(pos[-1])}), including the K/V projection of all {pmax} positions "
@@ -168,11 +213,12 @@ def main():
         run.layer(x, L, kv, out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        run.layer(x, L, kv, out)
-    e1.record()
-    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        e0.record()
+        for _ in range(args.steps):
+            run.layer(x, L, kv, out)
+        e1.record()
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     assert torch.isfinite(out).all(), "non-finite output"
 
@@ -231,6 +277,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "gpu_clock": clk.summary(),
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(line), flush=True)

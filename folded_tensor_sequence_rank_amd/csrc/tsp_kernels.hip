@@ -1905,46 +1905,62 @@ static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
     gemm_kernel<T, BM, BN, EPI, false, NW, WGM><<<nt, NW * 64, 0, s>>>(a);
 }
 
-// Tile choice: the shape whose estimated time (rounds of 256 concurrent
-// tiles x tile area / relative efficiency) is smallest.  Larger tiles read
-// fewer LDS bytes per MFMA; 128x128 is for small problems.
+// Tile choice.  With every CU holding work the tile shapes reach about the
+// same MFMA rate per CU; what differs is how a shape's tile count fills 256
+// CUs (4-wave tiles run two workgroups per CU, and a CU with only one of them
+// runs it well below that rate).  Measured on the layer's projections at
+// 2048, 8192 and 16384 local tokens of the 7B shape:
+//  * fp32-accumulator GEMMs (O, W2): 256x256 (ping-pong) when that makes at
+//    least one full round of 256 tiles; else 128x128 (4 waves) for K <= 2048
+//    and 128x256 for longer K;
+//  * QKV: 128x192 when 256x192 needs more than one round; otherwise the
+//    estimate below (256x192 at 8192 tokens, 128x128 at 2048);
+//  * W1/W3 (two B operands): 128x64 (4 waves) when 128x192 leaves CUs idle,
+//    128x96 (4 waves) up to two rounds of 128x192, else the estimate.
+// The estimate: rounds of 256 tiles x tile area / relative efficiency.
 template <int EPI>
 static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
+  auto tiles = [&](int bm, int bn) {
+    return (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+  };
   struct Cand { int bm, bn; double eff; };
-  const Cand single[] = {{256, 256, 1.0}, {256, 192, 0.95}, {128, 128, 0.55}};
-  const Cand dual[] = {{256, 128, 1.0}, {128, 64, 0.5}, {128, 192, 0.8}};
-  const Cand* cs = EPI == EPI_SWIGLU ? dual : single;
-  const int nc = 3;
-  int best = 0;
-  double bt = 1e300;
-  for (int c = 0; c < nc; c++) {
-    const int64_t tiles = (int64_t)((a.M + cs[c].bm - 1) / cs[c].bm) * ((a.N + cs[c].bn - 1) / cs[c].bn);
-    const double t = (double)((tiles + 255) / 256) * cs[c].bm * cs[c].bn / cs[c].eff;
-    if (t < bt * 0.999) { bt = t; best = c; }
-  }
-#ifndef TSP_ACC_SMALLK_TILE
-#define TSP_ACC_SMALLK_TILE 0
-#endif
-#ifndef TSP_W13_TILE
-#define TSP_W13_TILE 0
-#endif
+  auto pick = [&](const Cand* cs, int nc) {
+    int best = 0;
+    double bt = 1e300;
+    for (int c = 0; c < nc; c++) {
+      const double t = (double)((tiles(cs[c].bm, cs[c].bn) + 255) / 256) * cs[c].bm * cs[c].bn / cs[c].eff;
+      if (t < bt * 0.999) {
+        bt = t;
+        best = c;
+      }
+    }
+    return best;
+  };
   if constexpr (EPI == EPI_SWIGLU) {
-    if (TSP_W13_TILE == 1 && best != 1) best = 2;
-    if (TSP_W13_TILE == 2 && best != 1) best = 3;
-    if (TSP_W13_TILE == 3) best = 0;
-    if (best == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
-    else if (best == 2) gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
-    else if (best == 3) gemm_go<bf16, 256, 192, EPI, 4, 2>(a, vec, s);
-    else gemm_go<bf16, 128, 64, EPI>(a, vec, s);
-  } else if ((EPI == EPI_ACC || EPI == EPI_RESID) && TSP_ACC_SMALLK_TILE != 0 && a.K <= 2048 &&
-             best == 0) {
-    // accumulate GEMMs with short K are bound by the fp32 accumulator traffic
-    if (TSP_ACC_SMALLK_TILE == 1) gemm_go<bf16, 128, 128, EPI, 4>(a, vec, s);
-    else gemm_go<bf16, 128, 128, EPI, 8>(a, vec, s);
+    const int64_t t192 = tiles(128, 192);
+    if (t192 < 256) {
+      gemm_go<bf16, 128, 64, EPI, 4, 2>(a, vec, s);
+    } else if (t192 <= 512) {
+      gemm_go<bf16, 128, 96, EPI, 4, 4>(a, vec, s);
+    } else {
+      const Cand dual[] = {{256, 128, 1.0}, {128, 192, 0.8}};
+      if (pick(dual, 2) == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
+      else gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
+    }
+  } else if constexpr (EPI == EPI_ACC || EPI == EPI_RESID) {
+    if (tiles(256, 256) >= 256) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
+    else if (a.K <= 2048) gemm_go<bf16, 128, 128, EPI, 4, 2>(a, vec, s);
+    else gemm_go<bf16, 128, 256, EPI, 8, 2>(a, vec, s);
   } else {
-    if (best == 0) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
-    else if (best == 1) gemm_go<bf16, 256, 192, EPI, 8, 4>(a, vec, s);
-    else gemm_go<bf16, 128, 128, EPI>(a, vec, s);
+    if (tiles(256, 192) > 256) {
+      gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
+    } else {
+      const Cand single[] = {{256, 256, 1.0}, {256, 192, 0.95}, {128, 128, 0.55}};
+      const int best = pick(single, 3);
+      if (best == 0) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
+      else if (best == 1) gemm_go<bf16, 256, 192, EPI, 8, 4>(a, vec, s);
+      else gemm_go<bf16, 128, 128, EPI>(a, vec, s);
+    }
   }
 }
 
