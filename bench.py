@@ -57,16 +57,20 @@ def flops_per_step(cfg, r):
     launches together): D QKV projections and D head-group attentions; the O
     and W2 projections over all shards (however they are grouped into
     launches); D W1/W3 projections."""
-    import oracle.tsp_oracle as O  # closed-form pair count only
-    T, h, D, F = cfg.local_tokens, cfg.hidden, cfg.fold, cfg.ffn
-    pairs = O.causal_pairs(cfg.seq, D, r)  # per head
-    return {"qkv": 2 * T * 3 * h * h, "attn": 4 * h * pairs, "oproj": 2 * T * h * h,
+    from folded_tensor_sequence_rank_amd import tsp
+    B = cfg.batch
+    T, h, D, F = B * cfg.local_tokens, cfg.hidden, cfg.fold, cfg.ffn
+    hk = cfg.kv_heads * cfg.head_dim  # K and V columns of the whole layer
+    # causal (query, key) pairs of the rank's queries: key p' <= query p
+    pos = tsp.zigzag_positions(cfg.seq, D, r)
+    pairs = B * int((pos + 1).sum())  # per head, over the micro-batch
+    return {"qkv": 2 * T * h * (h + 2 * hk), "attn": 4 * h * pairs, "oproj": 2 * T * h * h,
             "w13": 2 * T * 2 * F * h, "w2": 2 * T * F * h}
 
 
 def bytes_per_launch(cfg):
     es = 2 if cfg.dtype == "bf16" else 4
-    T, h = cfg.local_tokens, cfg.hidden
+    T, h = cfg.batch * cfg.local_tokens, cfg.hidden
     return {"rmsnorm": 2 * T * h * es + h * es}
 
 
@@ -175,7 +179,6 @@ def main():
     import numpy as np
     import torch
 
-    import oracle.tsp_oracle as O
     import synth
     from folded_tensor_sequence_rank_amd import tsp
     from gpu_harness import RankRun, fill_kv, layer_dev, new_kv, to_dev
@@ -197,7 +200,10 @@ def main():
     del w
     xs = []
     for q in range(cfg.fold):
-        xs.append(to_dev(synth.gen_rows(cfg, tsp.zigzag_positions(cfg.seq, cfg.fold, q)), cfg))
+        pos = tsp.zigzag_positions(cfg.seq, cfg.fold, q)
+        # sequence-major rows of every sequence of the micro-batch
+        xs.append(to_dev(np.concatenate([synth.gen_rows(cfg, pos, seq_index=b)
+                                         for b in range(cfg.batch)]), cfg))
     kv = new_kv(cfg)
     fill_kv(cfg, L, xs, kv, skip=r)
     x = xs[r]
@@ -222,8 +228,8 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     assert torch.isfinite(out).all(), "non-finite output"
 
-    T = cfg.local_tokens
-    f_alg = O.flops_rank(cfg.hidden, cfg.ffn, cfg.seq, cfg.fold, r)
+    T = cfg.batch * cfg.local_tokens
+    f_alg = sum(flops_per_step(cfg, r).values())
     tflops = f_alg / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
 
@@ -270,7 +276,9 @@ def main():
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "hidden": cfg.hidden, "heads": cfg.n_heads,
                    "head_dim": cfg.head_dim, "ffn": cfg.ffn, "seq": cfg.seq, "fold": cfg.fold,
-                   "rank": r, "local_tokens": T, "parallelism": "tsp-rank-share"},
+                   "rank": r, "batch": cfg.batch, "local_tokens": T,
+                   "kv_heads": cfg.kv_heads, "rope_theta": cfg.rope_theta,
+                   "parallelism": "tsp-rank-share"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "frac_of_peak": round(tflops / peak, 4),
         "flops_per_step": f_alg,

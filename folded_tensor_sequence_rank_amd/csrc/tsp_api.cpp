@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
@@ -49,11 +50,16 @@ int fail(int code, const char* fmt, ...) {
                   __LINE__);                                                                \
   } while (0)
 
+// S, C and T are per sequence; the micro-batch holds B sequences, so the
+// rank has BT = B*T local rows and the gathered K/V BS = B*S positions per head.
+// Hkv K/V heads, Hkd = Hkv/D of them per shard, ks = Hkd*d K (V) rows per
+// shard; rope_theta = 0 means no rotary embedding.
 struct Dims {
-  int64_t h, H, d, F, D, r, S, C, T, Hd, hs, Fs;
+  int64_t h, H, d, F, D, r, S, C, T, Hd, hs, Fs, B, BT, BS, Hkv, Hkd, ks;
   size_t es;
   Dtype dt;
   float eps;
+  float rope_theta;
   uint32_t flags;
 };
 
@@ -77,6 +83,17 @@ int check_dims(const tsp_dims* p, Dims* o) {
     return fail(TSP_E_SHAPE, "seq %lld is not a multiple of 2*fold", (long long)p->seq);
   if (p->seq % 8) return fail(TSP_E_SHAPE, "seq %lld is not a multiple of 8", (long long)p->seq);
   if (p->hidden % 8) return fail(TSP_E_SHAPE, "hidden %d is not a multiple of 8", p->hidden);
+  if (p->batch < 0) return fail(TSP_E_INVAL, "batch %d is negative", p->batch);
+  if ((int64_t)std::max(p->batch, 1) * p->seq > INT32_MAX)
+    return fail(TSP_E_SHAPE, "batch * seq exceeds 2^31 - 1 positions");
+  if (p->n_kv_heads < 0) return fail(TSP_E_INVAL, "n_kv_heads %d is negative", p->n_kv_heads);
+  const int32_t hkv = p->n_kv_heads ? p->n_kv_heads : p->n_heads;
+  if (p->n_heads % hkv)
+    return fail(TSP_E_SHAPE, "n_heads %d %% n_kv_heads %d != 0", p->n_heads, hkv);
+  if (hkv % p->fold) return fail(TSP_E_SHAPE, "n_kv_heads %d %% fold %d != 0", hkv, p->fold);
+  if (!(p->rope_theta >= 0.f) || !std::isfinite(p->rope_theta) ||
+      (p->rope_theta > 0.f && p->rope_theta <= 1.f))
+    return fail(TSP_E_INVAL, "rope_theta must be 0 or a finite value > 1");
   o->h = p->hidden;
   o->H = p->n_heads;
   o->d = p->head_dim;
@@ -89,6 +106,13 @@ int check_dims(const tsp_dims* p, Dims* o) {
   o->Hd = o->H / o->D;
   o->hs = o->h / o->D;
   o->Fs = o->F / o->D;
+  o->Hkv = hkv;
+  o->Hkd = hkv / o->D;
+  o->ks = o->Hkd * o->d;
+  o->rope_theta = p->rope_theta;
+  o->B = std::max(p->batch, 1);
+  o->BT = o->B * o->T;
+  o->BS = o->B * o->S;
   o->dt = p->dtype == TSP_BF16 ? BF16 : F32;
   o->es = p->dtype == TSP_BF16 ? 2 : 4;
   o->eps = p->eps;
@@ -106,7 +130,9 @@ struct MlpWs {
   size_t xn, y, gg, slotw[2], bw[2], end;
 };
 
-size_t attn_shard_elems(const Dims& d) { return 4 * (size_t)d.hs * d.h; }
+// Q | K | V rows of a packed attention shard, then W_O (h rows of hs).
+size_t qkv_rows(const Dims& d) { return (size_t)(d.hs + 2 * d.ks); }
+size_t attn_shard_elems(const Dims& d) { return (qkv_rows(d) + d.hs) * d.h; }
 size_t mlp_shard_elems(const Dims& d) { return 3 * (size_t)d.Fs * d.h; }
 
 // Accumulation groups.  The O projections (and W2 projections) of G
@@ -121,24 +147,28 @@ size_t mlp_shard_elems(const Dims& d) { return 3 * (size_t)d.Fs * d.h; }
 int64_t acc_group(const Dims& d) {
   return std::max<int64_t>(1, std::min<int64_t>(TSP_ACC_GROUP, d.D / 2));
 }
-size_t kv_block_elems(const Dims& d) { return 2 * (size_t)d.Hd * d.S * d.d; }
+size_t kv_block_elems(const Dims& d) { return 2 * (size_t)d.Hkd * d.BS * d.d; }
+size_t kv_v_offset(const Dims& d) { return (size_t)d.Hkd * d.BS * d.d; }  // elements before Vt_j
 
-AttnPlan plan_of(const Dims& d) { return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)d.Hd); }
+// The B sequences' items run side by side like extra heads.
+AttnPlan plan_of(const Dims& d) {
+  return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(d.Hd * d.B));
+}
 
 AttnWs attn_ws(const Dims& d, size_t base) {
   AttnWs w;
   size_t o = base;
-  const size_t act = al((size_t)d.T * d.h * d.es);
+  const size_t act = al((size_t)d.BT * d.h * d.es);
   w.xn = o; o += act;
-  w.y = o; o += al((size_t)d.T * d.h * 4);
+  w.y = o; o += al((size_t)d.BT * d.h * 4);
   const int64_t G = acc_group(d);
-  w.q = o; o += al((size_t)d.T * d.hs * d.es);
-  w.o = o; o += al((size_t)d.T * G * d.hs * d.es);  // [T][G*hs]
-  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(3 * (size_t)d.hs * d.h * d.es); }
+  w.q = o; o += al((size_t)d.BT * d.hs * d.es);
+  w.o = o; o += al((size_t)d.BT * G * d.hs * d.es);  // [B*T][G*hs]
+  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(qkv_rows(d) * d.h * d.es); }
   for (int s = 0; s < 2; s++) { w.slotkv[s] = o; o += al(kv_block_elems(d) * d.es); }
   for (int s = 0; s < 2; s++) { w.bo[s] = o; o += al((size_t)d.h * G * d.hs * d.es); }  // [h][G*hs]
   const AttnPlan p = plan_of(d);
-  const size_t nslot = p.split ? (size_t)d.Hd * p.nqt * p.maxseg * p.bq : 0;
+  const size_t nslot = p.split ? (size_t)d.Hd * d.B * p.nqt * p.maxseg * p.bq : 0;
   w.op = o; o += al(nslot * d.d * 4);
   w.ml = o; o += al(nslot * 2 * 4);
   w.end = o;
@@ -149,16 +179,16 @@ MlpWs mlp_ws(const Dims& d, size_t base) {
   MlpWs w;
   size_t o = base;
   const int64_t G = acc_group(d);
-  w.xn = o; o += al((size_t)d.T * d.h * d.es);
-  w.y = o; o += al((size_t)d.T * d.h * 4);
-  w.gg = o; o += al((size_t)d.T * G * d.Fs * d.es);  // [T][G*Fs]
+  w.xn = o; o += al((size_t)d.BT * d.h * d.es);
+  w.y = o; o += al((size_t)d.BT * d.h * 4);
+  w.gg = o; o += al((size_t)d.BT * G * d.Fs * d.es);  // [B*T][G*Fs]
   for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(2 * (size_t)d.Fs * d.h * d.es); }
   for (int s = 0; s < 2; s++) { w.bw[s] = o; o += al((size_t)d.h * G * d.Fs * d.es); }  // [h][G*Fs]
   w.end = o;
   return w;
 }
 
-size_t kv_ws_bytes(const Dims& d) { return al((size_t)d.T * d.h * d.es); }
+size_t kv_ws_bytes(const Dims& d) { return al((size_t)d.BT * d.h * d.es); }
 
 bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
@@ -280,19 +310,20 @@ int copy_remote_kv(Ctx& c, const char* kv_block, char* slot) {
   const size_t es = d.es;
   const int64_t ranges[2][2] = {{0, d.r * d.C}, {(d.r + 1) * d.C, (2 * d.D - 1 - d.r) * d.C}};
   const char* srcK = kv_block;
-  const char* srcV = kv_block + (size_t)d.Hd * d.S * d.d * es;
+  const char* srcV = kv_block + kv_v_offset(d) * es;
   char* dstK = slot;
-  char* dstV = slot + (size_t)d.Hd * d.S * d.d * es;
-  for (auto& rg : ranges) {
-    const int64_t a = rg[0], n = rg[1] - rg[0];
-    if (n <= 0) continue;
-    const size_t kp = (size_t)d.S * d.d * es;  // one head's K plane
-    HIP_TRY(hipMemcpy2DAsync(dstK + a * d.d * es, kp, srcK + a * d.d * es, kp, n * d.d * es,
-                             d.Hd, hipMemcpyDeviceToDevice, c.cs));
-    const size_t vp = (size_t)d.S * es;  // one V^T row
-    HIP_TRY(hipMemcpy2DAsync(dstV + a * es, vp, srcV + a * es, vp, n * es, d.Hd * d.d,
-                             hipMemcpyDeviceToDevice, c.cs));
-  }
+  char* dstV = slot + kv_v_offset(d) * es;
+  for (int64_t b = 0; b < d.B; b++)  // sequence b: key rows [b*S, (b+1)*S)
+    for (auto& rg : ranges) {
+      const int64_t a = b * d.S + rg[0], n = rg[1] - rg[0];
+      if (n <= 0) continue;
+      const size_t kp = (size_t)d.BS * d.d * es;  // one head's K plane
+      HIP_TRY(hipMemcpy2DAsync(dstK + a * d.d * es, kp, srcK + a * d.d * es, kp, n * d.d * es,
+                               d.Hkd, hipMemcpyDeviceToDevice, c.cs));
+      const size_t vp = (size_t)d.BS * es;  // one V^T row
+      HIP_TRY(hipMemcpy2DAsync(dstV + a * es, vp, srcV + a * es, vp, n * es, d.Hkd * d.d,
+                               hipMemcpyDeviceToDevice, c.cs));
+    }
   return TSP_OK;
 }
 
@@ -302,9 +333,10 @@ GemmArgs gemm_base() {
   return g;
 }
 
-// QKV projection of this rank's tokens with packed shard w (rows [col0, 3hs)
-// of its first block), scattered to Q (if col0 == 0) and to K/V at the
-// tokens' global positions.
+// QKV projection of this rank's tokens with packed shard w (rows
+// [col0, hs + 2ks) of its first block), scattered to Q (if col0 == 0) and to
+// K/V at the tokens' global positions, Q and K rotated when rope_theta > 0.
+// col0 is 0 or hs.
 int qkv_gemm(Ctx& c, const void* xn, const char* w, int col0, void* q, char* kvslot) {
   const Dims& d = *c.d;
   GemmArgs g = gemm_base();
@@ -312,17 +344,20 @@ int qkv_gemm(Ctx& c, const void* xn, const char* w, int col0, void* q, char* kvs
   g.lda = d.h;
   g.B = w + (size_t)col0 * d.h * d.es;
   g.ldb = d.h;
-  g.M = (int)d.T;
-  g.N = (int)(3 * d.hs - col0);
+  g.M = (int)d.BT;
+  g.N = (int)(qkv_rows(d) - col0);
   g.K = (int)d.h;
   g.Q = q;
   g.Kd = kvslot;
-  g.Vt = kvslot + (size_t)d.Hd * d.S * d.d * d.es;
+  g.Vt = kvslot + kv_v_offset(d) * d.es;
   g.hs = (int)d.hs;
+  g.ks = (int)d.ks;
+  g.rope_l2 = d.rope_theta > 0.f ? std::log2((double)d.rope_theta) : 0.0;
   g.hd = (int)d.d;
   g.col0 = col0;
   g.S = d.S;
   g.T = d.T;
+  g.batch = (int)d.B;
   g.chunk = d.C;
   g.rank = (int)d.r;
   g.fold = (int)d.D;
@@ -340,7 +375,7 @@ int acc_gemm(Ctx& c, const void* a, int64_t K, int64_t ld, const char* w, float*
   g.lda = ld;
   g.B = w;
   g.ldb = ld;
-  g.M = (int)d.T;
+  g.M = (int)d.BT;
   g.N = (int)d.h;
   g.K = (int)K;
   g.Y = y;
@@ -363,11 +398,11 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
   const Dims& d = *c.d;
   char* ws = c.ws;
   const size_t es = d.es;
-  const size_t qkvbytes = 3 * (size_t)d.hs * d.h * es;
+  const size_t qkvbytes = qkv_rows(d) * d.h * es;
   const size_t kvbytes = kv_block_elems(d) * es;
   const int64_t G = acc_group(d);
   const AttnPlan plan = plan_of(d);
-  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws + L.xn, d.T, (int)d.h, d.eps, c.s)));
+  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws + L.xn, d.BT, (int)d.h, d.eps, c.s)));
   for (int64_t j = 0; j < d.D; j++) {  // broadcast iteration j: shard of rank j
     const int s = (int)(j & 1);
     const int64_t gi = j / G, gp = j % G;  // accumulation group, position in it
@@ -408,21 +443,23 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     memset(&a, 0, sizeof a);
     a.Q = ws + L.q;
     a.K = slotkv;
-    a.Vt = slotkv + (size_t)d.Hd * d.S * d.d * es;
+    a.Vt = slotkv + kv_v_offset(d) * es;
     if (kv_in_place(d)) {
       a.Kg = kvj;
-      a.Vtg = kvj + (size_t)d.Hd * d.S * d.d * es;
+      a.Vtg = kvj + kv_v_offset(d) * es;
     }
     a.O = ws + L.o + gp * d.hs * es;  // this shard's columns of the group's [T][G*hs]
     a.Op = (float*)(ws + L.op);
     a.ML = (float*)(ws + L.ml);
     a.T = d.T;
     a.S = d.S;
+    a.batch = (int)d.B;
     a.chunk = d.C;
     a.ldo = (int)(G * d.hs);
     a.rank = (int)d.r;
     a.fold = (int)d.D;
     a.Hd = (int)d.Hd;
+    a.grp = (int)(d.H / d.Hkv);
     a.nqt = plan.nqt;
     a.lseg = plan.lseg;
     a.maxseg = plan.maxseg;
@@ -452,7 +489,7 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
   const size_t es = d.es;
   const size_t w13bytes = 2 * (size_t)d.Fs * d.h * es;
   const int64_t G = acc_group(d);
-  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.T, (int)d.h, d.eps, c.s)));
+  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.BT, (int)d.h, d.eps, c.s)));
   for (int64_t t = 0; t < d.D; t++) {  // ring step t: shard (r + t) mod D
     const int64_t j = (d.r + t) % d.D;
     const int s = (int)(t & 1);
@@ -487,7 +524,7 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
     g.B = w;
     g.B3 = w + (size_t)d.Fs * d.h * es;
     g.ldb = d.h;
-    g.M = (int)d.T;
+    g.M = (int)d.BT;
     g.N = (int)d.Fs;
     g.K = (int)d.h;
     g.C = ws + L.gg + gp * d.Fs * es;  // this shard's columns of the group's [T][G*Fs]
@@ -534,7 +571,7 @@ size_t tsp_workspace_bytes(const tsp_dims* dims, int which) {
     case TSP_WS_ATTN: return attn_ws(d, 0).end;
     case TSP_WS_MLP: return mlp_ws(d, 0).end;
     case TSP_WS_LAYER: {
-      const size_t x1 = al((size_t)d.T * d.h * d.es);
+      const size_t x1 = al((size_t)d.BT * d.h * d.es);
       const AttnWs a = attn_ws(d, x1);
       return mlp_ws(d, a.end).end;
     }
@@ -617,7 +654,7 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1, const v
       (rc = check_shards(w_mlp, d.D, "w_mlp")))
     return rc;
   const size_t x1off = 0;
-  const AttnWs A = attn_ws(d, al((size_t)d.T * d.h * d.es));
+  const AttnWs A = attn_ws(d, al((size_t)d.BT * d.h * d.es));
   const MlpWs M = mlp_ws(d, A.end);
   if (ws_bytes < M.end) return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, M.end);
   Ctx c{&d, (char*)ws};
@@ -640,7 +677,7 @@ int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1, const void
     return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, kv_ws_bytes(d));
   Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr,
         (d.flags & TSP_F_PROFILE) != 0};
-  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws, d.T, (int)d.h, d.eps, c.s)));
+  TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws, d.BT, (int)d.h, d.eps, c.s)));
   const size_t kvbytes = kv_block_elems(d) * d.es;
   for (int64_t j = 0; j < d.D; j++) {
     TIMED(c, TSP_K_QKV,

@@ -29,33 +29,41 @@ struct GemmArgs {
   int beta;
   const void* R;
   int64_t ldr;
-  // EPI_QKV: column c (after adding col0) is part c / hs (0 Q, 1 K, 2 V),
-  // head (c % hs) / hd, dim c % hd.  Q is [heads][T][hd]; K is
-  // [heads][S][hd]; Vt is [heads][hd][S]; local row m sits at global
-  // position zigzag(m).
+  // EPI_QKV: column c (after adding col0) is Q for c < hs (head c / hd, dim
+  // c % hd), then K for ks columns and V for ks columns (K/V head
+  // (c - hs) % ks / hd).  With B = batch sequences (0 means 1) of length S and
+  // T local rows each, Q is [heads][B*T][hd], K is [kv heads][B*S][hd] and Vt
+  // is [kv heads][hd][B*S]; local row m = b*T + i of sequence b sits at row
+  // b*S + zigzag(i).  rope_l2 = log2(theta) > 0 rotates Q and K at the row's
+  // position in its sequence (0: no rotation).
   void* Q;
   void* Kd;
   void* Vt;
-  int hs, hd, col0;
+  int hs, ks, hd, col0;
+  double rope_l2;
   int64_t S, T;
   int64_t chunk;
   int rank, fold;
+  int batch;
 };
 
+// B = batch sequences; T local rows and S positions per sequence.
 struct AttnArgs {
-  const void* Q;   // [Hd][T][HD]
-  const void* K;   // [Hd][S][HD]
-  const void* Vt;  // [Hd][HD][S]
+  const void* Q;   // [Hd][B*T][HD]
+  const void* K;   // [Hd/grp][B*S][HD]
+  const void* Vt;  // [Hd/grp][HD][B*S]
   // Other ranks' rows read in place (same layouts as K / Vt), or null when K
   // and Vt hold every row.  With them, K and Vt are read only in the rank's
   // own chunks, and chunk boundaries fall on 64-key tile boundaries.
   const void* Kg;
   const void* Vtg;
-  void* O;         // [T][ldo]; head t writes columns [t*HD, (t+1)*HD)
-  float* Op;       // partial outputs of split items [Hd][nqt][maxseg][128][HD]
-  float* ML;       // partial (max, sum) [Hd][nqt][maxseg][128][2]
+  void* O;         // [B*T][ldo]; head t writes columns [t*HD, (t+1)*HD)
+  float* Op;       // partial outputs of split items [Hd][B][nqt][maxseg][128][HD]
+  float* ML;       // partial (max, sum) [Hd][B][nqt][maxseg][128][2]
   int64_t T, S, chunk;
   int ldo, rank, fold, Hd;
+  int batch;
+  int grp;  // query heads per K/V head (0 means 1)
   int nqt, lseg, maxseg, nitems;
   float scale_log2;  // log2(e) / sqrt(HD)
   float sum_cap;     // largest 32-key block sum of exponentials before the reference max is raised

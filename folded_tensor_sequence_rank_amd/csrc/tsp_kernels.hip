@@ -74,6 +74,26 @@ __device__ __host__ inline int64_t zig(int64_t row, int64_t C, int rank, int fol
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotary position embedding (RoFormer, section 3.2) of four consecutive head
+// dims e..e+3 (e even): pair (2i, 2i+1) turns by p * theta^(-2i/d).  The angle
+// is formed and reduced modulo 2 pi in double precision (at p ~ 1e5 a
+// single-precision product would be off by ~1e-2 rad); sine and cosine of the
+// reduced angle are single precision.
+__device__ inline void rope_pairs(float* v, int e, int64_t p, int hd, double l2theta) {
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int i = e / 2 + t;
+    const double ang = (double)p * exp2(-(double)(2 * i) / hd * l2theta);
+    const double k = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
+    const float red = (float)fma(-k, 6.283185307179586, ang);
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    const float u = v[2 * t], w = v[2 * t + 1];
+    v[2 * t] = u * cs - w * sn;
+    v[2 * t + 1] = u * sn + w * cs;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, fp32 math, one wave per row.
 // HBM-bound: reads the row once for the sum of squares and once more (from
@@ -716,8 +736,18 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   for (int i = 0; i < MB; i++) {
     const int m = m0 + wm * WM + i * 32 + lr;
     if (m >= g.M) continue;
-    int64_t pos = m;
-    if constexpr (EPI == EPI_QKV) pos = zig(m, g.chunk, g.rank, g.fold);
+    int64_t pos = m, spos = m;
+    int64_t qrows = g.T, krows = g.S;  // Q rows and K/V positions per head
+    if constexpr (EPI == EPI_QKV) {
+      // local row m = b*T + i of sequence b sits at position zigzag(i) of its
+      // sequence, key row b*S + zigzag(i)
+      const int nbt = g.batch > 0 ? g.batch : 1;
+      const int64_t sq = m / g.T;
+      spos = zig(m - sq * g.T, g.chunk, g.rank, g.fold);
+      pos = sq * g.S + spos;
+      qrows = nbt * g.T;
+      krows = nbt * g.S;
+    }
 #pragma unroll
     for (int j = 0; j < NB; j++) {
       float v[16], w[16];
@@ -823,22 +853,23 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
         for (int q = 0; q < 4; q++) {
           if (!ok[q]) continue;
           const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
-          // hs and hd are multiples of 4, so the four columns share part and head.
+          // hs, ks and hd are multiples of 4, so the four columns share part and head.
           const int c = n + g.col0;
-          const int part = c / g.hs;
-          const int rem = c - part * g.hs;
+          const int part = c < g.hs ? 0 : (c < g.hs + g.ks ? 1 : 2);
+          const int rem = part == 0 ? c : c - g.hs - (part - 1) * g.ks;
           const int head = rem / g.hd;
           const int e = rem - head * g.hd;
+          float o4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+          if (part < 2 && g.rope_l2 > 0.0) rope_pairs(o4, e, spos, g.hd, g.rope_l2);
           if (part == 0) {
-            store4<T>((T*)g.Q + ((int64_t)head * g.T + m) * g.hd + e, v[4 * q], v[4 * q + 1],
-                      v[4 * q + 2], v[4 * q + 3]);
+            store4<T>((T*)g.Q + ((int64_t)head * qrows + m) * g.hd + e, o4[0], o4[1], o4[2], o4[3]);
           } else if (part == 1) {
-            store4<T>((T*)g.Kd + ((int64_t)head * g.S + pos) * g.hd + e, v[4 * q], v[4 * q + 1],
-                      v[4 * q + 2], v[4 * q + 3]);
+            store4<T>((T*)g.Kd + ((int64_t)head * krows + pos) * g.hd + e, o4[0], o4[1], o4[2],
+                      o4[3]);
           } else {
-            T* pv = (T*)g.Vt + ((int64_t)head * g.hd + e) * g.S + pos;
+            T* pv = (T*)g.Vt + ((int64_t)head * g.hd + e) * krows + pos;
 #pragma unroll
-            for (int t = 0; t < 4; t++) pv[(int64_t)t * g.S] = from_f<T>(v[4 * q + t]);
+            for (int t = 0; t < 4; t++) pv[(int64_t)t * krows] = from_f<T>(o4[t]);
           }
         }
       }
@@ -950,6 +981,25 @@ __device__ __attribute__((always_inline)) inline int first_tile_past(const AttnA
   return l;
 }
 
+// Micro-batch: sequences of one call (0 means 1).
+__device__ __host__ inline int batch_of(const AttnArgs& a) { return a.batch > 0 ? a.batch : 1; }
+
+// K/V head read by query head `head` (grouped-query attention).
+__device__ __attribute__((always_inline)) inline int kv_head(const AttnArgs& a, int head) {
+  return a.grp > 1 ? head / a.grp : head;
+}
+
+// Workgroup -> (head, sequence sb, work item): heads innermost, then the
+// sequences of the micro-batch, then the items.
+__device__ __attribute__((always_inline)) inline void block_item(const AttnArgs& a, int& head, int& sb,
+                                                                 int& item) {
+  const int nb = batch_of(a);
+  head = blockIdx.x % a.Hd;
+  const int r = blockIdx.x / a.Hd;
+  sb = r % nb;
+  item = r / nb;
+}
+
 __device__ __attribute__((always_inline)) inline bool decode_item(const AttnArgs& a, int item, int& qt, int& seg, int& nseg,
                                    int64_t& kend) {
   for (seg = 0; seg < a.maxseg; seg++) {
@@ -990,10 +1040,14 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int head = blockIdx.x % a.Hd;
+  int head, sb, item;
+  block_item(a, head, sb, item);
   int qt, seg, nseg;
   int64_t kend;
-  if (!decode_item(a, blockIdx.x / a.Hd, qt, seg, nseg, kend)) return;
+  if (!decode_item(a, item, qt, seg, nseg, kend)) return;
+  // sequence sb: its local rows, its key rows and the V^T row stride
+  const int nb = batch_of(a);
+  const int64_t BS = (int64_t)nb * a.S, BT = (int64_t)nb * a.T;
 
   // Positions fit in 32 bits (S < 2^31).
   const int kend32 = (int)kend;
@@ -1015,9 +1069,10 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   const int kend_w = wok ? (int)zig(min(T32, row0 + 32 * QB) - 1, C32, a.rank, a.fold) + 1 : 0;
   const int qmin_w = wok ? (int)zig(row0, C32, a.rank, a.fold) : 0;
 
-  const T* Qh = (const T*)a.Q + (int64_t)head * a.T * HD;
-  const T* Kh = (const T*)a.K + (int64_t)head * a.S * HD;
-  const T* Vh = (const T*)a.Vt + (int64_t)head * HD * a.S;
+  const int kvh = kv_head(a, head);
+  const T* Qh = (const T*)a.Q + ((int64_t)head * BT + (int64_t)sb * a.T) * HD;
+  const T* Kh = (const T*)a.K + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD;
+  const T* Vh = (const T*)a.Vt + (int64_t)kvh * HD * BS + (int64_t)sb * a.S;
 
   frag qf[QB][QK];
 #pragma unroll
@@ -1049,8 +1104,8 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   // V^T rows d (64 keys each).
   const bool split_src = a.Kg != nullptr;
   const OwnChunks own_tile(a);
-  const T* Kgh = split_src ? (const T*)a.Kg + (int64_t)head * a.S * HD : Kh;
-  const T* Vgh = split_src ? (const T*)a.Vtg + (int64_t)head * HD * a.S : Vh;
+  const T* Kgh = split_src ? (const T*)a.Kg + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD : Kh;
+  const T* Vgh = split_src ? (const T*)a.Vtg + (int64_t)kvh * HD * BS + (int64_t)sb * a.S : Vh;
   constexpr int KJ = (KI + 3) / 4, VJ = (VI + 3) / 4;  // wave loads per tile per wave
   int krow[KJ], voff[VJ], vkey[VJ];
   uint32_t koff[KJ];
@@ -1067,7 +1122,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     const int d = b / VROWB, p = (b % VROWB) >> 4;
     const int c = swz<VCH>(p, d);
     vkey[j] = c * V;
-    voff[j] = (int)(((int64_t)d * a.S + c * V) * ES);
+    voff[j] = (int)(((int64_t)d * BS + c * V) * ES);
   }
   // Loads [lo, hi) of this wave's KJ + VJ loads of a tile (K first).
   auto issue_part = [&](int k0, int buf, int lo, int hi) {
@@ -1075,7 +1130,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     char* sV = sK + KT_BYTES;
     const bool mine = !split_src || own_tile(k0);
     const brsrc rK = make_rsrc(mine ? Kh : Kgh, (uint64_t)a.S * HD * ES);
-    const brsrc rV = make_rsrc(mine ? Vh : Vgh, (uint64_t)HD * a.S * ES);
+    const brsrc rV = make_rsrc(mine ? Vh : Vgh, (uint64_t)((HD - 1) * BS + a.S) * ES);
 #pragma unroll
     for (int j = 0; j < KJ; j++) {
       if (j >= lo && j < hi && (KI % 4 == 0 || wave + 4 * j < KI))
@@ -1303,7 +1358,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     if (nseg == 1) {
       if (qok[b]) {
         const float inv = 1.0f / lt;
-        T* orow = (T*)a.O + row * a.ldo + head * HD;
+        T* orow = (T*)a.O + ((int64_t)sb * a.T + row) * a.ldo + head * HD;
 #pragma unroll
         for (int d = 0; d < DB; d++)
 #pragma unroll
@@ -1316,7 +1371,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
       }
     } else {
       const int64_t slot =
-          (((int64_t)head * a.nqt + qt) * a.maxseg + seg) * kBQ + wave * 32 * QB + 32 * b + lr;
+          ((((int64_t)head * nb + sb) * a.nqt + qt) * a.maxseg + seg) * kBQ + wave * 32 * QB + 32 * b + lr;
       float* op = a.Op + slot * HD;
 #pragma unroll
       for (int d = 0; d < DB; d++)
@@ -1378,10 +1433,14 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int head = blockIdx.x % a.Hd;
+  int head, sb, item;
+  block_item(a, head, sb, item);
   int qt, seg, nseg;
   int64_t kend;
-  if (!decode_item(a, blockIdx.x / a.Hd, qt, seg, nseg, kend)) return;
+  if (!decode_item(a, item, qt, seg, nseg, kend)) return;
+  // sequence sb: its local rows, its key rows and the V^T row stride
+  const int nb = batch_of(a);
+  const int64_t BS = (int64_t)nb * a.S, BT = (int64_t)nb * a.T;
   const int kend32 = (int)kend;
   const int kbeg = seg * a.lseg;
   const int kfin = min(kend32, kbeg + a.lseg);
@@ -1394,9 +1453,10 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   const int kend_w = wok ? (int)zig(min(T32, row0 + 32) - 1, C32, a.rank, a.fold) + 1 : 0;
   const int qmin_w = wok ? (int)zig(row0, C32, a.rank, a.fold) : 0;
 
-  const T* Qh = (const T*)a.Q + (int64_t)head * a.T * HD;
-  const T* Kh = (const T*)a.K + (int64_t)head * a.S * HD;
-  const T* Vh = (const T*)a.Vt + (int64_t)head * HD * a.S;
+  const int kvh = kv_head(a, head);
+  const T* Qh = (const T*)a.Q + ((int64_t)head * BT + (int64_t)sb * a.T) * HD;
+  const T* Kh = (const T*)a.K + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD;
+  const T* Vh = (const T*)a.Vt + (int64_t)kvh * HD * BS + (int64_t)sb * a.S;
   frag qf[QK];
 #pragma unroll
   for (int ks = 0; ks < QK; ks++)
@@ -1405,8 +1465,8 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   // Direct loads, as in attn_kernel.
   const bool split_src = a.Kg != nullptr;
   const OwnChunks own_tile(a);
-  const T* Kgh = split_src ? (const T*)a.Kg + (int64_t)head * a.S * HD : Kh;
-  const T* Vgh = split_src ? (const T*)a.Vtg + (int64_t)head * HD * a.S : Vh;
+  const T* Kgh = split_src ? (const T*)a.Kg + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD : Kh;
+  const T* Vgh = split_src ? (const T*)a.Vtg + (int64_t)kvh * HD * BS + (int64_t)sb * a.S : Vh;
   int krow[KJ], vkey[VJ];
   uint32_t koff[KJ], voff[VJ];
 #pragma unroll
@@ -1422,7 +1482,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     const int d = b / VROWB, p = (b % VROWB) >> 4;
     const int c = swz<VCH>(p, d);
     vkey[j] = c * V;
-    voff[j] = (uint32_t)(((int64_t)d * a.S + c * V) * ES);
+    voff[j] = (uint32_t)(((int64_t)d * BS + c * V) * ES);
   }
   char* const sK0 = smem;
   char* const sV0 = smem + 2 * KT;
@@ -1444,7 +1504,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     }
   };
   auto issueV = [&](int k0, int buf) {
-    const brsrc rV = make_rsrc(!split_src || own_tile(k0) ? Vh : Vgh, (uint64_t)HD * a.S * ES);
+    const brsrc rV = make_rsrc(!split_src || own_tile(k0) ? Vh : Vgh, (uint64_t)((HD - 1) * BS + a.S) * ES);
     if (k0 + BKV <= kend32) {
 #pragma unroll
       for (int j = 0; j < VJ; j++)
@@ -1739,7 +1799,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   if (nseg == 1) {
     if (qok) {
       const float inv = 1.0f / lt;
-      T* orow = (T*)a.O + row * a.ldo + head * HD;
+      T* orow = (T*)a.O + ((int64_t)sb * a.T + row) * a.ldo + head * HD;
 #pragma unroll
       for (int d = 0; d < DB; d++)
 #pragma unroll
@@ -1748,7 +1808,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
                     o[d][4 * q + 2] * inv, o[d][4 * q + 3] * inv);
     }
   } else {
-    const int64_t slot = (((int64_t)head * a.nqt + qt) * a.maxseg + seg) * kBQ + wave * 32 + lr;
+    const int64_t slot = ((((int64_t)head * nb + sb) * a.nqt + qt) * a.maxseg + seg) * kBQ + wave * 32 + lr;
     float* op = a.Op + slot * HD;
 #pragma unroll
     for (int d = 0; d < DB; d++)
@@ -1771,13 +1831,16 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t rid = gid / DQ;
   const int dq = (int)(gid % DQ);
-  const int64_t head = rid / a.T, row = rid % a.T;
+  const int nb = batch_of(a);
+  const int64_t BT = (int64_t)nb * a.T;
+  const int64_t head = rid / BT, rowg = rid % BT;  // rowg = sb * T + row
   if (head >= a.Hd) return;
+  const int64_t sb = rowg / a.T, row = rowg % a.T;
   const int qt = (int)(row / kBQ);
   const int64_t kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold);
   const int nseg = (int)((kend + a.lseg - 1) / a.lseg);
   if (nseg == 1) return;
-  const int64_t base = ((head * a.nqt + qt) * a.maxseg) * kBQ + (row % kBQ);
+  const int64_t base = (((head * nb + sb) * a.nqt + qt) * a.maxseg) * kBQ + (row % kBQ);
   float mx = -INFINITY;
   for (int s = 0; s < nseg; s++) mx = fmaxf(mx, a.ML[2 * (base + s * kBQ)]);
   float L = 0.f;
@@ -1794,7 +1857,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
     acc.w += w * v.w;
   }
   const float inv = 1.0f / L;
-  store4<T>((T*)a.O + row * a.ldo + head * HD + 4 * dq, acc.x * inv, acc.y * inv, acc.z * inv,
+  store4<T>((T*)a.O + rowg * a.ldo + head * HD + 4 * dq, acc.x * inv, acc.y * inv, acc.z * inv,
             acc.w * inv);
 }
 
@@ -1955,11 +2018,13 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
     if (tiles(256, 192) > 256) {
       gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
     } else {
-      const Cand single[] = {{256, 256, 1.0}, {256, 192, 0.95}, {128, 128, 0.55}};
-      const int best = pick(single, 3);
+      // 128x192 fills the chip at the narrow N of grouped K/V (hs + 2ks)
+      const Cand single[] = {{256, 256, 1.0}, {256, 192, 0.95}, {128, 128, 0.55}, {128, 192, 0.8}};
+      const int best = pick(single, 4);
       if (best == 0) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
       else if (best == 1) gemm_go<bf16, 256, 192, EPI, 8, 4>(a, vec, s);
-      else gemm_go<bf16, 128, 128, EPI>(a, vec, s);
+      else if (best == 2) gemm_go<bf16, 128, 128, EPI>(a, vec, s);
+      else gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
     }
   }
 }
@@ -1993,11 +2058,11 @@ template <typename T, int HD>
 static void attn_go(const AttnArgs& a, const AttnPlan& p, int part, hipStream_t s) {
   if (part == 0) {
     if (TSP_ATTN_PIPE && sizeof(T) == 2 && HD == 128)
-      attn_pipe_kernel<<<p.nitems * a.Hd, 256, 0, s>>>(a);
+      attn_pipe_kernel<<<p.nitems * a.Hd * batch_of(a), 256, 0, s>>>(a);
     else
-      attn_kernel<T, HD><<<p.nitems * a.Hd, 256, 0, s>>>(a);
+      attn_kernel<T, HD><<<p.nitems * a.Hd * batch_of(a), 256, 0, s>>>(a);
   } else if (p.split) {
-    const int64_t n = (int64_t)a.Hd * a.T * (HD / 4);
+    const int64_t n = (int64_t)a.Hd * batch_of(a) * a.T * (HD / 4);
     attn_combine_kernel<T, HD><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
   }
 }

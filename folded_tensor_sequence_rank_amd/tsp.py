@@ -42,7 +42,9 @@ class TspDims(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("fold", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("seq", ctypes.c_int64), ("eps", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float)]
 
 
 _lib = None
@@ -90,10 +92,14 @@ def header_symbols() -> List[str]:
 
 def make_dims(cfg, rank: int, flags: int = 0, seq: Optional[int] = None) -> TspDims:
     """TspDims from any object with hidden, n_heads, head_dim, ffn, fold, seq,
-    eps and dtype ("bf16" or "f32") attributes."""
+    eps and dtype ("bf16" or "f32") attributes, and optionally batch (the
+    micro-batch of sequences, default 1), n_kv_heads (default n_heads) and
+    rope_theta (default 0: no rotary embedding)."""
     return TspDims(cfg.hidden, cfg.n_heads, cfg.head_dim, cfg.ffn, cfg.fold, rank,
                    cfg.seq if seq is None else seq, cfg.eps,
-                   TSP_BF16 if cfg.dtype == "bf16" else TSP_F32, flags)
+                   TSP_BF16 if cfg.dtype == "bf16" else TSP_F32, flags,
+                   int(getattr(cfg, "batch", 1)), int(getattr(cfg, "n_kv_heads", 0) or 0),
+                   float(getattr(cfg, "rope_theta", 0.0) or 0.0))
 
 
 def _check(rc: int):
@@ -178,17 +184,20 @@ def tsp_profile_read(reset: bool = True) -> dict:
 # ----------------------------------------------------------------------------
 
 def pack_attn_shards(wq, wk, wv, wo, fold: int):
-    """Packed attention shards from math-layout [h, h] weights (Q = n @ wq):
-    per shard j the output-major blocks of W_Q, W_K, W_V columns of head
-    group j, then the output-major block of W_O's rows of that group."""
+    """Packed attention shards from math-layout weights (Q = n @ wq; wq, wo
+    [h, h]; wk, wv [h, Hkv*d]): per shard j the output-major blocks of the
+    W_Q columns of head group j and of the W_K, W_V columns of K/V head group
+    j, then the output-major block of W_O's rows of head group j."""
     import torch
     h = wq.shape[0]
     hs = h // fold
+    ks = wk.shape[1] // fold
     out = []
     for j in range(fold):
         c = slice(j * hs, (j + 1) * hs)
-        out.append(torch.cat([wq[:, c].t().reshape(-1), wk[:, c].t().reshape(-1),
-                              wv[:, c].t().reshape(-1), wo[c, :].t().reshape(-1)]).contiguous())
+        k = slice(j * ks, (j + 1) * ks)
+        out.append(torch.cat([wq[:, c].t().reshape(-1), wk[:, k].t().reshape(-1),
+                              wv[:, k].t().reshape(-1), wo[c, :].t().reshape(-1)]).contiguous())
     return out
 
 
@@ -206,5 +215,6 @@ def pack_mlp_shards(w1, w3, w2, fold: int):
 
 
 def kv_elems(cfg) -> int:
-    """Elements of the gathered K/V buffer: D blocks of 2 * (H/D) * S * d."""
-    return 2 * cfg.n_heads * cfg.seq * cfg.head_dim
+    """Elements of the gathered K/V buffer: D blocks of 2 * (Hkv/D) * B * S * d."""
+    hkv = int(getattr(cfg, "n_kv_heads", 0) or cfg.n_heads)
+    return 2 * hkv * cfg.seq * cfg.head_dim * int(getattr(cfg, "batch", 1))

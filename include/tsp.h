@@ -23,39 +23,64 @@
  * ---------------------------------------------------------------------------
  * Notation: h hidden, H heads, d = h/H head dim, F FFN width, S sequence
  * length, D fold degree, r rank.  C = S/(2D) zigzag chunk, T = S/D = 2C local
- * tokens, Hd = H/D heads per shard, hs = h/D = Hd*d, Fs = F/D.
+ * tokens, Hd = H/D heads per shard, hs = h/D = Hd*d, Fs = F/D.  Hkv K/V heads
+ * (Hkv = H unless dims->n_kv_heads says otherwise), Hkd = Hkv/D K/V heads per
+ * shard, ks = Hkd*d, g = H/Hkv query heads per K/V head.
  * b = element size (2 for bf16, 4 for fp32).
  *
  * Layer (pre-norm): x1 = x + Attn(RMSNorm(x; g1)) W_O,
  *                   out = x1 + (silu(n2 W1) * (n2 W3)) W2, n2 = RMSNorm(x1; g2).
  * RMSNorm(x; g) = x / sqrt(mean(x^2) + eps) * g.  Attention is causal
- * (key position <= query position), scale 1/sqrt(d), every head has its own
- * K/V, no bias or positional encoding.
+ * (key position <= query position), scale 1/sqrt(d), no bias.  Query head t
+ * reads K/V head t / g (grouped-query attention; g = 1 gives every head its
+ * own K/V, the pages' setting).
+ *
+ * Positional encoding.  The pages name none, and by default there is none.
+ * With dims->rope_theta = theta > 0, Q and K carry the rotary position
+ * embedding of RoFormer (Su et al., "RoFormer: Enhanced Transformer with
+ * Rotary Position Embedding", section 3.2): in every head, the pair of dims
+ * (2i, 2i+1) of the row at position p is rotated by the angle
+ * p * theta^(-2i/d), i = 0 .. d/2-1, with
+ *   out[2i]   = u cos(a) - v sin(a),   out[2i+1] = u sin(a) + v cos(a),
+ * (u, v) being the pair before rotation.  p is the token's global position in
+ * its sequence, so a rank's zigzag rows carry the angles of the positions
+ * they hold, not of their local order.  Angles are reduced modulo 2 pi in
+ * double precision before the single-precision sine and cosine.
  *
  * Zigzag layout (section 2, attention layers): the sequence is cut into 2D
  * chunks of C tokens; rank r holds chunk r then chunk 2D-1-r.  Local row
  * i < C is global position r*C + i; local row C + i is (2D-1-r)*C + i.
+ *
+ * Micro-batch (section 2, results: TSP leaves room for larger micro-batches):
+ * B = dims->batch independent sequences of length S share the weights.  Each
+ * is zigzag-partitioned as above; local activations are sequence-major,
+ * [B*T][h], rows [b*T, (b+1)*T) being sequence b's T local rows, and every
+ * query attends only to keys of its own sequence.
  *
  * Weight shards (section 2: attention shards pack W_Q, W_K, W_V, W_O; the MLP
  * shards are W1, W3, W2).  Shard j covers heads [j*Hd, (j+1)*Hd) and FFN
  * columns [j*Fs, (j+1)*Fs).  Every matrix block is stored "output-major"
  * (each row is one output feature, its input features contiguous), so a
  * projection y = a W reads block row n as column n of W:
- *   attention shard j, 4*hs*h elements, contiguous:
- *     [0,    hs) rows x h cols : row n = column j*hs + n of W_Q
- *     [hs, 2hs)  rows x h cols : row n = column j*hs + n of W_K
- *     [2hs,3hs)  rows x h cols : row n = column j*hs + n of W_V
- *     then h rows x hs cols    : row n, col k = W_O[j*hs + k][n]
+ *   attention shard j, (2*hs + 2*ks)*h elements, contiguous (4*hs*h when
+ *   Hkv = H); W_K and W_V have Hkv*d columns, shard j holding K/V heads
+ *   [j*Hkd, (j+1)*Hkd), which serve its query heads:
+ *     [0, hs)           rows x h cols : row n = column j*hs + n of W_Q
+ *     [hs, hs+ks)       rows x h cols : row n = column j*ks + n of W_K
+ *     [hs+ks, hs+2ks)   rows x h cols : row n = column j*ks + n of W_V
+ *     then h rows x hs cols           : row n, col k = W_O[j*hs + k][n]
  *   MLP shard j, 3*Fs*h elements, contiguous:
  *     Fs rows x h cols : row n = column j*Fs + n of W1 (gate, through silu)
  *     Fs rows x h cols : row n = column j*Fs + n of W3 (linear branch)
  *     h rows x Fs cols : row n, col k = W2[j*Fs + k][n]
  *
- * Gathered K/V (the all-gather's result), D blocks of 2*Hd*S*d elements;
+ * Gathered K/V (the all-gather's result), D blocks of 2*Hkd*B*S*d elements;
  * block j = [K_j | Vt_j]:
- *     K_j  [Hd][S][d] : K_j[t][p][e]  = K of head j*Hd+t, position p, dim e
- *     Vt_j [Hd][d][S] : Vt_j[t][e][p] = V of head j*Hd+t, position p, dim e
+ *     K_j  [Hkd][B*S][d] : K_j[t][b*S + p][e]  = K of K/V head j*Hkd+t, sequence b, position p, dim e
+ *     Vt_j [Hkd][d][B*S] : Vt_j[t][e][b*S + p] = V of K/V head j*Hkd+t, sequence b, position p, dim e
  * V is stored transposed so that the P.V contraction reads keys contiguously.
+ * K is stored after the rotary embedding when rope_theta > 0.  With B = 1 and
+ * Hkv = H these are [Hd][S][d] and [Hd][d][S].
  *
  * ---------------------------------------------------------------------------
  * Conventions for every entry point
@@ -92,8 +117,10 @@ enum { TSP_BF16 = 0, TSP_F32 = 1 };
 
 enum {
   TSP_OK = 0,
-  TSP_E_INVAL = -1,     /* null pointer, rank outside [0, D), negative size */
-  TSP_E_SHAPE = -2,     /* h != H*d, H % D, F % D, S % 2D, S % 8, unsupported d */
+  TSP_E_INVAL = -1,     /* null pointer, rank outside [0, D), negative size, batch,
+                           n_kv_heads or rope_theta */
+  TSP_E_SHAPE = -2,     /* h != H*d, H % D, F % D, S % 2D, S % 8, unsupported d,
+                           H % Hkv, Hkv % D */
   TSP_E_ALIGN = -3,     /* a device pointer is not 16-byte aligned */
   TSP_E_WORKSPACE = -4, /* ws_bytes < tsp_workspace_bytes(...) */
   TSP_E_DTYPE = -5,     /* dtype is neither TSP_BF16 nor TSP_F32 */
@@ -140,6 +167,9 @@ typedef struct tsp_dims {
   float eps;        /* RMSNorm epsilon (inside the square root) */
   int32_t dtype;    /* TSP_BF16 or TSP_F32 */
   uint32_t flags;   /* TSP_F_* */
+  int32_t batch;    /* B, micro-batch of independent sequences (0 means 1) */
+  int32_t n_kv_heads; /* Hkv, K/V heads; 0 means H.  H % Hkv == 0, Hkv % D == 0 */
+  float rope_theta;   /* rotary embedding base theta; 0 means no rotary embedding */
 } tsp_dims;
 
 /* Bytes of workspace an entry point needs for these dims (0 on bad dims). */
@@ -165,11 +195,11 @@ int tsp_zigzag_positions(int64_t seq, int32_t fold, int32_t rank, int64_t* out);
  * causal window needs, positions < (2D-r)*C, from `kv`: read in place when
  * C % 64 == 0, else first copied next to its own), and the partial
  * O-projection of head group j is accumulated locally in fp32.
- *   x      [T][h]   local rows in zigzag order
+ *   x      [B*T][h] local rows in zigzag order, sequence-major
  *   g1     [h]      RMSNorm gain
  *   w_attn D device pointers to packed attention shards (layout above)
  *   kv     gathered K/V (layout above); only other ranks' rows are read
- *   x1     [T][h]   output
+ *   x1     [B*T][h] output
  *   ws     workspace of at least tsp_workspace_bytes(dims, TSP_WS_ATTN) bytes
  */
 int tsp_attn_shard(const tsp_dims* dims, const void* x, const void* g1,
@@ -182,8 +212,8 @@ int tsp_attn_shard(const tsp_dims* dims, const void* x, const void* g1,
  * (own shard first, read in place; the others are copied into a workspace
  * slot on the side stream); the partial outputs are summed locally in fp32,
  * so no all-reduce is needed.
- *   x1    [T][h], g2 [h], w_mlp D device pointers to packed MLP shards,
- *   out   [T][h], ws >= tsp_workspace_bytes(dims, TSP_WS_MLP).
+ *   x1    [B*T][h], g2 [h], w_mlp D device pointers to packed MLP shards,
+ *   out   [B*T][h], ws >= tsp_workspace_bytes(dims, TSP_WS_MLP).
  */
 int tsp_mlp_shard(const tsp_dims* dims, const void* x1, const void* g2,
                   const void* const* w_mlp, void* out,
@@ -204,7 +234,7 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1,
  * the all-gather rebuilds full-length K/V along the sequence): writes K and
  * V of rank r's local tokens, for every head, at their global positions into
  * `kv` (layout above).  Rows of other ranks are left untouched.
- *   x [T][h], g1 [h], w_attn D device pointers, ws >= tsp_workspace_bytes(dims, TSP_WS_KV).
+ *   x [B*T][h], g1 [h], w_attn D device pointers, ws >= tsp_workspace_bytes(dims, TSP_WS_KV).
  */
 int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1,
                  const void* const* w_attn, void* kv,

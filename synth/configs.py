@@ -27,6 +27,9 @@ class LayerConfig:
     w_std: float = 0.02  # weights ~ N(0, w_std^2)
     x_std: float = 1.0   # activations ~ N(0, x_std^2)
     gamma: str = "ones"  # RMSNorm gain: "ones" or "normal" (1 + N(0, 0.1^2))
+    batch: int = 1       # B, micro-batch of independent sequences of length seq
+    n_kv_heads: int = 0  # Hkv, K/V heads of grouped-query attention (0: one per head)
+    rope_theta: float = 0.0  # rotary embedding base (0: no positional encoding)
 
     @property
     def chunk(self) -> int:      # C = S / (2D)
@@ -35,6 +38,10 @@ class LayerConfig:
     @property
     def local_tokens(self) -> int:  # T = S / D
         return self.seq // self.fold
+
+    @property
+    def kv_heads(self) -> int:   # Hkv
+        return self.n_kv_heads or self.n_heads
 
     @property
     def heads_per_shard(self) -> int:
@@ -57,6 +64,15 @@ CONFIGS = {
     "7b_s64k": LayerConfig("7b_s64k", 4096, 32, 128, 11008, 65536, 8, (3,)),
     # Attention-dominated 128K context; the first and last rank both run.
     "7b_s128k": LayerConfig("7b_s128k", 4096, 32, 128, 11008, 131072, 8, (0, 7)),
+    # The 16K shape with a micro-batch of 4 sequences (8192 local rows).
+    "7b_s16k_b4": LayerConfig("7b_s16k_b4", 4096, 32, 128, 11008, 16384, 8, (3,), batch=4),
+    # The 64K shape with the rotary embedding (base 10^4) that 7B dense models
+    # commonly use, and with it grouped-query attention over 8 K/V heads (one
+    # per rank).  The pages name neither; both are extensions of the layer.
+    "7b_rope_s64k": LayerConfig("7b_rope_s64k", 4096, 32, 128, 11008, 65536, 8, (3,),
+                                rope_theta=10000.0),
+    "7b_gqa8_rope_s64k": LayerConfig("7b_gqa8_rope_s64k", 4096, 32, 128, 11008, 65536, 8, (3,),
+                                     n_kv_heads=8, rope_theta=10000.0),
     # Every rank of a 4-layer stack at fold 4, run one after another.
     "7b_fold4_s32k_4layer": LayerConfig("7b_fold4_s32k_4layer", 4096, 32, 128, 11008,
                                         32768, 4, (0, 1, 2, 3), 4),

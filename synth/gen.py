@@ -43,29 +43,33 @@ def _rng(seed: int, layer: int, tid: int, *extra: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, layer, tid, *extra])))
 
 
-def gen_x_rows(cfg, lo: int, hi: int, layer: int = 0) -> np.ndarray:
-    """Rows [lo, hi) of the input activations x_full [S, h] (float32)."""
+def gen_x_rows(cfg, lo: int, hi: int, layer: int = 0, seq_index: int = 0) -> np.ndarray:
+    """Rows [lo, hi) of the input activations x_full [S, h] (float32) of
+    sequence seq_index of a micro-batch (sequence 0 is the single-sequence
+    stream; each other sequence draws from a stream of its own)."""
+    extra = (seq_index,) if seq_index else ()
     if hi <= lo:
         return np.zeros((0, cfg.hidden), np.float32)
     out = np.empty((hi - lo, cfg.hidden), np.float32)
     b0, b1 = lo // ROW_BLOCK, (hi - 1) // ROW_BLOCK
     for b in range(b0, b1 + 1):
         rows = min(ROW_BLOCK, cfg.seq - b * ROW_BLOCK)
-        blk = _rng(cfg.seed, layer, _TID["x"], b).standard_normal((rows, cfg.hidden), np.float32)
+        blk = _rng(cfg.seed, layer, _TID["x"], b, *extra).standard_normal((rows, cfg.hidden),
+                                                                          np.float32)
         blk *= np.float32(cfg.x_std)
         s, e = max(lo, b * ROW_BLOCK), min(hi, b * ROW_BLOCK + rows)
         out[s - lo:e - lo] = blk[s - b * ROW_BLOCK:e - b * ROW_BLOCK]
     return _finish(out, cfg.dtype)
 
 
-def gen_rows(cfg, positions: np.ndarray, layer: int = 0) -> np.ndarray:
+def gen_rows(cfg, positions: np.ndarray, layer: int = 0, seq_index: int = 0) -> np.ndarray:
     """x_full rows at arbitrary global positions (in the order given)."""
     positions = np.asarray(positions, dtype=np.int64)
     if positions.size == 0:
         return np.zeros((0, cfg.hidden), np.float32)
     lo, hi = int(positions.min()), int(positions.max()) + 1
     # Draw the covering blocks once, then gather.
-    blk = gen_x_rows(cfg, lo, hi, layer)
+    blk = gen_x_rows(cfg, lo, hi, layer, seq_index)
     return blk[positions - lo]
 
 
@@ -82,8 +86,8 @@ def gen_gamma(cfg, which: str, layer: int = 0) -> np.ndarray:
 class LayerWeights:
     g1: np.ndarray  # [h]
     wq: np.ndarray  # [h, h]
-    wk: np.ndarray  # [h, h]
-    wv: np.ndarray  # [h, h]
+    wk: np.ndarray  # [h, Hkv*d]
+    wv: np.ndarray  # [h, Hkv*d]
     wo: np.ndarray  # [h, h]
     g2: np.ndarray  # [h]
     w1: np.ndarray  # [h, F]  gate branch (passed through silu)
@@ -93,6 +97,7 @@ class LayerWeights:
 
 def gen_weights(cfg, layer: int = 0) -> LayerWeights:
     h, F = cfg.hidden, cfg.ffn
+    hk = (cfg.n_kv_heads or cfg.n_heads) * cfg.head_dim
     std = np.float32(cfg.w_std)
 
     def w(name, shape):
@@ -100,8 +105,8 @@ def gen_weights(cfg, layer: int = 0) -> LayerWeights:
                        cfg.dtype)
 
     return LayerWeights(
-        g1=gen_gamma(cfg, "g1", layer), wq=w("wq", (h, h)), wk=w("wk", (h, h)),
-        wv=w("wv", (h, h)), wo=w("wo", (h, h)), g2=gen_gamma(cfg, "g2", layer),
+        g1=gen_gamma(cfg, "g1", layer), wq=w("wq", (h, h)), wk=w("wk", (h, hk)),
+        wv=w("wv", (h, hk)), wo=w("wo", (h, h)), g2=gen_gamma(cfg, "g2", layer),
         w1=w("w1", (h, F)), w3=w("w3", (h, F)), w2=w("w2", (F, h)))
 
 

@@ -24,7 +24,7 @@ sys.path.insert(0, ROOT)
 import oracle.tsp_oracle as O  # noqa: E402
 import synth  # noqa: E402
 
-WORKLOADS = ["7b_s64k", "7b_s128k", "7b_fold4_s32k_4layer"]
+WORKLOADS = ["7b_s64k", "7b_s128k", "7b_fold4_s32k_4layer", "7b_rope_s64k", "7b_gqa8_rope_s64k"]
 
 
 def source_hash():
@@ -55,7 +55,7 @@ def main(names):
             x = synth.gen_x_rows(cfg, 0, pmax)
             w = synth.gen_weights(cfg)
             for r, (local, pos) in rows.items():
-                x1 = O.attention_block_rows(x, w, cfg.n_heads, cfg.eps, pos)
+                x1 = O.attention_block_rows(x, w, cfg.n_heads, cfg.eps, pos, cfg.rope_theta)
                 y = O.mlp_block(x1, w, cfg.eps)
                 out[f"r{r}_local"] = local
                 out[f"r{r}_pos"] = pos
@@ -67,7 +67,7 @@ def main(names):
             x = synth.gen_x_rows(cfg, 0, cfg.seq)
             ws = [synth.gen_weights(cfg, l) for l in range(cfg.layers)]
             allpos = np.concatenate([p for _, p in rows.values()])
-            y = O.stack_rows(x, ws, cfg.n_heads, cfg.eps, allpos)
+            y = O.stack_rows(x, ws, cfg.n_heads, cfg.eps, allpos, cfg.rope_theta)
             k = 0
             for r, (local, pos) in rows.items():
                 out[f"r{r}_local"] = local

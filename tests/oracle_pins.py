@@ -17,6 +17,12 @@ What the pins rest on:
     against the unsharded layer;
   * special cases: the first position sees only itself; zero queries give
     the causal prefix mean of V; a zero W1 turns the MLP off.
+  * for the extensions the pages do not describe (rotary embedding,
+    grouped-query attention): the Llama decoder layer and rotary embedding of
+    the transformers library, in float64 on the CPU (its rotary angles are
+    formed in float32, hence the 1e-4 bounds at small positions); torch's
+    scaled_dot_product_attention with enable_gqa; and the relative-position
+    property of rotated dot products.
 """
 import math
 import os
@@ -222,6 +228,144 @@ def pin_stack(o):
     assert o.rel_fro(o.stack_rows(x, ws, cfg.n_heads, cfg.eps, rows), want[rows]) < 1e-12
 
 
+# ---------------------------------------------------------------- rotary embedding, GQA
+
+def _llama():
+    from transformers import LlamaConfig
+    from transformers.models.llama import modeling_llama as ml
+    return LlamaConfig, ml
+
+
+def _half_split(d):
+    """Dim order of the Llama rotary convention (pairs (i, i + d/2)) in terms
+    of the RoFormer order (pairs (2i, 2i+1)): Llama dim i is RoFormer dim
+    2i, Llama dim d/2 + i is RoFormer dim 2i + 1."""
+    return np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+
+
+def pin_rope_llama(o):
+    LlamaConfig, ml = _llama()
+    for d, theta in [(16, 10000.0), (128, 10000.0), (8, 500.0)]:
+        cfg = LlamaConfig(hidden_size=d, num_attention_heads=1, num_key_value_heads=1, head_dim=d,
+                          rope_theta=theta, max_position_embeddings=1024)
+        rot = ml.LlamaRotaryEmbedding(cfg).double()
+        pos = np.array([0, 1, 2, 3, 7, 31, 64, 100, 255])
+        x = _rng(11).standard_normal((pos.size, d))
+        P = _half_split(d)
+        xt = torch.from_numpy(x[:, P])[None, None]          # [1, 1, R, d]
+        cos, sin = rot(xt[0], torch.from_numpy(pos)[None])
+        want, _ = ml.apply_rotary_pos_emb(xt, xt, cos, sin)
+        got = o.rope(x, pos, theta)[:, P]
+        err = np.abs(got - want[0, 0].numpy()).max()
+        assert err < 1e-4, (d, theta, err)
+        assert np.array_equal(o.rope(x, pos, 0.0), x)
+
+
+def pin_rope_relative(o):
+    """Rotated dot products depend on the position difference only; rows at
+    position 0 are unchanged; each pair keeps its length."""
+    rng = _rng(12)
+    d = 16
+    q, k = rng.standard_normal((2, 1, d))
+    for theta in (10000.0, 50.0):
+        for m, n, c in [(5, 3, 0), (5, 3, 17), (0, 9, 1000), (40000, 39990, 90000)]:
+            a = o.rope(q, [m], theta) @ o.rope(k, [n], theta).T
+            b = o.rope(q, [m + c], theta) @ o.rope(k, [n + c], theta).T
+            assert abs(a - b).max() < 1e-9 * (1 + abs(a).max()), (theta, m, n, c)
+        r = o.rope(q, [123], theta)
+        assert np.allclose(r[:, 0::2] ** 2 + r[:, 1::2] ** 2, q[:, 0::2] ** 2 + q[:, 1::2] ** 2)
+        assert np.array_equal(o.rope(q, [0], theta), q)
+        # the lowest pair turns by exactly the position (in radians), counter-clockwise
+        e = np.zeros((1, d)); e[0, 0] = 1.0
+        assert np.allclose(o.rope(e, [1], theta)[0, :2], [math.cos(1.0), math.sin(1.0)], atol=1e-15)
+
+
+def _gqa(cfg, hkv, theta=0.0):
+    return cfg.with_(n_kv_heads=hkv, rope_theta=theta)
+
+
+def pin_gqa_torch(o):
+    """Grouped-query attention against torch's enable_gqa attention, by way of
+    the torch layer composition (no rotary embedding)."""
+    T = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    for cfg in [_gqa(TINY, 2), _gqa(TINY, 1), _gqa(TINY.with_(n_heads=8, head_dim=8), 4)]:
+        w, x = _weights(cfg), _x(cfg)
+        H, h, d, hkv = cfg.n_heads, cfg.hidden, cfg.head_dim, cfg.n_kv_heads
+        assert o.kv_heads(w, H) == hkv
+        X = T(x)
+        S = X.shape[0]
+        n1 = Fn.rms_norm(X, (h,), weight=T(w.g1), eps=cfg.eps)
+        heads = lambda m, nh: (n1 @ T(m)).reshape(S, nh, d).transpose(0, 1).contiguous()
+        a = Fn.scaled_dot_product_attention(heads(w.wq, H), heads(w.wk, hkv), heads(w.wv, hkv),
+                                            is_causal=True, enable_gqa=True)
+        want = (X + a.transpose(0, 1).reshape(S, h) @ T(w.wo)).numpy()
+        got = o.attention_block_rows(x, w, H, cfg.eps, np.arange(S))
+        assert o.rel_fro(got, want) < 1e-12, (cfg.n_heads, hkv, o.rel_fro(got, want))
+
+
+def llama_layer(x, w, cfg):
+    """The layer as transformers' Llama decoder layer (float64, CPU), the
+    oracle's weights loaded into it with Q and K columns put in its rotary
+    dim order."""
+    LlamaConfig, ml = _llama()
+    H, d, hkv = cfg.n_heads, cfg.head_dim, cfg.kv_heads
+    lc = LlamaConfig(hidden_size=cfg.hidden, num_attention_heads=H, num_key_value_heads=hkv,
+                     head_dim=d, intermediate_size=cfg.ffn, rms_norm_eps=cfg.eps,
+                     rope_theta=cfg.rope_theta, max_position_embeddings=max(2048, cfg.seq),
+                     attention_bias=False, mlp_bias=False)
+    lc._attn_implementation = "eager"
+    layer = ml.LlamaDecoderLayer(lc, layer_idx=0).double().eval()
+    rot = ml.LlamaRotaryEmbedding(lc).double()
+    P = _half_split(d)
+    cols = lambda nh: np.concatenate([t * d + P for t in range(nh)])
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float64)))
+    sd = {"self_attn.q_proj.weight": T(w.wq[:, cols(H)].T), "self_attn.k_proj.weight": T(w.wk[:, cols(hkv)].T),
+          "self_attn.v_proj.weight": T(w.wv.T), "self_attn.o_proj.weight": T(w.wo.T),
+          "mlp.gate_proj.weight": T(w.w1.T), "mlp.up_proj.weight": T(w.w3.T),
+          "mlp.down_proj.weight": T(w.w2.T), "input_layernorm.weight": T(w.g1),
+          "post_attention_layernorm.weight": T(w.g2)}
+    layer.load_state_dict(sd)
+    X = T(x)[None]
+    pos = torch.arange(X.shape[1])[None]
+    S = X.shape[1]
+    mask = torch.full((S, S), -math.inf, dtype=torch.float64).triu(1)[None, None]
+    with torch.no_grad():
+        out = layer(X, attention_mask=mask, position_ids=pos, position_embeddings=rot(X, pos))
+    return (out[0] if isinstance(out, tuple) else out)[0].numpy()
+
+
+def pin_layer_llama(o):
+    """Rotary embedding and grouped-query attention in the whole layer."""
+    # weights of std 0.2 make the attention sharp enough that the rotation
+    # changes the output by O(1) (checked below), so a wrong angle shows
+    base = TINY.with_(seq=64, fold=2, w_std=0.2)
+    for cfg in [_gqa(base, 2, 10000.0), _gqa(base, 4, 100.0), _gqa(base, 1, 10000.0),
+                _gqa(base.with_(hidden=64, n_heads=2, head_dim=32), 2, 10000.0)]:
+        w, x = _weights(cfg), _x(cfg)
+        want = llama_layer(x, w, cfg)
+        got = o.layer_unsharded(x, w, cfg.n_heads, cfg.eps, cfg.rope_theta)
+        assert o.rel_fro(got, want) < 1e-5, (cfg.n_kv_heads, cfg.rope_theta, o.rel_fro(got, want))
+    cfg = _gqa(base, 2, 10000.0)
+    w, x = _weights(cfg), _x(cfg)
+    assert o.rel_fro(o.layer_unsharded(x, w, cfg.n_heads, cfg.eps, 0.0), llama_layer(x, w, cfg)) > 0.1
+
+
+def pin_fold_rope_gqa(o):
+    """The literal D-rank schedule with the rotary embedding applied at the
+    ranks' global (zigzag) positions, and grouped K/V shards, equals the
+    unsharded layer."""
+    base = TINY.with_(seq=64, w_std=0.2)
+    for cfg in [_gqa(base.with_(fold=2), 2, 10000.0), _gqa(base, 4, 100.0),
+                _gqa(base.with_(fold=2, n_heads=8, head_dim=8), 2, 10000.0)]:
+        w, x = _weights(cfg), _x(cfg)
+        want = o.layer_unsharded(x, w, cfg.n_heads, cfg.eps, cfg.rope_theta)
+        parts = o.fold_schedule(x, w, cfg.n_heads, cfg.eps, cfg.fold, rope_theta=cfg.rope_theta)
+        assert o.rel_fro(o.unzigzag(parts, cfg.seq, cfg.fold), want) < 1e-12, cfg
+        r = cfg.fold - 1
+        got = o.rank_share(x, w, cfg.n_heads, cfg.eps, cfg.seq, cfg.fold, r, cfg.rope_theta)
+        assert o.rel_fro(got, parts[r]) < 1e-12
+
+
 def pin_flops(o):
     """Sum of the ranks' FLOPs equals the unsharded layer's (equal per-device
     compute), and each rank's share is exactly 1/D of it."""
@@ -238,4 +382,5 @@ def pin_flops(o):
 ALL_PINS = [pin_zigzag_statement, pin_zigzag_partition, pin_zigzag_balance, pin_unzigzag,
             pin_rmsnorm_torch, pin_silu_torch, pin_attention_torch, pin_attention_loops,
             pin_attention_special, pin_layer_torch, pin_mlp_zero_gate, pin_fold_bruteforce,
-            pin_mlp_partials, pin_stack, pin_flops]
+            pin_mlp_partials, pin_stack, pin_flops, pin_rope_llama, pin_rope_relative,
+            pin_gqa_torch, pin_layer_llama, pin_fold_rope_gqa]

@@ -76,6 +76,15 @@ def _call_attn(dims, x=16, g=16, w=None, kv=16, out=16, ws=16, ws_bytes=1 << 40)
     ("head_dim", "head_dim", 96, "TSP_E_SHAPE"),
     ("seq_2D", "seq", 65536 + 8, "TSP_E_SHAPE"),
     ("ffn_D", "ffn", 11001, "TSP_E_SHAPE"),
+    ("batch_neg", "batch", -2, "TSP_E_INVAL"),
+    ("batch_positions", "batch", 1 << 15, "TSP_E_SHAPE"),   # B*S past 2^31 - 1
+    ("kv_heads_neg", "n_kv_heads", -8, "TSP_E_INVAL"),
+    ("kv_heads_divide_H", "n_kv_heads", 24, "TSP_E_SHAPE"),   # 32 % 24
+    ("kv_heads_fold", "n_kv_heads", 4, "TSP_E_SHAPE"),        # 4 K/V heads over 8 ranks
+    ("rope_neg", "rope_theta", -1.0, "TSP_E_INVAL"),
+    ("rope_nan", "rope_theta", float("nan"), "TSP_E_INVAL"),
+    ("rope_inf", "rope_theta", float("inf"), "TSP_E_INVAL"),
+    ("rope_below_one", "rope_theta", 0.5, "TSP_E_INVAL"),
 ])
 def test_bad_dims(case, field, value, status):
     d = tsp.make_dims(C3, 3)
@@ -110,8 +119,44 @@ def test_empty_sequence_is_a_no_op():
 
 
 def test_dims_struct_layout():
-    assert ctypes.sizeof(tsp.TspDims) == 48
+    assert ctypes.sizeof(tsp.TspDims) == 56
     assert tsp.TspDims.seq.offset == 24 and tsp.TspDims.flags.offset == 40
+    assert tsp.TspDims.batch.offset == 44
+    assert tsp.TspDims.n_kv_heads.offset == 48 and tsp.TspDims.rope_theta.offset == 52
+
+
+def test_gqa_rope_dims_and_workspace():
+    """n_kv_heads 0 means H; grouped K/V shrink the K/V slots and the gathered
+    buffer by H/Hkv; the rotary embedding needs no memory."""
+    mha = tsp.make_dims(C3, 3)
+    same = tsp.make_dims(C3.with_(n_kv_heads=32, rope_theta=10000.0), 3)
+    gqa = tsp.make_dims(C3.with_(n_kv_heads=8), 3)
+    assert mha.n_kv_heads == 0 and same.n_kv_heads == 32 and abs(same.rope_theta - 1e4) < 1e-3
+    for which in (tsp.TSP_WS_ATTN, tsp.TSP_WS_MLP, tsp.TSP_WS_LAYER, tsp.TSP_WS_KV):
+        assert tsp.workspace_bytes(same, which) == tsp.workspace_bytes(mha, which)
+    a_mha = tsp.workspace_bytes(mha, tsp.TSP_WS_ATTN)
+    a_gqa = tsp.workspace_bytes(gqa, tsp.TSP_WS_ATTN)
+    # two K/V slots of 2 * (H/D) * S * d elements shrink to 2 * (Hkv/D) * S * d
+    slot = 2 * 4 * 65536 * 128 * 2
+    assert a_mha - a_gqa >= 2 * (slot - slot // 4)
+    assert tsp.workspace_bytes(gqa, tsp.TSP_WS_MLP) == tsp.workspace_bytes(mha, tsp.TSP_WS_MLP)
+    assert tsp.kv_elems(C3.with_(n_kv_heads=8)) * 4 == tsp.kv_elems(C3)
+
+
+def test_micro_batch_workspace():
+    """batch 0 means 1; the activations, K/V slots and attention partials
+    grow with the micro-batch while the weight slots do not."""
+    one = tsp.make_dims(C3, 3)
+    zero = tsp.make_dims(C3, 3)
+    zero.batch = 0
+    four = tsp.make_dims(C3.with_(batch=4), 3)
+    for which in (tsp.TSP_WS_ATTN, tsp.TSP_WS_MLP, tsp.TSP_WS_LAYER, tsp.TSP_WS_KV):
+        w1 = tsp.workspace_bytes(one, which)
+        assert tsp.workspace_bytes(zero, which) == w1
+        w4 = tsp.workspace_bytes(four, which)
+        assert w1 < w4 <= 4 * w1 + 4096, (which, w1, w4)
+    assert tsp.workspace_bytes(four, tsp.TSP_WS_KV) >= 4 * 8192 * 4096 * 2
+    assert tsp.kv_elems(C3.with_(batch=4)) == 4 * tsp.kv_elems(C3)
 
 
 def test_product_fails_loudly_without_library(monkeypatch, tmp_path):

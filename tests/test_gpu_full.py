@@ -50,7 +50,7 @@ def _inputs(cfg, layer=0):
     return L
 
 
-@pytest.mark.parametrize("name", ["7b_s64k", "7b_s128k"])
+@pytest.mark.parametrize("name", ["7b_s64k", "7b_s128k", "7b_rope_s64k", "7b_gqa8_rope_s64k"])
 def test_full_size_single_layer(name):
     cfg = synth.get_config(name)
     g = _golden(name)

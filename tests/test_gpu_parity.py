@@ -225,3 +225,155 @@ def test_7b_s16k_rank3_full():
     xr = x_full[pos[r]].astype(np.float64)
     _check(cfg, "x1", f64(x1), x1_ref, xr, xr)
     _check(cfg, "out", f64(out), out_ref, f64(x1), x1_ref)
+
+
+# Micro-batch: B independent sequences per call.  One workload per attention
+# path: pipelined bf16 with the other ranks' K/V read in place, ragged bf16
+# with the K/V copy, fp32, and query tiles split over key segments.
+BATCH = {
+    "bf16_d128_inplace_b2": SMALL["bf16_d128_inplace"].with_(batch=2),
+    "bf16_d128_ragged_b3": SMALL["bf16_d128_ragged"].with_(batch=3),
+    "f32_d64_b2": SMALL["f32_d64"].with_(batch=2),
+    "split_b2": _cfg(hidden=512, n_heads=4, head_dim=128, ffn=1024, seq=8192, fold=2, batch=2),
+}
+
+
+def _batch_setup(cfg):
+    """Weights, each sequence's activations (its own seeded stream), every
+    rank's sequence-major local rows and the gathered K/V of all ranks."""
+    B, S = cfg.batch, cfg.seq
+    w = synth.gen_weights(cfg)
+    L = layer_dev(cfg, w)
+    xf = [synth.gen_x_rows(cfg, 0, S, seq_index=b) for b in range(B)]
+    pos = [O.zigzag_positions(S, cfg.fold, r) for r in range(cfg.fold)]
+    xs = [to_dev(np.concatenate([xf[b][pos[r]] for b in range(B)]), cfg) for r in range(cfg.fold)]
+    return w, L, xf, pos, xs
+
+
+@pytest.mark.parametrize("case", sorted(BATCH))
+def test_micro_batch(case):
+    """Each sequence of the batch against the oracle run on that sequence
+    alone; the layer call equals the attention and MLP calls."""
+    cfg = BATCH[case]
+    B, T = cfg.batch, cfg.local_tokens
+    say(f"[gpu] micro-batch parity {case}: B={B} S={cfg.seq} D={cfg.fold} d={cfg.head_dim} {cfg.dtype}")
+    w, L, xf, pos, xs = _batch_setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    for r in sorted({0, cfg.fold - 1}):
+        run = RankRun(cfg, r)
+        x1 = run.attn(xs[r], L, kv)
+        out = run.mlp(x1, L)
+        lay = run.layer(xs[r], L, kv)
+        torch.cuda.synchronize()
+        assert torch.equal(lay, out), "layer call differs from attention + MLP calls"
+        g1, g2 = f64(x1), f64(out)
+        for b in range(B):
+            rows = slice(b * T, (b + 1) * T)
+            x1_ref = O.attention_block_rows(xf[b], w, cfg.n_heads, cfg.eps, pos[r])
+            out_ref = O.mlp_block(x1_ref, w, cfg.eps)
+            xr = xf[b][pos[r]].astype(np.float64)
+            _check(cfg, f"rank {r} sequence {b} x1", g1[rows], x1_ref, xr, xr)
+            _check(cfg, f"rank {r} sequence {b} out", g2[rows], out_ref, g1[rows], x1_ref)
+
+
+def test_7b_s16k_batch2_rank3():
+    """The 7B shape at 16K context, fold 8, rank 3, two sequences per call:
+    every output row of both against the oracle."""
+    cfg = synth.get_config("7b_s16k").with_(batch=2)
+    r, T = cfg.ranks[0], cfg.local_tokens
+    say(f"[gpu] 7B shape S={cfg.seq} D={cfg.fold} B=2 rank {r}: full rank parity")
+    w, L, xf, pos, xs = _batch_setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv, skip=r)
+    run = RankRun(cfg, r)
+    x1 = run.attn(xs[r], L, kv)
+    out = run.mlp(x1, L)
+    torch.cuda.synchronize()
+    say("    GPU done; oracle running")
+    g1, g2 = f64(x1), f64(out)
+    for b in range(2):
+        rows = slice(b * T, (b + 1) * T)
+        x1_ref = O.attention_block_rows(xf[b], w, cfg.n_heads, cfg.eps, pos[r])
+        out_ref = O.mlp_block(x1_ref, w, cfg.eps)
+        xr = xf[b][pos[r]].astype(np.float64)
+        _check(cfg, f"sequence {b} x1", g1[rows], x1_ref, xr, xr)
+        _check(cfg, f"sequence {b} out", g2[rows], out_ref, g1[rows], x1_ref)
+
+
+# Rotary embedding and grouped-query attention (extensions of the layer that
+# the pages do not describe).  Low-residual activations make the attention
+# half dominate the output, and weights giving attention scores of std ~0.5
+# (w_std^2 * h) make the rotation change that half by O(1) while keeping the
+# bf16 rounding of Q and K, which grows with the scores, well inside the bar.
+# Each case checks that dropping the rotation would change the output far
+# beyond the bar, so a wrong angle or K/V head cannot pass.  One workload per attention
+# path: fp32 (d = 16), bf16 d = 64, pipelined bf16 d = 128 reading the other
+# ranks' K/V in place, ragged bf16 d = 128 with the K/V copy, and query tiles
+# split over key segments with two sequences per call.
+ROPE = {
+    "tiny_f32_gqa2_rope": TINY.with_(fold=2, n_kv_heads=2, rope_theta=10000.0, x_std=0.02,
+                                     w_std=0.2),
+    "bf16_d64_gqa2_rope500": _cfg(hidden=256, n_heads=4, head_dim=64, ffn=512, seq=1024, fold=2,
+                                  n_kv_heads=2, rope_theta=500.0, x_std=0.02, w_std=0.045),
+    "bf16_d128_inplace_gqa4_rope": _cfg(hidden=1024, n_heads=8, ffn=1376, seq=2048, fold=4,
+                                        n_kv_heads=4, rope_theta=10000.0, x_std=0.02,
+                                        w_std=0.022),
+    "bf16_d128_ragged_rope": _cfg(hidden=512, n_heads=4, rope_theta=10000.0, x_std=0.02,
+                                  w_std=0.03),
+    "split_gqa2_rope_b2": _cfg(hidden=512, n_heads=4, head_dim=128, ffn=1024, seq=8192, fold=2,
+                               batch=2, n_kv_heads=2, rope_theta=10000.0, x_std=0.02,
+                               w_std=0.03),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ROPE))
+def test_rope_gqa(case):
+    cfg = ROPE[case]
+    B, T = cfg.batch, cfg.local_tokens
+    say(f"[gpu] rotary/GQA parity {case}: H={cfg.n_heads} Hkv={cfg.kv_heads} theta={cfg.rope_theta} "
+        f"B={B} S={cfg.seq} D={cfg.fold} d={cfg.head_dim} {cfg.dtype}")
+    w, L, xf, pos, xs = _batch_setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    for r in sorted({0, cfg.fold - 1}):
+        run = RankRun(cfg, r)
+        x1 = run.attn(xs[r], L, kv)
+        out = run.mlp(x1, L)
+        lay = run.layer(xs[r], L, kv)
+        torch.cuda.synchronize()
+        assert torch.equal(lay, out), "layer call differs from attention + MLP calls"
+        g1, g2 = f64(x1), f64(out)
+        for b in range(B):
+            rows = slice(b * T, (b + 1) * T)
+            x1_ref = O.attention_block_rows(xf[b], w, cfg.n_heads, cfg.eps, pos[r], cfg.rope_theta)
+            out_ref = O.mlp_block(x1_ref, w, cfg.eps)
+            xr = xf[b][pos[r]].astype(np.float64)
+            _check(cfg, f"rank {r} sequence {b} x1", g1[rows], x1_ref, xr, xr)
+            _check(cfg, f"rank {r} sequence {b} out", g2[rows], out_ref, g1[rows], x1_ref)
+            plain = O.attention_block_rows(xf[b], w, cfg.n_heads, cfg.eps, pos[r], 0.0)
+            seen = rel_fro(g1[rows] - xr, plain - xr)
+            say(f"    without the rotation the attention delta would differ by {seen:.2e}")
+            assert seen > 10 * tol(cfg), "the rotation barely changes this case"
+
+
+def test_7b_s16k_gqa8_rope_rank3():
+    """The 7B shape at 16K context, fold 8, rank 3, with the rotary embedding
+    (base 10^4) and 8 K/V heads (one per rank): every output row against the
+    oracle."""
+    cfg = synth.get_config("7b_s16k").with_(n_kv_heads=8, rope_theta=10000.0)
+    r = cfg.ranks[0]
+    say(f"[gpu] 7B shape S={cfg.seq} D={cfg.fold} Hkv=8 rotary rank {r}: full rank parity")
+    w, x_full, L, xs, pos = _setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv, skip=r)
+    run = RankRun(cfg, r)
+    x1 = run.attn(xs[r], L, kv)
+    out = run.mlp(x1, L)
+    torch.cuda.synchronize()
+    say("    GPU done; oracle running")
+    x1_ref = O.attention_block_rows(x_full, w, cfg.n_heads, cfg.eps, pos[r], cfg.rope_theta)
+    out_ref = O.mlp_block(x1_ref, w, cfg.eps)
+    xr = x_full[pos[r]].astype(np.float64)
+    _check(cfg, "x1", f64(x1), x1_ref, xr, xr)
+    _check(cfg, "out", f64(out), out_ref, f64(x1), x1_ref)

@@ -31,18 +31,30 @@ MUTATIONS = {
                                     "np.arange(kmax)[None, :] >= pb[:, None]"),
     "attn_no_mask": ("sc[np.arange(kmax)[None, :] > pb[:, None]] = -np.inf", "pass"),
     "attn_no_normalise": ("/ e.sum(axis=1, keepdims=True)", ""),
-    "wo_transposed": ("x1 = xs[rows] + a @ np.asarray(w.wo, F64)",
-                      "x1 = xs[rows] + a @ np.asarray(w.wo, F64).T"),
-    "no_attention_residual": ("x1 = xs[rows] + a @ np.asarray(w.wo, F64)",
-                              "x1 = a @ np.asarray(w.wo, F64)"),
+    "wo_transposed": ("return xs[rows] + a @ np.asarray(w.wo, F64)",
+                      "return xs[rows] + a @ np.asarray(w.wo, F64).T"),
+    "no_attention_residual": ("return xs[rows] + a @ np.asarray(w.wo, F64)",
+                              "return a @ np.asarray(w.wo, F64)"),
     "gate_on_wrong_branch": ("(silu(n @ np.asarray(w1, F64)) * (n @ np.asarray(w3, F64)))",
                              "(silu(n @ np.asarray(w3, F64)) * (n @ np.asarray(w1, F64)))"),
-    "no_mlp_residual": ("return x1 + swiglu_mlp(n2, w.w1, w.w3, w.w2)",
-                        "return swiglu_mlp(n2, w.w1, w.w3, w.w2)"),
-    "norm2_on_input": ("n2 = rmsnorm(x1, w.g2, eps)\n    return x1",
-                       "n2 = rmsnorm(xs[rows], w.g2, eps)\n    return x1"),
-    "head_slice_off_by_one": ("k_t = n1 @ np.asarray(w.wk[:, c], F64)",
-                              "k_t = n1 @ np.asarray(np.roll(w.wk, 1, axis=1)[:, c], F64)"),
+    "no_mlp_residual": ("return x1 + swiglu_mlp(rmsnorm(x1, w.g2, eps), w.w1, w.w3, w.w2)",
+                        "return swiglu_mlp(rmsnorm(x1, w.g2, eps), w.w1, w.w3, w.w2)"),
+    "norm2_on_input": ("    return mlp_block(x1, w, eps)\n",
+                       "    return x1 + swiglu_mlp(rmsnorm(np.asarray(x_full, F64)[rows], w.g2, eps),"
+                       " w.w1, w.w3, w.w2)\n"),
+    "head_slice_off_by_one": ("k_t = rope(n1 @ np.asarray(w.wk[:, kc], F64)",
+                              "k_t = rope(n1 @ np.asarray(np.roll(w.wk, 1, axis=1)[:, kc], F64)"),
+    "rope_turns_clockwise": ("out[:, 0::2] = u * c - v * s\n    out[:, 1::2] = u * s + v * c",
+                             "out[:, 0::2] = u * c + v * s\n    out[:, 1::2] = -u * s + v * c"),
+    "rope_frequency_exponent": ("** (-2.0 * np.arange(d // 2) / d)", "** (-1.0 * np.arange(d // 2) / d)"),
+    "rope_query_local_positions": ("rope(q[:, c], rows, rope_theta)",
+                                   "rope(q[:, c], np.arange(rows.size), rope_theta)"),
+    "rope_keys_not_rotated": ("k_t = rope(n1 @ np.asarray(w.wk[:, kc], F64), np.arange(P), rope_theta)",
+                              "k_t = n1 @ np.asarray(w.wk[:, kc], F64)"),
+    "gqa_heads_interleaved": ("kc = slice((t // grp) * d, (t // grp + 1) * d)",
+                              "kc = slice((t % (n_heads // grp)) * d, (t % (n_heads // grp) + 1) * d)"),
+    "fold_rope_local_positions": ("return np.concatenate([rope(m[:, t * d:(t + 1) * d], p, rope_theta)",
+                                  "return np.concatenate([rope(m[:, t * d:(t + 1) * d], np.arange(p.size), rope_theta)"),
     "pairs_count_strict": ("np.sum(zigzag_positions(S, D, r) + 1)", "np.sum(zigzag_positions(S, D, r))"),
     "flops_missing_o_proj": ("return 8 * T * h * h + 6", "return 6 * T * h * h + 6"),
     "fold_missing_partial": ("y[r] += o @ wo_j", "y[r] = o @ wo_j"),
