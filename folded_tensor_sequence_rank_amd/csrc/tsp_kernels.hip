@@ -79,11 +79,12 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // is formed and reduced modulo 2 pi in double precision (at p ~ 1e5 a
 // single-precision product would be off by ~1e-2 rad); sine and cosine of the
 // reduced angle are single precision.
-__device__ inline void rope_pairs(float* v, int e, int64_t p, int hd, double l2theta) {
+// l2c = log2(theta) / d.
+__device__ inline void rope_pairs(float* v, int e, int64_t p, double l2c) {
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     const int i = e / 2 + t;
-    const double ang = (double)p * exp2(-(double)(2 * i) / hd * l2theta);
+    const double ang = (double)p * exp2(-(double)(2 * i) * l2c);
     const double k = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
     const float red = (float)fma(-k, 6.283185307179586, ang);
     float sn, cs;
@@ -860,7 +861,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
           const int head = rem / g.hd;
           const int e = rem - head * g.hd;
           float o4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-          if (part < 2 && g.rope_l2 > 0.0) rope_pairs(o4, e, spos, g.hd, g.rope_l2);
+          if (part < 2 && g.rope_l2 > 0.0) rope_pairs(o4, e, spos, g.rope_l2 / g.hd);
           if (part == 0) {
             store4<T>((T*)g.Q + ((int64_t)head * qrows + m) * g.hd + e, o4[0], o4[1], o4[2], o4[3]);
           } else if (part == 1) {

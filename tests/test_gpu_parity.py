@@ -377,3 +377,35 @@ def test_7b_s16k_gqa8_rope_rank3():
     xr = x_full[pos[r]].astype(np.float64)
     _check(cfg, "x1", f64(x1), x1_ref, xr, xr)
     _check(cfg, "out", f64(out), out_ref, f64(x1), x1_ref)
+
+
+# Degenerate zigzags: one and two tokens per chunk (S = 2D, 4D), so every
+# GEMM, attention tile and K/V copy is almost all ragged tail; with three
+# sequences, grouped K/V and the rotary embedding on, and with 128-dim heads
+# (the pipelined kernel's shape, here on the copied-K/V path since C % 64 != 0).
+EDGE = {
+    "c1_fold8_b3_gqa2_rope": _cfg(hidden=256, n_heads=16, head_dim=16, ffn=176, seq=16, fold=8,
+                                  batch=3, n_kv_heads=8, rope_theta=10000.0),
+    "c2_fold4_gqa2_rope_f32": _cfg(hidden=128, n_heads=8, head_dim=16, ffn=176, seq=16, fold=4,
+                                   n_kv_heads=4, rope_theta=100.0, dtype="f32"),
+    "c1_fold4_d128_b2": _cfg(hidden=512, n_heads=4, head_dim=128, ffn=688, seq=8, fold=4, batch=2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_degenerate_chunks(case):
+    cfg = EDGE[case]
+    B, T = cfg.batch, cfg.local_tokens
+    say(f"[gpu] degenerate zigzag {case}: C={cfg.chunk} S={cfg.seq} D={cfg.fold} B={B} "
+        f"Hkv={cfg.kv_heads} theta={cfg.rope_theta} d={cfg.head_dim} {cfg.dtype}")
+    w, L, xf, pos, xs = _batch_setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    for r in range(cfg.fold):
+        run = RankRun(cfg, r)
+        out = run.layer(xs[r], L, kv)
+        torch.cuda.synchronize()
+        g = f64(out)
+        for b in range(B):
+            ref = O.rank_share(xf[b], w, cfg.n_heads, cfg.eps, cfg.seq, cfg.fold, r, cfg.rope_theta)
+            _check(cfg, f"rank {r} sequence {b} out", g[b * T:(b + 1) * T], ref)
