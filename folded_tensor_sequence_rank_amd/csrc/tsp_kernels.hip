@@ -1977,8 +1977,10 @@ static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
 //  * fp32-accumulator GEMMs (O, W2): 256x256 (ping-pong) when that makes at
 //    least one full round of 256 tiles; else 128x128 (4 waves) for K <= 2048
 //    and 128x256 for longer K;
-//  * QKV: 128x192 when 256x192 needs more than one round; otherwise the
-//    estimate below (256x192 at 8192 tokens, 128x128 at 2048);
+//  * QKV: 128x192 when 256x192 needs more than one round; else 4-wave
+//    128x192 tiles (two per CU) when they fill at least 3/4 of the 512
+//    slots (8192 tokens), else 4-wave 128x128 when they fill half (the
+//    narrow N of grouped K/V), else the estimate below (128x128 at 2048);
 //  * W1/W3 (two B operands): 128x64 (4 waves) when 128x192 leaves CUs idle,
 //    128x96 (4 waves) up to two rounds of 128x192, else the estimate.
 // The estimate: rounds of 256 tiles x tile area / relative efficiency.
@@ -2018,6 +2020,11 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
   } else {
     if (tiles(256, 192) > 256) {
       gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
+    } else if (tiles(128, 192) >= 384) {
+      // one round of 4-wave 128x192 tiles, two per CU, filling >= 3/4 of them
+      gemm_go<bf16, 128, 192, EPI, 4, 2>(a, vec, s);
+    } else if (tiles(128, 128) >= 256) {
+      gemm_go<bf16, 128, 128, EPI>(a, vec, s);
     } else {
       // 128x192 fills the chip at the narrow N of grouped K/V (hs + 2ks)
       const Cand single[] = {{256, 256, 1.0}, {256, 192, 0.95}, {128, 128, 0.55}, {128, 192, 0.8}};

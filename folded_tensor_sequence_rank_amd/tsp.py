@@ -135,6 +135,32 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
+def _check_sizes(dims: TspDims, which: int, **bufs):
+    """Byte sizes of the tensors passed for one call against what the dims
+    make the library read or write (the C ABI takes plain pointers and
+    cannot check them).  Integer addresses are not checked, nor are calls
+    whose dims the library rejects (it reports those itself)."""
+    if workspace_bytes(dims, which) == 0:
+        return
+    es = 2 if dims.dtype == TSP_BF16 else 4
+    h, D, d = dims.hidden, dims.fold, dims.head_dim
+    B = max(dims.batch, 1)
+    rows = B * (dims.seq // D)
+    hs = h // D
+    ks = (dims.n_kv_heads or dims.n_heads) * d // D
+    need = {"x": rows * h, "x1": rows * h, "out": rows * h, "g1": h, "g2": h,
+            "kv": 2 * (dims.n_kv_heads or dims.n_heads) * B * dims.seq * d,
+            "w_attn": (hs + 2 * ks) * h + h * hs, "w_mlp": 3 * (dims.ffn // D) * h}
+    for name, t in bufs.items():
+        ts = t if name in ("w_attn", "w_mlp") else [t]
+        if name in ("w_attn", "w_mlp") and len(ts) != D:
+            raise ValueError(f"{name}: {len(ts)} shards for fold {D}")
+        for i, u in enumerate(ts):
+            if hasattr(u, "numel") and _nbytes(u) < need[name] * es:
+                raise ValueError(f"{name}{'' if len(ts) == 1 else f'[{i}]'}: {_nbytes(u)} bytes, "
+                                 f"the dims need {need[name] * es}")
+
+
 def workspace_bytes(dims: TspDims, which: int) -> int:
     return int(lib().tsp_workspace_bytes(ctypes.byref(dims), which))
 
@@ -147,18 +173,21 @@ def zigzag_positions(seq: int, fold: int, rank: int) -> np.ndarray:
 
 
 def tsp_attn_shard(dims, x, g1, w_attn, kv, x1, ws, stream=None, copy_stream=None):
+    _check_sizes(dims, TSP_WS_ATTN, x=x, g1=g1, w_attn=w_attn, kv=kv, x1=x1)
     _check(lib().tsp_attn_shard(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
                                 _ptr(x1), _ptr(ws), _nbytes(ws), _stream(stream),
                                 None if copy_stream is None else _stream(copy_stream)))
 
 
 def tsp_mlp_shard(dims, x1, g2, w_mlp, out, ws, stream=None, copy_stream=None):
+    _check_sizes(dims, TSP_WS_MLP, x1=x1, g2=g2, w_mlp=w_mlp, out=out)
     _check(lib().tsp_mlp_shard(ctypes.byref(dims), _ptr(x1), _ptr(g2), _ptrs(w_mlp), _ptr(out),
                                _ptr(ws), _nbytes(ws), _stream(stream),
                                None if copy_stream is None else _stream(copy_stream)))
 
 
 def tsp_layer_shard(dims, x, g1, w_attn, kv, g2, w_mlp, out, ws, stream=None, copy_stream=None):
+    _check_sizes(dims, TSP_WS_LAYER, x=x, g1=g1, w_attn=w_attn, kv=kv, g2=g2, w_mlp=w_mlp, out=out)
     _check(lib().tsp_layer_shard(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
                                  _ptr(g2), _ptrs(w_mlp), _ptr(out), _ptr(ws), _nbytes(ws),
                                  _stream(stream),
@@ -166,6 +195,7 @@ def tsp_layer_shard(dims, x, g1, w_attn, kv, g2, w_mlp, out, ws, stream=None, co
 
 
 def tsp_kv_shard(dims, x, g1, w_attn, kv, ws, stream=None):
+    _check_sizes(dims, TSP_WS_KV, x=x, g1=g1, w_attn=w_attn, kv=kv)
     _check(lib().tsp_kv_shard(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
                               _ptr(ws), _nbytes(ws), _stream(stream)))
 

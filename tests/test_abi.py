@@ -164,3 +164,24 @@ def test_product_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tsp, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         tsp.lib()
+
+
+def test_binding_rejects_undersized_tensors():
+    """The binding checks tensor sizes against the dims before any launch (CPU
+    tensors stand in: nothing is enqueued when a check fails)."""
+    import torch
+    cfg = C3.with_(batch=4)
+    d = tsp.make_dims(cfg, 3)
+    T, h = cfg.local_tokens, cfg.hidden
+    one_seq = torch.empty(T * h, dtype=torch.bfloat16)          # one sequence's rows only
+    g = torch.empty(h, dtype=torch.bfloat16)
+    shards = [torch.empty(4 * 512 * 4096, dtype=torch.bfloat16) for _ in range(8)]
+    kv = torch.empty(1, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="x: .* the dims need"):
+        tsp.tsp_kv_shard(d, one_seq, g, shards, kv, torch.empty(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="kv"):
+        tsp.tsp_kv_shard(d, torch.empty(4 * T * h, dtype=torch.bfloat16), g, shards, kv,
+                         torch.empty(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="shards for fold"):
+        tsp.tsp_kv_shard(d, torch.empty(4 * T * h, dtype=torch.bfloat16), g, shards[:7], kv,
+                         torch.empty(256, dtype=torch.uint8))
