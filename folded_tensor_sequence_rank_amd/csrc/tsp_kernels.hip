@@ -97,8 +97,9 @@ __device__ inline void rope_pairs(float* v, int e, int64_t p, double l2c) {
 
 // ---------------------------------------------------------------------------
 // RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, fp32 math, one wave per row.
-// HBM-bound: reads the row once for the sum of squares and once more (from
-// cache) for the scaled write.
+// HBM-bound.  Rows of up to 64*RC 16-byte chunks (8192 bf16, 4096 fp32) are
+// read once into registers, all loads in flight together, and scaled from
+// there; wider or unaligned rows are read a second time for the scaled write.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* __restrict__ x,
@@ -106,6 +107,7 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* __restrict__ x,
                                                       T* __restrict__ y, int64_t rows, int h,
                                                       float eps) {
   constexpr int V = 16 / sizeof(T);
+  constexpr int RC = 16;  // 16-byte chunks per lane held in registers
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -113,6 +115,37 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* __restrict__ x,
   T* yr = y + row * h;
   const bool vec = (h % V) == 0;
   float ss = 0.f;
+  if (vec && h / V <= 64 * RC) {
+    const int nc = h / V;
+    Chunk<T> v[RC];
+#pragma unroll
+    for (int k = 0; k < RC; k++) {
+      const int c = lane + 64 * k;
+      v[k].raw = c < nc ? *(const u32x4*)(xr + (int64_t)c * V) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < RC; k++)
+#pragma unroll
+      for (int i = 0; i < V; i++) {
+        const float f = to_f(v[k].e[i]);
+        ss += f * f;
+      }
+#pragma unroll
+    for (int o = 32; o; o >>= 1) ss += __shfl_xor(ss, o);
+    const float rs = 1.0f / sqrtf(ss / (float)h + eps);
+#pragma unroll
+    for (int k = 0; k < RC; k++) {
+      const int c = lane + 64 * k;
+      if (c < nc) {
+        Chunk<T> w, out;
+        w.raw = *(const u32x4*)(g + (int64_t)c * V);
+#pragma unroll
+        for (int i = 0; i < V; i++) out.e[i] = from_f<T>(to_f(v[k].e[i]) * rs * to_f(w.e[i]));
+        *(u32x4*)(yr + (int64_t)c * V) = out.raw;
+      }
+    }
+    return;
+  }
   if (vec) {
     for (int c = lane; c < h / V; c += 64) {
       Chunk<T> v;
