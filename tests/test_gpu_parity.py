@@ -321,6 +321,9 @@ ROPE = {
                                         w_std=0.022),
     "bf16_d128_ragged_rope": _cfg(hidden=512, n_heads=4, rope_theta=10000.0, x_std=0.02,
                                   w_std=0.03),
+    # one K/V head for all four query heads (multi-query attention), fold 1
+    "bf16_d64_mqa_fold1_rope": _cfg(hidden=256, n_heads=4, head_dim=64, ffn=512, seq=512, fold=1,
+                                    n_kv_heads=1, rope_theta=10000.0, x_std=0.02, w_std=0.045),
     "split_gqa2_rope_b2": _cfg(hidden=512, n_heads=4, head_dim=128, ffn=1024, seq=8192, fold=2,
                                batch=2, n_kv_heads=2, rope_theta=10000.0, x_std=0.02,
                                w_std=0.03),
