@@ -412,3 +412,42 @@ def test_degenerate_chunks(case):
         for b in range(B):
             ref = O.rank_share(xf[b], w, cfg.n_heads, cfg.eps, cfg.seq, cfg.fold, r, cfg.rope_theta)
             _check(cfg, f"rank {r} sequence {b} out", g[b * T:(b + 1) * T], ref)
+
+
+def test_rope_largest_positions_f32():
+    """The rotary embedding at positions up to 131071 (rank 0 of 8 holds the
+    last zigzag chunk), in fp32.  The rotated K rows that tsp_kv_shard writes
+    into the gathered K/V are compared element by element with the oracle's:
+    angles formed in single precision would be off by ~1e-3 rad here and
+    move K by ~7e-4 (relative), far beyond the 2e-5 bar.  Sampled rows of the
+    attention half are checked at the fp32 bar as well."""
+    cfg = _cfg(hidden=256, n_heads=8, head_dim=32, ffn=512, seq=131072, fold=8, dtype="f32",
+               rope_theta=10000.0, x_std=0.02, w_std=0.06)
+    r, d, S = 0, cfg.head_dim, cfg.seq
+    say(f"[gpu] rotary embedding at positions up to {S - 1}, fp32, rank {r}")
+    w, x_full, L, xs, pos = _setup(cfg)
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    x1 = RankRun(cfg, r).attn(xs[r], L, kv)
+    torch.cuda.synchronize()
+    C = cfg.chunk
+    local = np.r_[0:8, C - 8:C, C:C + 8, 2 * C - 24:2 * C]   # chunk edges; the last rows end at S - 1
+    p = pos[r][local]
+    assert p.max() == S - 1
+    # K and V of every head at these positions: block j holds head j (one per shard)
+    kvh = f64(kv).reshape(cfg.fold, 2, S, d)  # [shard][K | V^T][...]
+    n1 = O.rmsnorm(x_full[p], w.g1, cfg.eps)
+    worst = 0.0
+    for j in range(cfg.fold):
+        c = slice(j * d, (j + 1) * d)
+        k_ref = O.rope(n1 @ np.asarray(w.wk[:, c], np.float64), p, cfg.rope_theta)
+        v_ref = n1 @ np.asarray(w.wv[:, c], np.float64)
+        k_gpu = kvh[j, 0][p]
+        v_gpu = kvh[j, 1].reshape(d, S)[:, p].T
+        ek, ev = rel_fro(k_gpu, k_ref), rel_fro(v_gpu, v_ref)
+        assert ek < 2e-5 and ev < 2e-5, (j, ek, ev)
+        worst = max(worst, ek)
+    say(f"    rotated K of all heads at positions {p.min()}..{p.max()}: rel error {worst:.2e} (bar 2e-5)")
+    ref = O.attention_block_rows(x_full, w, cfg.n_heads, cfg.eps, p, cfg.rope_theta)
+    xr = x_full[p].astype(np.float64)
+    _check(cfg, "x1 (sampled rows)", f64(x1)[local], ref, xr, xr)
