@@ -2013,7 +2013,7 @@ static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
 //  * QKV: 128x192 when 256x192 needs more than one round; else 4-wave
 //    128x192 tiles (two per CU) when they fill at least 3/4 of the 512
 //    slots (8192 tokens), else 4-wave 128x128 when they fill half (the
-//    narrow N of grouped K/V), else the estimate below (128x128 at 2048);
+//    narrow N of grouped K/V), else 4-wave 64x64 (2048 tokens);
 //  * W1/W3 (two B operands): 128x64 (4 waves) when 128x192 leaves CUs idle,
 //    128x96 (4 waves) up to two rounds of 128x192, else the estimate.
 // The estimate: rounds of 256 tiles x tile area / relative efficiency.
@@ -2059,13 +2059,8 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
     } else if (tiles(128, 128) >= 256) {
       gemm_go<bf16, 128, 128, EPI>(a, vec, s);
     } else {
-      // 128x192 fills the chip at the narrow N of grouped K/V (hs + 2ks)
-      const Cand single[] = {{256, 256, 1.0}, {256, 192, 0.95}, {128, 128, 0.55}, {128, 192, 0.8}};
-      const int best = pick(single, 4);
-      if (best == 0) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
-      else if (best == 1) gemm_go<bf16, 256, 192, EPI, 8, 4>(a, vec, s);
-      else if (best == 2) gemm_go<bf16, 128, 128, EPI>(a, vec, s);
-      else gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
+      // few rows (2048 tokens): 4-wave 64x64 tiles, three or more per CU
+      gemm_go<bf16, 64, 64, EPI>(a, vec, s);
     }
   }
 }
