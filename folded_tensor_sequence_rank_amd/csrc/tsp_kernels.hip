@@ -2008,8 +2008,7 @@ static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
 // runs it well below that rate).  Measured on the layer's projections at
 // 2048, 8192 and 16384 local tokens of the 7B shape:
 //  * fp32-accumulator GEMMs (O, W2): 256x256 (ping-pong) when that makes at
-//    least one full round of 256 tiles; else 128x128 (4 waves) for K <= 2048
-//    and 128x256 for longer K;
+//    least one full round of 256 tiles; else 128x128 (4 waves);
 //  * QKV: 128x192 when 256x192 needs more than one round; else 4-wave
 //    128x192 tiles (two per CU) when they fill at least 3/4 of the 512
 //    slots (8192 tokens), else 4-wave 128x128 when they fill half (the
@@ -2048,8 +2047,7 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
     }
   } else if constexpr (EPI == EPI_ACC || EPI == EPI_RESID) {
     if (tiles(256, 256) >= 256) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
-    else if (a.K <= 2048) gemm_go<bf16, 128, 128, EPI, 4, 2>(a, vec, s);
-    else gemm_go<bf16, 128, 256, EPI, 8, 2>(a, vec, s);
+    else gemm_go<bf16, 128, 128, EPI, 4, 2>(a, vec, s);
   } else {
     if (tiles(256, 192) > 256) {
       gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
