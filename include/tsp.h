@@ -102,6 +102,12 @@
  *     copy; tsp_last_error() gives the detail (thread-local).
  *   - Calls that share a workspace must not overlap in time.
  *   - An empty sequence (S == 0) is valid and enqueues nothing.
+ *   - Calls may be captured into a HIP graph (stream capture on `stream`):
+ *     everything they enqueue is a kernel, an asynchronous copy or an event
+ *     record / wait between `stream` and `copy_stream`, with no host
+ *     synchronisation and no memset node.  Make the first call of a host
+ *     thread on a device outside capture (it creates the library's events),
+ *     and do not capture calls made with TSP_F_PROFILE.
  */
 #ifndef TSP_H
 #define TSP_H
