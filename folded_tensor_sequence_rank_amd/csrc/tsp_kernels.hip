@@ -271,16 +271,6 @@ __device__ inline float halves_max(float x) {
   return x;
 #endif
 }
-// acc + v.x + v.y for a pair of bf16 values, in one instruction.
-__device__ inline float add_pair(bf16 x, bf16 y, float acc) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 v = {x, y}, one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
-#else
-  return acc + (float)x + (float)y;
-#endif
-}
 __device__ inline float halves_sum(float x) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -342,15 +332,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   constexpr int STAGE = (BM + NBR) * 128;
   constexpr int NB3 = DUAL ? NB : 1;
   static_assert(BM % 64 == 0 && BN % 64 == 0 || BN == 192 || BN == 96, "tile");
-#ifndef TSP_GEMM_PP
-#define TSP_GEMM_PP 1
-#endif
   // Ping-pong schedule (below): 8 waves, 16-bit operands, and the split A
   // buffers plus the three-slot B ring must fit in LDS.  Used for the
   // 256x256 single-B tiles, where it measured faster than the lockstep loop
   // (on 256x192 it did not).
   constexpr int PPLDS = 2 * BM * 128 + 3 * NBR * 128;
-  constexpr bool PP = TSP_GEMM_PP && VEC && NW == 8 && sizeof(T) == 2 && PPLDS <= 160 * 1024 &&
+  constexpr bool PP = VEC && NW == 8 && sizeof(T) == 2 && PPLDS <= 160 * 1024 &&
                       (NBR / 32) % 2 == 0 && BM == 256 && BN == 256 && !DUAL;
   __shared__ __attribute__((aligned(16))) char smem[PP ? PPLDS : 2 * STAGE];
 
@@ -415,44 +402,27 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
       }
   };
   // Interleave the fragment reads of the next k-step with this k-step's
-  // MFMAs (TSP_GEMM_SCHED 2: each read after a group of MFMAs).
-#ifndef TSP_GEMM_SCHED
-#define TSP_GEMM_SCHED 2  // per fragment read: MFMAs first, then the read (1: read first; 3: reads first)
-#endif
+  // MFMAs: each read after a group of MFMAs.
   auto interleave = [&]() {
     constexpr int NR = MB + NB + NB3 * (DUAL ? 1 : 0);
     constexpr int NM = MB * NB * (DUAL ? 2 : 1);
     constexpr int PER = NM / NR > 0 ? NM / NR : 1;
-    if constexpr (TSP_GEMM_SCHED == 1) {
 #pragma unroll
-      for (int q = 0; q < NR; q++) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then MFMAs
-      }
-    } else if constexpr (TSP_GEMM_SCHED == 2) {
-#pragma unroll
-      for (int q = 0; q < NR; q++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // then one DS read
-      }
-    } else if constexpr (TSP_GEMM_SCHED == 3) {
-      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // all reads first
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    for (int q = 0; q < NR; q++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // then one DS read
     }
   };
   // k-steps 0 .. KS-2 of buffer buf (fragments of step 0 already in set 0).
-#ifndef TSP_GEMM_SETPRIO
-#define TSP_GEMM_SETPRIO 1  // raise wave priority around the MFMA-heavy k-steps
-#endif
   auto compute_head = [&](int buf) {
-    if (TSP_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(1);  // wave priority up around the MFMA-heavy k-steps
 #pragma unroll
     for (int ks = 0; ks + 1 < KS; ks++) {
       fetch(buf, ks + 1, (ks + 1) & 1);
       mfmas(ks & 1);
       interleave();
     }
-    if (TSP_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   constexpr int LAST = (KS - 1) & 1;  // register set of the last k-step
 
@@ -511,13 +481,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
       // rows of tile kt+2; both land before the barrier that ends its mma(kt).
       // A buffers are rewritten two phases after their last reader, B slots
       // three phases after theirs (B(kt+2) replaces B(kt-1)).
-#ifndef TSP_PP_AGPR
-#define TSP_PP_AGPR 1
-#endif
       // Naming an accumulation register here makes the compiler select the
       // MFMA form whose accumulator lives in AGPRs: the accumulators then
       // stay out of the VGPR banks that the other wave's LDS reads fill.
-      if (TSP_PP_AGPR) asm volatile("" ::: "a0");
+      asm volatile("" ::: "a0");
       const int grp = wave >> 2, w4 = wave & 3;
       constexpr int AH = BM / 2;                 // A rows per group
       constexpr int RA2 = AH / 32, RB = NBR / 32, RB2 = RB / 2;
@@ -610,9 +577,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
           fetch_all(kt);
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           bar();
-          if (TSP_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(1);
+          __builtin_amdgcn_s_setprio(1);
           mma_all();
-          if (TSP_GEMM_SETPRIO) __builtin_amdgcn_s_setprio(0);
+          __builtin_amdgcn_s_setprio(0);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           // group 1's last phase needs no barrier: no wave waits for it
           if (grp == 0 || kt + 1 < nk) bar();
@@ -955,12 +922,6 @@ constexpr int kBKV = 64;   // keys per tile
 #ifndef TSP_ATTN_VPRE
 #define TSP_ATTN_VPRE 2      // 16-key steps of V^T fragments read before the softmax
 #endif
-#ifndef TSP_ATTN_ISSUE
-#define TSP_ATTN_ISSUE 0     // where the next tile's loads go: 0 top, 1 after S, 2 split
-#endif
-#ifndef TSP_ATTN_PERMLANE
-#define TSP_ATTN_PERMLANE 1  // cross-half max through the lane swap, not LDS
-#endif
 #ifndef TSP_ATTN128_WAVES
 #define TSP_ATTN128_WAVES 2  // waves per SIMD the 128-dim bf16 kernel is sized for
 #endif
@@ -1158,8 +1119,8 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     vkey[j] = c * V;
     voff[j] = (int)(((int64_t)d * BS + c * V) * ES);
   }
-  // Loads [lo, hi) of this wave's KJ + VJ loads of a tile (K first).
-  auto issue_part = [&](int k0, int buf, int lo, int hi) {
+  // This wave's KJ + VJ loads of a tile (K first).
+  auto issue = [&](int k0, int buf) {
     char* sK = smem + buf * STAGE;
     char* sV = sK + KT_BYTES;
     const bool mine = !split_src || own_tile(k0);
@@ -1167,18 +1128,17 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     const brsrc rV = make_rsrc(mine ? Vh : Vgh, (uint64_t)((HD - 1) * BS + a.S) * ES);
 #pragma unroll
     for (int j = 0; j < KJ; j++) {
-      if (j >= lo && j < hi && (KI % 4 == 0 || wave + 4 * j < KI))
+      if (KI % 4 == 0 || wave + 4 * j < KI)
         buffer_to_lds16(rK, sK + (wave + 4 * j) * 1024, k0 + krow[j] < kend32 ? koff[j] : kOOB,
                         (uint32_t)(k0 * HD * ES));
     }
 #pragma unroll
     for (int j = 0; j < VJ; j++) {
-      if (KJ + j >= lo && KJ + j < hi && (VI % 4 == 0 || wave + 4 * j < VI))
+      if (VI % 4 == 0 || wave + 4 * j < VI)
         buffer_to_lds16(rV, sV + (wave + 4 * j) * 1024,
                         k0 + vkey[j] < kend32 ? (uint32_t)voff[j] : kOOB, (uint32_t)(k0 * ES));
     }
   };
-  auto issue = [&](int k0, int buf) { issue_part(k0, buf, 0, KJ + VJ); };
   // A V^T chunk that straddles kend was loaded whole: zero its keys >= kend.
   auto fixup = [&](int k0, int buf) {
     char* sV = smem + buf * STAGE + KT_BYTES;
@@ -1193,19 +1153,12 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   };
 
   const float cs = a.scale_log2;
-  // The next tile's loads are issued inside compute, spread over its phases
-  // (nk0 < 0: none), so that they do not queue up behind each other at the
-  // top of the tile.
-  constexpr int NL = KJ + VJ;
-  auto compute = [&](int buf, int k0, auto mask_tag, int nk0, int nbuf) {
+  auto compute = [&](int buf, int k0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* sK = smem + buf * STAGE;
     const char* sV = sK + KT_BYTES;
     f32x16 s[QB][NKB];
-#ifndef TSP_ATTN_SETPRIO
-#define TSP_ATTN_SETPRIO 1  // raise wave priority around MFMA blocks
-#endif
-    if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(1);  // raise wave priority around MFMA blocks
 #pragma unroll
     for (int kb = 0; kb < NKB; kb++) {
 #pragma unroll
@@ -1227,11 +1180,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
       __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    if (TSP_ATTN_ISSUE >= 1 && nk0 >= 0) {
-      issue_part(nk0, nbuf, 0, TSP_ATTN_ISSUE == 1 ? NL : NL / 2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    __builtin_amdgcn_s_setprio(0);
     // V^T fragments of the whole tile, read while the products above run
     // and the softmax below computes (the K fragments' registers are free).
     auto vfrag = [&](int st, int d) {
@@ -1274,11 +1223,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
           xs[i & 3] = fmaxf(xs[i & 3], s[b][kb][i]);
         }
       float x = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
-#if TSP_ATTN_PERMLANE
       x = halves_max(x);
-#else
-      x = fmaxf(x, __shfl_xor(x, 32));
-#endif
       mt[b] = x * cs;  // log2 units (scale > 0, so -inf stays -inf)
     }
     bool grow = false;
@@ -1320,12 +1265,8 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
       l[b] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (TSP_ATTN_ISSUE == 2 && nk0 >= 0) {
-      issue_part(nk0, nbuf, NL / 2, NL);
-      __builtin_amdgcn_sched_barrier(0);
-    }
     // O^T += V^T . P^T
-    if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < PK; st++) {
 #pragma unroll
@@ -1342,7 +1283,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
         __builtin_amdgcn_sched_group_barrier(0x008, QB, 2);
       }
     }
-    if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   const int ntiles = (kfin - kbeg + BKV - 1) / BKV;
@@ -1374,13 +1315,12 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     }
     const bool more = t + NSTAGE - 1 < ntiles;
     const int nk0 = more ? k0 + (NSTAGE - 1) * BKV : -1, nbuf = (t + NSTAGE - 1) % NSTAGE;
-    if (more && (TSP_ATTN_ISSUE == 0 || k0 >= kend_w)) issue(nk0, nbuf);
-    const int cnk0 = TSP_ATTN_ISSUE == 0 ? -1 : nk0;
+    if (more) issue(nk0, nbuf);
     if (k0 < kend_w) {
       if (!wfull || k0 + BKV - 1 > qmin_w)
-        compute(t % NSTAGE, k0, std::true_type{}, cnk0, nbuf);
+        compute(t % NSTAGE, k0, std::true_type{});
       else
-        compute(t % NSTAGE, k0, std::false_type{}, cnk0, nbuf);
+        compute(t % NSTAGE, k0, std::false_type{});
     }
   }
 
@@ -1439,15 +1379,6 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 // iteration t reads K(t+1) and V^T(t) and loads K(t+2) and V^T(t+1), one
 // barrier per tile as before.
 // ---------------------------------------------------------------------------
-#ifndef TSP_ATTN_PIPE
-#define TSP_ATTN_PIPE 1  // use the pipelined kernel for bf16, head_dim 128
-#endif
-#ifndef TSP_ATTN_SUMCHECK
-#define TSP_ATTN_SUMCHECK 1  // lazy softmax reference checked on block sums (no per-tile max)
-#endif
-#ifndef TSP_ATTN_DOTSUM
-#define TSP_ATTN_DOTSUM 0  // 1: row sums from bf16 pairs (one instruction per two keys)
-#endif
 #ifndef TSP_PIPE_DIST
 #define TSP_PIPE_DIST 3    // LDS fragment reads kept in flight ahead of the MFMAs
 #endif
@@ -1604,17 +1535,11 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     return halves_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]))) * cs;
   };
   // P fragments of one 32-key block (16-key steps 2kb, 2kb+1).
-  // One element e of a P fragment and its part of the row sum.  With
-  // TSP_ATTN_DOTSUM the sum takes the bf16 values the V^T product uses, a
-  // pair per instruction once the pair's second element is in.
+  // One element e of a P fragment and its part of the row sum.
   auto pel = [&](float x, float nm, frag& pv, int e, float* ls) {
     const float p = fast_exp2(fmaf(x, cs, nm));
     pv[e] = (bf16)p;
-#if TSP_ATTN_DOTSUM
-    if (e & 1) ls[(e >> 1) & 3] = add_pair(pv[e - 1], pv[e], ls[(e >> 1) & 3]);
-#else
     ls[e & 3] += p;
-#endif
   };
   auto exps = [&](const f32x16& sb, float nm, frag& p0, frag& p1, float* ls) {
 #pragma unroll
@@ -1719,7 +1644,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       s[0] = f32x16{0};
       s[1] = f32x16{0};
       __builtin_amdgcn_sched_barrier(0);
-      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const frag f = kq[i % PD];
@@ -1733,8 +1658,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       }
       pin(pf[2], pf[3], ls);
       __builtin_amdgcn_sched_barrier(0);
-      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-#if TSP_ATTN_SUMCHECK
+      __builtin_amdgcn_s_setprio(0);
       {
         // The block's exponentials used the running reference m.  A score
         // more than 2^64 above it (or a non-finite sum) is caught on the
@@ -1755,21 +1679,11 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       }
       if (needmask(k0 + BKV)) mask_rows(s, k0 + BKV);
       const float nm2 = m == -INFINITY ? 0.f : -m;
-#else
-      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      // row max of S(t+1), rescale factor
-      if (needmask(k0 + BKV)) mask_rows(s, k0 + BKV);
-      const float mt = row_max(s);
-      const bool grow = __any(mt > m + 8.0f);
-      const float mn = grow ? fmaxf(m, mt) : m;
-      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-      const float nm2 = mn == -INFINITY ? 0.f : -mn;
-#endif
       __builtin_amdgcn_sched_barrier(0);
       // phase B: the V^T(t) products with the first block of S(t+1)'s softmax
       frag pn[2];
       float ls2[4] = {0.f, 0.f, 0.f, 0.f};
-      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const frag f = vq[i % PD];
@@ -1780,8 +1694,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       }
       pin(pn[0], pn[1], ls2);
       __builtin_amdgcn_sched_barrier(0);
-      if (TSP_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-#if TSP_ATTN_SUMCHECK
+      __builtin_amdgcn_s_setprio(0);
       {
         float lsb = (ls2[0] + ls2[1]) + (ls2[2] + ls2[3]);
         if (__any(!(lsb <= kSumCap))) {
@@ -1798,15 +1711,6 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
         }
         l += lsb;
       }
-#else
-      if (grow) {
-#pragma unroll
-        for (int d = 0; d < DB; d++) o[d] *= alpha;
-        l *= alpha;
-      }
-      l += (ls2[0] + ls2[1]) + (ls2[2] + ls2[3]);
-      m = mn;
-#endif
       pf[0] = pn[0];
       pf[1] = pn[1];
       sh = s[1];
@@ -1815,14 +1719,12 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
       exps(sh, nm, pf[2], pf[3], ls);
       float lsa = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-#if TSP_ATTN_SUMCHECK
       if (__any(!(lsa <= kSumCap))) {
         raise_ref(fmaxf(m, block_max(sh)), pf, 2);
         float lr4[4] = {0.f, 0.f, 0.f, 0.f};
         exps(sh, m == -INFINITY ? 0.f : -m, pf[2], pf[3], lr4);
         lsa = (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]);
       }
-#endif
       l += lsa;
       pv_product(P, pf, o);
     }
@@ -2091,7 +1993,7 @@ hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
 template <typename T, int HD>
 static void attn_go(const AttnArgs& a, const AttnPlan& p, int part, hipStream_t s) {
   if (part == 0) {
-    if (TSP_ATTN_PIPE && sizeof(T) == 2 && HD == 128)
+    if (sizeof(T) == 2 && HD == 128)
       attn_pipe_kernel<<<p.nitems * a.Hd * batch_of(a), 256, 0, s>>>(a);
     else
       attn_kernel<T, HD><<<p.nitems * a.Hd * batch_of(a), 256, 0, s>>>(a);
