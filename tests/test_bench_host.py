@@ -43,3 +43,13 @@ def test_only_cpu_baseline_imports_the_oracle():
     top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
     assert not any("oracle" in ast.dump(n) for n in top)
     assert users == {"cpu_baseline"}, users
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU's share is the measurement; --gpus N > 1 exits with a message
+    before touching any device."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "single MI355X" in r.stderr and r.stdout == ""
