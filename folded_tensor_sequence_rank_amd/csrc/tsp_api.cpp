@@ -560,6 +560,95 @@ int check_shards(const void* const* w, int64_t D, const char* what) {
   return TSP_OK;
 }
 
+// ---- backward of the MLP half -------------------------------------------
+// Workspace: the recomputed n2 and its transpose, dout transposed, the fp32
+// products a = n2 W1^T, b = n2 W3^T and dg = dout W2 of one shard, [da | db]
+// and g = silu(a) b with their transposes, the shard's W2 and W1|W3 blocks
+// transposed, the fp32 gradient of n2 and the per-row rstd.
+struct MlpBwdWs {
+  size_t n2, n2t, dot, a, b, dg, dab, dabt, gm, gmt, w2t, w13t, dn, rs, end;
+};
+
+MlpBwdWs mlp_bwd_ws(const Dims& d) {
+  MlpBwdWs w;
+  size_t o = 0;
+  const size_t T = d.BT, h = d.h, F = d.Fs, es = d.es;
+  w.n2 = o; o += al(T * h * es);
+  w.n2t = o; o += al(T * h * es);
+  w.dot = o; o += al(T * h * es);
+  w.a = o; o += al(T * F * 4);
+  w.b = o; o += al(T * F * 4);
+  w.dg = o; o += al(T * F * 4);
+  w.dab = o; o += al(T * 2 * F * es);
+  w.dabt = o; o += al(T * 2 * F * es);
+  w.gm = o; o += al(T * F * es);
+  w.gmt = o; o += al(T * F * es);
+  w.w2t = o; o += al(F * h * es);
+  w.w13t = o; o += al(2 * F * h * es);
+  w.dn = o; o += al(T * h * 4);
+  w.rs = o; o += al(T * 4);
+  w.end = o;
+  return w;
+}
+
+// y = a . b^T in fp32 (a [M][K] pitch lda, b [N][K] pitch ldb), or y += when accumulate.
+int plain_gemm(Ctx& c, const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t N,
+               int64_t K, float* y, int64_t ldy, bool accumulate) {
+  GemmArgs g = gemm_base();
+  g.A = a;
+  g.lda = lda;
+  g.B = b;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.Y = y;
+  g.ldy = ldy;
+  g.beta = accumulate ? 1 : 0;
+  HIP_TRY(launch_gemm(c.d->dt, EPI_ACC, g, c.s));
+  return TSP_OK;
+}
+
+int mlp_bwd_body(Ctx& c, const MlpBwdWs& L, const void* x1, const void* g2, const void* const* w_mlp,
+                 const void* dout, void* dx1, float* dg2, float* const* dw_mlp) {
+  const Dims& d = *c.d;
+  char* ws = c.ws;
+  const int64_t T = d.BT, h = d.h, F = d.Fs;
+  const size_t es = d.es;
+  float* fa = (float*)(ws + L.a);
+  float* fb = (float*)(ws + L.b);
+  float* fdg = (float*)(ws + L.dg);
+  float* dn = (float*)(ws + L.dn);
+  HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.n2, T, (int)h, d.eps, c.s));
+  HIP_TRY(launch_transpose(d.dt, ws + L.n2, ws + L.n2t, T, h, h, T, c.s));
+  HIP_TRY(launch_transpose(d.dt, dout, ws + L.dot, T, h, h, T, c.s));
+  HIP_TRY(launch_fill32(dg2, 0u, (size_t)h * 4, c.s));
+  int rc = 0;
+  for (int64_t t = 0; t < d.D; t++) {  // the ring order of the forward: own shard first
+    const int64_t j = (d.r + t) % d.D;
+    const char* w1 = (const char*)w_mlp[j];
+    const char* w3 = w1 + (size_t)F * h * es;
+    const char* w2 = w1 + 2 * (size_t)F * h * es;  // [h][F]
+    if ((rc = plain_gemm(c, ws + L.n2, h, w1, h, T, F, h, fa, F, false))) return rc;
+    if ((rc = plain_gemm(c, ws + L.n2, h, w3, h, T, F, h, fb, F, false))) return rc;
+    HIP_TRY(launch_transpose(d.dt, w2, ws + L.w2t, h, F, F, h, c.s));
+    if ((rc = plain_gemm(c, dout, h, ws + L.w2t, h, T, F, h, fdg, F, false))) return rc;
+    HIP_TRY(launch_swiglu_bwd(d.dt, fa, fb, fdg, ws + L.dab, ws + L.gm, T, F, c.s));
+    // dn2 (+)= [da | db] . [W1; W3]  (B operand: the W1|W3 block transposed)
+    HIP_TRY(launch_transpose(d.dt, w1, ws + L.w13t, 2 * F, h, h, 2 * F, c.s));
+    if ((rc = plain_gemm(c, ws + L.dab, 2 * F, ws + L.w13t, 2 * F, T, h, 2 * F, dn, h, t > 0))) return rc;
+    // this rank's partial weight gradients of shard j, in the shard's layout
+    HIP_TRY(launch_transpose(d.dt, ws + L.dab, ws + L.dabt, T, 2 * F, 2 * F, T, c.s));
+    HIP_TRY(launch_transpose(d.dt, ws + L.gm, ws + L.gmt, T, F, F, T, c.s));
+    if ((rc = plain_gemm(c, ws + L.dabt, T, ws + L.n2t, T, 2 * F, h, T, dw_mlp[j], h, false))) return rc;
+    if ((rc = plain_gemm(c, ws + L.dot, T, ws + L.gmt, T, h, F, T, dw_mlp[j] + 2 * F * h, F, false)))
+      return rc;
+  }
+  HIP_TRY(launch_rmsnorm_bwd(d.dt, x1, g2, dn, dout, dx1, (float*)(ws + L.rs), dg2, T, (int)h, d.eps,
+                             c.s));
+  return TSP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -576,6 +665,7 @@ size_t tsp_workspace_bytes(const tsp_dims* dims, int which) {
       return mlp_ws(d, a.end).end;
     }
     case TSP_WS_KV: return kv_ws_bytes(d);
+    case TSP_WS_MLP_BWD: return mlp_bwd_ws(d).end;
     default: return 0;
   }
 }
@@ -640,6 +730,24 @@ int tsp_mlp_shard(const tsp_dims* dims, const void* x1, const void* g2, const vo
   if ((rc = begin(c, (hipStream_t)stream, (hipStream_t)copy_stream, d.flags))) return rc;
   if ((rc = mlp_body(c, L, x1, g2, w_mlp, out))) return rc;
   return finish(c);
+}
+
+int tsp_mlp_shard_backward(const tsp_dims* dims, const void* x1, const void* g2,
+                           const void* const* w_mlp, const void* dout, void* dx1, float* dg2,
+                           float* const* dw_mlp, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if ((rc = check_ptrs({x1, g2, dout, dx1, dg2, ws})) || (rc = check_shards(w_mlp, d.D, "w_mlp")) ||
+      (rc = check_shards((const void* const*)dw_mlp, d.D, "dw_mlp")))
+    return rc;
+  const MlpBwdWs L = mlp_bwd_ws(d);
+  if (ws_bytes < L.end)
+    return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.end);
+  Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr, false};
+  return mlp_bwd_body(c, L, x1, g2, w_mlp, dout, dx1, dg2, dw_mlp);
 }
 
 int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,

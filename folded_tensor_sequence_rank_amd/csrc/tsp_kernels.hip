@@ -1798,6 +1798,102 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Backward of the MLP half (the gradient reading of the oracle's backward
+// module: each rank's rows, partial weight gradients).  The products run on
+// the projection GEMM; these kernels supply its transposed operands and the
+// elementwise and row-wise steps.
+// ---------------------------------------------------------------------------
+
+// out[c][r] = in[r][c] for an R x C matrix (row pitches ldi, ldo), through a
+// 64 x 64 LDS tile (one padding column against bank conflicts).
+template <typename T>
+__global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ in, T* __restrict__ out,
+                                                        int64_t R, int64_t C, int64_t ldi, int64_t ldo) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? in[r * ldi + c] : from_f<T>(0.f);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) out[c * ldo + r] = tile[tx][i];
+  }
+}
+
+// SwiGLU backward per element, a = n W1, b = n W3 and dg = dout W2^T given in
+// fp32 [rows][F] (pitch F): da = dg b silu'(a), db = dg silu(a) into
+// dab [rows][2F] (da in columns [0, F), db in [F, 2F)), and the forward
+// product g = silu(a) b into g [rows][F].
+template <typename T>
+__global__ void __launch_bounds__(256) swiglu_bwd_kernel(const float* __restrict__ a,
+                                                         const float* __restrict__ b,
+                                                         const float* __restrict__ dg,
+                                                         T* __restrict__ dab, T* __restrict__ g,
+                                                         int64_t rows, int64_t F) {
+  const int64_t n = rows * F;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / F, c = i - r * F;
+    const float av = a[i], bv = b[i], gv = dg[i];
+    const float sg = 1.0f / (1.0f + expf(-av));
+    const float s = av * sg;
+    dab[r * 2 * F + c] = from_f<T>(gv * bv * sg * (1.0f + av * (1.0f - sg)));
+    dab[r * 2 * F + F + c] = from_f<T>(gv * s);
+    g[i] = from_f<T>(s * bv);
+  }
+}
+
+// RMSNorm backward, one wave per row: with r = (mean(x^2) + eps)^(-1/2) and
+// u = dn g, dx = res + r u - x r^3 <u, x> / h (res: the residual gradient
+// that passes the norm), and rs[row] = r for the gain's gradient.
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const T* __restrict__ x, const T* __restrict__ g,
+                                                          const float* __restrict__ dn,
+                                                          const T* __restrict__ res, T* __restrict__ dx,
+                                                          float* __restrict__ rs, int64_t rows, int h,
+                                                          float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* xr = x + row * h;
+  const float* dr = dn + row * h;
+  float ss = 0.f, ux = 0.f;
+  for (int i = lane; i < h; i += 64) {
+    const float xv = to_f(xr[i]);
+    ss += xv * xv;
+    ux += dr[i] * to_f(g[i]) * xv;
+  }
+#pragma unroll
+  for (int o = 32; o; o >>= 1) {
+    ss += __shfl_xor(ss, o);
+    ux += __shfl_xor(ux, o);
+  }
+  const float r = 1.0f / sqrtf(ss / (float)h + eps);
+  const float k = r * r * r * ux / (float)h;
+  for (int i = lane; i < h; i += 64) {
+    const float xv = to_f(xr[i]);
+    dx[row * h + i] = from_f<T>(to_f(res[row * h + i]) + r * dr[i] * to_f(g[i]) - xv * k);
+  }
+  if (lane == 0) rs[row] = r;
+}
+
+// Gain gradient: dgain[c] += sum over rows of dn[row][c] x[row][c] rs[row].
+// Each thread sums a run of 256 rows of one column, then adds it atomically.
+template <typename T>
+__global__ void __launch_bounds__(256) gain_grad_kernel(const T* __restrict__ x, const float* __restrict__ dn,
+                                                        const float* __restrict__ rs, float* __restrict__ dgain,
+                                                        int64_t rows, int h) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= h) return;
+  const int64_t r0 = (int64_t)blockIdx.y * 256, r1 = r0 + 256 < rows ? r0 + 256 : rows;
+  float acc = 0.f;
+  for (int64_t r = r0; r < r1; r++) acc += dn[r * h + c] * to_f(x[r * h + c]) * rs[r];
+  atomicAdd(dgain + c, acc);
+}
+
+// ---------------------------------------------------------------------------
 // Small helpers for the shard stream's debug modes.
 // ---------------------------------------------------------------------------
 __global__ void fill32_kernel(uint32_t* p, uint32_t pat, size_t n) {
@@ -2031,6 +2127,46 @@ hipError_t launch_fill32(void* p, uint32_t pattern, size_t bytes, hipStream_t s)
   if (n == 0) return hipSuccess;
   const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
   fill32_kernel<<<grid, 256, 0, s>>>((uint32_t*)p, pattern, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(Dtype dt, const void* in, void* out, int64_t R, int64_t C, int64_t ldi,
+                            int64_t ldo, hipStream_t s) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
+  if (dt == BF16)
+    transpose_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)in, (bf16*)out, R, C, ldi, ldo);
+  else
+    transpose_kernel<float><<<grid, 256, 0, s>>>((const float*)in, (float*)out, R, C, ldi, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(Dtype dt, const float* a, const float* b, const float* dg, void* dab, void* g,
+                             int64_t rows, int64_t F, hipStream_t s) {
+  const int64_t n = rows * F;
+  if (n <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
+  if (dt == BF16)
+    swiglu_bwd_kernel<bf16><<<grid, 256, 0, s>>>(a, b, dg, (bf16*)dab, (bf16*)g, rows, F);
+  else
+    swiglu_bwd_kernel<float><<<grid, 256, 0, s>>>(a, b, dg, (float*)dab, (float*)g, rows, F);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const float* dn, const void* res,
+                              void* dx, float* rs, float* dgain, int64_t rows, int h, float eps,
+                              hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 rg((unsigned)((rows + 3) / 4)), cg((unsigned)((h + 255) / 256), (unsigned)((rows + 255) / 256));
+  if (dt == BF16) {
+    rmsnorm_bwd_kernel<bf16><<<rg, 256, 0, s>>>((const bf16*)x, (const bf16*)g, dn, (const bf16*)res,
+                                               (bf16*)dx, rs, rows, h, eps);
+    gain_grad_kernel<bf16><<<cg, 256, 0, s>>>((const bf16*)x, dn, rs, dgain, rows, h);
+  } else {
+    rmsnorm_bwd_kernel<float><<<rg, 256, 0, s>>>((const float*)x, (const float*)g, dn, (const float*)res,
+                                                (float*)dx, rs, rows, h, eps);
+    gain_grad_kernel<float><<<cg, 256, 0, s>>>((const float*)x, dn, rs, dgain, rows, h);
+  }
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libtsp.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "tsp.h")
 
 TSP_BF16, TSP_F32 = 0, 1
-TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV = 1, 2, 3, 4
+TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV, TSP_WS_MLP_BWD = 1, 2, 3, 4, 5
 TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP, TSP_F_PROFILE = 1, 2, 4, 8
 TSP_F_RESCALE_TEST = 16
 KERNELS = ["rmsnorm", "qkv", "attn", "merge", "oproj", "w13", "w2"]  # TSP_K_* order
@@ -74,9 +74,11 @@ def lib() -> ctypes.CDLL:
         L.tsp_mlp_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_layer_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_kv_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp]
+        L.tsp_mlp_shard_backward.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _pp, _vp, _sz, _vp]
         L.tsp_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         for f in ("tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
+                  "tsp_mlp_shard_backward",
                   "tsp_zigzag_positions", "tsp_profile_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -198,6 +200,26 @@ def tsp_kv_shard(dims, x, g1, w_attn, kv, ws, stream=None):
     _check_sizes(dims, TSP_WS_KV, x=x, g1=g1, w_attn=w_attn, kv=kv)
     _check(lib().tsp_kv_shard(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
                               _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def tsp_mlp_shard_backward(dims, x1, g2, w_mlp, dout, dx1, dg2, dw_mlp, ws, stream=None):
+    """Backward of the MLP half (include/tsp.h): dx1 in the dims' dtype, and
+    this rank's partial gradients dg2 [h] and dw_mlp (D fp32 tensors of
+    3*Fs*h elements in the packed shard layout)."""
+    _check_sizes(dims, TSP_WS_MLP_BWD, x1=x1, g2=g2, w_mlp=w_mlp, out=dout)
+    _check_sizes(dims, TSP_WS_MLP_BWD, x=dx1)
+    D, h = dims.fold, dims.hidden
+    if hasattr(dg2, "numel") and _nbytes(dg2) < 4 * h:
+        raise ValueError(f"dg2: {_nbytes(dg2)} bytes, the dims need {4 * h}")
+    need = 4 * 3 * (dims.ffn // D) * h
+    if len(dw_mlp) != D:
+        raise ValueError(f"dw_mlp: {len(dw_mlp)} shards for fold {D}")
+    for i, t in enumerate(dw_mlp):
+        if hasattr(t, "numel") and _nbytes(t) < need:
+            raise ValueError(f"dw_mlp[{i}]: {_nbytes(t)} bytes, the dims need {need}")
+    _check(lib().tsp_mlp_shard_backward(ctypes.byref(dims), _ptr(x1), _ptr(g2), _ptrs(w_mlp),
+                                        _ptr(dout), _ptr(dx1), _ptr(dg2), _ptrs(dw_mlp), _ptr(ws),
+                                        _nbytes(ws), _stream(stream)))
 
 
 def tsp_profile_read(reset: bool = True) -> dict:

@@ -134,7 +134,7 @@ enum {
 };
 
 /* Workspace kinds for tsp_workspace_bytes. */
-enum { TSP_WS_ATTN = 1, TSP_WS_MLP = 2, TSP_WS_LAYER = 3, TSP_WS_KV = 4 };
+enum { TSP_WS_ATTN = 1, TSP_WS_MLP = 2, TSP_WS_LAYER = 3, TSP_WS_KV = 4, TSP_WS_MLP_BWD = 5 };
 
 /* Debug flags (tsp_dims.flags).  Results must be identical with or without
  * the first four; they exist to expose missing stream hand-offs in tests.
@@ -245,6 +245,32 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1,
 int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1,
                  const void* const* w_attn, void* kv,
                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the MLP half for rank r's rows (training; the pages describe
+ * only the forward schedules, so this follows the plainest reading of them:
+ * the gradient of the rank's own rows goes through the MLP locally, and each
+ * weight shard gets a PARTIAL gradient from these rows, which a
+ * reduce-scatter over the D ranks would sum at the shard's owner, the reverse
+ * of the ring).  With n2 = RMSNorm(x1; g2), a_j = n2 W1_j, b_j = n2 W3_j,
+ * out = x1 + sum_j (silu(a_j) * b_j) W2_j and the output gradient dout:
+ *   x1     [B*T][h]  the forward input of the MLP half
+ *   g2     [h]       RMSNorm gain
+ *   w_mlp  D device pointers to packed MLP shards (as tsp_mlp_shard)
+ *   dout   [B*T][h]  gradient of out
+ *   dx1    [B*T][h]  output: gradient of x1 (dout through the residual plus the
+ *                    MLP branch through the norm), in dims->dtype
+ *   dg2    [h] fp32  output: this rank's partial gradient of g2 (overwritten)
+ *   dw_mlp D device pointers, each 3*Fs*h fp32 elements: output, this rank's
+ *          partial gradient of shard j in the shard's packed layout (dW1 rows,
+ *          dW3 rows, then the dW2 block), overwritten
+ *   ws     workspace of at least tsp_workspace_bytes(dims, TSP_WS_MLP_BWD) bytes
+ * Everything is enqueued on `stream` (no side stream); products accumulate in
+ * fp32, [da | db] and g = silu(a) b are stored in dims->dtype as GEMM operands.
+ */
+int tsp_mlp_shard_backward(const tsp_dims* dims, const void* x1, const void* g2,
+                           const void* const* w_mlp, const void* dout, void* dx1, float* dg2,
+                           float* const* dw_mlp, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Per-kernel timing of calls made with TSP_F_PROFILE: every kernel the

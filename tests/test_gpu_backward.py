@@ -1,0 +1,78 @@
+"""GPU parity of the MLP half's backward (tsp_mlp_shard_backward) against the
+backward oracle on the same rank's rows: the input gradient, this rank's
+partial gradient of the norm gain, and its partial gradient of every weight
+shard (unpacked from the shard layout)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.tsp_oracle as O
+import oracle.tsp_oracle_bwd as B
+import synth
+from folded_tensor_sequence_rank_amd import tsp
+from gpu_harness import DEV, f64, layer_dev, rel_fro, say, to_dev, tol
+from test_gpu_parity import _check as _delta_check
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(**kw):
+    base = dict(name="case", hidden=512, n_heads=4, head_dim=128, ffn=1376, seq=2048, fold=4,
+                ranks=(1,), layers=1, dtype="bf16")
+    base.update(kw)
+    return synth.LayerConfig(**base)
+
+
+CASES = {
+    "tiny_fp32": synth.get_config("tiny_fp32"),
+    "bf16_h512_fold4": _cfg(gamma="normal"),
+    "bf16_ragged_fs": _cfg(hidden=256, n_heads=4, head_dim=64, ffn=688, seq=1600, fold=4),  # F/D = 172, C = 200
+    "f32_d64_fold2_b2": _cfg(hidden=128, n_heads=2, head_dim=64, ffn=344, seq=512, fold=2, dtype="f32",
+                             batch=2),
+    "7b_s16k_rank3": synth.get_config("7b_s16k"),
+}
+
+
+def _check(cfg, name, got, want):
+    e = rel_fro(got, want)
+    say(f"    {name}: rel {e:.3e} (bar {tol(cfg)})")
+    assert np.isfinite(e) and e <= tol(cfg), (name, e)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_mlp_backward(case):
+    cfg = CASES[case]
+    r, D, h, Fs = cfg.ranks[0], cfg.fold, cfg.hidden, cfg.ffn // cfg.fold
+    say(f"[gpu] MLP backward {case}: h={h} F={cfg.ffn} S={cfg.seq} D={D} B={cfg.batch} rank {r} {cfg.dtype}")
+    w = synth.gen_weights(cfg)
+    L = layer_dev(cfg, w)
+    pos = O.zigzag_positions(cfg.seq, D, r)
+    # x1 and the output gradient: seeded synthetic rows of each sequence
+    x1 = np.concatenate([synth.gen_rows(cfg, pos, seq_index=b) for b in range(cfg.batch)])
+    dout = np.concatenate([synth.gen_rows(cfg, pos, layer=7, seq_index=b) for b in range(cfg.batch)])
+    x1_d, dout_d = to_dev(x1, cfg), to_dev(dout, cfg)
+    x1, dout = f64(x1_d), f64(dout_d)  # the values the GPU receives
+    dims = tsp.make_dims(cfg, r)
+    ws = torch.empty(max(tsp.workspace_bytes(dims, tsp.TSP_WS_MLP_BWD), 256), dtype=torch.uint8, device=DEV)
+    dx1 = torch.empty_like(x1_d)
+    dg2 = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    dw = [torch.full((3 * Fs * h,), float("nan"), dtype=torch.float32, device=DEV) for _ in range(D)]
+    tsp.tsp_mlp_shard_backward(dims, x1_d, L.g2, L.w_mlp, dout_d, dx1, dg2, dw, ws)
+    torch.cuda.synchronize()
+    say("    GPU done; oracle running")
+    g2 = np.asarray(w.g2, np.float64)
+    n2 = O.rmsnorm(x1, g2, cfg.eps)
+    dn2 = np.zeros_like(n2)
+    for j in range(D):
+        c = slice(j * Fs, (j + 1) * Fs)
+        dn, dw1, dw3, dw2 = B.swiglu_backward(n2, w.w1[:, c], w.w3[:, c], w.w2[c, :], dout)
+        dn2 += dn
+        got = f64(dw[j])
+        _check(cfg, f"shard {j} dW1 (partial)", got[:Fs * h].reshape(Fs, h), dw1.T)
+        _check(cfg, f"shard {j} dW3 (partial)", got[Fs * h:2 * Fs * h].reshape(Fs, h), dw3.T)
+        _check(cfg, f"shard {j} dW2 (partial)", got[2 * Fs * h:].reshape(h, Fs), dw2.T)
+    dxn, dg = B.rmsnorm_backward(x1, g2, cfg.eps, dn2)
+    # whole output, and the MLP branch (dx1 - dout) beyond dx1's own storage
+    # rounding, as for the forward blocks
+    _delta_check(cfg, "dx1", f64(dx1), dout + dxn, dout, dout)
+    _check(cfg, "dg2 (partial)", f64(dg2), dg)
