@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=32,
                     help="local rows of the rank's second chunk the oracle computes")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--mlp-backward", action="store_true",
+                    help="time the MLP half's backward (tsp_mlp_shard_backward) instead of the layer")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB three times (a kernel of known "
                          "traffic for scaling HBM counters)")
@@ -168,6 +170,55 @@ def cpu_baseline(cfg, r, rows):
                        f"mean wall time")}
 
 
+def mlp_backward_bench(args):
+    """The MLP half's backward for one rank's rows at the workload's shape:
+    algorithmic FLOPs 12*T*h*F (twice the forward's), plus 4*T*h*F to
+    recompute n2 W1 and n2 W3, which the call does rather than store them."""
+    import numpy as np
+    import torch
+
+    import synth
+    from folded_tensor_sequence_rank_amd import tsp
+    from gpu_harness import layer_dev, to_dev
+
+    cfg = synth.get_config(args.workload)
+    r = cfg.ranks[0] if args.rank is None else args.rank
+    torch.cuda.set_device(0)
+    D, h, Fs = cfg.fold, cfg.hidden, cfg.ffn // cfg.fold
+    L = layer_dev(cfg, synth.gen_weights(cfg))
+    pos = tsp.zigzag_positions(cfg.seq, D, r)
+    x1 = to_dev(np.concatenate([synth.gen_rows(cfg, pos, seq_index=b) for b in range(cfg.batch)]), cfg)
+    dout = to_dev(np.concatenate([synth.gen_rows(cfg, pos, layer=7, seq_index=b)
+                                  for b in range(cfg.batch)]), cfg)
+    dims = tsp.make_dims(cfg, r)
+    ws = torch.empty(tsp.workspace_bytes(dims, tsp.TSP_WS_MLP_BWD), dtype=torch.uint8, device="cuda")
+    dx1 = torch.empty_like(x1)
+    dg2 = torch.empty(h, dtype=torch.float32, device="cuda")
+    dw = [torch.empty(3 * Fs * h, dtype=torch.float32, device="cuda") for _ in range(D)]
+    run = lambda: tsp.tsp_mlp_shard_backward(dims, x1, L.g2, L.w_mlp, dout, dx1, dg2, dw, ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    T = cfg.batch * cfg.local_tokens
+    f_alg = 12 * T * h * cfg.ffn
+    tflops = f_alg / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "TFLOP/s of the MLP half's backward per TSP layer shard (7B shape)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "rank": r, "batch": cfg.batch, "local_tokens": T},
+        "frac_of_peak": round(tflops / (PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS), 4),
+        "flops_per_step": f_alg, "recompute_flops_per_step": 4 * T * h * cfg.ffn}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -175,6 +226,9 @@ def main():
               "single MI355X (one rank at its real shape); multi-GPU runs are not part of it.",
               file=sys.stderr)
         sys.exit(2)
+    if args.mlp_backward:
+        mlp_backward_bench(args)
+        return
 
     import numpy as np
     import torch

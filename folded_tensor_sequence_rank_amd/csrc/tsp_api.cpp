@@ -562,11 +562,12 @@ int check_shards(const void* const* w, int64_t D, const char* what) {
 
 // ---- backward of the MLP half -------------------------------------------
 // Workspace: the recomputed n2 and its transpose, dout transposed, the fp32
-// products a = n2 W1^T, b = n2 W3^T and dg = dout W2 of one shard, [da | db]
+// products [a | b] = n2 [W1 | W3] (one GEMM over the shard's contiguous W1|W3
+// block) and dg = dout W2 of one shard, [da | db]
 // and g = silu(a) b with their transposes, the shard's W2 and W1|W3 blocks
 // transposed, the fp32 gradient of n2 and the per-row rstd.
 struct MlpBwdWs {
-  size_t n2, n2t, dot, a, b, dg, dab, dabt, gm, gmt, w2t, w13t, dn, rs, end;
+  size_t n2, n2t, dot, ab, dg, dab, dabt, gm, gmt, w2t, w13t, dn, rs, end;
 };
 
 MlpBwdWs mlp_bwd_ws(const Dims& d) {
@@ -576,8 +577,7 @@ MlpBwdWs mlp_bwd_ws(const Dims& d) {
   w.n2 = o; o += al(T * h * es);
   w.n2t = o; o += al(T * h * es);
   w.dot = o; o += al(T * h * es);
-  w.a = o; o += al(T * F * 4);
-  w.b = o; o += al(T * F * 4);
+  w.ab = o; o += al(T * 2 * F * 4);
   w.dg = o; o += al(T * F * 4);
   w.dab = o; o += al(T * 2 * F * es);
   w.dabt = o; o += al(T * 2 * F * es);
@@ -615,8 +615,7 @@ int mlp_bwd_body(Ctx& c, const MlpBwdWs& L, const void* x1, const void* g2, cons
   char* ws = c.ws;
   const int64_t T = d.BT, h = d.h, F = d.Fs;
   const size_t es = d.es;
-  float* fa = (float*)(ws + L.a);
-  float* fb = (float*)(ws + L.b);
+  float* fab = (float*)(ws + L.ab);
   float* fdg = (float*)(ws + L.dg);
   float* dn = (float*)(ws + L.dn);
   HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.n2, T, (int)h, d.eps, c.s));
@@ -627,13 +626,11 @@ int mlp_bwd_body(Ctx& c, const MlpBwdWs& L, const void* x1, const void* g2, cons
   for (int64_t t = 0; t < d.D; t++) {  // the ring order of the forward: own shard first
     const int64_t j = (d.r + t) % d.D;
     const char* w1 = (const char*)w_mlp[j];
-    const char* w3 = w1 + (size_t)F * h * es;
     const char* w2 = w1 + 2 * (size_t)F * h * es;  // [h][F]
-    if ((rc = plain_gemm(c, ws + L.n2, h, w1, h, T, F, h, fa, F, false))) return rc;
-    if ((rc = plain_gemm(c, ws + L.n2, h, w3, h, T, F, h, fb, F, false))) return rc;
+    if ((rc = plain_gemm(c, ws + L.n2, h, w1, h, T, 2 * F, h, fab, 2 * F, false))) return rc;
     HIP_TRY(launch_transpose(d.dt, w2, ws + L.w2t, h, F, F, h, c.s));
     if ((rc = plain_gemm(c, dout, h, ws + L.w2t, h, T, F, h, fdg, F, false))) return rc;
-    HIP_TRY(launch_swiglu_bwd(d.dt, fa, fb, fdg, ws + L.dab, ws + L.gm, T, F, c.s));
+    HIP_TRY(launch_swiglu_bwd(d.dt, fab, fdg, ws + L.dab, ws + L.gm, T, F, c.s));
     // dn2 (+)= [da | db] . [W1; W3]  (B operand: the W1|W3 block transposed)
     HIP_TRY(launch_transpose(d.dt, w1, ws + L.w13t, 2 * F, h, h, 2 * F, c.s));
     if ((rc = plain_gemm(c, ws + L.dab, 2 * F, ws + L.w13t, 2 * F, T, h, 2 * F, dn, h, t > 0))) return rc;

@@ -92,8 +92,9 @@ hipError_t launch_spin(uint64_t ticks, hipStream_t s);
 // Backward of the MLP half.
 hipError_t launch_transpose(Dtype dt, const void* in, void* out, int64_t R, int64_t C, int64_t ldi,
                             int64_t ldo, hipStream_t s);
-hipError_t launch_swiglu_bwd(Dtype dt, const float* a, const float* b, const float* dg, void* dab, void* g,
-                             int64_t rows, int64_t F, hipStream_t s);
+// ab: [rows][2F] fp32, a = n W1 then b = n W3; dg: [rows][F] fp32.
+hipError_t launch_swiglu_bwd(Dtype dt, const float* ab, const float* dg, void* dab, void* g, int64_t rows,
+                             int64_t F, hipStream_t s);
 // dx = res + RMSNorm'(x)^T dn; dgain += the gain's gradient (not zeroed here).
 hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const float* dn, const void* res,
                               void* dx, float* rs, float* dgain, int64_t rows, int h, float eps,

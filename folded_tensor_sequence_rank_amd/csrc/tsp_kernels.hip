@@ -1823,20 +1823,20 @@ __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ in
   }
 }
 
-// SwiGLU backward per element, a = n W1, b = n W3 and dg = dout W2^T given in
-// fp32 [rows][F] (pitch F): da = dg b silu'(a), db = dg silu(a) into
+// SwiGLU backward per element, a = n W1 and b = n W3 given in fp32 side by
+// side ([rows][2F]: a in columns [0, F), b in [F, 2F)) and dg = dout W2^T in
+// fp32 [rows][F]: da = dg b silu'(a), db = dg silu(a) into
 // dab [rows][2F] (da in columns [0, F), db in [F, 2F)), and the forward
 // product g = silu(a) b into g [rows][F].
 template <typename T>
-__global__ void __launch_bounds__(256) swiglu_bwd_kernel(const float* __restrict__ a,
-                                                         const float* __restrict__ b,
+__global__ void __launch_bounds__(256) swiglu_bwd_kernel(const float* __restrict__ ab,
                                                          const float* __restrict__ dg,
                                                          T* __restrict__ dab, T* __restrict__ g,
                                                          int64_t rows, int64_t F) {
   const int64_t n = rows * F;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int64_t r = i / F, c = i - r * F;
-    const float av = a[i], bv = b[i], gv = dg[i];
+    const float av = ab[r * 2 * F + c], bv = ab[r * 2 * F + F + c], gv = dg[i];
     const float sg = 1.0f / (1.0f + expf(-av));
     const float s = av * sg;
     dab[r * 2 * F + c] = from_f<T>(gv * bv * sg * (1.0f + av * (1.0f - sg)));
@@ -2141,15 +2141,15 @@ hipError_t launch_transpose(Dtype dt, const void* in, void* out, int64_t R, int6
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(Dtype dt, const float* a, const float* b, const float* dg, void* dab, void* g,
-                             int64_t rows, int64_t F, hipStream_t s) {
+hipError_t launch_swiglu_bwd(Dtype dt, const float* ab, const float* dg, void* dab, void* g, int64_t rows,
+                             int64_t F, hipStream_t s) {
   const int64_t n = rows * F;
   if (n <= 0) return hipSuccess;
   const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
   if (dt == BF16)
-    swiglu_bwd_kernel<bf16><<<grid, 256, 0, s>>>(a, b, dg, (bf16*)dab, (bf16*)g, rows, F);
+    swiglu_bwd_kernel<bf16><<<grid, 256, 0, s>>>(ab, dg, (bf16*)dab, (bf16*)g, rows, F);
   else
-    swiglu_bwd_kernel<float><<<grid, 256, 0, s>>>(a, b, dg, (float*)dab, (float*)g, rows, F);
+    swiglu_bwd_kernel<float><<<grid, 256, 0, s>>>(ab, dg, (float*)dab, (float*)g, rows, F);
   return hipGetLastError();
 }
 
