@@ -570,6 +570,25 @@ struct MlpBwdWs {
   size_t n2, n2t, dot, ab, dg, dab, dabt, gm, gmt, w2t, w13t, dn, rs, end;
 };
 
+// Attention-core backward: the recomputed forward output of the group, the
+// per-row log-sum-exp and rowsum(dO * O), and the forward's split partials.
+struct AttnBwdWs {
+  size_t o, lse, dl, op, ml, end;
+};
+AttnBwdWs attn_bwd_ws(const Dims& d) {
+  AttnBwdWs w;
+  size_t o = 0;
+  w.o = o; o += al((size_t)d.BT * d.hs * d.es);
+  w.lse = o; o += al((size_t)d.Hd * d.BT * 4);
+  w.dl = o; o += al((size_t)d.Hd * d.BT * 4);
+  const AttnPlan p = plan_of(d);
+  const size_t nslot = p.split ? (size_t)d.Hd * d.B * p.nqt * p.maxseg * p.bq : 0;
+  w.op = o; o += al(nslot * d.d * 4);
+  w.ml = o; o += al(nslot * 2 * 4);
+  w.end = o;
+  return w;
+}
+
 MlpBwdWs mlp_bwd_ws(const Dims& d) {
   MlpBwdWs w;
   size_t o = 0;
@@ -663,6 +682,7 @@ size_t tsp_workspace_bytes(const tsp_dims* dims, int which) {
     }
     case TSP_WS_KV: return kv_ws_bytes(d);
     case TSP_WS_MLP_BWD: return mlp_bwd_ws(d).end;
+    case TSP_WS_ATTN_BWD: return attn_bwd_ws(d).end;
     default: return 0;
   }
 }
@@ -768,6 +788,77 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1, const v
   if ((rc = attn_body(c, A, x, g1, w_attn, kv, x1))) return rc;
   if ((rc = mlp_body(c, M, x1, g2, w_mlp, out))) return rc;
   return finish(c);
+}
+
+int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, const void* dout, float* dq,
+                           float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if (d.dt != TSP_BF16) return fail(TSP_E_DTYPE, "the attention backward runs in bf16 only");
+  if (d.d != 64 && d.d != 128) return fail(TSP_E_SHAPE, "the attention backward needs head_dim 64 or 128");
+  if ((rc = check_ptrs({q, kv, dout, dq, dk, dv, ws}))) return rc;
+  const AttnBwdWs L = attn_bwd_ws(d);
+  if (ws_bytes < L.end) return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.end);
+  const hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const void* vt = (const char*)kv + kv_v_offset(d) * d.es;
+  // forward recomputation: the group's output and each row's log-sum-exp
+  const AttnPlan plan = plan_of(d);
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.Q = q;
+  a.K = kv;
+  a.Vt = vt;
+  a.O = w + L.o;
+  a.Op = (float*)(w + L.op);
+  a.ML = (float*)(w + L.ml);
+  a.LSE = (float*)(w + L.lse);
+  a.T = d.T;
+  a.S = d.S;
+  a.batch = (int)d.B;
+  a.chunk = d.C;
+  a.ldo = (int)d.hs;
+  a.rank = (int)d.r;
+  a.fold = (int)d.D;
+  a.Hd = (int)d.Hd;
+  a.grp = (int)(d.H / d.Hkv);
+  a.nqt = plan.nqt;
+  a.lseg = plan.lseg;
+  a.maxseg = plan.maxseg;
+  a.nitems = plan.nitems;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
+  a.sum_cap = 18446744073709551616.0f;
+  HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 0, s));
+  if (plan.split) HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 1, s));
+  AttnBwdArgs b;
+  memset(&b, 0, sizeof b);
+  b.Q = q;
+  b.K = kv;
+  b.Vt = vt;
+  b.O = w + L.o;
+  b.dO = dout;
+  b.LSE = (const float*)(w + L.lse);
+  b.Dl = (float*)(w + L.dl);
+  b.dQ = dq;
+  b.dK = dk;
+  b.dV = dv;
+  b.T = d.T;
+  b.S = d.S;
+  b.chunk = d.C;
+  b.ldo = (int)d.hs;
+  b.rank = (int)d.r;
+  b.fold = (int)d.D;
+  b.batch = (int)d.B;
+  b.grp = (int)(d.H / d.Hkv);
+  b.Hd = (int)d.Hd;
+  b.Hkd = (int)d.Hkd;
+  b.scale_log2 = a.scale_log2;
+  b.scale = (float)(1.0 / std::sqrt((double)d.d));
+  for (int part = 0; part < 3; part++) HIP_TRY(launch_attn_bwd((int)d.d, b, part, s));
+  return TSP_OK;
 }
 
 int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,

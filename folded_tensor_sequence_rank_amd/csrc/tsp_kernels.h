@@ -60,6 +60,7 @@ struct AttnArgs {
   void* O;         // [B*T][ldo]; head t writes columns [t*HD, (t+1)*HD)
   float* Op;       // partial outputs of split items [Hd][B][nqt][maxseg][128][HD]
   float* ML;       // partial (max, sum) [Hd][B][nqt][maxseg][128][2]
+  float* LSE;      // optional: per row log2 of its softmax normaliser, [Hd][B*T]
   int64_t T, S, chunk;
   int ldo, rank, fold, Hd;
   int batch;
@@ -99,5 +100,24 @@ hipError_t launch_swiglu_bwd(Dtype dt, const float* ab, const float* dg, void* d
 hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const float* dn, const void* res,
                               void* dx, float* rs, float* dgain, int64_t rows, int h, float eps,
                               hipStream_t s);
+
+// Backward of the attention core (bf16, head dim 64 or 128).
+struct AttnBwdArgs {
+  const void* Q;     // [Hd][B*T][HD] rotated queries
+  const void* K;     // [Hkd][B*S][HD]
+  const void* Vt;    // [Hkd][HD][B*S]
+  const void* O;     // [B*T][ldo] forward output, head t at columns t*HD
+  const void* dO;    // [B*T][ldo] its gradient
+  const float* LSE;  // [Hd][B*T] log2 of each row's softmax normaliser (scaled scores)
+  float* Dl;         // [Hd][B*T] rowsum(dO * O)
+  float* dQ;         // [Hd][B*T][HD]
+  float* dK;         // [Hkd][B*S][HD]
+  float* dV;         // [Hkd][B*S][HD]
+  int64_t T, S, chunk;
+  int ldo, rank, fold, batch, grp, Hd, Hkd;
+  float scale_log2, scale;
+};
+// part 0: Dl; 1: dK and dV; 2: dQ.
+hipError_t launch_attn_bwd(int head_dim, const AttnBwdArgs& a, int part, hipStream_t s);
 
 }  // namespace tsp

@@ -1332,6 +1332,7 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
     if (nseg == 1) {
       if (qok[b]) {
         const float inv = 1.0f / lt;
+        if (a.LSE && lg == 0) a.LSE[((int64_t)head * nb + sb) * a.T + row] = m[b] + log2f(lt);
         T* orow = (T*)a.O + ((int64_t)sb * a.T + row) * a.ldo + head * HD;
 #pragma unroll
         for (int d = 0; d < DB; d++)
@@ -1735,6 +1736,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   if (nseg == 1) {
     if (qok) {
       const float inv = 1.0f / lt;
+      if (a.LSE && lg == 0) a.LSE[((int64_t)head * nb + sb) * a.T + row] = m + log2f(lt);
       T* orow = (T*)a.O + ((int64_t)sb * a.T + row) * a.ldo + head * HD;
 #pragma unroll
       for (int d = 0; d < DB; d++)
@@ -1793,6 +1795,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
     acc.w += w * v.w;
   }
   const float inv = 1.0f / L;
+  if (a.LSE && dq == 0) a.LSE[rid] = mx + log2f(L);
   store4<T>((T*)a.O + rowg * a.ldo + head * HD + 4 * dq, acc.x * inv, acc.y * inv, acc.z * inv,
             acc.w * inv);
 }
@@ -1891,6 +1894,263 @@ __global__ void __launch_bounds__(256) gain_grad_kernel(const T* __restrict__ x,
   float acc = 0.f;
   for (int64_t r = r0; r < r1; r++) acc += dn[r * h + c] * to_f(x[r * h + c]) * rs[r];
   atomicAdd(dgain + c, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the causal attention core (FlashAttention's recomputation:
+// the probabilities are rebuilt from the forward's per-row log-sum-exp, so no
+// S x S matrix is stored).  With P the probabilities of a query block
+// against a key block, dP = dO V^T, dS = P (dP - rowsum(dO O)):
+//   dV = P^T dO,  dK = dS^T Q / sqrt(d),  dQ = dS K / sqrt(d).
+// Two kernels, neither with atomics: one owns a key block and walks the query
+// blocks that can see it (dK, dV), the other owns a query block and walks
+// its keys (dQ, recomputing P and dP).  Every product runs on the 32x32x16
+// bf16 MFMA with both operands read from LDS contiguous in k, so the blocks
+// that serve as a k-major operand in one product and a row-major one in
+// another are staged in both layouts.
+// ---------------------------------------------------------------------------
+constexpr int kAB = 64;       // rows of a query or key block
+constexpr int kTP = kAB + 8;  // LDS row pitch of the transposed tiles (elements)
+
+// Position of local row i of a rank's zigzag rows (chunks r and 2D-1-r).
+__device__ inline int64_t zz_pos(int64_t i, int64_t C, int r, int D) {
+  return i < C ? (int64_t)r * C + i : (2 * (int64_t)D - 1 - r) * C + (i - C);
+}
+
+// c += A B for one 32x32 block, A element (m, k) at A[m * lda + k], B element
+// (k, n) at B[n * ldb + k] (both contiguous in k).
+__device__ inline void lds_mma(f32x16& c, const bf16* A, int lda, const bf16* B, int ldb, int kdim,
+                               int lane) {
+  const int r = lane & 31, kh = (lane >> 5) * 8;
+  for (int k = 0; k < kdim; k += 16) {
+    const bf16x8 fa = *(const bf16x8*)(A + r * lda + k + kh);
+    const bf16x8 fb = *(const bf16x8*)(B + r * ldb + k + kh);
+    c = MF<bf16>::mma(fa, fb, c);
+  }
+}
+
+// Rows [0, nvalid) of a 64-row tile (row stride ld elements) into LDS as
+// dst[row][HD] (pitch HD + 8) and, when TR, dstT[col][row] (pitch kTP); rows
+// past nvalid are zero.
+template <int HD, bool TR>
+__device__ inline void stage_rows(bf16* dst, bf16* dstT, const bf16* src, int64_t ld, int nvalid, int tid) {
+  constexpr int VPR = HD / 8;
+  for (int v = tid; v < kAB * VPR; v += 256) {
+    const int row = v / VPR, c = (v % VPR) * 8;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row < nvalid) x = *(const u32x4*)(src + row * ld + c);
+    *(u32x4*)(dst + row * (HD + 8) + c) = x;
+    if (TR) {
+      const bf16* e = (const bf16*)&x;
+#pragma unroll
+      for (int j = 0; j < 8; j++) dstT[(c + j) * kTP + row] = e[j];
+    }
+  }
+}
+
+// V^T columns [k0, k0 + 64) (keys) of one head into LDS as Vs[key][HD]; keys
+// at or past S are zero.  S and k0 are multiples of 8.
+template <int HD>
+__device__ inline void stage_vt(bf16* Vs, const bf16* vt, int64_t ldv, int64_t nkeys, int tid) {
+  for (int v = tid; v < HD * (kAB / 8); v += 256) {
+    const int dim = v / (kAB / 8), kc = (v % (kAB / 8)) * 8;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (kc < nkeys) x = *(const u32x4*)(vt + dim * ldv + kc);
+    const bf16* e = (const bf16*)&x;
+#pragma unroll
+    for (int j = 0; j < 8; j++) Vs[(kc + j) * (HD + 8) + dim] = e[j];
+  }
+}
+
+// Dl = rowsum(dO * O) per head and row; one wave per (head, row).
+template <int HD>
+__global__ void __launch_bounds__(256) attn_bwd_delta_kernel(AttnBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t BT = (int64_t)a.batch * a.T;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)a.Hd * BT) return;
+  const int64_t t = item / BT, rowg = item % BT;
+  const bf16* o = (const bf16*)a.O + rowg * a.ldo + t * HD;
+  const bf16* g = (const bf16*)a.dO + rowg * a.ldo + t * HD;
+  float s = 0.f;
+  for (int e = lane; e < HD; e += 64) s += (float)o[e] * (float)g[e];
+  for (int off = 32; off; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) a.Dl[item] = s;
+}
+
+// P and dS of the wave's 32x32 block (rows qh of the query block, columns kh
+// of the key block) from the scores s and dp = dO V^T, in place.
+__device__ inline void probs_and_ds(f32x16& s, f32x16& dp, const float* ls, const float* dl, int64_t q0,
+                                    int64_t k0, int qh, int kh, int lane, const AttnBwdArgs& a) {
+  const int64_t key = k0 + 32 * kh + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int m = 32 * qh + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+    const int64_t qi = q0 + m;
+    const bool ok = qi < a.T && key <= zz_pos(qi, a.chunk, a.rank, a.fold);
+    const float p = ok ? fast_exp2(s[i] * a.scale_log2 - ls[m]) : 0.f;
+    s[i] = p;
+    dp[i] = p * (dp[i] - dl[m]);
+  }
+}
+
+// One work-group per (64-key block, K/V head, sequence): dK and dV of those
+// keys, summed over the head's query heads and every query row of the rank
+// that attends to them.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  constexpr int P = HD + 8;
+  constexpr int NT = HD / 64;  // 32x32 output blocks per wave
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kAB * P];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kAB * P];
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kAB * P];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[kAB * P];
+  __shared__ __attribute__((aligned(16))) bf16 Qt[HD * kTP];
+  __shared__ __attribute__((aligned(16))) bf16 dOt[HD * kTP];
+  __shared__ __attribute__((aligned(16))) bf16 Pt[kAB * kTP];
+  __shared__ __attribute__((aligned(16))) bf16 dSt[kAB * kTP];
+  __shared__ float ls[kAB], dl[kAB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t k0 = (int64_t)blockIdx.x * kAB;
+  const int hk = blockIdx.y, b = blockIdx.z;
+  const int64_t BS = (int64_t)a.batch * a.S, BT = (int64_t)a.batch * a.T;
+  const int64_t nkeys = std::min<int64_t>(kAB, a.S - k0);
+  stage_rows<HD, false>(Ks, nullptr, (const bf16*)a.K + ((int64_t)hk * BS + (int64_t)b * a.S + k0) * HD, HD,
+                        (int)nkeys, tid);
+  stage_vt<HD>(Vs, (const bf16*)a.Vt + (int64_t)hk * HD * BS + (int64_t)b * a.S + k0, BS, nkeys, tid);
+  // first local row whose position reaches k0 (positions grow with the row)
+  const int64_t C = a.chunk, ca = (int64_t)a.rank * C, cb = (2 * (int64_t)a.fold - 1 - a.rank) * C;
+  const int64_t first = k0 <= ca ? 0 : k0 < ca + C ? k0 - ca : k0 <= cb ? C : k0 < cb + C ? C + k0 - cb : a.T;
+  const int qh = w >> 1, kh = w & 1;  // this wave's block of P and dS
+  f32x16 dk[NT], dv[NT];
+#pragma unroll
+  for (int u = 0; u < NT; u++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) dk[u][i] = dv[u][i] = 0.f;
+  for (int g = 0; g < a.grp; g++) {
+    const int64_t t = (int64_t)hk * a.grp + g;
+    for (int64_t q0 = first / kAB * kAB; q0 < a.T; q0 += kAB) {
+      const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
+      __syncthreads();  // the previous block's tiles are no longer read
+      stage_rows<HD, true>(Qs, Qt, (const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, tid);
+      stage_rows<HD, true>(dOs, dOt, (const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq,
+                           tid);
+      if (tid < kAB) {
+        const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
+        ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
+        dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
+      }
+      __syncthreads();
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
+      lds_mma(s, Qs + 32 * qh * P, P, Ks + 32 * kh * P, P, HD, lane);
+      lds_mma(dp, dOs + 32 * qh * P, P, Vs + 32 * kh * P, P, HD, lane);
+      probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
+      {  // P^T and dS^T as [key][query]: 4 consecutive queries per store
+        const int n = 32 * kh + (lane & 31);
+#pragma unroll
+        for (int gi = 0; gi < 4; gi++) {
+          const int m = 32 * qh + 8 * gi + 4 * (lane >> 5);
+          bf16 pv[4] = {(bf16)s[4 * gi], (bf16)s[4 * gi + 1], (bf16)s[4 * gi + 2], (bf16)s[4 * gi + 3]};
+          bf16 dv4[4] = {(bf16)dp[4 * gi], (bf16)dp[4 * gi + 1], (bf16)dp[4 * gi + 2], (bf16)dp[4 * gi + 3]};
+          *(u32x2*)(Pt + n * kTP + m) = *(const u32x2*)pv;
+          *(u32x2*)(dSt + n * kTP + m) = *(const u32x2*)dv4;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < NT; u++) {
+        const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
+        lds_mma(dv[u], Pt + 32 * ch * kTP, kTP, dOt + 32 * dt * kTP, kTP, kAB, lane);
+        lds_mma(dk[u], dSt + 32 * ch * kTP, kTP, Qt + 32 * dt * kTP, kTP, kAB, lane);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NT; u++) {
+    const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int64_t key = k0 + 32 * ch + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (key < a.S) {
+        const int64_t off = ((int64_t)hk * BS + (int64_t)b * a.S + key) * HD + 32 * dt + (lane & 31);
+        a.dK[off] = dk[u][i] * a.scale;
+        a.dV[off] = dv[u][i];
+      }
+    }
+  }
+}
+
+// One work-group per (64-row query block, query head, sequence): dQ of those
+// rows over every key they attend to.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int P = HD + 8;
+  constexpr int NT = HD / 64;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kAB * P];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[kAB * P];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kAB * P];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kAB * P];
+  __shared__ __attribute__((aligned(16))) bf16 Kt[HD * kTP];
+  __shared__ __attribute__((aligned(16))) bf16 dSs[kAB * kTP];
+  __shared__ float ls[kAB], dl[kAB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t q0 = (int64_t)blockIdx.x * kAB;
+  const int64_t t = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t hk = t / a.grp;
+  const int64_t BS = (int64_t)a.batch * a.S;
+  const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
+  const int64_t kend = zz_pos(q0 + nq - 1, a.chunk, a.rank, a.fold) + 1;  // keys [0, kend)
+  stage_rows<HD, false>(Qs, nullptr, (const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, tid);
+  stage_rows<HD, false>(dOs, nullptr, (const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq,
+                        tid);
+  if (tid < kAB) {
+    const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
+    ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
+    dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
+  }
+  const int qh = w >> 1, kh = w & 1;
+  f32x16 dq[NT];
+#pragma unroll
+  for (int u = 0; u < NT; u++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) dq[u][i] = 0.f;
+  for (int64_t k0 = 0; k0 < kend; k0 += kAB) {
+    const int64_t nkeys = std::min<int64_t>(kAB, a.S - k0);
+    __syncthreads();
+    stage_rows<HD, true>(Ks, Kt, (const bf16*)a.K + (hk * BS + (int64_t)b * a.S + k0) * HD, HD, (int)nkeys, tid);
+    stage_vt<HD>(Vs, (const bf16*)a.Vt + hk * HD * BS + (int64_t)b * a.S + k0, BS, nkeys, tid);
+    __syncthreads();
+    f32x16 s, dp;
+#pragma unroll
+    for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
+    lds_mma(s, Qs + 32 * qh * P, P, Ks + 32 * kh * P, P, HD, lane);
+    lds_mma(dp, dOs + 32 * qh * P, P, Vs + 32 * kh * P, P, HD, lane);
+    probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
+    {
+      const int n = 32 * kh + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; i++) dSs[(32 * qh + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * kTP + n] = (bf16)dp[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NT; u++) {
+      const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
+      lds_mma(dq[u], dSs + 32 * ch * kTP, kTP, Kt + 32 * dt * kTP, kTP, kAB, lane);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NT; u++) {
+    const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int m = 32 * ch + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (m < nq)
+        a.dQ[((t * a.batch + b) * a.T + q0 + m) * HD + 32 * dt + (lane & 31)] = dq[u][i] * a.scale;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2173,6 +2433,25 @@ hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const floa
 hipError_t launch_spin(uint64_t ticks, hipStream_t s) {
   spin_kernel<<<1, 64, 0, s>>>(ticks);
   return hipGetLastError();
+}
+
+template <int HD>
+hipError_t attn_bwd_hd(const AttnBwdArgs& a, int part, hipStream_t s) {
+  if (part == 0) {
+    const int64_t items = (int64_t)a.Hd * a.batch * a.T;
+    attn_bwd_delta_kernel<HD><<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a);
+  } else if (part == 1) {
+    attn_bwd_dkdv_kernel<HD><<<dim3((unsigned)((a.S + kAB - 1) / kAB), a.Hkd, a.batch), 256, 0, s>>>(a);
+  } else {
+    attn_bwd_dq_kernel<HD><<<dim3((unsigned)((a.T + kAB - 1) / kAB), a.Hd, a.batch), 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(int hd, const AttnBwdArgs& a, int part, hipStream_t s) {
+  if (hd == 128) return attn_bwd_hd<128>(a, part, s);
+  if (hd == 64) return attn_bwd_hd<64>(a, part, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tsp

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libtsp.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "tsp.h")
 
 TSP_BF16, TSP_F32 = 0, 1
-TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV, TSP_WS_MLP_BWD = 1, 2, 3, 4, 5
+TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV, TSP_WS_MLP_BWD, TSP_WS_ATTN_BWD = 1, 2, 3, 4, 5, 6
 TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP, TSP_F_PROFILE = 1, 2, 4, 8
 TSP_F_RESCALE_TEST = 16
 KERNELS = ["rmsnorm", "qkv", "attn", "merge", "oproj", "w13", "w2"]  # TSP_K_* order
@@ -75,10 +75,11 @@ def lib() -> ctypes.CDLL:
         L.tsp_layer_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_kv_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp]
         L.tsp_mlp_shard_backward.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _pp, _vp, _sz, _vp]
+        L.tsp_attn_core_backward.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.tsp_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         for f in ("tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
-                  "tsp_mlp_shard_backward",
+                  "tsp_mlp_shard_backward", "tsp_attn_core_backward",
                   "tsp_zigzag_positions", "tsp_profile_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -220,6 +221,26 @@ def tsp_mlp_shard_backward(dims, x1, g2, w_mlp, dout, dx1, dg2, dw_mlp, ws, stre
     _check(lib().tsp_mlp_shard_backward(ctypes.byref(dims), _ptr(x1), _ptr(g2), _ptrs(w_mlp),
                                         _ptr(dout), _ptr(dx1), _ptr(dg2), _ptrs(dw_mlp), _ptr(ws),
                                         _nbytes(ws), _stream(stream)))
+
+
+def tsp_attn_core_backward(dims, q, kv, dout, dq, dk, dv, ws, stream=None):
+    """Backward of the attention core for one shard's head group
+    (include/tsp.h): dq [Hd][B*T][d], and this rank's partial dk, dv
+    [Hkd][B*S][d], all fp32."""
+    D, d = dims.fold, dims.head_dim
+    B = max(dims.batch, 1)
+    T = dims.seq // D
+    Hd = dims.n_heads // D
+    Hkd = (dims.n_kv_heads or dims.n_heads) // D
+    es = 2 if dims.dtype == TSP_BF16 else 4
+    need = {"q": Hd * B * T * d * es, "kv": 2 * Hkd * B * dims.seq * d * es,
+            "dout": B * T * Hd * d * es, "dq": Hd * B * T * d * 4, "dk": Hkd * B * dims.seq * d * 4,
+            "dv": Hkd * B * dims.seq * d * 4}
+    for name, t in (("q", q), ("kv", kv), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if hasattr(t, "numel") and _nbytes(t) < need[name]:
+            raise ValueError(f"{name}: {_nbytes(t)} bytes, the dims need {need[name]}")
+    _check(lib().tsp_attn_core_backward(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(dout), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def tsp_profile_read(reset: bool = True) -> dict:

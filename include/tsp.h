@@ -134,7 +134,14 @@ enum {
 };
 
 /* Workspace kinds for tsp_workspace_bytes. */
-enum { TSP_WS_ATTN = 1, TSP_WS_MLP = 2, TSP_WS_LAYER = 3, TSP_WS_KV = 4, TSP_WS_MLP_BWD = 5 };
+enum {
+  TSP_WS_ATTN = 1,
+  TSP_WS_MLP = 2,
+  TSP_WS_LAYER = 3,
+  TSP_WS_KV = 4,
+  TSP_WS_MLP_BWD = 5,
+  TSP_WS_ATTN_BWD = 6
+};
 
 /* Debug flags (tsp_dims.flags).  Results must be identical with or without
  * the first four; they exist to expose missing stream hand-offs in tests.
@@ -271,6 +278,35 @@ int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1,
 int tsp_mlp_shard_backward(const tsp_dims* dims, const void* x1, const void* g2,
                            const void* const* w_mlp, const void* dout, void* dx1, float* dg2,
                            float* const* dw_mlp, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the causal attention core for one shard's head group (Hd = H/D
+ * query heads, Hkd = Hkv/D K/V heads) over rank r's rows, training as above.
+ * The gradient is that of o = softmax(q k^T / sqrt(d), keys at or before the
+ * query's global zigzag position) v ("Folding Tensor and Sequence
+ * Parallelism ...", section 2: each rank's queries attend to the gathered
+ * full-length K/V), computed as FlashAttention does: the forward's per-row
+ * log-sum-exp is recomputed from q and kv, then the probabilities are rebuilt
+ * block by block, so nothing of size S x S is stored.
+ *   q     [Hd][B*T][d]      the group's rotated queries (the QKV step's layout)
+ *   kv    K [Hkd][B*S][d], then V^T [Hkd][d][B*S]: every position's keys
+ *         (rotated) and values, as tsp_attn_shard reads them
+ *   dout  [B*T][Hd*d]       gradient of the group's attention output, head t
+ *                           at columns [t*d, (t+1)*d)
+ *   dq    [Hd][B*T][d] fp32 output: gradient of q (overwritten)
+ *   dk    [Hkd][B*S][d] fp32 output: this rank's PARTIAL gradient of every
+ *                           position's key, zero where no query of the rank
+ *                           attends (a reduce-scatter over the ranks, the
+ *                           reverse of the K/V all-gather, would sum them at
+ *                           each position's owner)
+ *   dv    [Hkd][B*S][d] fp32 output: the same for the values
+ *   ws    workspace of at least tsp_workspace_bytes(dims, TSP_WS_ATTN_BWD) bytes
+ * bf16 only (TSP_E_DTYPE otherwise), head_dim 64 or 128 (TSP_E_SHAPE
+ * otherwise).  Products accumulate in fp32; the probabilities and dS enter
+ * the MFMA products in bf16.  Everything is enqueued on `stream`.
+ */
+int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, const void* dout,
+                           float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Per-kernel timing of calls made with TSP_F_PROFILE: every kernel the

@@ -185,3 +185,14 @@ def test_binding_rejects_undersized_tensors():
     with pytest.raises(ValueError, match="shards for fold"):
         tsp.tsp_kv_shard(d, torch.empty(4 * T * h, dtype=torch.bfloat16), g, shards[:7], kv,
                          torch.empty(256, dtype=torch.uint8))
+
+
+def test_attention_backward_rejects_unsupported_before_gpu():
+    """bf16 only, head_dim 64 or 128: rejected from the dims alone."""
+    L = tsp.lib()
+    for cfg, want in ((TINY, "TSP_E_DTYPE"),
+                      (synth.LayerConfig(name="d32", hidden=256, n_heads=8, head_dim=32, ffn=512, seq=512,
+                                         fold=2, ranks=(0,), layers=1, dtype="bf16"), "TSP_E_SHAPE")):
+        dims = tsp.make_dims(cfg, 0)
+        rc = L.tsp_attn_core_backward(ctypes.byref(dims), None, None, None, None, None, None, None, 0, None)
+        assert tsp.STATUS[rc] == want, (cfg.name, rc, L.tsp_last_error())
