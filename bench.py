@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--mlp-backward", action="store_true",
                     help="time the MLP half's backward (tsp_mlp_shard_backward) instead of the layer")
+    ap.add_argument("--attn-backward", action="store_true",
+                    help="time the attention core's backward for one head group instead")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB three times (a kernel of known "
                          "traffic for scaling HBM counters)")
@@ -219,6 +221,60 @@ def mlp_backward_bench(args):
         "flops_per_step": f_alg, "recompute_flops_per_step": 4 * T * h * cfg.ffn}), flush=True)
 
 
+def attn_backward_bench(args):
+    """The attention core's backward for one head group (H/D query heads) of
+    one rank's rows at the workload's shape.  Algorithmic FLOPs 8*d per
+    (query, visible key) pair and head: dP = dO V^T, dV = P^T dO, dQ = dS K,
+    dK = dS^T Q.  The call also recomputes 10*d per pair: the forward (scores
+    and P V) for the log-sum-exp, and the scores in both backward kernels plus
+    dP in the dQ kernel."""
+    import torch
+
+    import synth
+    from folded_tensor_sequence_rank_amd import tsp
+
+    cfg = synth.get_config(args.workload)
+    r = cfg.ranks[0] if args.rank is None else args.rank
+    torch.cuda.set_device(0)
+    D, d, S, Bn = cfg.fold, cfg.head_dim, cfg.seq, cfg.batch
+    T = S // D
+    Hd, Hkd = cfg.n_heads // D, cfg.kv_heads // D
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234 + r)
+    bf = torch.bfloat16
+    q = torch.randn((Hd, Bn * T, d), generator=g, device="cuda").to(bf)
+    kv = torch.randn((2 * Hkd * Bn * S * d,), generator=g, device="cuda").to(bf)
+    do = torch.randn((Bn * T, Hd * d), generator=g, device="cuda").to(bf)
+    dq = torch.empty((Hd, Bn * T, d), device="cuda")
+    dk = torch.empty((Hkd, Bn * S, d), device="cuda")
+    dv = torch.empty((Hkd, Bn * S, d), device="cuda")
+    dims = tsp.make_dims(cfg, r)
+    ws = torch.empty(tsp.workspace_bytes(dims, tsp.TSP_WS_ATTN_BWD), dtype=torch.uint8, device="cuda")
+    run = lambda: tsp.tsp_attn_core_backward(dims, q, kv, do, dq, dk, dv, ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    pairs = int((tsp.zigzag_positions(S, D, r) + 1).sum())
+    f_alg = 8 * d * pairs * Hd * Bn
+    tflops = f_alg / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "TFLOP/s of the attention core's backward per head group (7B shape)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "rank": r, "batch": Bn, "local_tokens": Bn * T, "heads": Hd,
+                   "kv_heads": Hkd},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": f_alg, "recompute_flops_per_step": 10 * d * pairs * Hd * Bn}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -228,6 +284,9 @@ def main():
         sys.exit(2)
     if args.mlp_backward:
         mlp_backward_bench(args)
+        return
+    if args.attn_backward:
+        attn_backward_bench(args)
         return
 
     import numpy as np

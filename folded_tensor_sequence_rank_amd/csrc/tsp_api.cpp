@@ -572,8 +572,11 @@ struct MlpBwdWs {
 
 // Attention-core backward: the recomputed forward output of the group, the
 // per-row log-sum-exp and rowsum(dO * O), and the forward's split partials.
+// Transposed copies for the backward kernels: Q and dO [d][Hd * BTp], K
+// [d][Hkd * B*S], V by rows [B*S][Hkd * d].
+int64_t bt_pitch(const Dims& d) { return (d.BT + 7) / 8 * 8; }
 struct AttnBwdWs {
-  size_t o, lse, dl, op, ml, end;
+  size_t o, lse, dl, qt, dot, kt, vr, op, ml, end;
 };
 AttnBwdWs attn_bwd_ws(const Dims& d) {
   AttnBwdWs w;
@@ -581,6 +584,10 @@ AttnBwdWs attn_bwd_ws(const Dims& d) {
   w.o = o; o += al((size_t)d.BT * d.hs * d.es);
   w.lse = o; o += al((size_t)d.Hd * d.BT * 4);
   w.dl = o; o += al((size_t)d.Hd * d.BT * 4);
+  w.qt = o; o += al((size_t)d.d * d.Hd * bt_pitch(d) * d.es);
+  w.dot = o; o += al((size_t)d.d * d.Hd * bt_pitch(d) * d.es);
+  w.kt = o; o += al((size_t)d.d * d.Hkd * d.BS * d.es);
+  w.vr = o; o += al((size_t)d.d * d.Hkd * d.BS * d.es);
   const AttnPlan p = plan_of(d);
   const size_t nslot = p.split ? (size_t)d.Hd * d.B * p.nqt * p.maxseg * p.bq : 0;
   w.op = o; o += al(nslot * d.d * 4);
@@ -857,6 +864,20 @@ int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, 
   b.Hkd = (int)d.Hkd;
   b.scale_log2 = a.scale_log2;
   b.scale = (float)(1.0 / std::sqrt((double)d.d));
+  b.BTp = bt_pitch(d);
+  b.Qt = w + L.qt;
+  b.dOt = w + L.dot;
+  b.Kt = w + L.kt;
+  b.Vr = w + L.vr;
+  const int64_t ldt = d.Hd * b.BTp;
+  for (int64_t t = 0; t < d.Hd; t++) {
+    HIP_TRY(launch_transpose(d.dt, (const char*)q + t * d.BT * d.d * d.es, w + L.qt + t * b.BTp * d.es, d.BT,
+                             d.d, d.d, ldt, s));
+    HIP_TRY(launch_transpose(d.dt, (const char*)dout + t * d.d * d.es, w + L.dot + t * b.BTp * d.es, d.BT, d.d,
+                             d.hs, ldt, s));
+  }
+  HIP_TRY(launch_transpose(d.dt, kv, w + L.kt, d.Hkd * d.BS, d.d, d.d, d.Hkd * d.BS, s));
+  HIP_TRY(launch_transpose(d.dt, vt, w + L.vr, d.Hkd * d.d, d.BS, d.BS, d.Hkd * d.d, s));
   for (int part = 0; part < 3; part++) HIP_TRY(launch_attn_bwd((int)d.d, b, part, s));
   return TSP_OK;
 }

@@ -113,7 +113,11 @@ struct AttnBwdArgs {
   float* dQ;         // [Hd][B*T][HD]
   float* dK;         // [Hkd][B*S][HD]
   float* dV;         // [Hkd][B*S][HD]
-  int64_t T, S, chunk;
+  const void* Qt;    // [HD][Hd*BTp]: head t's queries at columns [t*BTp, t*BTp + B*T)
+  const void* dOt;   // [HD][Hd*BTp]: dO, the same way
+  const void* Kt;    // [HD][Hkd*B*S]
+  const void* Vr;    // [B*S][Hkd*HD]: V by rows
+  int64_t T, S, chunk, BTp;
   int ldo, rank, fold, batch, grp, Hd, Hkd;
   float scale_log2, scale;
 };

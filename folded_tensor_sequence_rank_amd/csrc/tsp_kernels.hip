@@ -1905,9 +1905,10 @@ __global__ void __launch_bounds__(256) gain_grad_kernel(const T* __restrict__ x,
 // Two kernels, neither with atomics: one owns a key block and walks the query
 // blocks that can see it (dK, dV), the other owns a query block and walks
 // its keys (dQ, recomputing P and dP).  Every product runs on the 32x32x16
-// bf16 MFMA with both operands read from LDS contiguous in k, so the blocks
-// that serve as a k-major operand in one product and a row-major one in
-// another are staged in both layouts.
+// bf16 MFMA with both operands read from LDS contiguous in k, so a block that
+// is contracted over its rows in one product and over its columns in another
+// is staged in both layouts, the second from a transposed copy made in HBM
+// before the kernels run (vector loads only, no element-wise transposes).
 // ---------------------------------------------------------------------------
 constexpr int kAB = 64;       // rows of a query or key block
 constexpr int kTP = kAB + 8;  // LDS row pitch of the transposed tiles (elements)
@@ -1929,38 +1930,41 @@ __device__ inline void lds_mma(f32x16& c, const bf16* A, int lda, const bf16* B,
   }
 }
 
-// Rows [0, nvalid) of a 64-row tile (row stride ld elements) into LDS as
-// dst[row][HD] (pitch HD + 8) and, when TR, dstT[col][row] (pitch kTP); rows
-// past nvalid are zero.
-template <int HD, bool TR>
-__device__ inline void stage_rows(bf16* dst, bf16* dstT, const bf16* src, int64_t ld, int nvalid, int tid) {
-  constexpr int VPR = HD / 8;
-  for (int v = tid; v < kAB * VPR; v += 256) {
-    const int row = v / VPR, c = (v % VPR) * 8;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < nvalid) x = *(const u32x4*)(src + row * ld + c);
-    *(u32x4*)(dst + row * (HD + 8) + c) = x;
-    if (TR) {
-      const bf16* e = (const bf16*)&x;
+// A tile of R rows x W columns (W a multiple of 8) of a bf16 matrix with row
+// stride ld, held in registers between its global load and its LDS store so
+// that the load of the next tile overlaps the current tile's products.
+// Element (i, j) is read when i < nr and j < nc, else zero.
+template <int R, int W>
+struct TileRegs {
+  static constexpr int NV = R * W / 8 / 256;
+  u32x4 v[NV];
+  __device__ inline void load(const bf16* src, int64_t ld, int nr, int nc, int tid) {
 #pragma unroll
-      for (int j = 0; j < 8; j++) dstT[(c + j) * kTP + row] = e[j];
+    for (int u = 0; u < NV; u++) {
+      const int e = tid + 256 * u, row = e / (W / 8), c = (e % (W / 8)) * 8;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      const bf16* p = src + row * ld + c;
+      if (row < nr && c < nc) {
+        if (c + 8 <= nc && ((uintptr_t)p & 15) == 0) {
+          x = *(const u32x4*)p;
+        } else {
+          bf16 t8[8];
+#pragma unroll
+          for (int j = 0; j < 8; j++) t8[j] = c + j < nc ? p[j] : (bf16)0.f;
+          x = *(const u32x4*)t8;
+        }
+      }
+      v[u] = x;
     }
   }
-}
-
-// V^T columns [k0, k0 + 64) (keys) of one head into LDS as Vs[key][HD]; keys
-// at or past S are zero.  S and k0 are multiples of 8.
-template <int HD>
-__device__ inline void stage_vt(bf16* Vs, const bf16* vt, int64_t ldv, int64_t nkeys, int tid) {
-  for (int v = tid; v < HD * (kAB / 8); v += 256) {
-    const int dim = v / (kAB / 8), kc = (v % (kAB / 8)) * 8;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (kc < nkeys) x = *(const u32x4*)(vt + dim * ldv + kc);
-    const bf16* e = (const bf16*)&x;
+  __device__ inline void store(bf16* dst, int pitch, int tid) const {
 #pragma unroll
-    for (int j = 0; j < 8; j++) Vs[(kc + j) * (HD + 8) + dim] = e[j];
+    for (int u = 0; u < NV; u++) {
+      const int e = tid + 256 * u, row = e / (W / 8), c = (e % (W / 8)) * 8;
+      *(u32x4*)(dst + row * pitch + c) = v[u];
+    }
   }
-}
+};
 
 // Dl = rowsum(dO * O) per head and row; one wave per (head, row).
 template <int HD>
@@ -1978,8 +1982,8 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(AttnBwdArgs a) {
   if (lane == 0) a.Dl[item] = s;
 }
 
-// P and dS of the wave's 32x32 block (rows qh of the query block, columns kh
-// of the key block) from the scores s and dp = dO V^T, in place.
+// P and dS of the wave's 32x32 block of the scores (rows qh of the query
+// block, columns kh of the key block), in place.
 __device__ inline void probs_and_ds(f32x16& s, f32x16& dp, const float* ls, const float* dl, int64_t q0,
                                     int64_t k0, int qh, int kh, int lane, const AttnBwdArgs& a) {
   const int64_t key = k0 + 32 * kh + (lane & 31);
@@ -1996,7 +2000,8 @@ __device__ inline void probs_and_ds(f32x16& s, f32x16& dp, const float* ls, cons
 
 // One work-group per (64-key block, K/V head, sequence): dK and dV of those
 // keys, summed over the head's query heads and every query row of the rank
-// that attends to them.
+// that attends to them.  Transposed copies: Qt [Hd][HD][BTp] and dOt (same),
+// Vr [B*S][Hkd*HD] (V by rows).
 template <int HD>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   constexpr int P = HD + 8;
@@ -2013,58 +2018,79 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t k0 = (int64_t)blockIdx.x * kAB;
   const int hk = blockIdx.y, b = blockIdx.z;
-  const int64_t BS = (int64_t)a.batch * a.S, BT = (int64_t)a.batch * a.T;
-  const int64_t nkeys = std::min<int64_t>(kAB, a.S - k0);
-  stage_rows<HD, false>(Ks, nullptr, (const bf16*)a.K + ((int64_t)hk * BS + (int64_t)b * a.S + k0) * HD, HD,
-                        (int)nkeys, tid);
-  stage_vt<HD>(Vs, (const bf16*)a.Vt + (int64_t)hk * HD * BS + (int64_t)b * a.S + k0, BS, nkeys, tid);
+  const int64_t BS = (int64_t)a.batch * a.S;
+  const int nkeys = (int)std::min<int64_t>(kAB, a.S - k0);
+  {
+    TileRegs<kAB, HD> rk, rv;
+    rk.load((const bf16*)a.K + ((int64_t)hk * BS + (int64_t)b * a.S + k0) * HD, HD, nkeys, HD, tid);
+    rv.load((const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + hk * HD, (int64_t)a.Hkd * HD, nkeys,
+            HD, tid);
+    rk.store(Ks, P, tid);
+    rv.store(Vs, P, tid);
+  }
   // first local row whose position reaches k0 (positions grow with the row)
   const int64_t C = a.chunk, ca = (int64_t)a.rank * C, cb = (2 * (int64_t)a.fold - 1 - a.rank) * C;
   const int64_t first = k0 <= ca ? 0 : k0 < ca + C ? k0 - ca : k0 <= cb ? C : k0 < cb + C ? C + k0 - cb : a.T;
+  const int64_t qs = first / kAB * kAB;
+  const int nqb = (int)((a.T - qs + kAB - 1) / kAB);
+  const int total = a.grp * nqb;  // (query head, query block) pairs, head-major
+  const int64_t ldt = (int64_t)a.Hd * a.BTp;
   const int qh = w >> 1, kh = w & 1;  // this wave's block of P and dS
   f32x16 dk[NT], dv[NT];
 #pragma unroll
   for (int u = 0; u < NT; u++)
 #pragma unroll
     for (int i = 0; i < 16; i++) dk[u][i] = dv[u][i] = 0.f;
-  for (int g = 0; g < a.grp; g++) {
-    const int64_t t = (int64_t)hk * a.grp + g;
-    for (int64_t q0 = first / kAB * kAB; q0 < a.T; q0 += kAB) {
-      const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
-      __syncthreads();  // the previous block's tiles are no longer read
-      stage_rows<HD, true>(Qs, Qt, (const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, tid);
-      stage_rows<HD, true>(dOs, dOt, (const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq,
-                           tid);
-      if (tid < kAB) {
-        const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
-        ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
-        dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
-      }
-      __syncthreads();
-      f32x16 s, dp;
+  TileRegs<kAB, HD> rq, rdo;
+  TileRegs<HD, kAB> rqt, rdot;
+  auto fetch = [&](int it) {
+    const int64_t t = (int64_t)hk * a.grp + it / nqb, q0 = qs + (int64_t)kAB * (it % nqb);
+    const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
+    const int64_t col = t * a.BTp + (int64_t)b * a.T + q0;
+    rq.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
+    rdo.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
+    rqt.load((const bf16*)a.Qt + col, ldt, HD, nq, tid);
+    rdot.load((const bf16*)a.dOt + col, ldt, HD, nq, tid);
+  };
+  if (total > 0) fetch(0);
+  for (int it = 0; it < total; it++) {
+    const int64_t t = (int64_t)hk * a.grp + it / nqb, q0 = qs + (int64_t)kAB * (it % nqb);
+    const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
+    __syncthreads();  // the previous block's tiles are no longer read
+    rq.store(Qs, P, tid);
+    rdo.store(dOs, P, tid);
+    rqt.store(Qt, kTP, tid);
+    rdot.store(dOt, kTP, tid);
+    if (tid < kAB) {
+      const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
+      ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
+      dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
+    }
+    __syncthreads();
+    if (it + 1 < total) fetch(it + 1);
+    f32x16 s, dp;
 #pragma unroll
-      for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
-      lds_mma(s, Qs + 32 * qh * P, P, Ks + 32 * kh * P, P, HD, lane);
-      lds_mma(dp, dOs + 32 * qh * P, P, Vs + 32 * kh * P, P, HD, lane);
-      probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
-      {  // P^T and dS^T as [key][query]: 4 consecutive queries per store
-        const int n = 32 * kh + (lane & 31);
+    for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
+    lds_mma(s, Qs + 32 * qh * P, P, Ks + 32 * kh * P, P, HD, lane);
+    lds_mma(dp, dOs + 32 * qh * P, P, Vs + 32 * kh * P, P, HD, lane);
+    probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
+    {  // P^T and dS^T as [key][query]: 4 consecutive queries per store
+      const int n = 32 * kh + (lane & 31);
 #pragma unroll
-        for (int gi = 0; gi < 4; gi++) {
-          const int m = 32 * qh + 8 * gi + 4 * (lane >> 5);
-          bf16 pv[4] = {(bf16)s[4 * gi], (bf16)s[4 * gi + 1], (bf16)s[4 * gi + 2], (bf16)s[4 * gi + 3]};
-          bf16 dv4[4] = {(bf16)dp[4 * gi], (bf16)dp[4 * gi + 1], (bf16)dp[4 * gi + 2], (bf16)dp[4 * gi + 3]};
-          *(u32x2*)(Pt + n * kTP + m) = *(const u32x2*)pv;
-          *(u32x2*)(dSt + n * kTP + m) = *(const u32x2*)dv4;
-        }
+      for (int gi = 0; gi < 4; gi++) {
+        const int m = 32 * qh + 8 * gi + 4 * (lane >> 5);
+        bf16 pv[4] = {(bf16)s[4 * gi], (bf16)s[4 * gi + 1], (bf16)s[4 * gi + 2], (bf16)s[4 * gi + 3]};
+        bf16 dv4[4] = {(bf16)dp[4 * gi], (bf16)dp[4 * gi + 1], (bf16)dp[4 * gi + 2], (bf16)dp[4 * gi + 3]};
+        *(u32x2*)(Pt + n * kTP + m) = *(const u32x2*)pv;
+        *(u32x2*)(dSt + n * kTP + m) = *(const u32x2*)dv4;
       }
-      __syncthreads();
+    }
+    __syncthreads();
 #pragma unroll
-      for (int u = 0; u < NT; u++) {
-        const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
-        lds_mma(dv[u], Pt + 32 * ch * kTP, kTP, dOt + 32 * dt * kTP, kTP, kAB, lane);
-        lds_mma(dk[u], dSt + 32 * ch * kTP, kTP, Qt + 32 * dt * kTP, kTP, kAB, lane);
-      }
+    for (int u = 0; u < NT; u++) {
+      const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
+      lds_mma(dv[u], Pt + 32 * ch * kTP, kTP, dOt + 32 * dt * kTP, kTP, kAB, lane);
+      lds_mma(dk[u], dSt + 32 * ch * kTP, kTP, Qt + 32 * dt * kTP, kTP, kAB, lane);
     }
   }
 #pragma unroll
@@ -2083,7 +2109,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 }
 
 // One work-group per (64-row query block, query head, sequence): dQ of those
-// rows over every key they attend to.
+// rows over every key they attend to.  The scores are formed transposed
+// (keys by rows), so each lane owns one query and dS is stored [query][key]
+// four keys at a time.  Transposed copies: Kt [HD][Hkd*B*S], Vr as above.
 template <int HD>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int P = HD + 8;
@@ -2094,7 +2122,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Vs[kAB * P];
   __shared__ __attribute__((aligned(16))) bf16 Kt[HD * kTP];
   __shared__ __attribute__((aligned(16))) bf16 dSs[kAB * kTP];
-  __shared__ float ls[kAB], dl[kAB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t q0 = (int64_t)blockIdx.x * kAB;
   const int64_t t = blockIdx.y;
@@ -2103,36 +2130,59 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
   const int64_t BS = (int64_t)a.batch * a.S;
   const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
   const int64_t kend = zz_pos(q0 + nq - 1, a.chunk, a.rank, a.fold) + 1;  // keys [0, kend)
-  stage_rows<HD, false>(Qs, nullptr, (const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, tid);
-  stage_rows<HD, false>(dOs, nullptr, (const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq,
-                        tid);
-  if (tid < kAB) {
-    const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
-    ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
-    dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
+  {
+    TileRegs<kAB, HD> r1, r2;
+    r1.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
+    r2.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
+    r1.store(Qs, P, tid);
+    r2.store(dOs, P, tid);
   }
-  const int qh = w >> 1, kh = w & 1;
+  const int kh = w >> 1, qh = w & 1;  // this wave's block of S^T: keys kh, queries qh
+  const int mq = 32 * qh + (lane & 31);  // the lane's query within the block
+  const bool qok = mq < nq;
+  const int64_t qpos = qok ? zz_pos(q0 + mq, a.chunk, a.rank, a.fold) : -1;
+  const int64_t rr = (t * a.batch + b) * a.T + q0 + mq;
+  const float lq = qok ? a.LSE[rr] : 0.f, dlq = qok ? a.Dl[rr] : 0.f;
   f32x16 dq[NT];
 #pragma unroll
   for (int u = 0; u < NT; u++)
 #pragma unroll
     for (int i = 0; i < 16; i++) dq[u][i] = 0.f;
+  const int64_t ldk = (int64_t)a.Hkd * BS;
+  TileRegs<kAB, HD> rk, rv;
+  TileRegs<HD, kAB> rkt;
+  auto fetch = [&](int64_t k0) {
+    const int nk = (int)std::min<int64_t>(kAB, a.S - k0);
+    rk.load((const bf16*)a.K + (hk * BS + (int64_t)b * a.S + k0) * HD, HD, nk, HD, tid);
+    rv.load((const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + hk * HD, (int64_t)a.Hkd * HD, nk, HD,
+            tid);
+    rkt.load((const bf16*)a.Kt + hk * BS + (int64_t)b * a.S + k0, ldk, HD, nk, tid);
+  };
+  fetch(0);
   for (int64_t k0 = 0; k0 < kend; k0 += kAB) {
-    const int64_t nkeys = std::min<int64_t>(kAB, a.S - k0);
     __syncthreads();
-    stage_rows<HD, true>(Ks, Kt, (const bf16*)a.K + (hk * BS + (int64_t)b * a.S + k0) * HD, HD, (int)nkeys, tid);
-    stage_vt<HD>(Vs, (const bf16*)a.Vt + hk * HD * BS + (int64_t)b * a.S + k0, BS, nkeys, tid);
+    rk.store(Ks, P, tid);
+    rv.store(Vs, P, tid);
+    rkt.store(Kt, kTP, tid);
     __syncthreads();
+    if (k0 + kAB < kend) fetch(k0 + kAB);
     f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
-    lds_mma(s, Qs + 32 * qh * P, P, Ks + 32 * kh * P, P, HD, lane);
-    lds_mma(dp, dOs + 32 * qh * P, P, Vs + 32 * kh * P, P, HD, lane);
-    probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
-    {
-      const int n = 32 * kh + (lane & 31);
+    lds_mma(s, Ks + 32 * kh * P, P, Qs + 32 * qh * P, P, HD, lane);
+    lds_mma(dp, Vs + 32 * kh * P, P, dOs + 32 * qh * P, P, HD, lane);
 #pragma unroll
-      for (int i = 0; i < 16; i++) dSs[(32 * qh + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * kTP + n] = (bf16)dp[i];
+    for (int gi = 0; gi < 4; gi++) {
+      const int kk = 32 * kh + 8 * gi + 4 * (lane >> 5);  // first of the lane's 4 keys
+      bf16 d4[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int i = 4 * gi + j;
+        const bool ok = k0 + kk + j <= qpos;
+        const float p = ok ? fast_exp2(s[i] * a.scale_log2 - lq) : 0.f;
+        d4[j] = (bf16)(p * (dp[i] - dlq));
+      }
+      *(u32x2*)(dSs + mq * kTP + kk) = *(const u32x2*)d4;
     }
     __syncthreads();
 #pragma unroll
