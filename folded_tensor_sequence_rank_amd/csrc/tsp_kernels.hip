@@ -1918,16 +1918,35 @@ __device__ inline int64_t zz_pos(int64_t i, int64_t C, int r, int D) {
   return i < C ? (int64_t)r * C + i : (2 * (int64_t)D - 1 - r) * C + (i - C);
 }
 
-// c += A B for one 32x32 block, A element (m, k) at A[m * lda + k], B element
-// (k, n) at B[n * ldb + k] (both contiguous in k).
-__device__ inline void lds_mma(f32x16& c, const bf16* A, int lda, const bf16* B, int ldb, int kdim,
-                               int lane) {
+// c += A B for one 32x32 block with B's fragments already in registers
+// (fb[k / 16] for k in [0, kdim)).
+template <int KS>
+__device__ inline void mma_regs_b(f32x16& c, const bf16* A, int lda, const bf16x8* fb, int lane) {
+  const int r = lane & 31, kh = (lane >> 5) * 8;
+#pragma unroll
+  for (int k = 0; k < KS; k++) c = MF<bf16>::mma(*(const bf16x8*)(A + r * lda + 16 * k + kh), fb[k], c);
+}
+
+// NT blocks c[u] += A B_u sharing the A operand (read once per k step); B_u
+// starts at B + u * bstep.
+template <int NT>
+__device__ inline void lds_mma_shared_a(f32x16* c, const bf16* A, int lda, const bf16* B, int ldb, int bstep,
+                                        int kdim, int lane) {
   const int r = lane & 31, kh = (lane >> 5) * 8;
   for (int k = 0; k < kdim; k += 16) {
     const bf16x8 fa = *(const bf16x8*)(A + r * lda + k + kh);
-    const bf16x8 fb = *(const bf16x8*)(B + r * ldb + k + kh);
-    c = MF<bf16>::mma(fa, fb, c);
+#pragma unroll
+    for (int u = 0; u < NT; u++) c[u] = MF<bf16>::mma(fa, *(const bf16x8*)(B + u * bstep + r * ldb + k + kh), c[u]);
   }
+}
+
+// Fragments of rows [0, 32) x k in [0, 16*KS) of an LDS block (pitch ld) as
+// an MFMA operand.
+template <int KS>
+__device__ inline void load_frags(bf16x8* f, const bf16* X, int ld, int lane) {
+  const int r = lane & 31, kh = (lane >> 5) * 8;
+#pragma unroll
+  for (int k = 0; k < KS; k++) f[k] = *(const bf16x8*)(X + r * ld + 16 * k + kh);
 }
 
 // A tile of R rows x W columns (W a multiple of 8) of a bf16 matrix with row
@@ -2028,6 +2047,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     rk.store(Ks, P, tid);
     rv.store(Vs, P, tid);
   }
+  const int qh = w >> 1, kh = w & 1;  // this wave's block of P and dS
+  __syncthreads();
+  bf16x8 kf[HD / 16], vf[HD / 16];  // the wave's key columns of K and V, all of d
+  load_frags<HD / 16>(kf, Ks + 32 * kh * P, P, lane);
+  load_frags<HD / 16>(vf, Vs + 32 * kh * P, P, lane);
   // first local row whose position reaches k0 (positions grow with the row)
   const int64_t C = a.chunk, ca = (int64_t)a.rank * C, cb = (2 * (int64_t)a.fold - 1 - a.rank) * C;
   const int64_t first = k0 <= ca ? 0 : k0 < ca + C ? k0 - ca : k0 <= cb ? C : k0 < cb + C ? C + k0 - cb : a.T;
@@ -2035,7 +2059,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   const int nqb = (int)((a.T - qs + kAB - 1) / kAB);
   const int total = a.grp * nqb;  // (query head, query block) pairs, head-major
   const int64_t ldt = (int64_t)a.Hd * a.BTp;
-  const int qh = w >> 1, kh = w & 1;  // this wave's block of P and dS
   f32x16 dk[NT], dv[NT];
 #pragma unroll
   for (int u = 0; u < NT; u++)
@@ -2043,10 +2066,18 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     for (int i = 0; i < 16; i++) dk[u][i] = dv[u][i] = 0.f;
   TileRegs<kAB, HD> rq, rdo;
   TileRegs<HD, kAB> rqt, rdot;
+  float rls = 0.f, rdl = 0.f;  // row tid's log-sum-exp and rowsum(dO O) (threads < 64)
   auto fetch = [&](int it) {
     const int64_t t = (int64_t)hk * a.grp + it / nqb, q0 = qs + (int64_t)kAB * (it % nqb);
     const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
     const int64_t col = t * a.BTp + (int64_t)b * a.T + q0;
+    if (tid < nq) {
+      const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
+      rls = a.LSE[rr];
+      rdl = a.Dl[rr];
+    } else {
+      rls = rdl = 0.f;
+    }
     rq.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
     rdo.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
     rqt.load((const bf16*)a.Qt + col, ldt, HD, nq, tid);
@@ -2054,25 +2085,23 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   };
   if (total > 0) fetch(0);
   for (int it = 0; it < total; it++) {
-    const int64_t t = (int64_t)hk * a.grp + it / nqb, q0 = qs + (int64_t)kAB * (it % nqb);
-    const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
+    const int64_t q0 = qs + (int64_t)kAB * (it % nqb);
     __syncthreads();  // the previous block's tiles are no longer read
     rq.store(Qs, P, tid);
     rdo.store(dOs, P, tid);
     rqt.store(Qt, kTP, tid);
     rdot.store(dOt, kTP, tid);
     if (tid < kAB) {
-      const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
-      ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
-      dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
+      ls[tid] = rls;
+      dl[tid] = rdl;
     }
     __syncthreads();
     if (it + 1 < total) fetch(it + 1);
     f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
-    lds_mma(s, Qs + 32 * qh * P, P, Ks + 32 * kh * P, P, HD, lane);
-    lds_mma(dp, dOs + 32 * qh * P, P, Vs + 32 * kh * P, P, HD, lane);
+    mma_regs_b<HD / 16>(s, Qs + 32 * qh * P, P, kf, lane);
+    mma_regs_b<HD / 16>(dp, dOs + 32 * qh * P, P, vf, lane);
     probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
     {  // P^T and dS^T as [key][query]: 4 consecutive queries per store
       const int n = 32 * kh + (lane & 31);
@@ -2086,11 +2115,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < NT; u++) {
-      const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
-      lds_mma(dv[u], Pt + 32 * ch * kTP, kTP, dOt + 32 * dt * kTP, kTP, kAB, lane);
-      lds_mma(dk[u], dSt + 32 * ch * kTP, kTP, Qt + 32 * dt * kTP, kTP, kAB, lane);
+    {  // blocks tau = w + 4u: key half w % 2, dim blocks w / 2 + 2u
+      const int ch = w & 1, dt = w >> 1;
+      lds_mma_shared_a<NT>(dv, Pt + 32 * ch * kTP, kTP, dOt + 32 * dt * kTP, kTP, 64 * kTP, kAB, lane);
+      lds_mma_shared_a<NT>(dk, dSt + 32 * ch * kTP, kTP, Qt + 32 * dt * kTP, kTP, 64 * kTP, kAB, lane);
     }
   }
 #pragma unroll
@@ -2113,15 +2141,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 // (keys by rows), so each lane owns one query and dS is stored [query][key]
 // four keys at a time.  Transposed copies: Kt [HD][Hkd*B*S], Vr as above.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int P = HD + 8;
   constexpr int NT = HD / 64;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kAB * P];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[kAB * P];
   __shared__ __attribute__((aligned(16))) bf16 Ks[kAB * P];
   __shared__ __attribute__((aligned(16))) bf16 Vs[kAB * P];
   __shared__ __attribute__((aligned(16))) bf16 Kt[HD * kTP];
   __shared__ __attribute__((aligned(16))) bf16 dSs[kAB * kTP];
+  bf16* const Qs = Ks;  // Q and dO pass through LDS once, into registers
+  bf16* const dOs = Vs;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t q0 = (int64_t)blockIdx.x * kAB;
   const int64_t t = blockIdx.y;
@@ -2138,6 +2166,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
     r2.store(dOs, P, tid);
   }
   const int kh = w >> 1, qh = w & 1;  // this wave's block of S^T: keys kh, queries qh
+  __syncthreads();
+  bf16x8 qf[HD / 16], of[HD / 16];  // the wave's queries of Q and dO, all of d
+  load_frags<HD / 16>(qf, Qs + 32 * qh * P, P, lane);
+  load_frags<HD / 16>(of, dOs + 32 * qh * P, P, lane);
   const int mq = 32 * qh + (lane & 31);  // the lane's query within the block
   const bool qok = mq < nq;
   const int64_t qpos = qok ? zz_pos(q0 + mq, a.chunk, a.rank, a.fold) : -1;
@@ -2169,8 +2201,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
     f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
-    lds_mma(s, Ks + 32 * kh * P, P, Qs + 32 * qh * P, P, HD, lane);
-    lds_mma(dp, Vs + 32 * kh * P, P, dOs + 32 * qh * P, P, HD, lane);
+    mma_regs_b<HD / 16>(s, Ks + 32 * kh * P, P, qf, lane);
+    mma_regs_b<HD / 16>(dp, Vs + 32 * kh * P, P, of, lane);
 #pragma unroll
     for (int gi = 0; gi < 4; gi++) {
       const int kk = 32 * kh + 8 * gi + 4 * (lane >> 5);  // first of the lane's 4 keys
@@ -2185,11 +2217,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
       *(u32x2*)(dSs + mq * kTP + kk) = *(const u32x2*)d4;
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < NT; u++) {
-      const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
-      lds_mma(dq[u], dSs + 32 * ch * kTP, kTP, Kt + 32 * dt * kTP, kTP, kAB, lane);
-    }
+    lds_mma_shared_a<NT>(dq, dSs + 32 * (w & 1) * kTP, kTP, Kt + 32 * (w >> 1) * kTP, kTP, 64 * kTP, kAB, lane);
   }
 #pragma unroll
   for (int u = 0; u < NT; u++) {
