@@ -2022,18 +2022,18 @@ __device__ inline void probs_and_ds(f32x16& s, f32x16& dp, const float* ls, cons
 // that attends to them.  Transposed copies: Qt [Hd][HD][BTp] and dOt (same),
 // Vr [B*S][Hkd*HD] (V by rows).
 template <int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   constexpr int P = HD + 8;
   constexpr int NT = HD / 64;  // 32x32 output blocks per wave
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kAB * P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kAB * P];
+  // Two work-groups per CU: K and V pass through the Q / dO space once, into
+  // registers, and P^T / dS^T reuse that space after each block's scores.
   __shared__ __attribute__((aligned(16))) bf16 Qs[kAB * P];
   __shared__ __attribute__((aligned(16))) bf16 dOs[kAB * P];
   __shared__ __attribute__((aligned(16))) bf16 Qt[HD * kTP];
   __shared__ __attribute__((aligned(16))) bf16 dOt[HD * kTP];
-  __shared__ __attribute__((aligned(16))) bf16 Pt[kAB * kTP];
-  __shared__ __attribute__((aligned(16))) bf16 dSt[kAB * kTP];
   __shared__ float ls[kAB], dl[kAB];
+  bf16* const Pt = Qs;
+  bf16* const dSt = dOs;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t k0 = (int64_t)blockIdx.x * kAB;
   const int hk = blockIdx.y, b = blockIdx.z;
@@ -2044,14 +2044,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     rk.load((const bf16*)a.K + ((int64_t)hk * BS + (int64_t)b * a.S + k0) * HD, HD, nkeys, HD, tid);
     rv.load((const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + hk * HD, (int64_t)a.Hkd * HD, nkeys,
             HD, tid);
-    rk.store(Ks, P, tid);
-    rv.store(Vs, P, tid);
+    rk.store(Qs, P, tid);
+    rv.store(dOs, P, tid);
   }
   const int qh = w >> 1, kh = w & 1;  // this wave's block of P and dS
   __syncthreads();
   bf16x8 kf[HD / 16], vf[HD / 16];  // the wave's key columns of K and V, all of d
-  load_frags<HD / 16>(kf, Ks + 32 * kh * P, P, lane);
-  load_frags<HD / 16>(vf, Vs + 32 * kh * P, P, lane);
+  load_frags<HD / 16>(kf, Qs + 32 * kh * P, P, lane);
+  load_frags<HD / 16>(vf, dOs + 32 * kh * P, P, lane);
   // first local row whose position reaches k0 (positions grow with the row)
   const int64_t C = a.chunk, ca = (int64_t)a.rank * C, cb = (2 * (int64_t)a.fold - 1 - a.rank) * C;
   const int64_t first = k0 <= ca ? 0 : k0 < ca + C ? k0 - ca : k0 <= cb ? C : k0 < cb + C ? C + k0 - cb : a.T;
@@ -2064,45 +2064,36 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   for (int u = 0; u < NT; u++)
 #pragma unroll
     for (int i = 0; i < 16; i++) dk[u][i] = dv[u][i] = 0.f;
-  TileRegs<kAB, HD> rq, rdo;
-  TileRegs<HD, kAB> rqt, rdot;
-  float rls = 0.f, rdl = 0.f;  // row tid's log-sum-exp and rowsum(dO O) (threads < 64)
-  auto fetch = [&](int it) {
+  for (int it = 0; it < total; it++) {
     const int64_t t = (int64_t)hk * a.grp + it / nqb, q0 = qs + (int64_t)kAB * (it % nqb);
     const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
     const int64_t col = t * a.BTp + (int64_t)b * a.T + q0;
-    if (tid < nq) {
-      const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
-      rls = a.LSE[rr];
-      rdl = a.Dl[rr];
-    } else {
-      rls = rdl = 0.f;
-    }
-    rq.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
-    rdo.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
-    rqt.load((const bf16*)a.Qt + col, ldt, HD, nq, tid);
-    rdot.load((const bf16*)a.dOt + col, ldt, HD, nq, tid);
-  };
-  if (total > 0) fetch(0);
-  for (int it = 0; it < total; it++) {
-    const int64_t q0 = qs + (int64_t)kAB * (it % nqb);
-    __syncthreads();  // the previous block's tiles are no longer read
-    rq.store(Qs, P, tid);
-    rdo.store(dOs, P, tid);
-    rqt.store(Qt, kTP, tid);
-    rdot.store(dOt, kTP, tid);
+    __syncthreads();  // the previous block's products no longer read LDS
     if (tid < kAB) {
-      ls[tid] = rls;
-      dl[tid] = rdl;
+      const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
+      ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
+      dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
+    }
+    {  // two tiles at a time (register pressure)
+      TileRegs<kAB, HD> r1;
+      TileRegs<HD, kAB> r2;
+      r1.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
+      r2.load((const bf16*)a.Qt + col, ldt, HD, nq, tid);
+      r1.store(Qs, P, tid);
+      r2.store(Qt, kTP, tid);
+      r1.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
+      r2.load((const bf16*)a.dOt + col, ldt, HD, nq, tid);
+      r1.store(dOs, P, tid);
+      r2.store(dOt, kTP, tid);
     }
     __syncthreads();
-    if (it + 1 < total) fetch(it + 1);
     f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
     mma_regs_b<HD / 16>(s, Qs + 32 * qh * P, P, kf, lane);
     mma_regs_b<HD / 16>(dp, dOs + 32 * qh * P, P, vf, lane);
     probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
+    __syncthreads();  // Q and dO read by every wave: their space takes P^T and dS^T
     {  // P^T and dS^T as [key][query]: 4 consecutive queries per store
       const int n = 32 * kh + (lane & 31);
 #pragma unroll
