@@ -1912,6 +1912,7 @@ __global__ void __launch_bounds__(256) gain_grad_kernel(const T* __restrict__ x,
 // ---------------------------------------------------------------------------
 constexpr int kAB = 64;       // rows of a query or key block
 constexpr int kTP = kAB + 8;  // LDS row pitch of the transposed tiles (elements)
+constexpr int kBK2 = 128;     // keys per work-group of the dK/dV kernel
 
 // Position of local row i of a rank's zigzag rows (chunks r and 2D-1-r).
 __device__ inline int64_t zz_pos(int64_t i, int64_t C, int r, int D) {
@@ -1953,14 +1954,14 @@ __device__ inline void load_frags(bf16x8* f, const bf16* X, int ld, int lane) {
 // stride ld, held in registers between its global load and its LDS store so
 // that the load of the next tile overlaps the current tile's products.
 // Element (i, j) is read when i < nr and j < nc, else zero.
-template <int R, int W>
+template <int R, int W, int NTH = 256>
 struct TileRegs {
-  static constexpr int NV = R * W / 8 / 256;
+  static constexpr int NV = R * W / 8 / NTH;
   u32x4 v[NV];
   __device__ inline void load(const bf16* src, int64_t ld, int nr, int nc, int tid) {
 #pragma unroll
     for (int u = 0; u < NV; u++) {
-      const int e = tid + 256 * u, row = e / (W / 8), c = (e % (W / 8)) * 8;
+      const int e = tid + NTH * u, row = e / (W / 8), c = (e % (W / 8)) * 8;
       u32x4 x = {0u, 0u, 0u, 0u};
       const bf16* p = src + row * ld + c;
       if (row < nr && c < nc) {
@@ -1979,7 +1980,7 @@ struct TileRegs {
   __device__ inline void store(bf16* dst, int pitch, int tid) const {
 #pragma unroll
     for (int u = 0; u < NV; u++) {
-      const int e = tid + 256 * u, row = e / (W / 8), c = (e % (W / 8)) * 8;
+      const int e = tid + NTH * u, row = e / (W / 8), c = (e % (W / 8)) * 8;
       *(u32x4*)(dst + row * pitch + c) = v[u];
     }
   }
@@ -2022,36 +2023,41 @@ __device__ inline void probs_and_ds(f32x16& s, f32x16& dp, const float* ls, cons
 // that attends to them.  Transposed copies: Qt [Hd][HD][BTp] and dOt (same),
 // Vr [B*S][Hkd*HD] (V by rows).
 template <int HD>
-__global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(512) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   constexpr int P = HD + 8;
-  constexpr int NT = HD / 64;  // 32x32 output blocks per wave
-  // Two work-groups per CU: K and V pass through the Q / dO space once, into
-  // registers, and P^T / dS^T reuse that space after each block's scores.
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kAB * P];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[kAB * P];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[HD * kTP];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[HD * kTP];
+  constexpr int NT = HD / 64;  // 32x32 output blocks of dK (and of dV) per wave
+  // Eight waves over 128 keys: each 64-row query block staged in LDS serves
+  // twice the keys of a 64-key block.  K and V pass through LDS once, into
+  // registers (the wave's 32 keys), in the space the loop's tiles use later.
+  constexpr int QS = 0, DOS = QS + kAB * P, QT = DOS + kAB * P, DOT = QT + HD * kTP, PT = DOT + HD * kTP,
+                DST = PT + kBK2 * kTP, NEL = DST + kBK2 * kTP;
+  static_assert(2 * kBK2 * P <= NEL, "K and V staging must fit in the loop's space");
+  __shared__ __attribute__((aligned(16))) bf16 sm[NEL];
   __shared__ float ls[kAB], dl[kAB];
-  bf16* const Pt = Qs;
-  bf16* const dSt = dOs;
+  bf16* const Qs = sm + QS;
+  bf16* const dOs = sm + DOS;
+  bf16* const Qt = sm + QT;
+  bf16* const dOt = sm + DOT;
+  bf16* const Pt = sm + PT;
+  bf16* const dSt = sm + DST;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t k0 = (int64_t)blockIdx.x * kAB;
+  const int64_t k0 = (int64_t)blockIdx.x * kBK2;
   const int hk = blockIdx.y, b = blockIdx.z;
   const int64_t BS = (int64_t)a.batch * a.S;
-  const int nkeys = (int)std::min<int64_t>(kAB, a.S - k0);
+  const int nkeys = (int)std::min<int64_t>(kBK2, a.S - k0);
   {
-    TileRegs<kAB, HD> rk, rv;
+    TileRegs<kBK2, HD, 512> rk;
     rk.load((const bf16*)a.K + ((int64_t)hk * BS + (int64_t)b * a.S + k0) * HD, HD, nkeys, HD, tid);
-    rv.load((const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + hk * HD, (int64_t)a.Hkd * HD, nkeys,
-            HD, tid);
-    rk.store(Qs, P, tid);
-    rv.store(dOs, P, tid);
+    rk.store(sm, P, tid);
+    rk.load((const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + hk * HD, (int64_t)a.Hkd * HD, nkeys, HD,
+            tid);
+    rk.store(sm + kBK2 * P, P, tid);
   }
-  const int qh = w >> 1, kh = w & 1;  // this wave's block of P and dS
+  const int qh = w & 1, kh = w >> 1;  // this wave's block of P and dS: queries qh, keys kh (of 4)
   __syncthreads();
-  bf16x8 kf[HD / 16], vf[HD / 16];  // the wave's key columns of K and V, all of d
-  load_frags<HD / 16>(kf, Qs + 32 * kh * P, P, lane);
-  load_frags<HD / 16>(vf, dOs + 32 * kh * P, P, lane);
+  bf16x8 kf[HD / 16], vf[HD / 16];  // the wave's 32 keys of K and V, all of d
+  load_frags<HD / 16>(kf, sm + 32 * kh * P, P, lane);
+  load_frags<HD / 16>(vf, sm + (kBK2 + 32 * kh) * P, P, lane);
   // first local row whose position reaches k0 (positions grow with the row)
   const int64_t C = a.chunk, ca = (int64_t)a.rank * C, cb = (2 * (int64_t)a.fold - 1 - a.rank) * C;
   const int64_t first = k0 <= ca ? 0 : k0 < ca + C ? k0 - ca : k0 <= cb ? C : k0 < cb + C ? C + k0 - cb : a.T;
@@ -2068,23 +2074,23 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     const int64_t t = (int64_t)hk * a.grp + it / nqb, q0 = qs + (int64_t)kAB * (it % nqb);
     const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
     const int64_t col = t * a.BTp + (int64_t)b * a.T + q0;
-    __syncthreads();  // the previous block's products no longer read LDS
+    __syncthreads();  // the previous block's products (and the K/V fragment loads) no longer read LDS
     if (tid < kAB) {
       const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
       ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
       dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
     }
-    {  // two tiles at a time (register pressure)
-      TileRegs<kAB, HD> r1;
-      TileRegs<HD, kAB> r2;
+    {
+      TileRegs<kAB, HD, 512> r1, r2;
+      TileRegs<HD, kAB, 512> r3, r4;
       r1.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
-      r2.load((const bf16*)a.Qt + col, ldt, HD, nq, tid);
+      r2.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
+      r3.load((const bf16*)a.Qt + col, ldt, HD, nq, tid);
+      r4.load((const bf16*)a.dOt + col, ldt, HD, nq, tid);
       r1.store(Qs, P, tid);
-      r2.store(Qt, kTP, tid);
-      r1.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
-      r2.load((const bf16*)a.dOt + col, ldt, HD, nq, tid);
-      r1.store(dOs, P, tid);
-      r2.store(dOt, kTP, tid);
+      r2.store(dOs, P, tid);
+      r3.store(Qt, kTP, tid);
+      r4.store(dOt, kTP, tid);
     }
     __syncthreads();
     f32x16 s, dp;
@@ -2093,7 +2099,6 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     mma_regs_b<HD / 16>(s, Qs + 32 * qh * P, P, kf, lane);
     mma_regs_b<HD / 16>(dp, dOs + 32 * qh * P, P, vf, lane);
     probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
-    __syncthreads();  // Q and dO read by every wave: their space takes P^T and dS^T
     {  // P^T and dS^T as [key][query]: 4 consecutive queries per store
       const int n = 32 * kh + (lane & 31);
 #pragma unroll
@@ -2106,18 +2111,16 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
       }
     }
     __syncthreads();
-    {  // blocks tau = w + 4u: key half w % 2, dim blocks w / 2 + 2u
-      const int ch = w & 1, dt = w >> 1;
-      lds_mma_shared_a<NT>(dv, Pt + 32 * ch * kTP, kTP, dOt + 32 * dt * kTP, kTP, 64 * kTP, kAB, lane);
-      lds_mma_shared_a<NT>(dk, dSt + 32 * ch * kTP, kTP, Qt + 32 * dt * kTP, kTP, 64 * kTP, kAB, lane);
-    }
+    // output blocks: keys kh (the wave's own 32), dim blocks qh + 2u
+    lds_mma_shared_a<NT>(dv, Pt + 32 * kh * kTP, kTP, dOt + 32 * qh * kTP, kTP, 64 * kTP, kAB, lane);
+    lds_mma_shared_a<NT>(dk, dSt + 32 * kh * kTP, kTP, Qt + 32 * qh * kTP, kTP, 64 * kTP, kAB, lane);
   }
 #pragma unroll
   for (int u = 0; u < NT; u++) {
-    const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
+    const int dt = qh + 2 * u;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const int64_t key = k0 + 32 * ch + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const int64_t key = k0 + 32 * kh + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       if (key < a.S) {
         const int64_t off = ((int64_t)hk * BS + (int64_t)b * a.S + key) * HD + 32 * dt + (lane & 31);
         a.dK[off] = dk[u][i] * a.scale;
@@ -2510,7 +2513,7 @@ hipError_t attn_bwd_hd(const AttnBwdArgs& a, int part, hipStream_t s) {
     const int64_t items = (int64_t)a.Hd * a.batch * a.T;
     attn_bwd_delta_kernel<HD><<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a);
   } else if (part == 1) {
-    attn_bwd_dkdv_kernel<HD><<<dim3((unsigned)((a.S + kAB - 1) / kAB), a.Hkd, a.batch), 256, 0, s>>>(a);
+    attn_bwd_dkdv_kernel<HD><<<dim3((unsigned)((a.S + kBK2 - 1) / kBK2), a.Hkd, a.batch), 512, 0, s>>>(a);
   } else {
     attn_bwd_dq_kernel<HD><<<dim3((unsigned)((a.T + kAB - 1) / kAB), a.Hd, a.batch), 256, 0, s>>>(a);
   }
