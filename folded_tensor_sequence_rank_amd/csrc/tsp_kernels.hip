@@ -1913,6 +1913,7 @@ __global__ void __launch_bounds__(256) gain_grad_kernel(const T* __restrict__ x,
 constexpr int kAB = 64;       // rows of a query or key block
 constexpr int kTP = kAB + 8;  // LDS row pitch of the transposed tiles (elements)
 constexpr int kBK2 = 128;     // keys per work-group of the dK/dV kernel
+constexpr int kBQ2 = 128;     // query rows per work-group of the dQ kernel
 
 // Position of local row i of a rank's zigzag rows (chunks r and 2D-1-r).
 __device__ inline int64_t zz_pos(int64_t i, int64_t C, int r, int D) {
@@ -2130,40 +2131,42 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   }
 }
 
-// One work-group per (64-row query block, query head, sequence): dQ of those
-// rows over every key they attend to.  The scores are formed transposed
-// (keys by rows), so each lane owns one query and dS is stored [query][key]
-// four keys at a time.  Transposed copies: Kt [HD][Hkd*B*S], Vr as above.
+// One work-group per (128-row query block, query head, sequence): dQ of
+// those rows over every key they attend to, eight waves, so that each staged
+// 64-key block serves 128 queries.  The scores are formed transposed (keys
+// by rows), so each lane owns one query and dS is stored [query][key] four
+// keys at a time.  Transposed copies: Kt [HD][Hkd*B*S], Vr as above.
 template <int HD>
-__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(512) attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int P = HD + 8;
-  constexpr int NT = HD / 64;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kAB * P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kAB * P];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[HD * kTP];
-  __shared__ __attribute__((aligned(16))) bf16 dSs[kAB * kTP];
-  bf16* const Qs = Ks;  // Q and dO pass through LDS once, into registers
-  bf16* const dOs = Vs;
+  constexpr int NT = HD / 64;  // 32x32 output blocks per wave
+  constexpr int KS = 0, VS = KS + kAB * P, KT = VS + kAB * P, DSS = KT + HD * kTP, NEL = DSS + kBQ2 * kTP;
+  static_assert(2 * kBQ2 * P <= NEL, "Q and dO staging must fit in the loop's space");
+  __shared__ __attribute__((aligned(16))) bf16 sm[NEL];
+  bf16* const Ks = sm + KS;
+  bf16* const Vs = sm + VS;
+  bf16* const Kt = sm + KT;
+  bf16* const dSs = sm + DSS;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t q0 = (int64_t)blockIdx.x * kAB;
+  const int64_t q0 = (int64_t)blockIdx.x * kBQ2;
   const int64_t t = blockIdx.y;
   const int b = blockIdx.z;
   const int64_t hk = t / a.grp;
   const int64_t BS = (int64_t)a.batch * a.S;
-  const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
+  const int nq = (int)std::min<int64_t>(kBQ2, a.T - q0);
   const int64_t kend = zz_pos(q0 + nq - 1, a.chunk, a.rank, a.fold) + 1;  // keys [0, kend)
-  {
-    TileRegs<kAB, HD> r1, r2;
-    r1.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
-    r2.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
-    r1.store(Qs, P, tid);
-    r2.store(dOs, P, tid);
+  {  // Q and dO pass through LDS once, into registers
+    TileRegs<kBQ2, HD, 512> r;
+    r.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
+    r.store(sm, P, tid);
+    r.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
+    r.store(sm + kBQ2 * P, P, tid);
   }
-  const int kh = w >> 1, qh = w & 1;  // this wave's block of S^T: keys kh, queries qh
+  const int qh = w >> 1, kh = w & 1;  // this wave's block of S^T: queries qh (of 4), keys kh
   __syncthreads();
-  bf16x8 qf[HD / 16], of[HD / 16];  // the wave's queries of Q and dO, all of d
-  load_frags<HD / 16>(qf, Qs + 32 * qh * P, P, lane);
-  load_frags<HD / 16>(of, dOs + 32 * qh * P, P, lane);
+  bf16x8 qf[HD / 16], of[HD / 16];  // the wave's 32 queries of Q and dO, all of d
+  load_frags<HD / 16>(qf, sm + 32 * qh * P, P, lane);
+  load_frags<HD / 16>(of, sm + (kBQ2 + 32 * qh) * P, P, lane);
   const int mq = 32 * qh + (lane & 31);  // the lane's query within the block
   const bool qok = mq < nq;
   const int64_t qpos = qok ? zz_pos(q0 + mq, a.chunk, a.rank, a.fold) : -1;
@@ -2175,8 +2178,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; i++) dq[u][i] = 0.f;
   const int64_t ldk = (int64_t)a.Hkd * BS;
-  TileRegs<kAB, HD> rk, rv;
-  TileRegs<HD, kAB> rkt;
+  TileRegs<kAB, HD, 512> rk, rv;
+  TileRegs<HD, kAB, 512> rkt;
   auto fetch = [&](int64_t k0) {
     const int nk = (int)std::min<int64_t>(kAB, a.S - k0);
     rk.load((const bf16*)a.K + (hk * BS + (int64_t)b * a.S + k0) * HD, HD, nk, HD, tid);
@@ -2186,7 +2189,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
   };
   fetch(0);
   for (int64_t k0 = 0; k0 < kend; k0 += kAB) {
-    __syncthreads();
+    __syncthreads();  // the previous block's products (and the Q/dO fragment loads) no longer read LDS
     rk.store(Ks, P, tid);
     rv.store(Vs, P, tid);
     rkt.store(Kt, kTP, tid);
@@ -2211,14 +2214,15 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs a) {
       *(u32x2*)(dSs + mq * kTP + kk) = *(const u32x2*)d4;
     }
     __syncthreads();
-    lds_mma_shared_a<NT>(dq, dSs + 32 * (w & 1) * kTP, kTP, Kt + 32 * (w >> 1) * kTP, kTP, 64 * kTP, kAB, lane);
+    // output blocks: queries qh (the wave's own 32), dim blocks kh + 2u
+    lds_mma_shared_a<NT>(dq, dSs + 32 * qh * kTP, kTP, Kt + 32 * kh * kTP, kTP, 64 * kTP, kAB, lane);
   }
 #pragma unroll
   for (int u = 0; u < NT; u++) {
-    const int tau = w + 4 * u, ch = tau & 1, dt = tau >> 1;
+    const int dt = kh + 2 * u;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const int m = 32 * ch + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const int m = 32 * qh + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       if (m < nq)
         a.dQ[((t * a.batch + b) * a.T + q0 + m) * HD + 32 * dt + (lane & 31)] = dq[u][i] * a.scale;
     }
@@ -2515,7 +2519,7 @@ hipError_t attn_bwd_hd(const AttnBwdArgs& a, int part, hipStream_t s) {
   } else if (part == 1) {
     attn_bwd_dkdv_kernel<HD><<<dim3((unsigned)((a.S + kBK2 - 1) / kBK2), a.Hkd, a.batch), 512, 0, s>>>(a);
   } else {
-    attn_bwd_dq_kernel<HD><<<dim3((unsigned)((a.T + kAB - 1) / kAB), a.Hd, a.batch), 256, 0, s>>>(a);
+    attn_bwd_dq_kernel<HD><<<dim3((unsigned)((a.T + kBQ2 - 1) / kBQ2), a.Hd, a.batch), 512, 0, s>>>(a);
   }
   return hipGetLastError();
 }
