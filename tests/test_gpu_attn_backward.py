@@ -88,3 +88,49 @@ def test_attention_core_backward(case):
                 assert e <= TOL, (b, hk, name, e)
                 # no query of the rank reaches past its last position
                 assert np.all(got[pos.max() + 1:] == 0.0), name
+
+
+def test_attention_core_backward_7b_s64k_rank3():
+    """The shape and launch the attention-backward benchmark times (7B head
+    group, S = 65536, fold 8, rank 3): dQ on 96 sampled rows of every head
+    (a row's dQ depends on that row alone), and dK, dV of K/V head 0 at every
+    position, the oracle summing all 8192 query rows in chunks."""
+    cfg = _cfg(hidden=4096, n_heads=32, head_dim=128, ffn=11008, seq=65536, fold=8)
+    r, D, d, S = 3, 8, 128, 65536
+    T, Hd = S // D, 4
+    say(f"[gpu] attention backward 7B group S={S} D={D} rank {r}")
+    rng = np.random.default_rng(4321)
+    q = _bf16(rng.standard_normal((Hd, T, d)))
+    k = _bf16(rng.standard_normal((Hd, S, d)))
+    v = _bf16(rng.standard_normal((Hd, S, d)))
+    do = _bf16(rng.standard_normal((T, Hd * d)))
+    kv = torch.cat([k.reshape(-1), v.transpose(1, 2).contiguous().reshape(-1)]).to(DEV)
+    dims = tsp.make_dims(cfg, r)
+    ws = torch.empty(tsp.workspace_bytes(dims, tsp.TSP_WS_ATTN_BWD), dtype=torch.uint8, device=DEV)
+    dq = torch.full((Hd, T, d), float("nan"), device=DEV)
+    dk = torch.full((Hd, S, d), float("nan"), device=DEV)
+    dv = torch.full((Hd, S, d), float("nan"), device=DEV)
+    tsp.tsp_attn_core_backward(dims, q.to(DEV), kv, do.to(DEV), dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    say("    GPU done; oracle running")
+    qn, kn, vn, don = f64(q), f64(k), f64(v), f64(do)
+    pos = O.zigzag_positions(S, D, r)
+    # both chunks' edges and interior rows
+    rows = np.unique(np.concatenate([[0, 1, T // 2 - 1, T // 2, T - 1], rng.integers(0, T, 91)]))
+    for t in range(Hd):
+        eq, _, _ = B.causal_attention_backward(qn[t, rows], pos[rows], kn[t], vn[t], don[rows, t * d:(t + 1) * d])
+        e = rel_fro(f64(dq[t, rows]), eq)
+        say(f"    head {t} dQ on {rows.size} rows: rel {e:.3e}")
+        assert e <= TOL, (t, e)
+    gk = np.zeros((S, d))
+    gv = np.zeros((S, d))
+    for c0 in range(0, T, 1024):
+        c = slice(c0, c0 + 1024)
+        _, ek, ev = B.causal_attention_backward(qn[0, c], pos[c], kn[0], vn[0], don[c, :d])
+        gk += ek
+        gv += ev
+    for name, got, want in (("dK", f64(dk[0]), gk), ("dV", f64(dv[0]), gv)):
+        e = rel_fro(got, want)
+        say(f"    K/V head 0 {name}: rel {e:.3e}")
+        assert e <= TOL, (name, e)
+        assert np.all(got[pos.max() + 1:] == 0.0), name
