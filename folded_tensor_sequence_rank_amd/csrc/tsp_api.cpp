@@ -63,6 +63,44 @@ struct Dims {
   uint32_t flags;
 };
 
+int64_t acc_group(const Dims& d);
+
+// The GEMM and attention kernels stage operands through buffer loads whose
+// byte offsets are 32-bit and which mark rows and chunks outside a matrix
+// with the offset 2^31 (past the range, so they read zero).  Every buffer
+// range they address must therefore stay at or below 2^31 bytes; larger
+// shapes are refused before anything is enqueued.
+constexpr uint64_t kMaxRange = 1ull << 31;
+
+int check_offsets(const Dims& d) {
+  const int64_t G = acc_group(d);
+  const uint64_t es = d.es, BT = d.BT, h = d.h;
+  // GEMM A operands, [B*T rows][K]: the normalised activations (K = h), an
+  // accumulation group's attention outputs (G*hs) or SwiGLU products (G*Fs),
+  // and in the MLP backward [da | db] (2*Fs) and its transpose.
+  const uint64_t widest = std::max<uint64_t>({(uint64_t)h, (uint64_t)(G * d.hs), (uint64_t)(G * d.Fs),
+                                              (uint64_t)(2 * d.Fs)});
+  const uint64_t a_op = BT * widest * es;
+  // GEMM B operands: the packed Q|K|V block, the W_O and W2 group buffers,
+  // the W1|W3 block and its transpose.
+  const uint64_t b_op = std::max<uint64_t>({(uint64_t)(d.hs + 2 * d.ks) * h, h * (uint64_t)(G * d.hs),
+                                            h * (uint64_t)(G * d.Fs), 2 * (uint64_t)d.Fs * h}) * es;
+  // Attention: one sequence's K plane of a K/V head, and the V^T plane of a
+  // K/V head over the micro-batch ((d-1) rows of B*S keys, then S).
+  const uint64_t k_plane = (uint64_t)d.S * d.d * es;
+  const uint64_t v_plane = ((uint64_t)(d.d - 1) * d.BS + d.S) * es;
+  struct {
+    const char* what;
+    uint64_t bytes;
+  } rs[] = {{"an activation GEMM operand", a_op}, {"a weight GEMM operand", b_op},
+            {"a K plane", k_plane}, {"a V^T plane", v_plane}};
+  for (auto& r : rs)
+    if (r.bytes > kMaxRange)
+      return fail(TSP_E_SHAPE, "%s would span %llu bytes; the kernels address at most 2^31 bytes per buffer",
+                  r.what, (unsigned long long)r.bytes);
+  return TSP_OK;
+}
+
 int check_dims(const tsp_dims* p, Dims* o) {
   if (!p) return fail(TSP_E_INVAL, "dims is NULL");
   if (p->dtype != TSP_BF16 && p->dtype != TSP_F32)
@@ -117,7 +155,7 @@ int check_dims(const tsp_dims* p, Dims* o) {
   o->es = p->dtype == TSP_BF16 ? 2 : 4;
   o->eps = p->eps;
   o->flags = p->flags;
-  return TSP_OK;
+  return check_offsets(*o);
 }
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -126,7 +126,12 @@ enum {
   TSP_E_INVAL = -1,     /* null pointer, rank outside [0, D), negative size, batch,
                            n_kv_heads or rope_theta */
   TSP_E_SHAPE = -2,     /* h != H*d, H % D, F % D, S % 2D, S % 8, unsupported d,
-                           H % Hkv, Hkv % D */
+                           H % Hkv, Hkv % D, or a buffer the kernels stage from
+                           would exceed 2^31 bytes: B*T*max(h, G*hs, G*Fs, 2*Fs)*b,
+                           G = max(1, min(4, D/2)) (activations, the grouped O / W2 operands, the MLP
+                           backward's [da | db]), the weight blocks, or one K/V
+                           head's K or V^T plane (the kernels use 32-bit byte
+                           offsets within each buffer) */
   TSP_E_ALIGN = -3,     /* a device pointer is not 16-byte aligned */
   TSP_E_WORKSPACE = -4, /* ws_bytes < tsp_workspace_bytes(...) */
   TSP_E_DTYPE = -5,     /* dtype is neither TSP_BF16 nor TSP_F32 */

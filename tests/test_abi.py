@@ -196,3 +196,39 @@ def test_attention_backward_rejects_unsupported_before_gpu():
         dims = tsp.make_dims(cfg, 0)
         rc = L.tsp_attn_core_backward(ctypes.byref(dims), None, None, None, None, None, None, None, 0, None)
         assert tsp.STATUS[rc] == want, (cfg.name, rc, L.tsp_last_error())
+
+
+@pytest.mark.parametrize("cfg,ok,what", [
+    # bf16 7B shape at 128K, fold 8.  The widest activation operand is the W2
+    # product's [B*T][G*Fs] (G = 4 shards of 1376 FFN columns): B*T*5504*2
+    # bytes stay within 2^31 up to B = 11.
+    (synth.get_config("7b_s128k").with_(batch=11), True, None),
+    (synth.get_config("7b_s128k").with_(batch=12), False, "activation GEMM operand"),
+    (synth.get_config("7b_s128k").with_(batch=33), False, "activation GEMM operand"),
+    # fp32 at 64K: 4-byte elements, B*T*5504*4 bytes, up to B = 11
+    (C3.with_(dtype="f32", batch=11), True, None),
+    (C3.with_(dtype="f32", batch=12), False, "activation GEMM operand"),
+])
+def test_shapes_past_32bit_offsets_are_refused(cfg, ok, what):
+    """The kernels address each buffer with 32-bit byte offsets and mark
+    out-of-matrix rows with offset 2^31, so every buffer they stage from must
+    span at most 2^31 bytes.  Larger shapes return TSP_E_SHAPE from the dims
+    alone (no workspace size, nothing enqueued).  With H % D == 0 the K and
+    V^T planes (B*S*d elements at most) never outgrow the activations
+    (B*T*h = B*S*d*H/D), so the activation operand is the first limit."""
+    d = tsp.make_dims(cfg, cfg.ranks[0])
+    ws = tsp.workspace_bytes(d, tsp.TSP_WS_LAYER)
+    if ok:
+        assert ws > 0, tsp.lib().tsp_last_error()
+        return
+    assert ws == 0
+    rc = _call_attn(d)
+    assert tsp.STATUS[rc] == "TSP_E_SHAPE", rc
+    assert what in tsp.lib().tsp_last_error().decode()
+    L = tsp.lib()
+    arr = (ctypes.c_void_p * cfg.fold)(*([4096] * cfg.fold))
+    for call in (lambda: L.tsp_layer_shard(ctypes.byref(d), 16, 16, arr, 16, 16, arr, 16, 16, 1 << 40,
+                                           None, None),
+                 lambda: L.tsp_mlp_shard(ctypes.byref(d), 16, 16, arr, 16, 16, 1 << 40, None, None),
+                 lambda: L.tsp_kv_shard(ctypes.byref(d), 16, 16, arr, 16, 16, 1 << 40, None)):
+        assert tsp.STATUS[call()] == "TSP_E_SHAPE"
