@@ -50,6 +50,9 @@ def parse():
                     help="time the MLP half's backward (tsp_mlp_shard_backward) instead of the layer")
     ap.add_argument("--attn-backward", action="store_true",
                     help="time the attention core's backward for one head group instead")
+    ap.add_argument("--kv-stream", action="store_true",
+                    help="headline with the other ranks' K/V copied through the side-stream slots "
+                         "(TSP_F_KV_STREAM) instead of read in place; both are reported either way")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB three times (a kernel of known "
                          "traffic for scaling HBM counters)")
@@ -96,9 +99,11 @@ def traffic_for(kernel):
 
 
 class ClockSampler:
-    """Samples the GPU's current graphics clock (MHz, through amdsmi, as
-    torch.cuda.clock_rate reports it) on a host thread while the timed steps
-    run; None where the query is unavailable."""
+    """Samples the graphics clock amdsmi reports (MHz, through
+    torch.cuda.clock_rate) on a host thread while the timed steps run; None
+    where the query is unavailable.  On this chip it reads the configured
+    clock, not the one the power limit lets the kernels run at: the effective
+    clock comes from the library's clock probe (effective_clock_mhz)."""
 
     def __init__(self):
         import threading
@@ -141,7 +146,13 @@ def cpu_model():
 
 
 def cpu_baseline(cfg, r, rows):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    layer_rows for `rows` local rows of the rank's second chunk (with the
+    rotary embedding and K/V heads of the workload).  The K/V projection of
+    every position those rows attend to is part of that call; it is timed
+    again on its own (the oracle's own steps: RMSNorm, n1 W_K rotated, n1 W_V,
+    once per query head as multihead_causal forms them) so that the rank's
+    own share can be reported without it."""
     import numpy as np
     import oracle.tsp_oracle as O
     import synth
@@ -158,18 +169,40 @@ def cpu_baseline(cfg, r, rows):
     reps = 3  # about 10 s of oracle work on the host cores
     t0 = time.perf_counter()
     for _ in range(reps):
-        O.layer_rows(x, w, cfg.n_heads, cfg.eps, pos)
+        O.layer_rows(x, w, cfg.n_heads, cfg.eps, pos, cfg.rope_theta)
     dt = (time.perf_counter() - t0) / reps
-    h, F = cfg.hidden, cfg.ffn
-    executed = (2 * rows * h * h + 2 * 2 * pmax * h * h + 4 * h * int(np.sum(pos + 1))
-                + 2 * rows * h * h + 6 * rows * h * F)
-    return {"value": executed / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    H, d, h, F = cfg.n_heads, cfg.head_dim, cfg.hidden, cfg.ffn
+    grp = H // cfg.kv_heads
+    allpos = np.arange(pmax)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        n1 = O.rmsnorm(np.asarray(x[:pmax], np.float64), w.g1, cfg.eps)
+        for t in range(H):
+            kc = slice((t // grp) * d, (t // grp + 1) * d)
+            O.rope(n1 @ np.asarray(w.wk[:, kc], np.float64), allpos, cfg.rope_theta)
+            n1 @ np.asarray(w.wv[:, kc], np.float64)
+    dkv = (time.perf_counter() - t0) / reps
+    pairs = int(np.sum(pos + 1))
+    # algorithmic FLOPs of the sample, counted as the GPU's are: Q and O of the
+    # rows, K and V (Hkv heads) of every position they attend to, causal pairs,
+    # the MLP of the rows
+    kv_alg = 2 * 2 * pmax * h * cfg.kv_heads * d
+    share_alg = 2 * rows * h * h + 4 * h * pairs + 2 * rows * h * h + 6 * rows * h * F
+    # what the oracle executes: it forms K and V once per query head
+    kv_exec = 2 * 2 * pmax * h * H * d
+    share_s = max(dt - dkv, 1e-9)
+    return {"value": round((kv_alg + share_alg) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt * reps, 3), "cpu": cpu_model(),
-            "sample": (f"{cfg.name}, rank {r}: fp64 numpy oracle layer_rows for the first {rows} "
-                       f"local rows of the second zigzag chunk (positions {int(pos[0])}.."
-                       f"{int(pos[-1])}), including the K/V projection of all {pmax} positions "
-                       f"they attend to, run {reps} times; value = FLOPs the oracle executed / "
-                       f"mean wall time")}
+            "kv_projection_s": round(dkv, 4), "rank_share_s": round(share_s, 4),
+            "rank_share_tflops": round(share_alg / share_s / 1e12, 6),
+            "executed_tflops": round((kv_exec + share_alg) / dt / 1e12, 6),
+            "sample": (f"{cfg.name}, rank {r}: fp64 numpy oracle layer_rows (rotary theta "
+                       f"{cfg.rope_theta}, {cfg.kv_heads} K/V heads) for the first {rows} local rows "
+                       f"of the second zigzag chunk (positions {int(pos[0])}..{int(pos[-1])}), "
+                       f"including the K/V projection of all {pmax} positions they attend to, run "
+                       f"{reps} times; value = the sample's algorithmic FLOPs (counted as the GPU's) / "
+                       f"mean wall time; kv_projection_s = that projection alone, timed separately "
+                       f"with the oracle's steps; rank_share_s = the rest")}
 
 
 def mlp_backward_bench(args):
@@ -328,27 +361,71 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
+    runs = {"in_place": run, "kv_stream": RankRun(cfg, r, flags=tsp.TSP_F_KV_STREAM)}
+    head = "kv_stream" if args.kv_stream else "in_place"
+    warm = []
     for _ in range(args.warmup):
-        run.layer(x, L, kv, out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with ClockSampler() as clk:
-        e0.record()
-        for _ in range(args.steps):
-            run.layer(x, L, kv, out)
-        e1.record()
+        t0 = time.perf_counter()
+        runs[head].layer(x, L, kv, out)
         torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+        warm.append((time.perf_counter() - t0) * 1e3)
+    est_ms = min(warm) if warm else 10.0  # a step's wall time, for sizing the clock probe
+
+    def timed(rr, probe=False):
+        """K steps bracketed by synchronisation, an event between steps; with
+        probe, the clock probe runs on a second stream over ~90% of them."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        samples, khz = None, 0
+        torch.cuda.synchronize()
+        if probe:
+            interval_us = 200
+            n = int(min(4e6 / interval_us, max(8, est_ms * 1e3 * args.steps * 0.9 / interval_us)))
+            samples = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+            ps = torch.cuda.Stream()
+            khz = tsp.tsp_clock_probe(samples, n, interval_us, stream=ps)
+        ev[0].record()
+        for i in range(args.steps):
+            rr.layer(x, L, kv, out)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+        return ev[0].elapsed_time(ev[-1]) / args.steps, per, (samples, khz)
+
+    with ClockSampler() as clk:
+        ms, step_times, (samples, khz) = timed(runs[head], probe=True)
     assert torch.isfinite(out).all(), "non-finite output"
+    # intervals inside the timed window: the probe starts with the first step
+    # and may run on after the last one
+    smp = samples.cpu().numpy().reshape(-1, 2)
+    smp = smp[smp[:, 0] - smp[0, 0] <= ms * args.steps * khz]
+    mhz = tsp.clock_mhz(smp, khz)
+    eff_clock = None if mhz.size == 0 else {
+        "median_mhz": round(float(np.median(mhz)), 1), "min_mhz": round(float(mhz.min()), 1),
+        "max_mhz": round(float(mhz.max()), 1), "intervals": int(mhz.size), "interval_us": 200,
+        "source": "tsp_clock_probe: shader-clock cycles per wall-clock tick, one wave beside the steps"}
+    other = "kv_stream" if head == "in_place" else "in_place"
+    for _ in range(args.warmup):
+        runs[other].layer(x, L, kv, out)
+    ms_other, per_other, _ = timed(runs[other])
 
     T = cfg.batch * cfg.local_tokens
     f_alg = sum(flops_per_step(cfg, r).values())
     tflops = f_alg / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
 
+    def step_stats(per):
+        v = sorted(per)
+        return {"median": round(v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2]), 4),
+                "min": round(v[0], 4), "max": round(v[-1], 4)}
+
+    variant = {"path": other, "ms_per_step": round(ms_other, 4),
+               "value": round(f_alg / (ms_other * 1e-3) / 1e12, 2),
+               "frac_of_peak": round(f_alg / (ms_other * 1e-3) / 1e12 / peak, 4),
+               "tokens_per_s": round(T / (ms_other * 1e-3), 1), "step_ms": step_stats(per_other)}
+
     kernels, roofline = {}, None
     if not args.no_profile:
-        prun = RankRun(cfg, r, flags=tsp.TSP_F_PROFILE)
+        prun = RankRun(cfg, r, flags=tsp.TSP_F_PROFILE | (tsp.TSP_F_KV_STREAM if head == "kv_stream" else 0))
         prun.layer(x, L, kv, out)
         torch.cuda.synchronize()
         tsp.tsp_profile_read(reset=True)
@@ -394,11 +471,15 @@ def main():
                    "parallelism": "tsp-rank-share"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "frac_of_peak": round(tflops / peak, 4),
+        "step_ms": step_stats(step_times),
+        "kv_path": head,
+        "kv_variant": variant,
         "flops_per_step": f_alg,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "gpu_clock": clk.summary(),
+        "effective_clock_mhz": eff_clock,
+        "gpu_clock_configured": clk.summary(),
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(line), flush=True)

@@ -338,8 +338,9 @@ int debug_before_fill(Ctx& c, void* slot, size_t bytes) {
 // The attention kernels read the other ranks' rows straight from the
 // gathered K/V when every zigzag chunk boundary falls on a 64-key tile
 // boundary (a tile then comes wholly from the rank's own rows or wholly from
-// the others'); otherwise those rows are first copied next to the rank's own.
-bool kv_in_place(const Dims& d) { return d.C % 64 == 0; }
+// the others'); otherwise, or when TSP_F_KV_STREAM asks for it, those rows
+// are first copied next to the rank's own on the side stream.
+bool kv_in_place(const Dims& d) { return d.C % 64 == 0 && !(d.flags & TSP_F_KV_STREAM); }
 
 // Rows of the gathered K/V that rank r needs from the others: its causal
 // window is [0, (2D-r)C), minus its own chunks r and 2D-1-r.
@@ -940,6 +941,23 @@ int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1, const void
                         (char*)kv + (size_t)j * kvbytes));
     if (rc) return rc;
   }
+  return TSP_OK;
+}
+
+int tsp_clock_probe(uint64_t* samples, int32_t n, int32_t interval_us, int32_t* wall_khz, void* stream) {
+  g_err.clear();
+  if (!samples || !wall_khz || n <= 0 || interval_us <= 0)
+    return fail(TSP_E_INVAL, "clock probe needs a buffer, a wall-clock rate pointer, n > 0 and interval > 0");
+  if (((uintptr_t)samples & 7) != 0) return fail(TSP_E_ALIGN, "samples must be 8-byte aligned");
+  if ((int64_t)n * interval_us > 4000000)
+    return fail(TSP_E_INVAL, "n * interval_us exceeds the probe's 4 s limit");
+  int dev = 0, khz = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  HIP_TRY(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+  if (khz <= 0) return fail(TSP_E_HIP, "device reports no wall-clock rate");
+  *wall_khz = khz;
+  const uint64_t ticks = (uint64_t)khz * (uint64_t)interval_us / 1000u;
+  HIP_TRY(launch_clock_probe(samples, n, ticks ? ticks : 1, (hipStream_t)stream));
   return TSP_OK;
 }
 

@@ -90,6 +90,9 @@ hipError_t launch_attention(Dtype dt, int head_dim, const AttnArgs& a, const Att
                             int part, hipStream_t s);
 hipError_t launch_fill32(void* p, uint32_t pattern, size_t bytes, hipStream_t s);
 hipError_t launch_spin(uint64_t ticks, hipStream_t s);
+// n (wall-clock tick, shader-clock cycle) pairs into out[2n], one every
+// `interval` wall-clock ticks (n * interval is bounded by the caller).
+hipError_t launch_clock_probe(uint64_t* out, int n, uint64_t interval, hipStream_t s);
 // Backward of the MLP half.
 hipError_t launch_transpose(Dtype dt, const void* in, void* out, int64_t R, int64_t C, int64_t ldi,
                             int64_t ldo, hipStream_t s);

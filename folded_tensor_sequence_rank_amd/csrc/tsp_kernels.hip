@@ -2245,6 +2245,28 @@ __global__ void spin_kernel(uint64_t ticks) {
   }
 }
 
+// Clock probe: one lane records n pairs (wall-clock ticks, shader-clock
+// cycles), one every `interval` wall-clock ticks.  The shader clock
+// (s_memtime) runs at the graphics clock the chip actually sustains; the wall
+// clock (s_memrealtime) at a fixed rate, so the ratio of their increments is
+// the effective clock while other kernels run beside the probe.  Every wait
+// ends: the wall clock only moves forward, and the launcher bounds n*interval.
+__global__ void clock_probe_kernel(uint64_t* __restrict__ out, int n, uint64_t interval) {
+  if (threadIdx.x != 0) return;
+  uint64_t next = wall_clock64();
+  for (int i = 0; i < n; i++) {
+    uint64_t rt = wall_clock64();
+    while (rt < next) {
+      __builtin_amdgcn_s_sleep(2);
+      rt = wall_clock64();
+    }
+    const uint64_t ck = clock64();
+    out[2 * i] = rt;
+    out[2 * i + 1] = ck;
+    next = rt + interval;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
@@ -2508,6 +2530,11 @@ hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const floa
 
 hipError_t launch_spin(uint64_t ticks, hipStream_t s) {
   spin_kernel<<<1, 64, 0, s>>>(ticks);
+  return hipGetLastError();
+}
+
+hipError_t launch_clock_probe(uint64_t* out, int n, uint64_t interval, hipStream_t s) {
+  clock_probe_kernel<<<1, 64, 0, s>>>(out, n, interval);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ TSP_BF16, TSP_F32 = 0, 1
 TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV, TSP_WS_MLP_BWD, TSP_WS_ATTN_BWD = 1, 2, 3, 4, 5, 6
 TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP, TSP_F_PROFILE = 1, 2, 4, 8
 TSP_F_RESCALE_TEST = 16
+TSP_F_KV_STREAM = 32
 KERNELS = ["rmsnorm", "qkv", "attn", "merge", "oproj", "w13", "w2"]  # TSP_K_* order
 STATUS = {0: "TSP_OK", -1: "TSP_E_INVAL", -2: "TSP_E_SHAPE", -3: "TSP_E_ALIGN",
           -4: "TSP_E_WORKSPACE", -5: "TSP_E_DTYPE", -6: "TSP_E_HIP"}
@@ -76,11 +77,13 @@ def lib() -> ctypes.CDLL:
         L.tsp_kv_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp]
         L.tsp_mlp_shard_backward.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _pp, _vp, _sz, _vp]
         L.tsp_attn_core_backward.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.tsp_clock_probe.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int32), _vp]
         L.tsp_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         for f in ("tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
                   "tsp_mlp_shard_backward", "tsp_attn_core_backward",
-                  "tsp_zigzag_positions", "tsp_profile_read"):
+                  "tsp_zigzag_positions", "tsp_profile_read", "tsp_clock_probe"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -250,6 +253,27 @@ def tsp_profile_read(reset: bool = True) -> dict:
     n = (ctypes.c_int64 * len(KERNELS))()
     _check(lib().tsp_profile_read(ms, n, 1 if reset else 0))
     return {k: (ms[i], n[i]) for i, k in enumerate(KERNELS)}
+
+
+def tsp_clock_probe(samples, n: int, interval_us: int, stream=None) -> int:
+    """Enqueue the clock probe (include/tsp.h) writing n (wall tick, shader
+    cycle) pairs into `samples` (an int64 device tensor of >= 2n elements);
+    returns the wall clock's rate in kHz."""
+    if hasattr(samples, "numel") and _nbytes(samples) < 16 * n:
+        raise ValueError(f"samples: {_nbytes(samples)} bytes, {n} samples need {16 * n}")
+    khz = ctypes.c_int32(0)
+    _check(lib().tsp_clock_probe(_ptr(samples), n, interval_us, ctypes.byref(khz), _stream(stream)))
+    return int(khz.value)
+
+
+def clock_mhz(samples: np.ndarray, wall_khz: int) -> np.ndarray:
+    """Effective clock (MHz) over each interval between consecutive probe
+    samples: shader cycles / wall ticks * wall-clock rate."""
+    s = np.asarray(samples, np.int64).reshape(-1, 2).astype(np.float64)
+    dt = np.diff(s[:, 0])
+    dc = np.diff(s[:, 1])
+    ok = dt > 0
+    return dc[ok] / dt[ok] * (wall_khz / 1000.0)
 
 
 # ----------------------------------------------------------------------------

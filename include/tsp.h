@@ -148,8 +148,8 @@ enum {
   TSP_WS_ATTN_BWD = 6
 };
 
-/* Debug flags (tsp_dims.flags).  Results must be identical with or without
- * the first four; they exist to expose missing stream hand-offs in tests.
+/* Flags (tsp_dims.flags).  Results must be identical with or without the
+ * first four; they exist to expose missing stream hand-offs in tests.
  * TSP_F_RESCALE_TEST changes only the rounding: the bf16 attention with
  * 128-dim heads keeps a lazy softmax reference max and raises it when a
  * 32-key block's exponentials sum past 2^64; with this flag the bound is 2,
@@ -159,7 +159,14 @@ enum {
   TSP_F_POISON_SLOTS = 2u, /* each slot is filled with NaN before it is refilled */
   TSP_F_NO_OVERLAP = 4u,   /* run the copies in order on the compute stream */
   TSP_F_PROFILE = 8u,      /* time each kernel launch with HIP events (tsp_profile_read) */
-  TSP_F_RESCALE_TEST = 16u /* softmax rescale bound 2 instead of 2^64 (see above) */
+  TSP_F_RESCALE_TEST = 16u, /* softmax rescale bound 2 instead of 2^64 (see above) */
+  /* Route the K/V all-gather's payload through the shard stream at every
+   * shape: the other ranks' rows of each head group are copied into a K/V slot
+   * on the side stream, overlapped with the previous group's compute, as they
+   * are when C % 64 != 0 (section 2, attention layers: the all-gather; section
+   * 3: transfers pipelined behind the GEMMs).  Without it they are read in
+   * place when C % 64 == 0.  Same results, bit for bit. */
+  TSP_F_KV_STREAM = 32u
 };
 
 /* Kernel classes reported by tsp_profile_read. */
@@ -211,7 +218,8 @@ int tsp_zigzag_positions(int64_t seq, int32_t fold, int32_t rank, int64_t* out);
  * Q_j/K_j/V_j, zigzag-aware causal flash attention runs over the gathered
  * K/V (the rank's own rows from the projection, the other ranks' rows its
  * causal window needs, positions < (2D-r)*C, from `kv`: read in place when
- * C % 64 == 0, else first copied next to its own), and the partial
+ * C % 64 == 0, else -- or always with TSP_F_KV_STREAM -- first copied next to
+ * its own on the side stream), and the partial
  * O-projection of head group j is accumulated locally in fp32.
  *   x      [B*T][h] local rows in zigzag order, sequence-major
  *   g1     [h]      RMSNorm gain
@@ -325,6 +333,20 @@ int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, 
  * few microseconds per launch, so calls timed this way are slightly slower.
  */
 int tsp_profile_read(double* ms, int64_t* n, int reset);
+
+/*
+ * Effective graphics clock, for measurement: enqueues on `stream` a one-wave
+ * kernel that writes n pairs (wall-clock tick, shader-clock cycle) into the
+ * device buffer samples[2n], one every interval_us microseconds, and writes
+ * the wall clock's rate (kHz) to *wall_khz.  The shader clock counts at the
+ * clock the chip sustains (under its power limit it runs below the
+ * configured one); so, launched on a second stream beside other work, the
+ * probe reads the clock that work ran at: f = delta(cycles) / delta(ticks) *
+ * wall_khz.  The probe occupies one wave slot of one CU and sleeps between
+ * samples.  TSP_E_INVAL if n <= 0, interval_us <= 0 or n * interval_us
+ * exceeds 4 s; TSP_E_ALIGN if samples is not 8-byte aligned.
+ */
+int tsp_clock_probe(uint64_t* samples, int32_t n, int32_t interval_us, int32_t* wall_khz, void* stream);
 
 #ifdef __cplusplus
 }

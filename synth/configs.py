@@ -64,6 +64,12 @@ CONFIGS = {
     "7b_s64k": LayerConfig("7b_s64k", 4096, 32, 128, 11008, 65536, 8, (3,)),
     # Attention-dominated 128K context; the first and last rank both run.
     "7b_s128k": LayerConfig("7b_s128k", 4096, 32, 128, 11008, 131072, 8, (0, 7)),
+    # The 64K shape with low-residual activations x ~ N(0, 0.02^2): RMSNorm
+    # rescales them, so Q/K/V and the attention output are as at x ~ N(0, 1),
+    # but the attention delta now dominates x1 and its bf16 storage rounding
+    # no longer hides a local error in it (a parity workload).
+    "7b_s64k_lowres": LayerConfig("7b_s64k_lowres", 4096, 32, 128, 11008, 65536, 8, (3,),
+                                  x_std=0.02),
     # The 16K shape with a micro-batch of 4 sequences (8192 local rows).
     "7b_s16k_b4": LayerConfig("7b_s16k_b4", 4096, 32, 128, 11008, 16384, 8, (3,), batch=4),
     # The 64K shape with the rotary embedding (base 10^4) that 7B dense models

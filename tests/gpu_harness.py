@@ -104,13 +104,4 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def rel_fro(a, ref) -> float:
-    a = np.asarray(a, np.float64)
-    ref = np.asarray(ref, np.float64)
-    n = np.linalg.norm(ref)
-    return float(np.linalg.norm(a - ref) / (n if n > 0 else 1.0))
-
-
-def tol(cfg) -> float:
-    """Relative Frobenius bound: 1e-2 for bf16 storage, 1e-4 for fp32."""
-    return 1e-2 if cfg.dtype == "bf16" else 1e-4
+from parity import rel_fro, tol  # noqa: E402,F401  (the parity bar lives in tests/parity.py)

@@ -232,3 +232,21 @@ def test_shapes_past_32bit_offsets_are_refused(cfg, ok, what):
                  lambda: L.tsp_mlp_shard(ctypes.byref(d), 16, 16, arr, 16, 16, 1 << 40, None, None),
                  lambda: L.tsp_kv_shard(ctypes.byref(d), 16, 16, arr, 16, 16, 1 << 40, None)):
         assert tsp.STATUS[call()] == "TSP_E_SHAPE"
+
+
+def test_clock_probe_argument_checks_on_the_host():
+    L = tsp.lib()
+    khz = ctypes.c_int32(0)
+    assert tsp.STATUS[L.tsp_clock_probe(None, 8, 100, ctypes.byref(khz), None)] == "TSP_E_INVAL"
+    assert tsp.STATUS[L.tsp_clock_probe(4096, 0, 100, ctypes.byref(khz), None)] == "TSP_E_INVAL"
+    assert tsp.STATUS[L.tsp_clock_probe(4096, 100000, 100, ctypes.byref(khz), None)] == "TSP_E_INVAL"
+    assert tsp.STATUS[L.tsp_clock_probe(4100, 8, 100, ctypes.byref(khz), None)] == "TSP_E_ALIGN"
+
+
+def test_clock_from_probe_samples():
+    """Shader cycles per wall tick times the wall rate: 100 MHz ticks and
+    2.0e9 cycles per second read as 2000 MHz."""
+    t = np.arange(0, 10) * 20000                  # 200 us apart at 100 MHz
+    c = 5_000_000 + np.arange(0, 10) * 400_000    # 2 GHz
+    mhz = tsp.clock_mhz(np.stack([t, c], axis=1).reshape(-1), 100_000)
+    assert np.allclose(mhz, 2000.0)
