@@ -50,6 +50,8 @@ def parse():
                     help="time the MLP half's backward (tsp_mlp_shard_backward) instead of the layer")
     ap.add_argument("--attn-backward", action="store_true",
                     help="time the attention core's backward for one head group instead")
+    ap.add_argument("--layer-backward", action="store_true",
+                    help="time the whole layer's backward of one rank (both parts) instead")
     ap.add_argument("--kv-stream", action="store_true",
                     help="headline with the other ranks' K/V copied through the side-stream slots "
                          "(TSP_F_KV_STREAM) instead of read in place; both are reported either way")
@@ -308,6 +310,94 @@ def attn_backward_bench(args):
         "flops_per_step": f_alg, "recompute_flops_per_step": 10 * d * pairs * Hd * Bn}), flush=True)
 
 
+def layer_backward_bench(args):
+    """The whole layer's backward for one rank at the workload's shape: part 1
+    (MLP half, then per head group the forward attention recomputed, dA and
+    dW_O, the attention core's gradients) and part 2 (dn1 through W_Q/K/V,
+    the partial dW_QKV, RMSNorm-1), timed together; the dK/dV exchange
+    between them (a collective on D GPUs) is not.  Its input, the summed
+    dK/dV of the rank's rows, is synthetic here.  Algorithmic FLOPs: twice
+    the forward's projections and MLP (data and weight gradients,
+    2 * (8 T h^2 + 6 T h F) at one K/V head per query head) and 8 d per
+    (query, visible key) pair and head (dP, dV, dQ, dK).  The recomputation
+    (forward attention, S and dP in the dQ kernel, the MLP's and QKV's
+    projections, the norms) is reported apart."""
+    import numpy as np
+    import torch
+
+    import synth
+    from folded_tensor_sequence_rank_amd import tsp
+    from gpu_harness import RankRun, fill_kv, layer_dev, new_kv, to_dev
+
+    cfg = synth.get_config(args.workload)
+    r = cfg.ranks[0] if args.rank is None else args.rank
+    torch.cuda.set_device(0)
+    D, h, d, H = cfg.fold, cfg.hidden, cfg.head_dim, cfg.n_heads
+    B, T = cfg.batch, cfg.local_tokens
+    BT, BS = B * T, B * cfg.seq
+    Hkv = cfg.kv_heads
+    hs, Fs, ks = h // D, cfg.ffn // D, Hkv * d // D
+    L = layer_dev(cfg, synth.gen_weights(cfg))
+    xs = [to_dev(np.concatenate([synth.gen_rows(cfg, tsp.zigzag_positions(cfg.seq, D, q), seq_index=b)
+                                 for b in range(B)]), cfg) for q in range(D)]
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    x = xs[r]
+    xs = None
+    x1 = RankRun(cfg, r).attn(x, L, kv)
+    dout = to_dev(np.concatenate([synth.gen_rows(cfg, tsp.zigzag_positions(cfg.seq, D, r), layer=7, seq_index=b)
+                                  for b in range(B)]), cfg)
+    dims = tsp.make_dims(cfg, r)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    ws1 = torch.empty(tsp.workspace_bytes(dims, tsp.TSP_WS_LAYER_BWD), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(tsp.workspace_bytes(dims, tsp.TSP_WS_LAYER_BWD_FINISH), dtype=torch.uint8, device="cuda")
+    dx1, dx = torch.empty_like(x), torch.empty_like(x)
+    dg1, dg2 = torch.empty(h, **f32), torch.empty(h, **f32)
+    dw_mlp = [torch.empty(3 * Fs * h, **f32) for _ in range(D)]
+    dw_o = [torch.empty(h * hs, **f32) for _ in range(D)]
+    dw_qkv = [torch.empty((hs + 2 * ks) * h, **f32) for _ in range(D)]
+    dq = torch.empty(H * BT * d, **f32)
+    dkv = torch.empty(2 * Hkv * BS * d, **f32)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4321)
+    dkv_own = torch.randn(2 * Hkv * BT * d, generator=g, **f32) * 1e-2
+
+    def step():
+        tsp.tsp_layer_shard_backward(dims, x, x1, L.g1, L.w_attn, kv, L.g2, L.w_mlp, dout, dx1, dg2, dw_mlp, dw_o,
+                                     dq, dkv, ws1)
+        tsp.tsp_layer_shard_backward_finish(dims, x, L.g1, L.w_attn, dx1, dq, dkv_own, dx, dg1, dw_qkv, ws2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    pairs = B * int((tsp.zigzag_positions(cfg.seq, D, r) + 1).sum())
+    proj = 2 * BT * h * (h + 2 * Hkv * d) + 2 * BT * h * h + 6 * BT * h * cfg.ffn
+    f_alg = 2 * proj + 8 * d * pairs * H
+    recompute = (4 * d * pairs * H          # forward attention for O and the log-sum-exp
+                 + 4 * d * pairs * H        # S and dP again in the dQ kernel
+                 + 4 * BT * h * cfg.ffn     # n2 W1 and n2 W3
+                 + 2 * BT * h * (h + 2 * Hkv * d))  # Q and the rank's own K/V rows
+    tflops = f_alg / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "TFLOP/s of one rank's whole-layer backward (7B shape)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "step_ms": {"median": round(per[len(per) // 2], 4), "min": round(per[0], 4), "max": round(per[-1], 4)},
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "rank": r, "batch": B, "local_tokens": BT},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": f_alg, "recompute_flops_per_step": recompute,
+        "executed_tflops": round((f_alg + recompute) / (ms * 1e-3) / 1e12, 2)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -320,6 +410,9 @@ def main():
         return
     if args.attn_backward:
         attn_backward_bench(args)
+        return
+    if args.layer_backward:
+        layer_backward_bench(args)
         return
 
     import numpy as np
@@ -392,17 +485,22 @@ def main():
         return ev[0].elapsed_time(ev[-1]) / args.steps, per, (samples, khz)
 
     with ClockSampler() as clk:
-        ms, step_times, (samples, khz) = timed(runs[head], probe=True)
+        ms, step_times, _ = timed(runs[head])
     assert torch.isfinite(out).all(), "non-finite output"
-    # intervals inside the timed window: the probe starts with the first step
-    # and may run on after the last one
+    # The effective clock, from a second pass of the same steps with the clock
+    # probe beside them.  Not during the timed steps: the probe's wave holds a
+    # slot on one CU, which keeps a full-register workgroup off that CU (a
+    # GEMM launch of exactly two rounds of 256 tiles then needs a third).
+    ms_probe, _, (samples, khz) = timed(runs[head], probe=True)
     smp = samples.cpu().numpy().reshape(-1, 2)
-    smp = smp[smp[:, 0] - smp[0, 0] <= ms * args.steps * khz]
+    smp = smp[smp[:, 0] - smp[0, 0] <= ms_probe * args.steps * khz]  # inside the steps
     mhz = tsp.clock_mhz(smp, khz)
     eff_clock = None if mhz.size == 0 else {
         "median_mhz": round(float(np.median(mhz)), 1), "min_mhz": round(float(mhz.min()), 1),
         "max_mhz": round(float(mhz.max()), 1), "intervals": int(mhz.size), "interval_us": 200,
-        "source": "tsp_clock_probe: shader-clock cycles per wall-clock tick, one wave beside the steps"}
+        "probe_pass_ms_per_step": round(ms_probe, 4),
+        "source": "tsp_clock_probe: shader-clock cycles per wall-clock tick, one wave beside a second pass "
+                  "of the steps (not the timed one)"}
     other = "kv_stream" if head == "in_place" else "in_place"
     for _ in range(args.warmup):
         runs[other].layer(x, L, kv, out)

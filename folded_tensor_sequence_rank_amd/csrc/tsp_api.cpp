@@ -344,10 +344,14 @@ bool kv_in_place(const Dims& d) { return d.C % 64 == 0 && !(d.flags & TSP_F_KV_S
 
 // Rows of the gathered K/V that rank r needs from the others: its causal
 // window is [0, (2D-r)C), minus its own chunks r and 2D-1-r.
-int copy_remote_kv(Ctx& c, const char* kv_block, char* slot) {
+// With all_rows, every other rank's rows (positions past the causal window
+// as well), so that the slot holds no stale row at all.
+int copy_remote_kv(Ctx& c, const char* kv_block, char* slot, bool all_rows = false) {
   const Dims& d = *c.d;
   const size_t es = d.es;
-  const int64_t ranges[2][2] = {{0, d.r * d.C}, {(d.r + 1) * d.C, (2 * d.D - 1 - d.r) * d.C}};
+  const int64_t ranges[3][2] = {{0, d.r * d.C},
+                                {(d.r + 1) * d.C, (2 * d.D - 1 - d.r) * d.C},
+                                {(2 * d.D - d.r) * d.C, all_rows ? d.S : 0}};
   const char* srcK = kv_block;
   const char* srcV = kv_block + kv_v_offset(d) * es;
   char* dstK = slot;
@@ -617,9 +621,9 @@ int64_t bt_pitch(const Dims& d) { return (d.BT + 7) / 8 * 8; }
 struct AttnBwdWs {
   size_t o, lse, dl, qt, dot, kt, vr, op, ml, end;
 };
-AttnBwdWs attn_bwd_ws(const Dims& d) {
+AttnBwdWs attn_bwd_ws(const Dims& d, size_t base = 0) {
   AttnBwdWs w;
-  size_t o = 0;
+  size_t o = base;
   w.o = o; o += al((size_t)d.BT * d.hs * d.es);
   w.lse = o; o += al((size_t)d.Hd * d.BT * 4);
   w.dl = o; o += al((size_t)d.Hd * d.BT * 4);
@@ -635,9 +639,9 @@ AttnBwdWs attn_bwd_ws(const Dims& d) {
   return w;
 }
 
-MlpBwdWs mlp_bwd_ws(const Dims& d) {
+MlpBwdWs mlp_bwd_ws(const Dims& d, size_t base = 0) {
   MlpBwdWs w;
-  size_t o = 0;
+  size_t o = base;
   const size_t T = d.BT, h = d.h, F = d.Fs, es = d.es;
   w.n2 = o; o += al(T * h * es);
   w.n2t = o; o += al(T * h * es);
@@ -711,6 +715,151 @@ int mlp_bwd_body(Ctx& c, const MlpBwdWs& L, const void* x1, const void* g2, cons
   return TSP_OK;
 }
 
+// ---- whole-layer backward workspaces ---------------------------------------
+// Part 1 (MLP half, then per head group the attention core and W_O): n1, dx1
+// transposed, the group's rotated Q and complete K/V slot, its output O
+// transposed, W_O's block transposed and dA; then the MLP backward's and the
+// attention-core backward's regions, which are used one after the other and
+// share their space.
+struct LayerBwdWs {
+  size_t n1, dx1t, q, slotkv, ot, wot, da, shared, end;
+  MlpBwdWs mlp;
+  AttnBwdWs attn;
+};
+LayerBwdWs layer_bwd_ws(const Dims& d) {
+  LayerBwdWs w;
+  size_t o = 0;
+  const size_t es = d.es;
+  w.n1 = o; o += al((size_t)d.BT * d.h * es);
+  w.dx1t = o; o += al((size_t)d.h * d.BT * es);
+  w.q = o; o += al((size_t)d.Hd * d.BT * d.d * es);
+  w.slotkv = o; o += al(kv_block_elems(d) * es);
+  w.ot = o; o += al((size_t)d.hs * d.BT * es);
+  w.wot = o; o += al((size_t)d.hs * d.h * es);
+  w.da = o; o += al((size_t)d.BT * d.hs * es);
+  w.shared = o;
+  w.mlp = mlp_bwd_ws(d, o);
+  w.attn = attn_bwd_ws(d, o);
+  w.end = std::max(w.mlp.end, w.attn.end);
+  return w;
+}
+// Part 2 (after the reduce-scatter of dK/dV): n1 and its transpose, one
+// shard's [dQ | dK | dV] and its transpose, the shard's Q|K|V block
+// transposed, dn1 (fp32) and the per-row rstd.
+struct LayerBwd2Ws {
+  size_t n1, n1t, g, gt, wt, dn, rs, end;
+};
+LayerBwd2Ws layer_bwd2_ws(const Dims& d) {
+  LayerBwd2Ws w;
+  size_t o = 0;
+  const size_t es = d.es, N = qkv_rows(d);
+  w.n1 = o; o += al((size_t)d.BT * d.h * es);
+  w.n1t = o; o += al((size_t)d.h * d.BT * es);
+  w.g = o; o += al((size_t)d.BT * N * es);
+  w.gt = o; o += al(N * d.BT * es);
+  w.wt = o; o += al((size_t)d.h * N * es);
+  w.dn = o; o += al((size_t)d.BT * d.h * 4);
+  w.rs = o; o += al((size_t)d.BT * 4);
+  w.end = o;
+  return w;
+}
+
+// ---- attention-core backward pieces ----------------------------------------
+int check_attn_bwd_dims(const Dims& d) {
+  if (d.dt != BF16) return fail(TSP_E_DTYPE, "the attention backward runs in bf16 only");
+  if (d.d != 64 && d.d != 128) return fail(TSP_E_SHAPE, "the attention backward needs head_dim 64 or 128");
+  return TSP_OK;
+}
+
+AttnArgs attn_args(const Dims& d, const AttnPlan& plan) {
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.T = d.T;
+  a.S = d.S;
+  a.batch = (int)d.B;
+  a.chunk = d.C;
+  a.rank = (int)d.r;
+  a.fold = (int)d.D;
+  a.Hd = (int)d.Hd;
+  a.grp = (int)(d.H / d.Hkv);
+  a.nqt = plan.nqt;
+  a.lseg = plan.lseg;
+  a.maxseg = plan.maxseg;
+  a.nitems = plan.nitems;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
+  a.sum_cap = 18446744073709551616.0f;
+  return a;
+}
+
+// The group's attention output O [B*T][hs] and per-row log-sum-exp, from its
+// rotated queries q and every position's K / V^T in kv.
+int attn_recompute(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv) {
+  const Dims& d = *c.d;
+  const AttnPlan plan = plan_of(d);
+  AttnArgs a = attn_args(d, plan);
+  a.Q = q;
+  a.K = kv;
+  a.Vt = (const char*)kv + kv_v_offset(d) * d.es;
+  a.O = c.ws + L.o;
+  a.Op = (float*)(c.ws + L.op);
+  a.ML = (float*)(c.ws + L.ml);
+  a.LSE = (float*)(c.ws + L.lse);
+  a.ldo = (int)d.hs;
+  HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 0, c.s));
+  if (plan.split) HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 1, c.s));
+  return TSP_OK;
+}
+
+// dq [Hd][B*T][d] and this rank's partial dk, dv [Hkd][B*S][d] (fp32) of the
+// group, given its recomputed O and log-sum-exp (in L) and dout [B*T][ldo].
+int attn_core_grads(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv, const void* dout, int ldo,
+                    float* dq, float* dk, float* dv) {
+  const Dims& d = *c.d;
+  const hipStream_t s = c.s;
+  char* w = c.ws;
+  const void* vt = (const char*)kv + kv_v_offset(d) * d.es;
+  AttnBwdArgs b;
+  memset(&b, 0, sizeof b);
+  b.Q = q;
+  b.K = kv;
+  b.Vt = vt;
+  b.O = w + L.o;
+  b.dO = dout;
+  b.LSE = (const float*)(w + L.lse);
+  b.Dl = (float*)(w + L.dl);
+  b.dQ = dq;
+  b.dK = dk;
+  b.dV = dv;
+  b.T = d.T;
+  b.S = d.S;
+  b.chunk = d.C;
+  b.ldo = ldo;
+  b.rank = (int)d.r;
+  b.fold = (int)d.D;
+  b.batch = (int)d.B;
+  b.grp = (int)(d.H / d.Hkv);
+  b.Hd = (int)d.Hd;
+  b.Hkd = (int)d.Hkd;
+  b.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
+  b.scale = (float)(1.0 / std::sqrt((double)d.d));
+  b.BTp = bt_pitch(d);
+  b.Qt = w + L.qt;
+  b.dOt = w + L.dot;
+  b.Kt = w + L.kt;
+  b.Vr = w + L.vr;
+  const int64_t ldt = d.Hd * b.BTp;
+  for (int64_t t = 0; t < d.Hd; t++) {
+    HIP_TRY(launch_transpose(d.dt, (const char*)q + t * d.BT * d.d * d.es, w + L.qt + t * b.BTp * d.es, d.BT,
+                             d.d, d.d, ldt, s));
+    HIP_TRY(launch_transpose(d.dt, (const char*)dout + t * d.d * d.es, w + L.dot + t * b.BTp * d.es, d.BT, d.d,
+                             ldo, ldt, s));
+  }
+  HIP_TRY(launch_transpose(d.dt, kv, w + L.kt, d.Hkd * d.BS, d.d, d.d, d.Hkd * d.BS, s));
+  HIP_TRY(launch_transpose(d.dt, vt, w + L.vr, d.Hkd * d.d, d.BS, d.BS, d.Hkd * d.d, s));
+  for (int part = 0; part < 3; part++) HIP_TRY(launch_attn_bwd((int)d.d, b, part, s));
+  return TSP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -729,6 +878,8 @@ size_t tsp_workspace_bytes(const tsp_dims* dims, int which) {
     case TSP_WS_KV: return kv_ws_bytes(d);
     case TSP_WS_MLP_BWD: return mlp_bwd_ws(d).end;
     case TSP_WS_ATTN_BWD: return attn_bwd_ws(d).end;
+    case TSP_WS_LAYER_BWD: return layer_bwd_ws(d).end;
+    case TSP_WS_LAYER_BWD_FINISH: return layer_bwd2_ws(d).end;
     default: return 0;
   }
 }
@@ -836,6 +987,132 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1, const v
   return finish(c);
 }
 
+int tsp_layer_shard_backward(const tsp_dims* dims, const void* x, const void* x1, const void* g1,
+                             const void* const* w_attn, const void* kv, const void* g2, const void* const* w_mlp,
+                             const void* dout, void* dx1, float* dg2, float* const* dw_mlp, float* const* dw_o,
+                             float* dq, float* dkv, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if ((rc = check_attn_bwd_dims(d))) return rc;
+  if ((rc = check_ptrs({x, x1, g1, kv, g2, dout, dx1, dg2, dq, dkv, ws})) ||
+      (rc = check_shards(w_attn, d.D, "w_attn")) || (rc = check_shards(w_mlp, d.D, "w_mlp")) ||
+      (rc = check_shards((const void* const*)dw_mlp, d.D, "dw_mlp")) ||
+      (rc = check_shards((const void* const*)dw_o, d.D, "dw_o")))
+    return rc;
+  const LayerBwdWs L = layer_bwd_ws(d);
+  if (ws_bytes < L.end) return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.end);
+  Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr, false};
+  char* w = c.ws;
+  const size_t es = d.es;
+  // MLP half: dx1, the gain's and every MLP shard's partial gradient
+  if ((rc = mlp_bwd_body(c, L.mlp, x1, g2, w_mlp, dout, dx1, dg2, dw_mlp))) return rc;
+  HIP_TRY(launch_rmsnorm(d.dt, x, g1, w + L.n1, d.BT, (int)d.h, d.eps, c.s));
+  HIP_TRY(launch_transpose(d.dt, dx1, w + L.dx1t, d.BT, d.h, d.h, d.BT, c.s));
+  const size_t qkvbytes = qkv_rows(d) * d.h * es;
+  const size_t kvbytes = kv_block_elems(d) * es;
+  const double l2c = d.rope_theta > 0.f ? std::log2((double)d.rope_theta) / (double)d.d : 0.0;
+  for (int64_t j = 0; j < d.D; j++) {  // head group j, in broadcast order
+    const char* wj = (const char*)w_attn[j];
+    float* dqj = dq + (size_t)j * d.Hd * d.BT * d.d;
+    float* dkj = dkv + (size_t)j * kv_block_elems(d);
+    float* dvj = dkj + kv_v_offset(d);
+    // the group's rotated Q, and its K/V complete: own rows projected here,
+    // every other rank's rows copied from the gathered buffer
+    if ((rc = copy_remote_kv(c, (const char*)kv + (size_t)j * kvbytes, w + L.slotkv, true))) return rc;
+    if ((rc = qkv_gemm(c, w + L.n1, wj, 0, w + L.q, w + L.slotkv))) return rc;
+    if ((rc = attn_recompute(c, L.attn, w + L.q, w + L.slotkv))) return rc;
+    // dA = dx1 W_O^T, and this rank's partial dW_O = dx1^T A (packed layout)
+    HIP_TRY(launch_transpose(d.dt, wj + qkvbytes, w + L.wot, d.h, d.hs, d.hs, d.h, c.s));
+    GemmArgs g = gemm_base();
+    g.A = dx1;
+    g.lda = d.h;
+    g.B = w + L.wot;
+    g.ldb = d.h;
+    g.M = (int)d.BT;
+    g.N = (int)d.hs;
+    g.K = (int)d.h;
+    g.C = w + L.da;
+    g.ldc = d.hs;
+    HIP_TRY(launch_gemm(d.dt, EPI_STORE, g, c.s));
+    HIP_TRY(launch_transpose(d.dt, w + L.attn.o, w + L.ot, d.BT, d.hs, d.hs, d.BT, c.s));
+    if ((rc = plain_gemm(c, w + L.dx1t, d.BT, w + L.ot, d.BT, d.h, d.hs, d.BT, dw_o[j], d.hs, false))) return rc;
+    // the attention core: dQ of the rank's rows, partial dK / dV of every position
+    if ((rc = attn_core_grads(c, L.attn, w + L.q, w + L.slotkv, w + L.da, (int)d.hs, dqj, dkj, dvj))) return rc;
+    if (l2c > 0.0) {  // gradients of the rotated Q and K, taken back through the rotation
+      HIP_TRY(launch_rope_inverse(dqj, d.BT, (int)d.Hd, (int)d.d, 0, d.T, d.C, (int)d.r, (int)d.D, l2c, c.s));
+      HIP_TRY(launch_rope_inverse(dkj, d.BS, (int)d.Hkd, (int)d.d, d.S, d.T, d.C, (int)d.r, (int)d.D, l2c, c.s));
+    }
+  }
+  return TSP_OK;
+}
+
+int tsp_kv_grad_reduce(const tsp_dims* dims, const float* const* dkv_parts, float* dkv_own, void* stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if (d.D > kMaxFold) return fail(TSP_E_SHAPE, "fold %lld exceeds %d", (long long)d.D, kMaxFold);
+  if (d.d % 4) return fail(TSP_E_SHAPE, "head_dim must be a multiple of 4");
+  if ((rc = check_ptrs({dkv_own})) || (rc = check_shards((const void* const*)dkv_parts, d.D, "dkv_parts")))
+    return rc;
+  KvGradReduceArgs a;
+  memset(&a, 0, sizeof a);
+  for (int64_t q = 0; q < d.D; q++) a.part[q] = dkv_parts[q];
+  a.own = dkv_own;
+  a.S = d.S;
+  a.T = d.T;
+  a.chunk = d.C;
+  a.batch = d.B;
+  a.rank = (int)d.r;
+  a.fold = (int)d.D;
+  a.hkd = (int)d.Hkd;
+  a.hd = (int)d.d;
+  HIP_TRY(launch_kv_grad_reduce(a, (hipStream_t)stream));
+  return TSP_OK;
+}
+
+int tsp_layer_shard_backward_finish(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,
+                                    const void* dx1, const float* dq, const float* dkv_own, void* dx, float* dg1,
+                                    float* const* dw_qkv, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if ((rc = check_attn_bwd_dims(d))) return rc;
+  if ((rc = check_ptrs({x, g1, dx1, dq, dkv_own, dx, dg1, ws})) || (rc = check_shards(w_attn, d.D, "w_attn")) ||
+      (rc = check_shards((const void* const*)dw_qkv, d.D, "dw_qkv")))
+    return rc;
+  const LayerBwd2Ws L = layer_bwd2_ws(d);
+  if (ws_bytes < L.end) return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.end);
+  Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr, false};
+  char* w = c.ws;
+  const int64_t N = (int64_t)qkv_rows(d);
+  float* dn = (float*)(w + L.dn);
+  HIP_TRY(launch_rmsnorm(d.dt, x, g1, w + L.n1, d.BT, (int)d.h, d.eps, c.s));
+  HIP_TRY(launch_transpose(d.dt, w + L.n1, w + L.n1t, d.BT, d.h, d.h, d.BT, c.s));
+  const size_t own_block = 2 * (size_t)d.Hkd * d.BT * d.d;  // one shard's [dK | dV] of the rank's rows
+  for (int64_t j = 0; j < d.D; j++) {
+    const float* dkj = dkv_own + (size_t)j * own_block;
+    const float* dvj = dkj + (size_t)d.Hkd * d.BT * d.d;
+    HIP_TRY(launch_qkv_grad_pack(d.dt, dq + (size_t)j * d.Hd * d.BT * d.d, dkj, dvj, w + L.g, d.BT, (int)d.hs,
+                                 (int)d.ks, (int)d.d, c.s));
+    // dn1 (+)= [dQ | dK | dV] . [W_Q; W_K; W_V]^T (B operand: the shard's block transposed)
+    HIP_TRY(launch_transpose(d.dt, w_attn[j], w + L.wt, N, d.h, d.h, N, c.s));
+    if ((rc = plain_gemm(c, w + L.g, N, w + L.wt, N, d.BT, d.h, N, dn, d.h, j > 0))) return rc;
+    // this rank's partial gradient of the shard's Q|K|V block: [dQ | dK | dV]^T n1
+    HIP_TRY(launch_transpose(d.dt, w + L.g, w + L.gt, d.BT, N, N, d.BT, c.s));
+    if ((rc = plain_gemm(c, w + L.gt, d.BT, w + L.n1t, d.BT, N, d.h, d.BT, dw_qkv[j], d.h, false))) return rc;
+  }
+  HIP_TRY(launch_fill32(dg1, 0u, (size_t)d.h * 4, c.s));
+  HIP_TRY(launch_rmsnorm_bwd(d.dt, x, g1, dn, dx1, dx, (float*)(w + L.rs), dg1, d.BT, (int)d.h, d.eps, c.s));
+  return TSP_OK;
+}
+
 int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, const void* dout, float* dq,
                            float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
@@ -843,82 +1120,14 @@ int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, 
   int rc = check_dims(dims, &d);
   if (rc) return rc;
   if (d.S == 0) return TSP_OK;
-  if (d.dt != TSP_BF16) return fail(TSP_E_DTYPE, "the attention backward runs in bf16 only");
-  if (d.d != 64 && d.d != 128) return fail(TSP_E_SHAPE, "the attention backward needs head_dim 64 or 128");
+  if ((rc = check_attn_bwd_dims(d))) return rc;
   if ((rc = check_ptrs({q, kv, dout, dq, dk, dv, ws}))) return rc;
   const AttnBwdWs L = attn_bwd_ws(d);
   if (ws_bytes < L.end) return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.end);
-  const hipStream_t s = (hipStream_t)stream;
-  char* w = (char*)ws;
-  const void* vt = (const char*)kv + kv_v_offset(d) * d.es;
+  Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr, false};
   // forward recomputation: the group's output and each row's log-sum-exp
-  const AttnPlan plan = plan_of(d);
-  AttnArgs a;
-  memset(&a, 0, sizeof a);
-  a.Q = q;
-  a.K = kv;
-  a.Vt = vt;
-  a.O = w + L.o;
-  a.Op = (float*)(w + L.op);
-  a.ML = (float*)(w + L.ml);
-  a.LSE = (float*)(w + L.lse);
-  a.T = d.T;
-  a.S = d.S;
-  a.batch = (int)d.B;
-  a.chunk = d.C;
-  a.ldo = (int)d.hs;
-  a.rank = (int)d.r;
-  a.fold = (int)d.D;
-  a.Hd = (int)d.Hd;
-  a.grp = (int)(d.H / d.Hkv);
-  a.nqt = plan.nqt;
-  a.lseg = plan.lseg;
-  a.maxseg = plan.maxseg;
-  a.nitems = plan.nitems;
-  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
-  a.sum_cap = 18446744073709551616.0f;
-  HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 0, s));
-  if (plan.split) HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 1, s));
-  AttnBwdArgs b;
-  memset(&b, 0, sizeof b);
-  b.Q = q;
-  b.K = kv;
-  b.Vt = vt;
-  b.O = w + L.o;
-  b.dO = dout;
-  b.LSE = (const float*)(w + L.lse);
-  b.Dl = (float*)(w + L.dl);
-  b.dQ = dq;
-  b.dK = dk;
-  b.dV = dv;
-  b.T = d.T;
-  b.S = d.S;
-  b.chunk = d.C;
-  b.ldo = (int)d.hs;
-  b.rank = (int)d.r;
-  b.fold = (int)d.D;
-  b.batch = (int)d.B;
-  b.grp = (int)(d.H / d.Hkv);
-  b.Hd = (int)d.Hd;
-  b.Hkd = (int)d.Hkd;
-  b.scale_log2 = a.scale_log2;
-  b.scale = (float)(1.0 / std::sqrt((double)d.d));
-  b.BTp = bt_pitch(d);
-  b.Qt = w + L.qt;
-  b.dOt = w + L.dot;
-  b.Kt = w + L.kt;
-  b.Vr = w + L.vr;
-  const int64_t ldt = d.Hd * b.BTp;
-  for (int64_t t = 0; t < d.Hd; t++) {
-    HIP_TRY(launch_transpose(d.dt, (const char*)q + t * d.BT * d.d * d.es, w + L.qt + t * b.BTp * d.es, d.BT,
-                             d.d, d.d, ldt, s));
-    HIP_TRY(launch_transpose(d.dt, (const char*)dout + t * d.d * d.es, w + L.dot + t * b.BTp * d.es, d.BT, d.d,
-                             d.hs, ldt, s));
-  }
-  HIP_TRY(launch_transpose(d.dt, kv, w + L.kt, d.Hkd * d.BS, d.d, d.d, d.Hkd * d.BS, s));
-  HIP_TRY(launch_transpose(d.dt, vt, w + L.vr, d.Hkd * d.d, d.BS, d.BS, d.Hkd * d.d, s));
-  for (int part = 0; part < 3; part++) HIP_TRY(launch_attn_bwd((int)d.d, b, part, s));
-  return TSP_OK;
+  if ((rc = attn_recompute(c, L, q, kv))) return rc;
+  return attn_core_grads(c, L, q, kv, dout, (int)d.hs, dq, dk, dv);
 }
 
 int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,

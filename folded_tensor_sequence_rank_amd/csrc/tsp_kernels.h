@@ -13,7 +13,8 @@ enum Epi {
   EPI_ACC = 1,    // Y = (beta ? Y : 0) + acc            (fp32 accumulator, in place)
   EPI_RESID = 2,  // C = R + (beta ? Y : 0) + acc         (residual add, output dtype)
   EPI_QKV = 3,    // scatter columns to Q / K / Vt at zigzag positions
-  EPI_SWIGLU = 4  // C = silu(A.B1^T) * (A.B3^T)           (two B operands)
+  EPI_SWIGLU = 4,  // C = silu(A.B1^T) * (A.B3^T)          (two B operands)
+  EPI_STORE = 5    // C = acc                               (output dtype)
 };
 
 struct GemmArgs {
@@ -103,6 +104,28 @@ hipError_t launch_swiglu_bwd(Dtype dt, const float* ab, const float* dg, void* d
 hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const float* dn, const void* res,
                               void* dx, float* rs, float* dgain, int64_t rows, int h, float eps,
                               hipStream_t s);
+
+// Rotations undone: every 4-dim group of v (fp32, rows of hd values, `rows`
+// rows per head, `heads` heads) turned back by its row's position.  Row m of
+// a head is position m % S of its sequence when S > 0 (gathered K/V rows), or
+// the zigzag position zig(m % T) when S == 0 (local rows).  l2c = log2(theta)/hd.
+hipError_t launch_rope_inverse(float* v, int64_t rows, int heads, int hd, int64_t S, int64_t T, int64_t chunk,
+                               int rank, int fold, double l2c, hipStream_t s);
+// own[j][c][t][b*T + i][e] = sum over the D ranks' partials part[q][j][c][t][b*S + zig(i)][e]
+// (j < D shards, c: K or V, t < hkd heads, e < hd): the sums a reduce-scatter of
+// per-position gradients delivers to rank `rank`, gathered at its local rows.
+constexpr int kMaxFold = 64;
+struct KvGradReduceArgs {
+  const float* part[kMaxFold];
+  float* own;
+  int64_t S, T, chunk, batch;
+  int rank, fold, hkd, hd;
+};
+hipError_t launch_kv_grad_reduce(const KvGradReduceArgs& a, hipStream_t s);
+// out[m][c] (row pitch hs + 2ks) from dq [hd-dim heads][rows][hd] for c < hs,
+// dk [..][rows][hd] for the next ks columns and dv for the last ks.
+hipError_t launch_qkv_grad_pack(Dtype dt, const float* dq, const float* dk, const float* dv, void* out,
+                                int64_t rows, int hs, int ks, int hd, hipStream_t s);
 
 // Backward of the attention core (bf16, head dim 64 or 128).
 struct AttnBwdArgs {

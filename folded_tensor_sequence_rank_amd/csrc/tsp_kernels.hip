@@ -828,6 +828,20 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
             }
           }
         }
+      } else if constexpr (EPI == EPI_STORE) {
+        const bool vc = (g.ldc & 3) == 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
+          T* pc = C + (int64_t)m * g.ldc + n;
+          if (full[q] && vc) {
+            store4<T>(pc, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          } else if (ok[q]) {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              if (n + e < g.N) pc[e] = from_f<T>(v[4 * q + e]);
+          }
+        }
       } else if constexpr (EPI == EPI_SWIGLU) {
         const bool vc = (g.ldc & 3) == 0;
 #pragma unroll
@@ -1383,6 +1397,9 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 #ifndef TSP_PIPE_DIST
 #define TSP_PIPE_DIST 3    // LDS fragment reads kept in flight ahead of the MFMAs
 #endif
+#ifndef TSP_ATTN_FOLD
+#define TSP_ATTN_FOLD 1    // softmax scale and offset folded into the S products (below)
+#endif
 
 __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   typedef bf16 T;
@@ -1513,8 +1530,35 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
 
   const float cs = a.scale_log2;
   const float kSumCap = a.sum_cap;
+  // Folded softmax offset.  The wave's queries are prescaled by cs, so scores
+  // arrive in log2 units, and every 32-key S block starts with one extra MFMA
+  // of a constant K fragment (a one at k = 0 in every key row) and a query
+  // fragment holding -m at k = 0 (m: the row's reference max, kept
+  // representable in bf16).  The block then holds s*cs - m and feeds the
+  // exponentials as it is: the per-score FMA moves onto the matrix unit, two
+  // MFMAs per 64-key tile.  S blocks already formed when m is raised are
+  // shifted by the change.
+  constexpr bool FOLD = TSP_ATTN_FOLD != 0;
+  frag kext = frag{0}, qext = frag{0};
+  if constexpr (FOLD) {
+    if (lg == 0) kext[0] = (bf16)1.0f;
+#pragma unroll
+    for (int ks = 0; ks < QK; ks++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) qf[ks][e] = (bf16)((float)qf[ks][e] * cs);
+  }
   // Online softmax state: reference max m (log2 units), row sum l, O^T.
   float m = -INFINITY, l = 0.f;
+  // (fold) the offset the S blocks in flight carry: m, or 0 while m is -inf
+  auto mref = [&]() { return m == -INFINITY ? 0.f : m; };
+  auto set_ref = [&](float mn) {  // m = mn (rounded to bf16 under the fold) and its query fragment
+    if constexpr (FOLD) {
+      m = mn == -INFINITY ? mn : (float)(bf16)mn;
+      if (lg == 0) qext[0] = (bf16)(-mref());
+    } else {
+      m = mn;
+    }
+  };
   f32x16 o[DB];
 #pragma unroll
   for (int d = 0; d < DB; d++) o[d] = f32x16{0};
@@ -1527,26 +1571,31 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       for (int i = 0; i < 16; i++)
         if (32 * kb + 16 * (i >> 3) + (i & 7) > lim) s[kb][i] = -INFINITY;
   };
-  auto row_max = [&](const f32x16* s) {
+  // Row max of one 32-key block / of both, in log2 units, for S blocks formed
+  // with the current reference.
+  auto block_max = [&](const f32x16& sb) {
     float xs[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) xs[i & 3] = fmaxf(xs[i & 3], s[kb][i]);
-    return halves_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]))) * cs;
+    for (int i = 0; i < 16; i++) xs[i & 3] = fmaxf(xs[i & 3], sb[i]);
+    const float mx = halves_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])));
+    return FOLD ? mx + mref() : mx * cs;
   };
-  // P fragments of one 32-key block (16-key steps 2kb, 2kb+1).
-  // One element e of a P fragment and its part of the row sum.
-  auto pel = [&](float x, float nm, frag& pv, int e, float* ls) {
-    const float p = fast_exp2(fmaf(x, cs, nm));
+  auto row_max = [&](const f32x16* s) { return fmaxf(block_max(s[0]), block_max(s[1])); };
+  // One element e of a P fragment and its part of the row sum (the first
+  // four elements of a run start the four partial sums).
+  auto pel = [&](float x, float nm, frag& pv, int e, float* ls, bool first) {
+    const float p = FOLD ? fast_exp2(x) : fast_exp2(fmaf(x, cs, nm));
     pv[e] = (bf16)p;
-    ls[e & 3] += p;
+    if (first)
+      ls[e & 3] = p;
+    else
+      ls[e & 3] += p;
   };
   auto exps = [&](const f32x16& sb, float nm, frag& p0, frag& p1, float* ls) {
 #pragma unroll
-    for (int t = 0; t < 8; t++) pel(sb[t], nm, p0, t, ls);
+    for (int t = 0; t < 8; t++) pel(sb[t], nm, p0, t, ls, t < 4);
 #pragma unroll
-    for (int t = 0; t < 8; t++) pel(sb[8 + t], nm, p1, t, ls);
+    for (int t = 0; t < 8; t++) pel(sb[8 + t], nm, p1, t, ls, false);
   };
   // Keeps a phase's softmax results inside the phase: without it the
   // compiler sinks the exponentials next to their later uses, out of the
@@ -1554,31 +1603,29 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   auto pin = [](frag& p0, frag& p1, float* ls) {
     asm volatile("" : "+v"(p0), "+v"(p1), "+v"(ls[0]), "+v"(ls[1]), "+v"(ls[2]), "+v"(ls[3]));
   };
-  // Row max of one 32-key block, in log2 units.
-  auto block_max = [&](const f32x16& sb) {
-    float xs[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int i = 0; i < 16; i++) xs[i & 3] = fmaxf(xs[i & 3], sb[i]);
-    return halves_max(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]))) * cs;
-  };
   auto scale_frag = [](frag& pv, float alpha) {
 #pragma unroll
     for (int e = 0; e < 8; e++) pv[e] = (bf16)((float)pv[e] * alpha);
   };
+  auto shift = [](f32x16& sb, float by) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) sb[i] += by;
+  };
   // Raise the reference max to mn: rescale O, the row sum and the P blocks
   // already formed (npf of them, in pf) by 2^(m - mn).
   auto raise_ref = [&](float mn, frag* pv, int npf) {
-    const float alpha = m == -INFINITY ? 1.f : fast_exp2(m - mn);
+    const float mold = m;
+    set_ref(mn);
+    const float alpha = mold == -INFINITY ? 1.f : fast_exp2(mold - m);
 #pragma unroll
     for (int d = 0; d < DB; d++) o[d] *= alpha;
     l *= alpha;
     for (int q = 0; q < npf; q++) scale_frag(pv[q], alpha);
-    m = mn;
   };
   auto s_product = [&](int buf, f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
-      s[kb] = f32x16{0};
+      s[kb] = FOLD ? M_::mma(kext, qext, f32x16{0}) : f32x16{0};
 #pragma unroll
       for (int ks = 0; ks < QK; ks++) s[kb] = M_::mma(kfrag(buf, kb, ks), qf[ks], s[kb]);
     }
@@ -1606,9 +1653,13 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   __syncthreads();
   if (ntw > 0) {
     f32x16 s[2];
-    s_product(0, s);
+    s_product(0, s);  // the reference is still -inf: no offset yet
     if (needmask(kbeg)) mask_rows(s, kbeg);
-    m = row_max(s);
+    set_ref(row_max(s));
+    if constexpr (FOLD) {
+      shift(s[0], -mref());
+      shift(s[1], -mref());
+    }
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
     exps(s[0], m == -INFINITY ? 0.f : -m, pf[0], pf[1], ls);
     l = (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -1642,8 +1693,13 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       // chains alternate, so no MFMA waits on the one just before it.
 #pragma unroll
       for (int i = 0; i < PD; i++) kq[i] = kfrag(kbuf, i & 1, i >> 1);
-      s[0] = f32x16{0};
-      s[1] = f32x16{0};
+      if constexpr (FOLD) {
+        s[0] = M_::mma(kext, qext, f32x16{0});
+        s[1] = M_::mma(kext, qext, f32x16{0});
+      } else {
+        s[0] = f32x16{0};
+        s[1] = f32x16{0};
+      }
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -1654,7 +1710,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
         else
           vq[i + PD - 16] = vfrag(vbuf, (i + PD - 16) >> 2, (i + PD - 16) & 3);
         s[i & 1] = M_::mma(f, qf[i >> 1], s[i & 1]);
-        pel(sh[i], nm, pf[2 + (i >> 3)], i & 7, ls);
+        pel(sh[i], nm, pf[2 + (i >> 3)], i & 7, ls, i < 4);
         __builtin_amdgcn_sched_barrier(0);
       }
       pin(pf[2], pf[3], ls);
@@ -1667,13 +1723,15 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
         // redo the block.
         float lsa = (ls[0] + ls[1]) + (ls[2] + ls[3]);
         if (__any(!(lsa <= kSumCap))) {
+          const float mold = mref();
           raise_ref(fmaxf(m, block_max(sh)), pf, 2);
+          if constexpr (FOLD) {  // sh and S(t+1) carry the old reference
+            shift(sh, mold - mref());
+            shift(s[0], mold - mref());
+            shift(s[1], mold - mref());
+          }
           float lr4[4] = {0.f, 0.f, 0.f, 0.f};
-          const float nmr = m == -INFINITY ? 0.f : -m;
-#pragma unroll
-          for (int t8 = 0; t8 < 8; t8++) pel(sh[t8], nmr, pf[2], t8, lr4);
-#pragma unroll
-          for (int t8 = 0; t8 < 8; t8++) pel(sh[8 + t8], nmr, pf[3], t8, lr4);
+          exps(sh, m == -INFINITY ? 0.f : -m, pf[2], pf[3], lr4);
           lsa = (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]);
         }
         l += lsa;
@@ -1690,7 +1748,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
         const frag f = vq[i % PD];
         if (i + PD < 16) vq[i % PD] = vfrag(vbuf, (i + PD) >> 2, (i + PD) & 3);
         o[i & 3] = M_::mma(f, pf[i >> 2], o[i & 3]);
-        pel(s[0][i], nm2, pn[i >> 3], i & 7, ls2);
+        pel(s[0][i], nm2, pn[i >> 3], i & 7, ls2, i < 4);
         __builtin_amdgcn_sched_barrier(0);
       }
       pin(pn[0], pn[1], ls2);
@@ -1701,13 +1759,14 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
         if (__any(!(lsb <= kSumCap))) {
           // O already holds tile t's products (formed with the old m);
           // take the max of both blocks of S(t+1) so its second block passes
+          const float mold = mref();
           raise_ref(fmaxf(m, row_max(s)), pf, 0);
+          if constexpr (FOLD) {
+            shift(s[0], mold - mref());
+            shift(s[1], mold - mref());
+          }
           float lr4[4] = {0.f, 0.f, 0.f, 0.f};
-          const float nmr = m == -INFINITY ? 0.f : -m;
-#pragma unroll
-          for (int t8 = 0; t8 < 8; t8++) pel(s[0][t8], nmr, pn[0], t8, lr4);
-#pragma unroll
-          for (int t8 = 0; t8 < 8; t8++) pel(s[0][8 + t8], nmr, pn[1], t8, lr4);
+          exps(s[0], m == -INFINITY ? 0.f : -m, pn[0], pn[1], lr4);
           lsb = (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]);
         }
         l += lsb;
@@ -1721,7 +1780,9 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       exps(sh, nm, pf[2], pf[3], ls);
       float lsa = (ls[0] + ls[1]) + (ls[2] + ls[3]);
       if (__any(!(lsa <= kSumCap))) {
+        const float mold = mref();
         raise_ref(fmaxf(m, block_max(sh)), pf, 2);
+        if constexpr (FOLD) shift(sh, mold - mref());
         float lr4[4] = {0.f, 0.f, 0.f, 0.f};
         exps(sh, m == -INFINITY ? 0.f : -m, pf[2], pf[3], lr4);
         lsa = (lr4[0] + lr4[1]) + (lr4[2] + lr4[3]);
@@ -1730,7 +1791,6 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       pv_product(P, pf, o);
     }
   }
-
   const float lt = halves_sum(l);
   const int64_t row = row0 + lr;
   if (nseg == 1) {
@@ -1894,6 +1954,80 @@ __global__ void __launch_bounds__(256) gain_grad_kernel(const T* __restrict__ x,
   float acc = 0.f;
   for (int64_t r = r0; r < r1; r++) acc += dn[r * h + c] * to_f(x[r * h + c]) * rs[r];
   atomicAdd(dgain + c, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Pieces of the whole layer's backward around the attention core.
+// ---------------------------------------------------------------------------
+
+// The rotation's backward: it is orthogonal, so the gradient turns back by
+// the opposite angle, i.e. the forward rotation at position -p.  One thread
+// per four dims of one row of one head.
+__global__ void __launch_bounds__(256) rope_inverse_kernel(float* __restrict__ v, int64_t rows, int heads,
+                                                           int hd, int64_t S, int64_t T, int64_t chunk,
+                                                           int rank, int fold, double l2c) {
+  const int q4 = hd / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)heads * rows * q4) return;
+  const int64_t row = (gid / q4) % rows;
+  const int e = (int)(gid % q4) * 4;
+  const int64_t p = S > 0 ? row % S : zig(row % T, chunk, rank, fold);
+  float* pv = v + (gid / q4) * hd + e;
+  float4 x = *(float4*)pv;
+  float w[4] = {x.x, x.y, x.z, x.w};
+  rope_pairs(w, e, -p, l2c);
+  *(float4*)pv = make_float4(w[0], w[1], w[2], w[3]);
+}
+
+// One thread per four dims of one local row of one (shard, K|V, head): the
+// sum over the ranks' partial gradients at that row's position.
+__global__ void __launch_bounds__(256) kv_grad_reduce_kernel(KvGradReduceArgs a) {
+  const int q4 = a.hd / 4;
+  const int64_t BT = a.batch * a.T, BS = a.batch * a.S;
+  const int64_t planes = (int64_t)a.fold * 2 * a.hkd;  // (shard, K|V, head) planes
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= planes * BT * q4) return;
+  const int e = (int)(gid % q4) * 4;
+  const int64_t m = (gid / q4) % BT;
+  const int64_t plane = gid / q4 / BT;
+  const int64_t b = m / a.T;
+  const int64_t src = plane * BS * a.hd + (b * a.S + zig(m - b * a.T, a.chunk, a.rank, a.fold)) * a.hd + e;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q = 0; q < a.fold; q++) {
+    const float4 x = *(const float4*)(a.part[q] + src);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  *(float4*)(a.own + plane * BT * a.hd + m * a.hd + e) = acc;
+}
+
+// [dQ | dK | dV] of one shard's head group side by side, in the GEMM operand
+// dtype: column c < hs is query head c / hd, then ks key and ks value columns.
+template <typename T>
+__global__ void __launch_bounds__(256) qkv_grad_pack_kernel(const float* __restrict__ dq,
+                                                            const float* __restrict__ dk,
+                                                            const float* __restrict__ dv, T* __restrict__ out,
+                                                            int64_t rows, int hs, int ks, int hd) {
+  const int n4 = (hs + 2 * ks) / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= rows * n4) return;
+  const int64_t m = gid / n4;
+  const int c = (int)(gid % n4) * 4;
+  const float* src;
+  int cc = c;
+  if (c < hs) {
+    src = dq;
+  } else if (c < hs + ks) {
+    src = dk;
+    cc = c - hs;
+  } else {
+    src = dv;
+    cc = c - hs - ks;
+  }
+  const float4 x = *(const float4*)(src + ((int64_t)(cc / hd) * rows + m) * hd + cc % hd);
+  store4<T>(out + m * (hs + 2 * ks) + c, x.x, x.y, x.z, x.w);
 }
 
 // ---------------------------------------------------------------------------
@@ -2401,7 +2535,7 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
       if (pick(dual, 2) == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
       else gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
     }
-  } else if constexpr (EPI == EPI_ACC || EPI == EPI_RESID) {
+  } else if constexpr (EPI == EPI_ACC || EPI == EPI_RESID || EPI == EPI_STORE) {
     if (tiles(256, 256) >= 256) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
     else gemm_go<bf16, 128, 128, EPI, 4, 2>(a, vec, s);
   } else {
@@ -2432,6 +2566,7 @@ hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
       case EPI_RESID: gemm_bf16<EPI_RESID>(a, vec, s); break;
       case EPI_QKV: gemm_bf16<EPI_QKV>(a, vec, s); break;
       case EPI_SWIGLU: gemm_bf16<EPI_SWIGLU>(a, vec, s); break;
+      case EPI_STORE: gemm_bf16<EPI_STORE>(a, vec, s); break;
     }
   } else {
     switch (epi) {
@@ -2439,6 +2574,7 @@ hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
       case EPI_RESID: gemm_go<float, 64, 64, EPI_RESID>(a, vec, s); break;
       case EPI_QKV: gemm_go<float, 64, 64, EPI_QKV>(a, vec, s); break;
       case EPI_SWIGLU: gemm_go<float, 64, 64, EPI_SWIGLU>(a, vec, s); break;
+      case EPI_STORE: gemm_go<float, 64, 64, EPI_STORE>(a, vec, s); break;
     }
   }
   return hipGetLastError();
@@ -2530,6 +2666,34 @@ hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const floa
 
 hipError_t launch_spin(uint64_t ticks, hipStream_t s) {
   spin_kernel<<<1, 64, 0, s>>>(ticks);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_inverse(float* v, int64_t rows, int heads, int hd, int64_t S, int64_t T, int64_t chunk,
+                               int rank, int fold, double l2c, hipStream_t s) {
+  const int64_t n = (int64_t)heads * rows * (hd / 4);
+  if (n <= 0) return hipSuccess;
+  rope_inverse_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(v, rows, heads, hd, S, T, chunk, rank, fold,
+                                                                   l2c);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_grad_reduce(const KvGradReduceArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.fold * 2 * a.hkd * a.batch * a.T * (a.hd / 4);
+  if (n <= 0) return hipSuccess;
+  kv_grad_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_grad_pack(Dtype dt, const float* dq, const float* dk, const float* dv, void* out,
+                                int64_t rows, int hs, int ks, int hd, hipStream_t s) {
+  const int64_t n = rows * ((hs + 2 * ks) / 4);
+  if (n <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (dt == BF16)
+    qkv_grad_pack_kernel<bf16><<<grid, 256, 0, s>>>(dq, dk, dv, (bf16*)out, rows, hs, ks, hd);
+  else
+    qkv_grad_pack_kernel<float><<<grid, 256, 0, s>>>(dq, dk, dv, (float*)out, rows, hs, ks, hd);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "tsp.h")
 
 TSP_BF16, TSP_F32 = 0, 1
 TSP_WS_ATTN, TSP_WS_MLP, TSP_WS_LAYER, TSP_WS_KV, TSP_WS_MLP_BWD, TSP_WS_ATTN_BWD = 1, 2, 3, 4, 5, 6
+TSP_WS_LAYER_BWD, TSP_WS_LAYER_BWD_FINISH = 7, 8
 TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP, TSP_F_PROFILE = 1, 2, 4, 8
 TSP_F_RESCALE_TEST = 16
 TSP_F_KV_STREAM = 32
@@ -77,12 +78,18 @@ def lib() -> ctypes.CDLL:
         L.tsp_kv_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp]
         L.tsp_mlp_shard_backward.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _pp, _vp, _sz, _vp]
         L.tsp_attn_core_backward.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.tsp_layer_shard_backward.argtypes = [D, _vp, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _vp, _pp,
+                                               _pp, _vp, _vp, _vp, _sz, _vp]
+        L.tsp_kv_grad_reduce.argtypes = [D, _pp, _vp, _vp]
+        L.tsp_layer_shard_backward_finish.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _vp, _vp, _pp, _vp,
+                                                      _sz, _vp]
         L.tsp_clock_probe.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int32), _vp]
         L.tsp_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         for f in ("tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
-                  "tsp_mlp_shard_backward", "tsp_attn_core_backward",
+                  "tsp_mlp_shard_backward", "tsp_attn_core_backward", "tsp_layer_shard_backward",
+                  "tsp_kv_grad_reduce", "tsp_layer_shard_backward_finish",
                   "tsp_zigzag_positions", "tsp_profile_read", "tsp_clock_probe"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -244,6 +251,74 @@ def tsp_attn_core_backward(dims, q, kv, dout, dq, dk, dv, ws, stream=None):
             raise ValueError(f"{name}: {_nbytes(t)} bytes, the dims need {need[name]}")
     _check(lib().tsp_attn_core_backward(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(dout), _ptr(dq),
                                         _ptr(dk), _ptr(dv), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def _need(name, t, nbytes):
+    if hasattr(t, "numel") and _nbytes(t) < nbytes:
+        raise ValueError(f"{name}: {_nbytes(t)} bytes, the dims need {nbytes}")
+
+
+def _bwd_sizes(dims):
+    D, d, h = dims.fold, dims.head_dim, dims.hidden
+    B = max(dims.batch, 1)
+    H, Hkv = dims.n_heads, dims.n_kv_heads or dims.n_heads
+    BT, BS = B * (dims.seq // D), B * dims.seq
+    hs, ks = h // D, Hkv * d // D
+    return {"dq": H * BT * d * 4, "dkv": 2 * Hkv * BS * d * 4, "dkv_own": 2 * Hkv * BT * d * 4,
+            "dw_o": h * hs * 4, "dw_qkv": (hs + 2 * ks) * h * 4, "dw_mlp": 3 * (dims.ffn // D) * h * 4,
+            "gain": h * 4}
+
+
+def tsp_layer_shard_backward(dims, x, x1, g1, w_attn, kv, g2, w_mlp, dout, dx1, dg2, dw_mlp, dw_o, dq, dkv,
+                             ws, stream=None):
+    """Part 1 of the whole layer's backward (include/tsp.h): dx1, the partial
+    dg2, dw_mlp and dw_o, the unrotated dq [H][B*T][d] and the partial dkv
+    [D][2][Hkv/D][B*S][d] (fp32)."""
+    _check_sizes(dims, TSP_WS_LAYER_BWD, x=x, g1=g1, w_attn=w_attn, kv=kv, g2=g2, w_mlp=w_mlp, out=dout)
+    _check_sizes(dims, TSP_WS_LAYER_BWD, x1=x1)
+    _check_sizes(dims, TSP_WS_LAYER_BWD, x=dx1)
+    n = _bwd_sizes(dims)
+    for name, t in (("dq", dq), ("dkv", dkv), ("dg2", dg2)):
+        _need(name, t, n[name] if name != "dg2" else n["gain"])
+    for name, ts in (("dw_mlp", dw_mlp), ("dw_o", dw_o)):
+        if len(ts) != dims.fold:
+            raise ValueError(f"{name}: {len(ts)} shards for fold {dims.fold}")
+        for i, t in enumerate(ts):
+            _need(f"{name}[{i}]", t, n[name])
+    _check(lib().tsp_layer_shard_backward(ctypes.byref(dims), _ptr(x), _ptr(x1), _ptr(g1), _ptrs(w_attn),
+                                          _ptr(kv), _ptr(g2), _ptrs(w_mlp), _ptr(dout), _ptr(dx1), _ptr(dg2),
+                                          _ptrs(dw_mlp), _ptrs(dw_o), _ptr(dq), _ptr(dkv), _ptr(ws),
+                                          _nbytes(ws), _stream(stream)))
+
+
+def tsp_kv_grad_reduce(dims, dkv_parts, dkv_own, stream=None):
+    """The dK/dV exchange's sums for rank dims.rank: dkv_own [D][2][Hkv/D][B*T][d]
+    (fp32) from the D ranks' part-1 dkv buffers."""
+    n = _bwd_sizes(dims)
+    if len(dkv_parts) != dims.fold:
+        raise ValueError(f"dkv_parts: {len(dkv_parts)} buffers for fold {dims.fold}")
+    for i, t in enumerate(dkv_parts):
+        _need(f"dkv_parts[{i}]", t, n["dkv"])
+    _need("dkv_own", dkv_own, n["dkv_own"])
+    _check(lib().tsp_kv_grad_reduce(ctypes.byref(dims), _ptrs(dkv_parts), _ptr(dkv_own), _stream(stream)))
+
+
+def tsp_layer_shard_backward_finish(dims, x, g1, w_attn, dx1, dq, dkv_own, dx, dg1, dw_qkv, ws, stream=None):
+    """Part 2 of the whole layer's backward (include/tsp.h): dx, the partial
+    dg1 and dw_qkv (fp32, packed Q|K|V block layout)."""
+    _check_sizes(dims, TSP_WS_LAYER_BWD_FINISH, x=x, g1=g1, w_attn=w_attn)
+    _check_sizes(dims, TSP_WS_LAYER_BWD_FINISH, x1=dx1, out=dx)
+    n = _bwd_sizes(dims)
+    _need("dq", dq, n["dq"])
+    _need("dkv_own", dkv_own, n["dkv_own"])
+    _need("dg1", dg1, n["gain"])
+    if len(dw_qkv) != dims.fold:
+        raise ValueError(f"dw_qkv: {len(dw_qkv)} shards for fold {dims.fold}")
+    for i, t in enumerate(dw_qkv):
+        _need(f"dw_qkv[{i}]", t, n["dw_qkv"])
+    _check(lib().tsp_layer_shard_backward_finish(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn),
+                                                 _ptr(dx1), _ptr(dq), _ptr(dkv_own), _ptr(dx), _ptr(dg1),
+                                                 _ptrs(dw_qkv), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def tsp_profile_read(reset: bool = True) -> dict:

@@ -145,7 +145,9 @@ enum {
   TSP_WS_LAYER = 3,
   TSP_WS_KV = 4,
   TSP_WS_MLP_BWD = 5,
-  TSP_WS_ATTN_BWD = 6
+  TSP_WS_ATTN_BWD = 6,
+  TSP_WS_LAYER_BWD = 7,
+  TSP_WS_LAYER_BWD_FINISH = 8
 };
 
 /* Flags (tsp_dims.flags).  Results must be identical with or without the
@@ -320,6 +322,79 @@ int tsp_mlp_shard_backward(const tsp_dims* dims, const void* x1, const void* g2,
  */
 int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, const void* dout,
                            float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of rank r's whole layer share (training), in two parts around the
+ * one exchange the gradient needs.  The pages give the forward schedules
+ * only ("Folding Tensor and Sequence Parallelism ...", section 2: attention
+ * shards broadcast, K/V all-gathered along the sequence, MLP shards on a
+ * ring, partial outputs summed locally); the backward follows the plainest
+ * reading of them: the rank takes the gradient of its own zigzag rows
+ * through the layer, forms a PARTIAL gradient of every weight shard from
+ * those rows (a reduce-scatter over the D ranks, the reverse of the
+ * broadcast and the ring, sums the partials at each shard's owner), and its
+ * queries produce gradients for the K/V of every position they attended to,
+ * which a reduce-scatter (the reverse of the K/V all-gather) sums at the
+ * positions' owners before the owners take them through W_K, W_V and the
+ * norm.  bf16 only with head_dim 64 or 128 (TSP_E_DTYPE / TSP_E_SHAPE
+ * otherwise), as the attention core's backward.  Everything is enqueued on
+ * `stream`; weight shards are read in place.
+ *
+ * Part 1, before the exchange.  With the forward's inputs and its
+ * attention-half output x1 (which training keeps), and the output gradient:
+ *   x, x1   [B*T][h]   the layer's input and tsp_attn_shard's output
+ *   g1, w_attn, kv, g2, w_mlp   as the forward (kv: the gathered K/V; every
+ *           other rank's rows are read, the rank's own are recomputed)
+ *   dout    [B*T][h]   gradient of the layer output
+ * outputs (all overwritten):
+ *   dx1     [B*T][h]   gradient of x1 (dout plus the MLP branch), dims->dtype
+ *   dg2     [h] fp32   partial gradient of g2
+ *   dw_mlp  D pointers, 3*Fs*h fp32 each: partial gradients of the MLP
+ *           shards in their packed layout (as tsp_mlp_shard_backward)
+ *   dw_o    D pointers, h*hs fp32 each: partial gradient of each shard's W_O
+ *           block in its packed layout (row n, column k: dW_O[j*hs + k][n])
+ *   dq      [H][B*T][d] fp32: gradient of the rank's queries before the
+ *           rotation (head t = j*Hd + u of shard j at block t)
+ *   dkv     D blocks of [2][Hkd][B*S][d] fp32 (block j: dK then dV of K/V
+ *           heads [j*Hkd, (j+1)*Hkd), every position of every sequence,
+ *           keys before the rotation): this rank's partial K/V gradients,
+ *           zero at positions none of its queries sees
+ *   ws      >= tsp_workspace_bytes(dims, TSP_WS_LAYER_BWD)
+ * The forward attention of each head group is recomputed (FlashAttention's
+ * way), as are RMSNorm-1, Q and the rank's own K/V rows.
+ */
+int tsp_layer_shard_backward(const tsp_dims* dims, const void* x, const void* x1, const void* g1,
+                             const void* const* w_attn, const void* kv, const void* g2,
+                             const void* const* w_mlp, const void* dout, void* dx1, float* dg2,
+                             float* const* dw_mlp, float* const* dw_o, float* dq, float* dkv,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The exchange's arithmetic for rank r (a harness helper, like tsp_kv_shard:
+ * on D GPUs a reduce-scatter does this): dkv_own = the sum over the D ranks'
+ * part-1 dkv buffers, taken at rank r's positions,
+ *   dkv_own[j][c][t][b*T + i][e] = sum_q dkv_parts[q][j][c][t][b*S + zig_r(i)][e],
+ * a [D][2][Hkd][B*T][d] fp32 buffer (c: K or V).  dkv_parts: D device
+ * pointers (host array).  TSP_E_SHAPE if D > 64.
+ */
+int tsp_kv_grad_reduce(const tsp_dims* dims, const float* const* dkv_parts, float* dkv_own, void* stream);
+
+/*
+ * Part 2, after the exchange: the rank's own rows through W_Q, W_K, W_V and
+ * RMSNorm-1.  With dq from part 1 and dkv_own from tsp_kv_grad_reduce:
+ *   dn1 = sum_j [dQ_j | dK_j | dV_j] [W_Q_j; W_K_j; W_V_j]^T
+ *   dx  [B*T][h]  = dx1 + RMSNorm-1's backward of dn1, dims->dtype
+ *   dg1 [h] fp32  partial gradient of g1 (overwritten)
+ *   dw_qkv D pointers, (hs + 2*ks)*h fp32 each: partial gradient of each
+ *          shard's Q|K|V block in its packed layout (row n, column k: the
+ *          gradient of that block's element), overwritten
+ *   ws  >= tsp_workspace_bytes(dims, TSP_WS_LAYER_BWD_FINISH)
+ * The W_O rows of a packed shard are not touched (part 1 gives dw_o).
+ */
+int tsp_layer_shard_backward_finish(const tsp_dims* dims, const void* x, const void* g1,
+                                    const void* const* w_attn, const void* dx1, const float* dq,
+                                    const float* dkv_own, void* dx, float* dg1, float* const* dw_qkv,
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Per-kernel timing of calls made with TSP_F_PROFILE: every kernel the
