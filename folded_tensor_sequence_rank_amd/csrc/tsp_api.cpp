@@ -20,6 +20,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -860,6 +861,32 @@ int attn_core_grads(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv, c
   return TSP_OK;
 }
 
+// ---- the allocation-free layer entry point --------------------------------
+// Its workspace is this file-scope device array, one copy per GPU, held from
+// module load until the process ends.  Host code never names it directly
+// (the name is a host-side stand-in, not a device address): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept per device.
+static __device__ __attribute__((aligned(256))) char scratch[TSP_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDev] = {};
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDev) return fail(TSP_E_HIP, "device index %d unsupported", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(TSP_E_HIP, "hipGetSymbolAddress returned a null scratch address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -982,6 +1009,34 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1, const v
   Ctx c{&d, (char*)ws};
   if ((rc = begin(c, (hipStream_t)stream, (hipStream_t)copy_stream, d.flags))) return rc;
   void* x1 = (char*)ws + x1off;
+  if ((rc = attn_body(c, A, x, g1, w_attn, kv, x1))) return rc;
+  if ((rc = mlp_body(c, M, x1, g2, w_mlp, out))) return rc;
+  return finish(c);
+}
+
+int tsp_layer_shard_noalloc(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,
+                            const void* kv, const void* g2, const void* const* w_mlp, void* out, void* stream,
+                            void* copy_stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if (d.flags & TSP_F_PROFILE)
+    return fail(TSP_E_INVAL, "TSP_F_PROFILE creates timing events per launch; use tsp_layer_shard to profile");
+  if ((rc = check_ptrs({x, g1, kv, g2, out})) || (rc = check_shards(w_attn, d.D, "w_attn")) ||
+      (rc = check_shards(w_mlp, d.D, "w_mlp")))
+    return rc;
+  const AttnWs A = attn_ws(d, al((size_t)d.BT * d.h * d.es));
+  const MlpWs M = mlp_ws(d, A.end);
+  if (M.end > (size_t)TSP_NOALLOC_SCRATCH_BYTES)
+    return fail(TSP_E_WORKSPACE, "this layer needs %zu bytes of scratch; the static scratch holds %llu",
+                M.end, (unsigned long long)TSP_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = scratch_ptr(&ws))) return rc;
+  Ctx c{&d, (char*)ws};
+  if ((rc = begin(c, (hipStream_t)stream, (hipStream_t)copy_stream, d.flags))) return rc;
+  void* x1 = ws;  // x1 first, as in tsp_layer_shard's workspace
   if ((rc = attn_body(c, A, x, g1, w_attn, kv, x1))) return rc;
   if ((rc = mlp_body(c, M, x1, g2, w_mlp, out))) return rc;
   return finish(c);

@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.tsp_mlp_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_layer_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_kv_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp]
+        L.tsp_layer_shard_noalloc.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _vp]
         L.tsp_mlp_shard_backward.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _pp, _vp, _sz, _vp]
         L.tsp_attn_core_backward.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.tsp_layer_shard_backward.argtypes = [D, _vp, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _vp, _pp,
@@ -90,7 +91,8 @@ def lib() -> ctypes.CDLL:
         for f in ("tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
                   "tsp_mlp_shard_backward", "tsp_attn_core_backward", "tsp_layer_shard_backward",
                   "tsp_kv_grad_reduce", "tsp_layer_shard_backward_finish",
-                  "tsp_zigzag_positions", "tsp_profile_read", "tsp_clock_probe"):
+                  "tsp_zigzag_positions", "tsp_profile_read", "tsp_clock_probe",
+                  "tsp_layer_shard_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,6 +207,18 @@ def tsp_layer_shard(dims, x, g1, w_attn, kv, g2, w_mlp, out, ws, stream=None, co
                                  _ptr(g2), _ptrs(w_mlp), _ptr(out), _ptr(ws), _nbytes(ws),
                                  _stream(stream),
                                  None if copy_stream is None else _stream(copy_stream)))
+
+
+def tsp_layer_shard_noalloc(dims, x, g1, w_attn, kv, g2, w_mlp, out, stream=None, copy_stream=None):
+    """tsp_layer_shard on the library's static scratch (include/tsp.h): no
+    workspace argument, no allocation."""
+    _check_sizes(dims, TSP_WS_LAYER, x=x, g1=g1, w_attn=w_attn, kv=kv, g2=g2, w_mlp=w_mlp, out=out)
+    _check(lib().tsp_layer_shard_noalloc(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
+                                         _ptr(g2), _ptrs(w_mlp), _ptr(out), _stream(stream),
+                                         None if copy_stream is None else _stream(copy_stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 def tsp_kv_shard(dims, x, g1, w_attn, kv, ws, stream=None):

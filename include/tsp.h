@@ -258,6 +258,31 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1,
                     void* ws, size_t ws_bytes, void* stream, void* copy_stream);
 
 /*
+ * tsp_layer_shard without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results (bit for bit) as tsp_layer_shard; the
+ * workspace is instead a static device array of TSP_NOALLOC_SCRATCH_BYTES
+ * (256 MiB: the 7B-shape layer share fits up to S = 4096 at D = 8) that the
+ * library holds on every GPU it runs on until the process ends.
+ *   - Returns TSP_E_WORKSPACE, before anything is enqueued, when the dims
+ *     need more than that (tsp_workspace_bytes(dims, TSP_WS_LAYER) tells).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on the same GPU (other streams, other host threads) race and
+ *     must not be made.  The array keeps the last call's contents; no result
+ *     depends on them.
+ *   - It calls no hipMalloc, hipFree or allocating library routine.  The
+ *     first call on a device looks up the array's device address once; as
+ *     with every entry point, the first call of a host thread on a device
+ *     creates that thread's HIP events.  TSP_F_PROFILE is refused
+ *     (TSP_E_INVAL): it creates timing events per launch.
+ */
+#define TSP_NOALLOC_SCRATCH_BYTES (256ull << 20)
+int tsp_layer_shard_noalloc(const tsp_dims* dims, const void* x, const void* g1,
+                            const void* const* w_attn, const void* kv, const void* g2,
+                            const void* const* w_mlp, void* out, void* stream, void* copy_stream);
+
+/*
  * Rank r's contribution to the K/V all-gather (section 2, attention layers:
  * the all-gather rebuilds full-length K/V along the sequence): writes K and
  * V of rank r's local tokens, for every head, at their global positions into

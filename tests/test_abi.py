@@ -234,6 +234,30 @@ def test_shapes_past_32bit_offsets_are_refused(cfg, ok, what):
         assert tsp.STATUS[call()] == "TSP_E_SHAPE"
 
 
+def test_noalloc_entry_point_refusals_on_the_host():
+    """tsp_layer_shard_noalloc refuses, before any HIP call, dims whose layer
+    workspace exceeds its static scratch (TSP_E_WORKSPACE) and the profiling
+    flag (TSP_E_INVAL); bad dims give the usual codes."""
+    L = tsp.lib()
+    arr = (ctypes.c_void_p * 8)(*([4096] * 8))
+
+    def call(d):
+        return L.tsp_layer_shard_noalloc(ctypes.byref(d), 16, 16, arr, 16, 16, arr, 16, None, None)
+
+    big = tsp.make_dims(C3, 3)
+    assert tsp.workspace_bytes(big, tsp.TSP_WS_LAYER) > tsp.NOALLOC_SCRATCH_BYTES
+    assert tsp.STATUS[call(big)] == "TSP_E_WORKSPACE"
+    assert "static scratch" in L.tsp_last_error().decode()
+    fits = tsp.make_dims(C3.with_(seq=4096), 3)
+    assert tsp.workspace_bytes(fits, tsp.TSP_WS_LAYER) <= tsp.NOALLOC_SCRATCH_BYTES
+    fits.flags = tsp.TSP_F_PROFILE
+    assert tsp.STATUS[call(fits)] == "TSP_E_INVAL"
+    bad = tsp.make_dims(C3, 3)
+    bad.rank = 9
+    assert tsp.STATUS[call(bad)] == "TSP_E_INVAL"
+    assert tsp.NOALLOC_SCRATCH_BYTES == 256 << 20
+
+
 def test_clock_probe_argument_checks_on_the_host():
     L = tsp.lib()
     khz = ctypes.c_int32(0)
