@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=32,
                     help="local rows of the rank's second chunk the oracle computes")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline steps only: no second K/V path, no clock-probe pass "
+                         "(for counter runs, which serialise every dispatch)")
     ap.add_argument("--mlp-backward", action="store_true",
                     help="time the MLP half's backward (tsp_mlp_shard_backward) instead of the layer")
     ap.add_argument("--attn-backward", action="store_true",
@@ -491,20 +494,22 @@ def main():
     # probe beside them.  Not during the timed steps: the probe's wave holds a
     # slot on one CU, which keeps a full-register workgroup off that CU (a
     # GEMM launch of exactly two rounds of 256 tiles then needs a third).
-    ms_probe, _, (samples, khz) = timed(runs[head], probe=True)
-    smp = samples.cpu().numpy().reshape(-1, 2)
-    smp = smp[smp[:, 0] - smp[0, 0] <= ms_probe * args.steps * khz]  # inside the steps
-    mhz = tsp.clock_mhz(smp, khz)
-    eff_clock = None if mhz.size == 0 else {
-        "median_mhz": round(float(np.median(mhz)), 1), "min_mhz": round(float(mhz.min()), 1),
-        "max_mhz": round(float(mhz.max()), 1), "intervals": int(mhz.size), "interval_us": 200,
-        "probe_pass_ms_per_step": round(ms_probe, 4),
-        "source": "tsp_clock_probe: shader-clock cycles per wall-clock tick, one wave beside a second pass "
-                  "of the steps (not the timed one)"}
-    other = "kv_stream" if head == "in_place" else "in_place"
-    for _ in range(args.warmup):
-        runs[other].layer(x, L, kv, out)
-    ms_other, per_other, _ = timed(runs[other])
+    eff_clock, other, ms_other, per_other = None, None, None, None
+    if not args.headline_only:
+        ms_probe, _, (samples, khz) = timed(runs[head], probe=True)
+        smp = samples.cpu().numpy().reshape(-1, 2)
+        smp = smp[smp[:, 0] - smp[0, 0] <= ms_probe * args.steps * khz]  # inside the steps
+        mhz = tsp.clock_mhz(smp, khz)
+        eff_clock = None if mhz.size == 0 else {
+            "median_mhz": round(float(np.median(mhz)), 1), "min_mhz": round(float(mhz.min()), 1),
+            "max_mhz": round(float(mhz.max()), 1), "intervals": int(mhz.size), "interval_us": 200,
+            "probe_pass_ms_per_step": round(ms_probe, 4),
+            "source": "tsp_clock_probe: shader-clock cycles per wall-clock tick, one wave beside a second "
+                      "pass of the steps (not the timed one)"}
+        other = "kv_stream" if head == "in_place" else "in_place"
+        for _ in range(args.warmup):
+            runs[other].layer(x, L, kv, out)
+        ms_other, per_other, _ = timed(runs[other])
 
     T = cfg.batch * cfg.local_tokens
     f_alg = sum(flops_per_step(cfg, r).values())
@@ -516,10 +521,10 @@ def main():
         return {"median": round(v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2]), 4),
                 "min": round(v[0], 4), "max": round(v[-1], 4)}
 
-    variant = {"path": other, "ms_per_step": round(ms_other, 4),
-               "value": round(f_alg / (ms_other * 1e-3) / 1e12, 2),
-               "frac_of_peak": round(f_alg / (ms_other * 1e-3) / 1e12 / peak, 4),
-               "tokens_per_s": round(T / (ms_other * 1e-3), 1), "step_ms": step_stats(per_other)}
+    variant = None if other is None else {
+        "path": other, "ms_per_step": round(ms_other, 4), "value": round(f_alg / (ms_other * 1e-3) / 1e12, 2),
+        "frac_of_peak": round(f_alg / (ms_other * 1e-3) / 1e12 / peak, 4),
+        "tokens_per_s": round(T / (ms_other * 1e-3), 1), "step_ms": step_stats(per_other)}
 
     kernels, roofline = {}, None
     if not args.no_profile:
