@@ -194,20 +194,52 @@ AttnPlan plan_of(const Dims& d) {
   return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(d.Hd * d.B));
 }
 
+// Shards per launch in the forward halves (TSP_F_SHARD_LAUNCH).  When one
+// shard's projection, N columns over the B*T rows, has fewer than 256 tiles
+// of 256 x 192, P consecutive shards share one launch: P is the largest
+// divisor of G not above D/4, so the two weight slots (2P shards) hold at
+// most half of the layer's Q|K|V or W1|W3 shards, as the W_O and W2 group
+// buffers do, and a launch never spans two accumulation groups.
+int64_t group_shards(const Dims& d) {
+  const int64_t G = acc_group(d);
+  int64_t P = 1;
+  for (int64_t p = 2; p <= G && p <= d.D / 4; p++)
+    if (G % p == 0) P = p;
+  return P;
+}
+int64_t launch_shards(const Dims& d, int64_t ncols) {
+  if (d.flags & TSP_F_SHARD_LAUNCH) return 1;
+  if (d.flags & TSP_F_GROUP_LAUNCH) return group_shards(d);
+  return ((d.BT + 255) / 256) * ((ncols + 191) / 192) < 256 ? group_shards(d) : 1;
+}
+int64_t attn_launch(const Dims& d) { return launch_shards(d, (int64_t)qkv_rows(d)); }
+int64_t mlp_launch(const Dims& d) { return launch_shards(d, d.Fs); }
+
+// Attention plan of a launch over np shards' heads.
+AttnPlan plan_for(const Dims& d, int64_t np) {
+  return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(np * d.Hd * d.B));
+}
+
+// Split-partial rows a launch over np shards needs.
+size_t split_rows(const Dims& d, int64_t np) {
+  const AttnPlan p = plan_for(d, np);
+  return p.split ? (size_t)(np * d.Hd * d.B) * p.nqt * p.maxseg * p.bq : 0;
+}
+
 AttnWs attn_ws(const Dims& d, size_t base) {
   AttnWs w;
   size_t o = base;
   const size_t act = al((size_t)d.BT * d.h * d.es);
   w.xn = o; o += act;
   w.y = o; o += al((size_t)d.BT * d.h * 4);
-  const int64_t G = acc_group(d);
-  w.q = o; o += al((size_t)d.BT * d.hs * d.es);
+  const int64_t G = acc_group(d), P = attn_launch(d);
+  w.q = o; o += al((size_t)P * d.BT * d.hs * d.es);  // [P*Hd][B*T][d]
   w.o = o; o += al((size_t)d.BT * G * d.hs * d.es);  // [B*T][G*hs]
-  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(qkv_rows(d) * d.h * d.es); }
-  for (int s = 0; s < 2; s++) { w.slotkv[s] = o; o += al(kv_block_elems(d) * d.es); }
+  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al((size_t)P * qkv_rows(d) * d.h * d.es); }
+  for (int s = 0; s < 2; s++) { w.slotkv[s] = o; o += al((size_t)P * kv_block_elems(d) * d.es); }
   for (int s = 0; s < 2; s++) { w.bo[s] = o; o += al((size_t)d.h * G * d.hs * d.es); }  // [h][G*hs]
-  const AttnPlan p = plan_of(d);
-  const size_t nslot = p.split ? (size_t)d.Hd * d.B * p.nqt * p.maxseg * p.bq : 0;
+  size_t nslot = split_rows(d, P);
+  if (d.D % P) nslot = std::max(nslot, split_rows(d, d.D % P));  // the last, shorter launch
   w.op = o; o += al(nslot * d.d * 4);
   w.ml = o; o += al(nslot * 2 * 4);
   w.end = o;
@@ -217,11 +249,12 @@ AttnWs attn_ws(const Dims& d, size_t base) {
 MlpWs mlp_ws(const Dims& d, size_t base) {
   MlpWs w;
   size_t o = base;
-  const int64_t G = acc_group(d);
+  const int64_t G = acc_group(d), P = mlp_launch(d);
   w.xn = o; o += al((size_t)d.BT * d.h * d.es);
   w.y = o; o += al((size_t)d.BT * d.h * 4);
   w.gg = o; o += al((size_t)d.BT * G * d.Fs * d.es);  // [B*T][G*Fs]
-  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(2 * (size_t)d.Fs * d.h * d.es); }
+  // [W1 of the launch's shards | their W3]
+  for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(2 * (size_t)P * d.Fs * d.h * d.es); }
   for (int s = 0; s < 2; s++) { w.bw[s] = o; o += al((size_t)d.h * G * d.Fs * d.es); }  // [h][G*Fs]
   w.end = o;
   return w;
@@ -380,8 +413,10 @@ GemmArgs gemm_base() {
 // QKV projection of this rank's tokens with packed shard w (rows
 // [col0, hs + 2ks) of its first block), scattered to Q (if col0 == 0) and to
 // K/V at the tokens' global positions, Q and K rotated when rope_theta > 0.
-// col0 is 0 or hs.
-int qkv_gemm(Ctx& c, const void* xn, const char* w, int col0, void* q, char* kvslot) {
+// col0 is 0 or hs.  With np > 1 (col0 == 0), w holds np packed Q|K|V blocks
+// back to back; shard u's Q goes to q + u*B*T*hs and its K/V to the kvslot
+// block u.
+int qkv_gemm(Ctx& c, const void* xn, const char* w, int col0, void* q, char* kvslot, int64_t np = 1) {
   const Dims& d = *c.d;
   GemmArgs g = gemm_base();
   g.A = xn;
@@ -389,11 +424,16 @@ int qkv_gemm(Ctx& c, const void* xn, const char* w, int col0, void* q, char* kvs
   g.B = w + (size_t)col0 * d.h * d.es;
   g.ldb = d.h;
   g.M = (int)d.BT;
-  g.N = (int)(qkv_rows(d) - col0);
+  g.N = (int)(np * qkv_rows(d) - col0);
   g.K = (int)d.h;
   g.Q = q;
   g.Kd = kvslot;
   g.Vt = kvslot + kv_v_offset(d) * d.es;
+  if (np > 1) {
+    g.shard_cols = (int)qkv_rows(d);
+    g.q_stride = d.BT * d.hs;
+    g.kv_stride = (int64_t)kv_block_elems(d);
+  }
   g.hs = (int)d.hs;
   g.ks = (int)d.ks;
   g.rope_l2 = d.rope_theta > 0.f ? std::log2((double)d.rope_theta) : 0.0;
@@ -444,55 +484,66 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
   const size_t es = d.es;
   const size_t qkvbytes = qkv_rows(d) * d.h * es;
   const size_t kvbytes = kv_block_elems(d) * es;
-  const int64_t G = acc_group(d);
-  const AttnPlan plan = plan_of(d);
+  const int64_t G = acc_group(d), P = attn_launch(d);
   TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws + L.xn, d.BT, (int)d.h, d.eps, c.s)));
-  for (int64_t j = 0; j < d.D; j++) {  // broadcast iteration j: shard of rank j
-    const int s = (int)(j & 1);
-    const int64_t gi = j / G, gp = j % G;  // accumulation group, position in it
+  // Broadcast iterations j0 .. j0 + np - 1 (shards of ranks j0 ..) per launch.
+  for (int64_t j0 = 0, li = 0; j0 < d.D; j0 += P, li++) {
+    const int64_t np = std::min<int64_t>(P, d.D - j0);
+    const int s = (int)(li & 1);
+    const int64_t gi = j0 / G, gp = j0 % G;  // accumulation group, position in it
     const int gb = (int)(gi & 1);
     char* slotw = ws + L.slotw[s];
     char* slotkv = ws + L.slotkv[s];
     char* bo = ws + L.bo[gb];
-    // ---- copy stream: receive shard j (Q|K|V into the slot, W_O next to
-    // its group's other W_O blocks); the other ranks' K_j/V_j rows are read
-    // in place from kv, or copied next to the rank's own rows when chunk
-    // boundaries do not fall on attention key tiles.
-    if (c.side && j >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeA[s], 0));
+    // ---- copy stream: receive the shards (Q|K|V into the slot, W_O next to
+    // its group's other W_O blocks); the other ranks' K/V rows are read in
+    // place from kv, or copied next to the rank's own rows when chunk
+    // boundaries do not fall on attention key tiles.  One shard per launch
+    // reads the rank's own shard in place.
+    if (c.side && li >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeA[s], 0));
     if (c.side && gp == 0 && gi >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeO[gb], 0));
-    int rc = debug_before_fill(c, slotw, qkvbytes);
+    int rc = debug_before_fill(c, slotw, np * qkvbytes);
     if (rc) return rc;
     if (c.d->flags & TSP_F_POISON_SLOTS) {
       const uint32_t nan = d.dt == BF16 ? 0x7FC07FC0u : 0x7FC00000u;
-      HIP_TRY(launch_fill32(slotkv, nan, kvbytes, c.cs));
+      HIP_TRY(launch_fill32(slotkv, nan, np * kvbytes, c.cs));
       if (gp == 0) HIP_TRY(launch_fill32(bo, nan, (size_t)d.h * G * d.hs * es, c.cs));
     }
-    if (j != d.r) HIP_TRY(hipMemcpyAsync(slotw, w_attn[j], qkvbytes, hipMemcpyDeviceToDevice, c.cs));
-    HIP_TRY(hipMemcpy2DAsync(bo + gp * d.hs * es, G * d.hs * es, (const char*)w_attn[j] + qkvbytes,
-                             d.hs * es, d.hs * es, d.h, hipMemcpyDeviceToDevice, c.cs));
-    const char* kvj = (const char*)kv + (size_t)j * kvbytes;
-    if (!kv_in_place(d)) {
-      rc = copy_remote_kv(c, kvj, slotkv);
-      if (rc) return rc;
+    for (int64_t u = 0; u < np; u++) {
+      const int64_t j = j0 + u;
+      if (np > 1 || j != d.r)
+        HIP_TRY(hipMemcpyAsync(slotw + u * qkvbytes, w_attn[j], qkvbytes, hipMemcpyDeviceToDevice, c.cs));
+      HIP_TRY(hipMemcpy2DAsync(bo + (gp + u) * d.hs * es, G * d.hs * es, (const char*)w_attn[j] + qkvbytes,
+                               d.hs * es, d.hs * es, d.h, hipMemcpyDeviceToDevice, c.cs));
+      if (!kv_in_place(d)) {
+        rc = copy_remote_kv(c, (const char*)kv + (size_t)j * kvbytes, slotkv + u * kvbytes);
+        if (rc) return rc;
+      }
     }
     if (c.side) {
       HIP_TRY(hipEventRecord(c.ev->readyA[s], c.cs));
       HIP_TRY(hipStreamWaitEvent(c.s, c.ev->readyA[s], 0));
     }
     // ---- compute stream
-    const char* w = j == d.r ? (const char*)w_attn[d.r] : slotw;
-    TIMED(c, TSP_K_QKV, rc = qkv_gemm(c, ws + L.xn, w, 0, ws + L.q, slotkv));
+    const char* w = np == 1 && j0 == d.r ? (const char*)w_attn[d.r] : slotw;
+    TIMED(c, TSP_K_QKV, rc = qkv_gemm(c, ws + L.xn, w, 0, ws + L.q, slotkv, np));
     if (rc) return rc;
+    const AttnPlan plan = plan_for(d, np);
     AttnArgs a;
     memset(&a, 0, sizeof a);
     a.Q = ws + L.q;
     a.K = slotkv;
     a.Vt = slotkv + kv_v_offset(d) * es;
     if (kv_in_place(d)) {
+      const char* kvj = (const char*)kv + (size_t)j0 * kvbytes;
       a.Kg = kvj;
       a.Vtg = kvj + kv_v_offset(d) * es;
     }
-    a.O = ws + L.o + gp * d.hs * es;  // this shard's columns of the group's [T][G*hs]
+    if (np > 1) {
+      a.kvh_per_shard = (int)d.Hkd;
+      a.shard_stride = (int64_t)kv_block_elems(d);
+    }
+    a.O = ws + L.o + gp * d.hs * es;  // these shards' columns of the group's [T][G*hs]
     a.Op = (float*)(ws + L.op);
     a.ML = (float*)(ws + L.ml);
     a.T = d.T;
@@ -502,7 +553,7 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     a.ldo = (int)(G * d.hs);
     a.rank = (int)d.r;
     a.fold = (int)d.D;
-    a.Hd = (int)d.Hd;
+    a.Hd = (int)(np * d.Hd);
     a.grp = (int)(d.H / d.Hkv);
     a.nqt = plan.nqt;
     a.lseg = plan.lseg;
@@ -514,10 +565,10 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     a.sum_cap = (d.flags & TSP_F_RESCALE_TEST) ? 2.0f : 18446744073709551616.0f;
     TIMED(c, TSP_K_ATTN, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 0, c.s)));
     if (plan.split) TIMED(c, TSP_K_MERGE, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 1, c.s)));
-    if (gp == G - 1 || j == d.D - 1) {  // group complete: one O projection over its shards
+    if (gp + np == G || j0 + np == d.D) {  // group complete: one O projection over its shards
       TIMED(c, TSP_K_OPROJ,
-            rc = acc_gemm(c, ws + L.o, (gp + 1) * d.hs, G * d.hs, bo, (float*)(ws + L.y), gi == 0,
-                          j == d.D - 1, x, x1));
+            rc = acc_gemm(c, ws + L.o, (gp + np) * d.hs, G * d.hs, bo, (float*)(ws + L.y), gi == 0,
+                          j0 + np == d.D, x, x1));
       if (rc) return rc;
       if (c.side) HIP_TRY(hipEventRecord(c.ev->freeO[gb], c.s));
     }
@@ -531,32 +582,43 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
   const Dims& d = *c.d;
   char* ws = c.ws;
   const size_t es = d.es;
-  const size_t w13bytes = 2 * (size_t)d.Fs * d.h * es;
-  const int64_t G = acc_group(d);
+  const size_t wbytes = (size_t)d.Fs * d.h * es;  // one shard's W1 (or W3) block
+  const int64_t G = acc_group(d), P = mlp_launch(d);
   TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.BT, (int)d.h, d.eps, c.s)));
-  for (int64_t t = 0; t < d.D; t++) {  // ring step t: shard (r + t) mod D
-    const int64_t j = (d.r + t) % d.D;
-    const int s = (int)(t & 1);
-    const int64_t gi = t / G, gp = t % G;
+  // Ring steps t0 .. t0 + np - 1 (shards (r + t) mod D) per launch.
+  for (int64_t t0 = 0, li = 0; t0 < d.D; t0 += P, li++) {
+    const int64_t np = std::min<int64_t>(P, d.D - t0);
+    const int s = (int)(li & 1);
+    const int64_t gi = t0 / G, gp = t0 % G;
     const int gb = (int)(gi & 1);
     char* bw = ws + L.bw[gb];
     const char* w = (const char*)w_mlp[d.r];
-    // ---- copy stream: W1|W3 of a remote shard into the slot; every shard's
-    // W2 block next to its group's others.
-    if (c.side && t >= 3) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeM[s], 0));
+    // ---- copy stream: W1|W3 of the launch's shards into the slot (the own
+    // shard is read in place when it runs alone); every shard's W2 block
+    // next to its group's others.  With one shard per launch, ring step 0
+    // uses no slot, so slot 0 is first refilled at step 2 and slot 1 at 3.
+    const bool slot_reused = np == 1 && P == 1 ? t0 >= 3 : li >= 2;
+    if (c.side && slot_reused) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeM[s], 0));
     if (c.side && gp == 0 && gi >= 2) HIP_TRY(hipStreamWaitEvent(c.cs, c.ev->freeW[gb], 0));
-    if (t > 0) {
+    if (P > 1 || t0 > 0) {
       char* slotw = ws + L.slotw[s];
-      int rc = debug_before_fill(c, slotw, w13bytes);
+      int rc = debug_before_fill(c, slotw, 2 * np * wbytes);
       if (rc) return rc;
-      HIP_TRY(hipMemcpyAsync(slotw, w_mlp[j], w13bytes, hipMemcpyDeviceToDevice, c.cs));
+      for (int64_t u = 0; u < np; u++) {
+        const char* src = (const char*)w_mlp[(d.r + t0 + u) % d.D];
+        HIP_TRY(hipMemcpyAsync(slotw + u * wbytes, src, wbytes, hipMemcpyDeviceToDevice, c.cs));
+        HIP_TRY(hipMemcpyAsync(slotw + (np + u) * wbytes, src + wbytes, wbytes, hipMemcpyDeviceToDevice, c.cs));
+      }
       w = slotw;
     }
     if ((c.d->flags & TSP_F_POISON_SLOTS) && gp == 0)
       HIP_TRY(launch_fill32(bw, d.dt == BF16 ? 0x7FC07FC0u : 0x7FC00000u,
                             (size_t)d.h * G * d.Fs * es, c.cs));
-    HIP_TRY(hipMemcpy2DAsync(bw + gp * d.Fs * es, G * d.Fs * es, (const char*)w_mlp[j] + w13bytes,
-                             d.Fs * es, d.Fs * es, d.h, hipMemcpyDeviceToDevice, c.cs));
+    for (int64_t u = 0; u < np; u++) {
+      const char* src = (const char*)w_mlp[(d.r + t0 + u) % d.D];
+      HIP_TRY(hipMemcpy2DAsync(bw + (gp + u) * d.Fs * es, G * d.Fs * es, src + 2 * wbytes, d.Fs * es,
+                               d.Fs * es, d.h, hipMemcpyDeviceToDevice, c.cs));
+    }
     if (c.side) {
       HIP_TRY(hipEventRecord(c.ev->readyM[s], c.cs));
       HIP_TRY(hipStreamWaitEvent(c.s, c.ev->readyM[s], 0));
@@ -566,19 +628,19 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
     g.A = ws + L.xn;
     g.lda = d.h;
     g.B = w;
-    g.B3 = w + (size_t)d.Fs * d.h * es;
+    g.B3 = w + np * wbytes;
     g.ldb = d.h;
     g.M = (int)d.BT;
-    g.N = (int)d.Fs;
+    g.N = (int)(np * d.Fs);
     g.K = (int)d.h;
-    g.C = ws + L.gg + gp * d.Fs * es;  // this shard's columns of the group's [T][G*Fs]
+    g.C = ws + L.gg + gp * d.Fs * es;  // these shards' columns of the group's [T][G*Fs]
     g.ldc = G * d.Fs;
     TIMED(c, TSP_K_W13, HIP_TRY(launch_gemm(d.dt, EPI_SWIGLU, g, c.s)));
     int rc = 0;
-    if (gp == G - 1 || t == d.D - 1) {  // group complete: one W2 projection over its shards
+    if (gp + np == G || t0 + np == d.D) {  // group complete: one W2 projection over its shards
       TIMED(c, TSP_K_W2,
-            rc = acc_gemm(c, ws + L.gg, (gp + 1) * d.Fs, G * d.Fs, bw, (float*)(ws + L.y), gi == 0,
-                          t == d.D - 1, x1, out));
+            rc = acc_gemm(c, ws + L.gg, (gp + np) * d.Fs, G * d.Fs, bw, (float*)(ws + L.y), gi == 0,
+                          t0 + np == d.D, x1, out));
       if (rc) return rc;
       if (c.side) HIP_TRY(hipEventRecord(c.ev->freeW[gb], c.s));
     }
@@ -616,9 +678,10 @@ struct MlpBwdWs {
 
 // Attention-core backward: the recomputed forward output of the group, the
 // per-row log-sum-exp and rowsum(dO * O), and the forward's split partials.
-// Transposed copies for the backward kernels: Q and dO [d][Hd * BTp], K
-// [d][Hkd * B*S], V by rows [B*S][Hkd * d].
-int64_t bt_pitch(const Dims& d) { return (d.BT + 7) / 8 * 8; }
+// Transposed copies for the backward kernels: Q and dO [d][Hd][B][Tp], K
+// [d][Hkd][B][Sp] (each sequence padded with zeros to a multiple of 64
+// rows), V by rows [B*S][Hkd * d].
+int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 struct AttnBwdWs {
   size_t o, lse, dl, qt, dot, kt, vr, op, ml, end;
 };
@@ -628,9 +691,9 @@ AttnBwdWs attn_bwd_ws(const Dims& d, size_t base = 0) {
   w.o = o; o += al((size_t)d.BT * d.hs * d.es);
   w.lse = o; o += al((size_t)d.Hd * d.BT * 4);
   w.dl = o; o += al((size_t)d.Hd * d.BT * 4);
-  w.qt = o; o += al((size_t)d.d * d.Hd * bt_pitch(d) * d.es);
-  w.dot = o; o += al((size_t)d.d * d.Hd * bt_pitch(d) * d.es);
-  w.kt = o; o += al((size_t)d.d * d.Hkd * d.BS * d.es);
+  w.qt = o; o += al((size_t)d.d * d.Hd * d.B * pad64(d.T) * d.es);
+  w.dot = o; o += al((size_t)d.d * d.Hd * d.B * pad64(d.T) * d.es);
+  w.kt = o; o += al((size_t)d.d * d.Hkd * d.B * pad64(d.S) * d.es);
   w.vr = o; o += al((size_t)d.d * d.Hkd * d.BS * d.es);
   const AttnPlan p = plan_of(d);
   const size_t nslot = p.split ? (size_t)d.Hd * d.B * p.nqt * p.maxseg * p.bq : 0;
@@ -843,19 +906,19 @@ int attn_core_grads(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv, c
   b.Hkd = (int)d.Hkd;
   b.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
   b.scale = (float)(1.0 / std::sqrt((double)d.d));
-  b.BTp = bt_pitch(d);
+  b.Tp = pad64(d.T);
+  b.Sp = pad64(d.S);
   b.Qt = w + L.qt;
   b.dOt = w + L.dot;
   b.Kt = w + L.kt;
   b.Vr = w + L.vr;
-  const int64_t ldt = d.Hd * b.BTp;
-  for (int64_t t = 0; t < d.Hd; t++) {
-    HIP_TRY(launch_transpose(d.dt, (const char*)q + t * d.BT * d.d * d.es, w + L.qt + t * b.BTp * d.es, d.BT,
-                             d.d, d.d, ldt, s));
-    HIP_TRY(launch_transpose(d.dt, (const char*)dout + t * d.d * d.es, w + L.dot + t * b.BTp * d.es, d.BT, d.d,
-                             ldo, ldt, s));
-  }
-  HIP_TRY(launch_transpose(d.dt, kv, w + L.kt, d.Hkd * d.BS, d.d, d.d, d.Hkd * d.BS, s));
+  // matrix z = t * B + b of each transposed copy is head (or K/V head) t, sequence b
+  HIP_TRY(launch_transpose_pad(d.dt, q, w + L.qt, d.T, b.Tp, d.d, d.d, d.Hd * d.B * b.Tp, d.Hd * d.B, d.B,
+                               d.BT * d.d, d.T * d.d, s));
+  HIP_TRY(launch_transpose_pad(d.dt, dout, w + L.dot, d.T, b.Tp, d.d, ldo, d.Hd * d.B * b.Tp, d.Hd * d.B, d.B,
+                               d.d, d.T * ldo, s));
+  HIP_TRY(launch_transpose_pad(d.dt, kv, w + L.kt, d.S, b.Sp, d.d, d.d, d.Hkd * d.B * b.Sp, d.Hkd * d.B, d.B,
+                               d.BS * d.d, d.S * d.d, s));
   HIP_TRY(launch_transpose(d.dt, vt, w + L.vr, d.Hkd * d.d, d.BS, d.BS, d.Hkd * d.d, s));
   for (int part = 0; part < 3; part++) HIP_TRY(launch_attn_bwd((int)d.d, b, part, s));
   return TSP_OK;

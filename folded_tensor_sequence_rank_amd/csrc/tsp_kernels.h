@@ -37,10 +37,15 @@ struct GemmArgs {
   // is [kv heads][hd][B*S]; local row m = b*T + i of sequence b sits at row
   // b*S + zigzag(i).  rope_l2 = log2(theta) > 0 rotates Q and K at the row's
   // position in its sequence (0: no rotation).
+  // Several shards in one launch (shard_cols > 0): column c belongs to shard
+  // c / shard_cols, whose Q, K and Vt start q_stride and kv_stride elements
+  // further on per shard.
   void* Q;
   void* Kd;
   void* Vt;
   int hs, ks, hd, col0;
+  int shard_cols;
+  int64_t q_stride, kv_stride;
   double rope_l2;
   int64_t S, T;
   int64_t chunk;
@@ -66,6 +71,11 @@ struct AttnArgs {
   int ldo, rank, fold, Hd;
   int batch;
   int grp;  // query heads per K/V head (0 means 1)
+  // Several shards in one launch (kvh_per_shard > 0): K/V head kvh is head
+  // kvh % kvh_per_shard of shard kvh / kvh_per_shard, whose K, Vt, Kg and Vtg
+  // blocks start shard_stride elements further on per shard.
+  int kvh_per_shard;
+  int64_t shard_stride;
   int nqt, lseg, maxseg, nitems;
   float scale_log2;  // log2(e) / sqrt(HD)
   float sum_cap;     // largest 32-key block sum of exponentials before the reference max is raised
@@ -97,6 +107,12 @@ hipError_t launch_clock_probe(uint64_t* out, int n, uint64_t interval, hipStream
 // Backward of the MLP half.
 hipError_t launch_transpose(Dtype dt, const void* in, void* out, int64_t R, int64_t C, int64_t ldi,
                             int64_t ldo, hipStream_t s);
+// Batched transpose into a row-padded layout: for z in [0, Z), r in [0, Rp),
+// c in [0, C): out[c * ldo + z * Rp + r] = r < R ? in[zoff + r * ldi + c] : 0,
+// zoff = (z / zdiv) * s1 + (z % zdiv) * s0.  Rp is a multiple of 64.
+hipError_t launch_transpose_pad(Dtype dt, const void* in, void* out, int64_t R, int64_t Rp, int64_t C,
+                                int64_t ldi, int64_t ldo, int64_t Z, int64_t zdiv, int64_t s1, int64_t s0,
+                                hipStream_t s);
 // ab: [rows][2F] fp32, a = n W1 then b = n W3; dg: [rows][F] fp32.
 hipError_t launch_swiglu_bwd(Dtype dt, const float* ab, const float* dg, void* dab, void* g, int64_t rows,
                              int64_t F, hipStream_t s);
@@ -139,11 +155,11 @@ struct AttnBwdArgs {
   float* dQ;         // [Hd][B*T][HD]
   float* dK;         // [Hkd][B*S][HD]
   float* dV;         // [Hkd][B*S][HD]
-  const void* Qt;    // [HD][Hd*BTp]: head t's queries at columns [t*BTp, t*BTp + B*T)
-  const void* dOt;   // [HD][Hd*BTp]: dO, the same way
-  const void* Kt;    // [HD][Hkd*B*S]
+  const void* Qt;    // [HD][Hd][B][Tp]: Q transposed, each sequence padded with zero rows to Tp
+  const void* dOt;   // [HD][Hd][B][Tp]: dO, the same way
+  const void* Kt;    // [HD][Hkd][B][Sp]: K transposed, each sequence padded with zero keys to Sp
   const void* Vr;    // [B*S][Hkd*HD]: V by rows
-  int64_t T, S, chunk, BTp;
+  int64_t T, S, chunk, Tp, Sp;  // Tp, Sp: T and S rounded up to a multiple of 64
   int ldo, rank, fold, batch, grp, Hd, Hkd;
   float scale_log2, scale;
 };

@@ -890,8 +890,18 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
         for (int q = 0; q < 4; q++) {
           if (!ok[q]) continue;
           const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
-          // hs, ks and hd are multiples of 4, so the four columns share part and head.
-          const int c = n + g.col0;
+          // hs, ks and hd are multiples of 4, so the four columns share shard, part and head.
+          int c = n + g.col0;
+          T* qb = (T*)g.Q;
+          T* kb = (T*)g.Kd;
+          T* vb = (T*)g.Vt;
+          if (g.shard_cols > 0) {
+            const int u = c / g.shard_cols;
+            c -= u * g.shard_cols;
+            qb += u * g.q_stride;
+            kb += u * g.kv_stride;
+            vb += u * g.kv_stride;
+          }
           const int part = c < g.hs ? 0 : (c < g.hs + g.ks ? 1 : 2);
           const int rem = part == 0 ? c : c - g.hs - (part - 1) * g.ks;
           const int head = rem / g.hd;
@@ -899,12 +909,11 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
           float o4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
           if (part < 2 && g.rope_l2 > 0.0) rope_pairs(o4, e, spos, g.rope_l2 / g.hd);
           if (part == 0) {
-            store4<T>((T*)g.Q + ((int64_t)head * qrows + m) * g.hd + e, o4[0], o4[1], o4[2], o4[3]);
+            store4<T>(qb + ((int64_t)head * qrows + m) * g.hd + e, o4[0], o4[1], o4[2], o4[3]);
           } else if (part == 1) {
-            store4<T>((T*)g.Kd + ((int64_t)head * krows + pos) * g.hd + e, o4[0], o4[1], o4[2],
-                      o4[3]);
+            store4<T>(kb + ((int64_t)head * krows + pos) * g.hd + e, o4[0], o4[1], o4[2], o4[3]);
           } else {
-            T* pv = (T*)g.Vt + ((int64_t)head * g.hd + e) * krows + pos;
+            T* pv = vb + ((int64_t)head * g.hd + e) * krows + pos;
 #pragma unroll
             for (int t = 0; t < 4; t++) pv[(int64_t)t * krows] = from_f<T>(o4[t]);
           }
@@ -1020,6 +1029,15 @@ __device__ __attribute__((always_inline)) inline int kv_head(const AttnArgs& a, 
   return a.grp > 1 ? head / a.grp : head;
 }
 
+// Offset (elements) of K/V head kvh's shard in K, Vt, Kg and Vtg; kvh becomes
+// the head's index within its shard.
+__device__ __attribute__((always_inline)) inline int64_t kv_shard_base(const AttnArgs& a, int& kvh) {
+  if (a.kvh_per_shard <= 0) return 0;
+  const int u = kvh / a.kvh_per_shard;
+  kvh -= u * a.kvh_per_shard;
+  return (int64_t)u * a.shard_stride;
+}
+
 // Workgroup -> (head, sequence sb, work item): heads innermost, then the
 // sequences of the micro-batch, then the items.
 __device__ __attribute__((always_inline)) inline void block_item(const AttnArgs& a, int& head, int& sb,
@@ -1100,10 +1118,11 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   const int kend_w = wok ? (int)zig(min(T32, row0 + 32 * QB) - 1, C32, a.rank, a.fold) + 1 : 0;
   const int qmin_w = wok ? (int)zig(row0, C32, a.rank, a.fold) : 0;
 
-  const int kvh = kv_head(a, head);
+  int kvh = kv_head(a, head);
+  const int64_t kvb = kv_shard_base(a, kvh);
   const T* Qh = (const T*)a.Q + ((int64_t)head * BT + (int64_t)sb * a.T) * HD;
-  const T* Kh = (const T*)a.K + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD;
-  const T* Vh = (const T*)a.Vt + (int64_t)kvh * HD * BS + (int64_t)sb * a.S;
+  const T* Kh = (const T*)a.K + kvb + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD;
+  const T* Vh = (const T*)a.Vt + kvb + (int64_t)kvh * HD * BS + (int64_t)sb * a.S;
 
   frag qf[QB][QK];
 #pragma unroll
@@ -1135,8 +1154,8 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
   // V^T rows d (64 keys each).
   const bool split_src = a.Kg != nullptr;
   const OwnChunks own_tile(a);
-  const T* Kgh = split_src ? (const T*)a.Kg + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD : Kh;
-  const T* Vgh = split_src ? (const T*)a.Vtg + (int64_t)kvh * HD * BS + (int64_t)sb * a.S : Vh;
+  const T* Kgh = split_src ? (const T*)a.Kg + kvb + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD : Kh;
+  const T* Vgh = split_src ? (const T*)a.Vtg + kvb + (int64_t)kvh * HD * BS + (int64_t)sb * a.S : Vh;
   constexpr int KJ = (KI + 3) / 4, VJ = (VI + 3) / 4;  // wave loads per tile per wave
   int krow[KJ], voff[VJ], vkey[VJ];
   uint32_t koff[KJ];
@@ -1461,10 +1480,11 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   const int kend_w = wok ? (int)zig(min(T32, row0 + 32) - 1, C32, a.rank, a.fold) + 1 : 0;
   const int qmin_w = wok ? (int)zig(row0, C32, a.rank, a.fold) : 0;
 
-  const int kvh = kv_head(a, head);
+  int kvh = kv_head(a, head);
+  const int64_t kvb = kv_shard_base(a, kvh);
   const T* Qh = (const T*)a.Q + ((int64_t)head * BT + (int64_t)sb * a.T) * HD;
-  const T* Kh = (const T*)a.K + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD;
-  const T* Vh = (const T*)a.Vt + (int64_t)kvh * HD * BS + (int64_t)sb * a.S;
+  const T* Kh = (const T*)a.K + kvb + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD;
+  const T* Vh = (const T*)a.Vt + kvb + (int64_t)kvh * HD * BS + (int64_t)sb * a.S;
   frag qf[QK];
 #pragma unroll
   for (int ks = 0; ks < QK; ks++)
@@ -1473,8 +1493,8 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   // Direct loads, as in attn_kernel.
   const bool split_src = a.Kg != nullptr;
   const OwnChunks own_tile(a);
-  const T* Kgh = split_src ? (const T*)a.Kg + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD : Kh;
-  const T* Vgh = split_src ? (const T*)a.Vtg + (int64_t)kvh * HD * BS + (int64_t)sb * a.S : Vh;
+  const T* Kgh = split_src ? (const T*)a.Kg + kvb + ((int64_t)kvh * BS + (int64_t)sb * a.S) * HD : Kh;
+  const T* Vgh = split_src ? (const T*)a.Vtg + kvb + (int64_t)kvh * HD * BS + (int64_t)sb * a.S : Vh;
   int krow[KJ], vkey[VJ];
   uint32_t koff[KJ], voff[VJ];
 #pragma unroll
@@ -1938,6 +1958,28 @@ __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ in
   }
 }
 
+// The batched, row-padded form: block (x, y, z) moves rows [64 x, 64 x + 64)
+// and columns [64 y, 64 y + 64) of matrix z, writing zeros for rows >= R.
+template <typename T>
+__global__ void __launch_bounds__(256) transpose_pad_kernel(const T* __restrict__ in, T* __restrict__ out,
+                                                            int64_t R, int64_t Rp, int64_t C, int64_t ldi,
+                                                            int64_t ldo, int64_t zdiv, int64_t s1, int64_t s0) {
+  __shared__ T tile[64][65];
+  const int64_t z = blockIdx.z;
+  const T* src = in + (z / zdiv) * s1 + (z % zdiv) * s0;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? src[r * ldi + c] : from_f<T>(0.f);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rp) out[c * ldo + z * Rp + r] = tile[tx][i];
+  }
+}
+
 // SwiGLU backward per element, a = n W1 and b = n W3 given in fp32 side by
 // side ([rows][2F]: a in columns [0, F), b in [F, 2F)) and dg = dout W2^T in
 // fp32 [rows][F]: da = dg b silu'(a), db = dg silu(a) into
@@ -2090,88 +2132,73 @@ __global__ void __launch_bounds__(256) qkv_grad_pack_kernel(const float* __restr
 //   dV = P^T dO,  dK = dS^T Q / sqrt(d),  dQ = dS K / sqrt(d).
 // Two kernels, neither with atomics: one owns a key block and walks the query
 // blocks that can see it (dK, dV), the other owns a query block and walks
-// its keys (dQ, recomputing P and dP).  Every product runs on the 32x32x16
-// bf16 MFMA with both operands read from LDS contiguous in k, so a block that
-// is contracted over its rows in one product and over its columns in another
-// is staged in both layouts, the second from a transposed copy made in HBM
-// before the kernels run (vector loads only, no element-wise transposes).
+// its keys (dQ, recomputing P and dP).
+//
+// Every product runs on the 32x32x16 bf16 MFMA.  A lane of its 32x32 result
+// holds one column and 16 rows; a lane of its first operand holds one row
+// and 8 consecutive k.  So a wave's P (or dS) block, formed with the keys
+// (queries in the dQ kernel) as columns, is already the first operand of
+// the next product, contracted over the rows, provided the rows come out in
+// the right order: the score product reads its first operand's rows through
+// the permutation perm_rows, after which register i of a lane holds row
+// 16 (i / 8) + 8 (lane / 32) + i % 8.  P and dS never pass through LDS.
+//
+// Tiles reach LDS by buffer->LDS loads, double-buffered, one barrier per
+// block: rows past a tile's valid range read as zero through the buffer's
+// range check.  The second operand of a product over the rows of Q, dO or K
+// comes from a transposed copy made in HBM before the kernels run, padded
+// per sequence to a multiple of 64 rows with zeros, so that those tiles are
+// always whole.
 // ---------------------------------------------------------------------------
-constexpr int kAB = 64;       // rows of a query or key block
-constexpr int kTP = kAB + 8;  // LDS row pitch of the transposed tiles (elements)
-constexpr int kBK2 = 128;     // keys per work-group of the dK/dV kernel
-constexpr int kBQ2 = 128;     // query rows per work-group of the dQ kernel
+constexpr int kAB = 64;    // rows of a query or key block
+constexpr int kBK2 = 128;  // keys per work-group of the dK/dV kernel
+constexpr int kBQ2 = 128;  // query rows per work-group of the dQ kernel
 
 // Position of local row i of a rank's zigzag rows (chunks r and 2D-1-r).
 __device__ inline int64_t zz_pos(int64_t i, int64_t C, int r, int D) {
   return i < C ? (int64_t)r * C + i : (2 * (int64_t)D - 1 - r) * C + (i - C);
 }
 
-// c += A B for one 32x32 block with B's fragments already in registers
-// (fb[k / 16] for k in [0, kdim)).
-template <int KS>
-__device__ inline void mma_regs_b(f32x16& c, const bf16* A, int lda, const bf16x8* fb, int lane) {
-  const int r = lane & 31, kh = (lane >> 5) * 8;
-#pragma unroll
-  for (int k = 0; k < KS; k++) c = MF<bf16>::mma(*(const bf16x8*)(A + r * lda + 16 * k + kh), fb[k], c);
+// First local row of rank r whose position reaches p (T if none): positions
+// grow with the local row, so the causal test key <= pos(row) is
+// row >= first_row_at(key).
+__device__ inline int64_t first_row_at(int64_t p, int64_t C, int r, int D, int64_t T) {
+  const int64_t ca = (int64_t)r * C, cb = (2 * (int64_t)D - 1 - r) * C;
+  return p <= ca ? 0 : p < ca + C ? p - ca : p <= cb ? C : p < cb + C ? C + p - cb : T;
 }
 
-// NT blocks c[u] += A B_u sharing the A operand (read once per k step); B_u
-// starts at B + u * bstep.
-template <int NT>
-__device__ inline void lds_mma_shared_a(f32x16* c, const bf16* A, int lda, const bf16* B, int ldb, int bstep,
-                                        int kdim, int lane) {
-  const int r = lane & 31, kh = (lane >> 5) * 8;
-  for (int k = 0; k < kdim; k += 16) {
-    const bf16x8 fa = *(const bf16x8*)(A + r * lda + k + kh);
+// Row read by first-operand lane row rho of a score product: swaps the middle
+// two groups of four in every 16 (0-3, 8-11, 4-7, 12-15), so that result
+// register i of a lane holds row 16 (i / 8) + 8 (lane / 32) + i % 8.
+__device__ inline int perm_rows(int rho) { return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1); }
+
+// 4 bytes per lane from buffer offset voff into LDS at lds + 4*lane.
+__device__ inline void buffer_to_lds4(brsrc r, void* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, voff, 0, 0, 0);
+#endif
+}
+
+// A tile of R rows of RB bytes (row r at byte r * ld of the buffer) into LDS
+// rows of RB bytes, 16-byte chunks XOR-swizzled with swz<RB / 16>: each wave
+// instruction moves 1 KB, spread over the work-group's NW waves.
+template <int R, int RB, int NW>
+__device__ inline void dma_tile(brsrc src, uint32_t ld, char* lds, int w, int lane) {
+  constexpr int NCH = RB / 16, RPI = 1024 / RB, NI = R * RB / 1024;
+  static_assert(NI % NW == 0, "the tile must split evenly over the waves");
 #pragma unroll
-    for (int u = 0; u < NT; u++) c[u] = MF<bf16>::mma(fa, *(const bf16x8*)(B + u * bstep + r * ldb + k + kh), c[u]);
+  for (int j = 0; j < NI / NW; j++) {
+    const int ins = w + NW * j;
+    const int row = ins * RPI + lane / NCH;
+    buffer_to_lds16(src, lds + ins * 1024, (uint32_t)row * ld + (uint32_t)swz<NCH>(lane % NCH, row) * 16, 0);
   }
 }
 
-// Fragments of rows [0, 32) x k in [0, 16*KS) of an LDS block (pitch ld) as
-// an MFMA operand.
-template <int KS>
-__device__ inline void load_frags(bf16x8* f, const bf16* X, int ld, int lane) {
-  const int r = lane & 31, kh = (lane >> 5) * 8;
-#pragma unroll
-  for (int k = 0; k < KS; k++) f[k] = *(const bf16x8*)(X + r * ld + 16 * k + kh);
+// The 16 bytes at logical chunk c of row r of such a tile.
+template <int RB>
+__device__ inline bf16x8 lds_chunk(const char* tile, int r, int c) {
+  return *(const bf16x8*)(tile + r * RB + swz<RB / 16>(c, r) * 16);
 }
-
-// A tile of R rows x W columns (W a multiple of 8) of a bf16 matrix with row
-// stride ld, held in registers between its global load and its LDS store so
-// that the load of the next tile overlaps the current tile's products.
-// Element (i, j) is read when i < nr and j < nc, else zero.
-template <int R, int W, int NTH = 256>
-struct TileRegs {
-  static constexpr int NV = R * W / 8 / NTH;
-  u32x4 v[NV];
-  __device__ inline void load(const bf16* src, int64_t ld, int nr, int nc, int tid) {
-#pragma unroll
-    for (int u = 0; u < NV; u++) {
-      const int e = tid + NTH * u, row = e / (W / 8), c = (e % (W / 8)) * 8;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      const bf16* p = src + row * ld + c;
-      if (row < nr && c < nc) {
-        if (c + 8 <= nc && ((uintptr_t)p & 15) == 0) {
-          x = *(const u32x4*)p;
-        } else {
-          bf16 t8[8];
-#pragma unroll
-          for (int j = 0; j < 8; j++) t8[j] = c + j < nc ? p[j] : (bf16)0.f;
-          x = *(const u32x4*)t8;
-        }
-      }
-      v[u] = x;
-    }
-  }
-  __device__ inline void store(bf16* dst, int pitch, int tid) const {
-#pragma unroll
-    for (int u = 0; u < NV; u++) {
-      const int e = tid + NTH * u, row = e / (W / 8), c = (e % (W / 8)) * 8;
-      *(u32x4*)(dst + row * pitch + c) = v[u];
-    }
-  }
-};
 
 // Dl = rowsum(dO * O) per head and row; one wave per (head, row).
 template <int HD>
@@ -2189,151 +2216,175 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(AttnBwdArgs a) {
   if (lane == 0) a.Dl[item] = s;
 }
 
-// P and dS of the wave's 32x32 block of the scores (rows qh of the query
-// block, columns kh of the key block), in place.
-__device__ inline void probs_and_ds(f32x16& s, f32x16& dp, const float* ls, const float* dl, int64_t q0,
-                                    int64_t k0, int qh, int kh, int lane, const AttnBwdArgs& a) {
-  const int64_t key = k0 + 32 * kh + (lane & 31);
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int m = 32 * qh + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    const int64_t qi = q0 + m;
-    const bool ok = qi < a.T && key <= zz_pos(qi, a.chunk, a.rank, a.fold);
-    const float p = ok ? fast_exp2(s[i] * a.scale_log2 - ls[m]) : 0.f;
-    s[i] = p;
-    dp[i] = p * (dp[i] - dl[m]);
-  }
-}
-
-// One work-group per (64-key block, K/V head, sequence): dK and dV of those
+// One work-group per (128-key block, K/V head, sequence): dK and dV of those
 // keys, summed over the head's query heads and every query row of the rank
-// that attends to them.  Transposed copies: Qt [Hd][HD][BTp] and dOt (same),
-// Vr [B*S][Hkd*HD] (V by rows).
+// that attends to them.  Eight waves: wave (kh, qh) owns keys 32 kh.. of the
+// block, with K and V in registers, and queries 32 qh.. of each 64-row query
+// block; it sums dK and dV of its keys over its queries in registers, and
+// the two query halves are added once at the end.  Per block: Q, dO (rows)
+// and Q^T, dO^T (from Qt, dOt [HD][Hd][B][Tp]), with the rows' LSE and Dl.
 template <int HD>
 __global__ void __launch_bounds__(512) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
-  constexpr int P = HD + 8;
-  constexpr int NT = HD / 64;  // 32x32 output blocks of dK (and of dV) per wave
-  // Eight waves over 128 keys: each 64-row query block staged in LDS serves
-  // twice the keys of a 64-key block.  K and V pass through LDS once, into
-  // registers (the wave's 32 keys), in the space the loop's tiles use later.
-  constexpr int QS = 0, DOS = QS + kAB * P, QT = DOS + kAB * P, DOT = QT + HD * kTP, PT = DOT + HD * kTP,
-                DST = PT + kBK2 * kTP, NEL = DST + kBK2 * kTP;
-  static_assert(2 * kBK2 * P <= NEL, "K and V staging must fit in the loop's space");
-  __shared__ __attribute__((aligned(16))) bf16 sm[NEL];
-  __shared__ float ls[kAB], dl[kAB];
-  bf16* const Qs = sm + QS;
-  bf16* const dOs = sm + DOS;
-  bf16* const Qt = sm + QT;
-  bf16* const dOt = sm + DOT;
-  bf16* const Pt = sm + PT;
-  bf16* const dSt = sm + DST;
+  constexpr int RB = HD * 2;         // bytes of a row of a row-major tile
+  constexpr int TB = kAB * HD * 2;   // bytes of a 64 x HD tile, either layout
+  constexpr int NKB = HD / 32;       // 32-wide blocks of the head dimension
+  constexpr int KS = HD / 16;        // k steps of a product over the head dimension
+  static_assert(2 * kBK2 * RB <= 8 * TB, "K and V staging must fit in the loop's space");
+  __shared__ __attribute__((aligned(1024))) char sm[2 * 4 * TB];  // two buffers of [Q | dO | Q^T | dO^T]
+  __shared__ float lsd[2][2][kAB];                                // per buffer: the rows' LSE, Dl
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int kh = w >> 1, qh = w & 1;
   const int64_t k0 = (int64_t)blockIdx.x * kBK2;
   const int hk = blockIdx.y, b = blockIdx.z;
   const int64_t BS = (int64_t)a.batch * a.S;
   const int nkeys = (int)std::min<int64_t>(kBK2, a.S - k0);
+  bf16x8 kf[KS], vf[KS];  // second operands of S and dP: the wave's 32 keys of K and V
   {
-    TileRegs<kBK2, HD, 512> rk;
-    rk.load((const bf16*)a.K + ((int64_t)hk * BS + (int64_t)b * a.S + k0) * HD, HD, nkeys, HD, tid);
-    rk.store(sm, P, tid);
-    rk.load((const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + hk * HD, (int64_t)a.Hkd * HD, nkeys, HD,
-            tid);
-    rk.store(sm + kBK2 * P, P, tid);
+    const bf16* kb = (const bf16*)a.K + ((int64_t)hk * BS + (int64_t)b * a.S + k0) * HD;
+    const bf16* vb = (const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + (int64_t)hk * HD;
+    const uint32_t ldv = (uint32_t)a.Hkd * RB;
+    dma_tile<kBK2, RB, 8>(make_rsrc(kb, (uint64_t)nkeys * RB), RB, sm, w, lane);
+    dma_tile<kBK2, RB, 8>(make_rsrc(vb, (uint64_t)(nkeys - 1) * ldv + RB), ldv, sm + kBK2 * RB, w, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int r = 32 * kh + l32;
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+      kf[k] = lds_chunk<RB>(sm, r, 2 * k + h);
+      vf[k] = lds_chunk<RB>(sm + kBK2 * RB, r, 2 * k + h);
+    }
+    __syncthreads();  // every wave holds its fragments before the loop's loads reuse the space
   }
-  const int qh = w & 1, kh = w >> 1;  // this wave's block of P and dS: queries qh, keys kh (of 4)
-  __syncthreads();
-  bf16x8 kf[HD / 16], vf[HD / 16];  // the wave's 32 keys of K and V, all of d
-  load_frags<HD / 16>(kf, sm + 32 * kh * P, P, lane);
-  load_frags<HD / 16>(vf, sm + (kBK2 + 32 * kh) * P, P, lane);
-  // first local row whose position reaches k0 (positions grow with the row)
-  const int64_t C = a.chunk, ca = (int64_t)a.rank * C, cb = (2 * (int64_t)a.fold - 1 - a.rank) * C;
-  const int64_t first = k0 <= ca ? 0 : k0 < ca + C ? k0 - ca : k0 <= cb ? C : k0 < cb + C ? C + k0 - cb : a.T;
-  const int64_t qs = first / kAB * kAB;
+  const int64_t qs = first_row_at(k0, a.chunk, a.rank, a.fold, a.T) / kAB * kAB;
   const int nqb = (int)((a.T - qs + kAB - 1) / kAB);
   const int total = a.grp * nqb;  // (query head, query block) pairs, head-major
-  const int64_t ldt = (int64_t)a.Hd * a.BTp;
-  f32x16 dk[NT], dv[NT];
-#pragma unroll
-  for (int u = 0; u < NT; u++)
-#pragma unroll
-    for (int i = 0; i < 16; i++) dk[u][i] = dv[u][i] = 0.f;
-  for (int it = 0; it < total; it++) {
+  const uint32_t ldt = (uint32_t)((int64_t)a.Hd * a.batch * a.Tp * 2);  // bytes per row of Qt, dOt
+  const uint32_t ldo = (uint32_t)a.ldo * 2;
+  auto issue = [&](int it, int buf) {
     const int64_t t = (int64_t)hk * a.grp + it / nqb, q0 = qs + (int64_t)kAB * (it % nqb);
     const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
-    const int64_t col = t * a.BTp + (int64_t)b * a.T + q0;
-    __syncthreads();  // the previous block's products (and the K/V fragment loads) no longer read LDS
-    if (tid < kAB) {
-      const int64_t rr = (t * a.batch + b) * a.T + q0 + tid;
-      ls[tid] = tid < nq ? a.LSE[rr] : 0.f;
-      dl[tid] = tid < nq ? a.Dl[rr] : 0.f;
+    char* base = sm + buf * 4 * TB;
+    const int64_t row0 = (t * a.batch + b) * a.T + q0;
+    dma_tile<kAB, RB, 8>(make_rsrc((const bf16*)a.Q + row0 * HD, (uint64_t)nq * RB), RB, base, w, lane);
+    dma_tile<kAB, RB, 8>(make_rsrc((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD,
+                                   (uint64_t)(nq - 1) * ldo + RB),
+                         ldo, base + TB, w, lane);
+    const int64_t col = (t * a.batch + b) * a.Tp + q0;
+    const uint64_t tbytes = (uint64_t)(HD - 1) * ldt + 128;
+    dma_tile<HD, 128, 8>(make_rsrc((const bf16*)a.Qt + col, tbytes), ldt, base + 2 * TB, w, lane);
+    dma_tile<HD, 128, 8>(make_rsrc((const bf16*)a.dOt + col, tbytes), ldt, base + 3 * TB, w, lane);
+    if (w == 0) {
+      buffer_to_lds4(make_rsrc(a.LSE + row0, (uint64_t)nq * 4), lsd[buf][0], (uint32_t)lane * 4);
+      buffer_to_lds4(make_rsrc(a.Dl + row0, (uint64_t)nq * 4), lsd[buf][1], (uint32_t)lane * 4);
     }
-    {
-      TileRegs<kAB, HD, 512> r1, r2;
-      TileRegs<HD, kAB, 512> r3, r4;
-      r1.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
-      r2.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
-      r3.load((const bf16*)a.Qt + col, ldt, HD, nq, tid);
-      r4.load((const bf16*)a.dOt + col, ldt, HD, nq, tid);
-      r1.store(Qs, P, tid);
-      r2.store(dOs, P, tid);
-      r3.store(Qt, kTP, tid);
-      r4.store(dOt, kTP, tid);
-    }
-    __syncthreads();
+  };
+  f32x16 dk[NKB], dv[NKB];
+#pragma unroll
+  for (int u = 0; u < NKB; u++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) dk[u][i] = dv[u][i] = 0.f;
+  // the lane's key (its column of S) is seen by local rows [qk, T)
+  const int64_t qk = first_row_at(k0 + 32 * kh + l32, a.chunk, a.rank, a.fold, a.T);
+  const int qr = 32 * qh + perm_rows(l32);  // the query row the lane feeds into S and dP
+  const int mb = 32 * qh + 8 * h;           // register i holds query block row mb + 16 (i / 8) + i % 8
+  if (total > 0) issue(0, 0);
+  for (int it = 0; it < total; it++) {
+    const int buf = it & 1;
+    const int64_t q0 = qs + (int64_t)kAB * (it % nqb);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // this block's tiles have landed, and no wave still reads the other buffer
+    if (it + 1 < total) issue(it + 1, buf ^ 1);
+    const char* Qs = sm + buf * 4 * TB;
+    const char* dOs = Qs + TB;
+    const char* Qt = Qs + 2 * TB;
+    const char* dOt = Qs + 3 * TB;
     f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
-    mma_regs_b<HD / 16>(s, Qs + 32 * qh * P, P, kf, lane);
-    mma_regs_b<HD / 16>(dp, dOs + 32 * qh * P, P, vf, lane);
-    probs_and_ds(s, dp, ls, dl, q0, k0, qh, kh, lane, a);
-    {  // P^T and dS^T as [key][query]: 4 consecutive queries per store
-      const int n = 32 * kh + (lane & 31);
 #pragma unroll
-      for (int gi = 0; gi < 4; gi++) {
-        const int m = 32 * qh + 8 * gi + 4 * (lane >> 5);
-        bf16 pv[4] = {(bf16)s[4 * gi], (bf16)s[4 * gi + 1], (bf16)s[4 * gi + 2], (bf16)s[4 * gi + 3]};
-        bf16 dv4[4] = {(bf16)dp[4 * gi], (bf16)dp[4 * gi + 1], (bf16)dp[4 * gi + 2], (bf16)dp[4 * gi + 3]};
-        *(u32x2*)(Pt + n * kTP + m) = *(const u32x2*)pv;
-        *(u32x2*)(dSt + n * kTP + m) = *(const u32x2*)dv4;
+    for (int k = 0; k < KS; k++) {
+      s = MF<bf16>::mma(lds_chunk<RB>(Qs, qr, 2 * k + h), kf[k], s);
+      dp = MF<bf16>::mma(lds_chunk<RB>(dOs, qr, 2 * k + h), vf[k], dp);
+    }
+    // P and dS as first operands over the wave's 32 queries: register i holds
+    // block row mb + 16 (i / 8) + i % 8, kept when that row is in [lo, hi)
+    const int lo = (int)std::min<int64_t>(std::max<int64_t>(qk - q0, 0), kAB) - mb;
+    const int hi = (int)std::min<int64_t>(a.T - q0, kAB) - mb;
+    bf16x8 pa[2], da[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; s2++) {
+      const float4* lp = (const float4*)&lsd[buf][0][mb + 16 * s2];
+      const float4* dq4 = (const float4*)&lsd[buf][1][mb + 16 * s2];
+      const float4 l0 = lp[0], l1 = lp[1], d0 = dq4[0], d1 = dq4[1];
+      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int i = 8 * s2 + j, c = 16 * s2 + j;
+        const float e = fast_exp2(s[i] * a.scale_log2 - lv[j]);
+        const float pr = (c >= lo && c < hi) ? e : 0.f;
+        pa[s2][j] = (bf16)pr;
+        da[s2][j] = (bf16)(pr * (dp[i] - dv8[j]));
       }
     }
-    __syncthreads();
-    // output blocks: keys kh (the wave's own 32), dim blocks qh + 2u
-    lds_mma_shared_a<NT>(dv, Pt + 32 * kh * kTP, kTP, dOt + 32 * qh * kTP, kTP, 64 * kTP, kAB, lane);
-    lds_mma_shared_a<NT>(dk, dSt + 32 * kh * kTP, kTP, Qt + 32 * qh * kTP, kTP, 64 * kTP, kAB, lane);
+    // dV += P^T dO and dK += dS^T Q for every 32-wide block of the head dimension
+#pragma unroll
+    for (int s2 = 0; s2 < 2; s2++) {
+      const int c = 4 * qh + 2 * s2 + h;  // the 8 queries' chunk in the transposed tiles
+#pragma unroll
+      for (int u = 0; u < NKB; u++) {
+        dv[u] = MF<bf16>::mma(pa[s2], lds_chunk<128>(dOt, 32 * u + l32, c), dv[u]);
+        dk[u] = MF<bf16>::mma(da[s2], lds_chunk<128>(Qt, 32 * u + l32, c), dk[u]);
+      }
+    }
   }
+  // The two query halves' sums meet in LDS; the qh = 0 waves store.
+  __syncthreads();
+  float* red = (float*)sm;  // [kh][dK | dV][NKB][16][64]
+  if (qh == 1) {
 #pragma unroll
-  for (int u = 0; u < NT; u++) {
-    const int dt = qh + 2 * u;
+    for (int u = 0; u < NKB; u++)
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int64_t key = k0 + 32 * kh + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (key < a.S) {
-        const int64_t off = ((int64_t)hk * BS + (int64_t)b * a.S + key) * HD + 32 * dt + (lane & 31);
-        a.dK[off] = dk[u][i] * a.scale;
-        a.dV[off] = dv[u][i];
+      for (int i = 0; i < 16; i++) {
+        red[(((kh * 2 + 0) * NKB + u) * 16 + i) * 64 + lane] = dk[u][i];
+        red[(((kh * 2 + 1) * NKB + u) * 16 + i) * 64 + lane] = dv[u][i];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int u = 0; u < NKB; u++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int64_t kk = k0 + 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (kk < a.S) {
+          const int64_t off = ((int64_t)hk * BS + (int64_t)b * a.S + kk) * HD + 32 * u + l32;
+          a.dK[off] = (dk[u][i] + red[(((kh * 2 + 0) * NKB + u) * 16 + i) * 64 + lane]) * a.scale;
+          a.dV[off] = dv[u][i] + red[(((kh * 2 + 1) * NKB + u) * 16 + i) * 64 + lane];
+        }
       }
     }
   }
 }
 
 // One work-group per (128-row query block, query head, sequence): dQ of
-// those rows over every key they attend to, eight waves, so that each staged
-// 64-key block serves 128 queries.  The scores are formed transposed (keys
-// by rows), so each lane owns one query and dS is stored [query][key] four
-// keys at a time.  Transposed copies: Kt [HD][Hkd*B*S], Vr as above.
+// those rows over every key they attend to.  Eight waves: wave (qh, kh) owns
+// queries 32 qh.. of the block, with Q and dO in registers, and keys 32 kh..
+// of each 64-key block; the scores are formed transposed (keys by rows), so
+// dS is the first operand of dQ = dS K.  The two key halves are added once
+// at the end.  Per key block: K and V (rows) and K^T (from Kt [HD][Hkd][B][Sp]).
 template <int HD>
 __global__ void __launch_bounds__(512) attn_bwd_dq_kernel(AttnBwdArgs a) {
-  constexpr int P = HD + 8;
-  constexpr int NT = HD / 64;  // 32x32 output blocks per wave
-  constexpr int KS = 0, VS = KS + kAB * P, KT = VS + kAB * P, DSS = KT + HD * kTP, NEL = DSS + kBQ2 * kTP;
-  static_assert(2 * kBQ2 * P <= NEL, "Q and dO staging must fit in the loop's space");
-  __shared__ __attribute__((aligned(16))) bf16 sm[NEL];
-  bf16* const Ks = sm + KS;
-  bf16* const Vs = sm + VS;
-  bf16* const Kt = sm + KT;
-  bf16* const dSs = sm + DSS;
+  constexpr int RB = HD * 2;
+  constexpr int TB = kAB * HD * 2;
+  constexpr int NKB = HD / 32;
+  constexpr int KS = HD / 16;
+  static_assert(2 * kBQ2 * RB <= 6 * TB, "Q and dO staging must fit in the loop's space");
+  __shared__ __attribute__((aligned(1024))) char sm[2 * 3 * TB];  // two buffers of [K | V | K^T]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int qh = w >> 1, kh = w & 1;
   const int64_t q0 = (int64_t)blockIdx.x * kBQ2;
   const int64_t t = blockIdx.y;
   const int b = blockIdx.z;
@@ -2341,76 +2392,105 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_kernel(AttnBwdArgs a) {
   const int64_t BS = (int64_t)a.batch * a.S;
   const int nq = (int)std::min<int64_t>(kBQ2, a.T - q0);
   const int64_t kend = zz_pos(q0 + nq - 1, a.chunk, a.rank, a.fold) + 1;  // keys [0, kend)
-  {  // Q and dO pass through LDS once, into registers
-    TileRegs<kBQ2, HD, 512> r;
-    r.load((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, HD, nq, HD, tid);
-    r.store(sm, P, tid);
-    r.load((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD, a.ldo, nq, HD, tid);
-    r.store(sm + kBQ2 * P, P, tid);
+  const uint32_t ldo = (uint32_t)a.ldo * 2;
+  bf16x8 qf[KS], of[KS];  // second operands of S^T and dP^T: the wave's 32 queries of Q and dO
+  {
+    dma_tile<kBQ2, RB, 8>(make_rsrc((const bf16*)a.Q + ((t * a.batch + b) * a.T + q0) * HD, (uint64_t)nq * RB),
+                          RB, sm, w, lane);
+    dma_tile<kBQ2, RB, 8>(make_rsrc((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD,
+                                    (uint64_t)(nq - 1) * ldo + RB),
+                          ldo, sm + kBQ2 * RB, w, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int r = 32 * qh + l32;
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+      qf[k] = lds_chunk<RB>(sm, r, 2 * k + h);
+      of[k] = lds_chunk<RB>(sm + kBQ2 * RB, r, 2 * k + h);
+    }
+    __syncthreads();
   }
-  const int qh = w >> 1, kh = w & 1;  // this wave's block of S^T: queries qh (of 4), keys kh
-  __syncthreads();
-  bf16x8 qf[HD / 16], of[HD / 16];  // the wave's 32 queries of Q and dO, all of d
-  load_frags<HD / 16>(qf, sm + 32 * qh * P, P, lane);
-  load_frags<HD / 16>(of, sm + (kBQ2 + 32 * qh) * P, P, lane);
-  const int mq = 32 * qh + (lane & 31);  // the lane's query within the block
+  const int mq = 32 * qh + l32;  // the lane's query (its column of S^T)
   const bool qok = mq < nq;
   const int64_t qpos = qok ? zz_pos(q0 + mq, a.chunk, a.rank, a.fold) : -1;
   const int64_t rr = (t * a.batch + b) * a.T + q0 + mq;
   const float lq = qok ? a.LSE[rr] : 0.f, dlq = qok ? a.Dl[rr] : 0.f;
-  f32x16 dq[NT];
+  const uint32_t ldk = (uint32_t)((int64_t)a.Hkd * a.batch * a.Sp * 2);  // bytes per row of Kt
+  const uint32_t ldv = (uint32_t)a.Hkd * RB;
+  auto issue = [&](int64_t kb0, int buf) {
+    const int nk = (int)std::min<int64_t>(kAB, a.S - kb0);
+    char* base = sm + buf * 3 * TB;
+    dma_tile<kAB, RB, 8>(make_rsrc((const bf16*)a.K + (hk * BS + (int64_t)b * a.S + kb0) * HD, (uint64_t)nk * RB),
+                         RB, base, w, lane);
+    dma_tile<kAB, RB, 8>(make_rsrc((const bf16*)a.Vr + ((int64_t)b * a.S + kb0) * a.Hkd * HD + hk * HD,
+                                   (uint64_t)(nk - 1) * ldv + RB),
+                         ldv, base + TB, w, lane);
+    dma_tile<HD, 128, 8>(make_rsrc((const bf16*)a.Kt + (hk * a.batch + b) * a.Sp + kb0,
+                                   (uint64_t)(HD - 1) * ldk + 128),
+                         ldk, base + 2 * TB, w, lane);
+  };
+  f32x16 dq[NKB];
 #pragma unroll
-  for (int u = 0; u < NT; u++)
+  for (int u = 0; u < NKB; u++)
 #pragma unroll
     for (int i = 0; i < 16; i++) dq[u][i] = 0.f;
-  const int64_t ldk = (int64_t)a.Hkd * BS;
-  TileRegs<kAB, HD, 512> rk, rv;
-  TileRegs<HD, kAB, 512> rkt;
-  auto fetch = [&](int64_t k0) {
-    const int nk = (int)std::min<int64_t>(kAB, a.S - k0);
-    rk.load((const bf16*)a.K + (hk * BS + (int64_t)b * a.S + k0) * HD, HD, nk, HD, tid);
-    rv.load((const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + hk * HD, (int64_t)a.Hkd * HD, nk, HD,
-            tid);
-    rkt.load((const bf16*)a.Kt + hk * BS + (int64_t)b * a.S + k0, ldk, HD, nk, tid);
-  };
-  fetch(0);
-  for (int64_t k0 = 0; k0 < kend; k0 += kAB) {
-    __syncthreads();  // the previous block's products (and the Q/dO fragment loads) no longer read LDS
-    rk.store(Ks, P, tid);
-    rv.store(Vs, P, tid);
-    rkt.store(Kt, kTP, tid);
-    __syncthreads();
-    if (k0 + kAB < kend) fetch(k0 + kAB);
+  const int kr = 32 * kh + perm_rows(l32);  // the key row the lane feeds into S^T and dP^T
+  const int nkb = (int)((kend + kAB - 1) / kAB);
+  if (nkb > 0) issue(0, 0);
+  for (int kb = 0; kb < nkb; kb++) {
+    const int buf = kb & 1;
+    const int64_t k0 = (int64_t)kb * kAB;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // this block's tiles have landed, and no wave still reads the other buffer
+    if (kb + 1 < nkb) issue(k0 + kAB, buf ^ 1);
+    const char* Ks = sm + buf * 3 * TB;
+    const char* Vs = Ks + TB;
+    const char* Kt = Ks + 2 * TB;
     f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
-    mma_regs_b<HD / 16>(s, Ks + 32 * kh * P, P, qf, lane);
-    mma_regs_b<HD / 16>(dp, Vs + 32 * kh * P, P, of, lane);
 #pragma unroll
-    for (int gi = 0; gi < 4; gi++) {
-      const int kk = 32 * kh + 8 * gi + 4 * (lane >> 5);  // first of the lane's 4 keys
-      bf16 d4[4];
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int i = 4 * gi + j;
-        const bool ok = k0 + kk + j <= qpos;
-        const float p = ok ? fast_exp2(s[i] * a.scale_log2 - lq) : 0.f;
-        d4[j] = (bf16)(p * (dp[i] - dlq));
-      }
-      *(u32x2*)(dSs + mq * kTP + kk) = *(const u32x2*)d4;
+    for (int k = 0; k < KS; k++) {
+      s = MF<bf16>::mma(lds_chunk<RB>(Ks, kr, 2 * k + h), qf[k], s);
+      dp = MF<bf16>::mma(lds_chunk<RB>(Vs, kr, 2 * k + h), of[k], dp);
     }
-    __syncthreads();
-    // output blocks: queries qh (the wave's own 32), dim blocks kh + 2u
-    lds_mma_shared_a<NT>(dq, dSs + 32 * qh * kTP, kTP, Kt + 32 * kh * kTP, kTP, 64 * kTP, kAB, lane);
-  }
-#pragma unroll
-  for (int u = 0; u < NT; u++) {
-    const int dt = kh + 2 * u;
+    // dS as the first operand over the wave's 32 keys: register i holds key
+    // k0 + 32 kh + 8 h + 16 (i / 8) + i % 8, kept while that key <= qpos
+    const int lim = (int)std::max<int64_t>(std::min<int64_t>(qpos - k0 - 32 * kh - 8 * h, kAB), -1);
+    bf16x8 da[2];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const int m = 32 * qh + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (m < nq)
-        a.dQ[((t * a.batch + b) * a.T + q0 + m) * HD + 32 * dt + (lane & 31)] = dq[u][i] * a.scale;
+      const int c = 16 * (i >> 3) + (i & 7);
+      const float e = fast_exp2(s[i] * a.scale_log2 - lq);
+      const float pr = c <= lim ? e : 0.f;
+      da[i >> 3][i & 7] = (bf16)(pr * (dp[i] - dlq));
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; s2++) {
+      const int c = 4 * kh + 2 * s2 + h;  // the 8 keys' chunk in the K^T tile
+#pragma unroll
+      for (int u = 0; u < NKB; u++) dq[u] = MF<bf16>::mma(da[s2], lds_chunk<128>(Kt, 32 * u + l32, c), dq[u]);
+    }
+  }
+  __syncthreads();
+  float* red = (float*)sm;  // [qh][NKB][16][64]
+  if (kh == 1) {
+#pragma unroll
+    for (int u = 0; u < NKB; u++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) red[((qh * NKB + u) * 16 + i) * 64 + lane] = dq[u][i];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int u = 0; u < NKB; u++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int m = 32 * qh + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (m < nq)
+          a.dQ[((t * a.batch + b) * a.T + q0 + m) * HD + 32 * u + l32] =
+              (dq[u][i] + red[((qh * NKB + u) * 16 + i) * 64 + lane]) * a.scale;
+      }
     }
   }
 }
@@ -2684,6 +2764,20 @@ hipError_t launch_transpose(Dtype dt, const void* in, void* out, int64_t R, int6
     transpose_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)in, (bf16*)out, R, C, ldi, ldo);
   else
     transpose_kernel<float><<<grid, 256, 0, s>>>((const float*)in, (float*)out, R, C, ldi, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_pad(Dtype dt, const void* in, void* out, int64_t R, int64_t Rp, int64_t C,
+                                int64_t ldi, int64_t ldo, int64_t Z, int64_t zdiv, int64_t s1, int64_t s0,
+                                hipStream_t s) {
+  if (Rp <= 0 || C <= 0 || Z <= 0) return hipSuccess;
+  if (Rp % 64 != 0 || Rp < R || zdiv <= 0 || Z > 65535 || (C + 63) / 64 > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(Rp / 64), (unsigned)((C + 63) / 64), (unsigned)Z);
+  if (dt == BF16)
+    transpose_pad_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)in, (bf16*)out, R, Rp, C, ldi, ldo, zdiv, s1, s0);
+  else
+    transpose_pad_kernel<float><<<grid, 256, 0, s>>>((const float*)in, (float*)out, R, Rp, C, ldi, ldo, zdiv, s1,
+                                                     s0);
   return hipGetLastError();
 }
 

@@ -131,6 +131,8 @@ def test_gqa_rope_dims_and_workspace():
     mha = tsp.make_dims(C3, 3)
     same = tsp.make_dims(C3.with_(n_kv_heads=32, rope_theta=10000.0), 3)
     gqa = tsp.make_dims(C3.with_(n_kv_heads=8), 3)
+    for dm in (mha, same, gqa):  # one shard per launch, so the slots hold one shard each
+        dm.flags |= tsp.TSP_F_SHARD_LAUNCH
     assert mha.n_kv_heads == 0 and same.n_kv_heads == 32 and abs(same.rope_theta - 1e4) < 1e-3
     for which in (tsp.TSP_WS_ATTN, tsp.TSP_WS_MLP, tsp.TSP_WS_LAYER, tsp.TSP_WS_KV):
         assert tsp.workspace_bytes(same, which) == tsp.workspace_bytes(mha, which)
@@ -141,6 +143,36 @@ def test_gqa_rope_dims_and_workspace():
     assert a_mha - a_gqa >= 2 * (slot - slot // 4)
     assert tsp.workspace_bytes(gqa, tsp.TSP_WS_MLP) == tsp.workspace_bytes(mha, tsp.TSP_WS_MLP)
     assert tsp.kv_elems(C3.with_(n_kv_heads=8)) * 4 == tsp.kv_elems(C3)
+
+
+def test_shards_per_launch_workspace():
+    """The forward halves run P = 2 shards of an accumulation group (G = 4 at
+    D = 8) per launch when one shard's projection has fewer than 256 tiles of
+    256 x 192 (7B: QKV 1536 columns, W1/W3 1376); the two weight slots, the
+    two K/V slots and the Q buffer then hold P shards each, 2P = D/2 shards
+    of the layer at most.  The flags force either choice."""
+    def ws(cfg, flags, which):
+        d = tsp.make_dims(cfg, 3)
+        d.flags |= flags
+        return tsp.workspace_bytes(d, which)
+    S16 = C3.with_(seq=16384)
+    # 64K: 32 x 8 = 256 tiles per shard, one shard per launch by default
+    assert ws(C3, 0, tsp.TSP_WS_ATTN) == ws(C3, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
+    assert ws(C3, 0, tsp.TSP_WS_MLP) == ws(C3, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP)
+    # 16K: 8 x 8 = 64 tiles per shard, two shards per launch by default
+    assert ws(S16, 0, tsp.TSP_WS_ATTN) == ws(S16, tsp.TSP_F_GROUP_LAUNCH, tsp.TSP_WS_ATTN)
+    assert ws(S16, 0, tsp.TSP_WS_MLP) == ws(S16, tsp.TSP_F_GROUP_LAUNCH, tsp.TSP_WS_MLP)
+    T, h, hs, Fs, es = 2048, 4096, 512, 1376, 2
+    qkv = (hs + 2 * hs) * h * es            # one packed Q|K|V block
+    kvslot = 2 * 4 * 16384 * 128 * es       # one shard's K and V^T over the sequence
+    grown = 2 * qkv + 2 * kvslot + T * hs * es  # a second shard in each of 2 slots, and in Q
+    diff = ws(S16, 0, tsp.TSP_WS_ATTN) - ws(S16, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
+    assert grown <= diff <= grown + 16 * 1024 * 1024, (diff, grown)  # + split partials, alignment
+    assert ws(S16, 0, tsp.TSP_WS_MLP) - ws(S16, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP) == 2 * 2 * Fs * h * es
+    # fold 4: G = 2 and D/4 = 1, so one shard per launch at any shape
+    f4 = C3.with_(seq=16384, fold=4)
+    assert ws(f4, 0, tsp.TSP_WS_ATTN) == ws(f4, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
+    assert ws(f4, tsp.TSP_F_GROUP_LAUNCH, tsp.TSP_WS_MLP) == ws(f4, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP)
 
 
 def test_micro_batch_workspace():
@@ -248,9 +280,9 @@ def test_noalloc_entry_point_refusals_on_the_host():
     assert tsp.workspace_bytes(big, tsp.TSP_WS_LAYER) > tsp.NOALLOC_SCRATCH_BYTES
     assert tsp.STATUS[call(big)] == "TSP_E_WORKSPACE"
     assert "static scratch" in L.tsp_last_error().decode()
-    fits = tsp.make_dims(C3.with_(seq=4096), 3)
+    fits = tsp.make_dims(C3.with_(seq=4096), 3, tsp.TSP_F_SHARD_LAUNCH)
     assert tsp.workspace_bytes(fits, tsp.TSP_WS_LAYER) <= tsp.NOALLOC_SCRATCH_BYTES
-    fits.flags = tsp.TSP_F_PROFILE
+    fits.flags |= tsp.TSP_F_PROFILE
     assert tsp.STATUS[call(fits)] == "TSP_E_INVAL"
     bad = tsp.make_dims(C3, 3)
     bad.rank = 9

@@ -209,6 +209,52 @@ def test_kv_stream_flag_bitwise(case):
     say(f"    {cfg.fold} ranks bitwise equal")
 
 
+# Several shards per launch (P = 2 at fold 8, 4 at fold 16): the QKV GEMM
+# scatters each shard's Q/K/V to its own block, the attention reads each
+# shard's K/V block (in place or from the slot), and the W1/W3 GEMM runs over
+# the shards' W1 and W3 blocks side by side.
+GROUPED = {
+    # C = 128: other ranks' K/V read in place
+    "fold8_inplace_d128": _cfg(hidden=1024, n_heads=8, head_dim=128, ffn=1376, seq=2048, fold=8),
+    # C = 25: K/V rows copied into each shard's slot block; GQA 2, rotary, two sequences
+    "fold8_ragged_gqa2_rope_b2": _cfg(hidden=512, n_heads=16, n_kv_heads=8, head_dim=32, ffn=704, seq=400,
+                                      fold=8, batch=2, rope_theta=10000.0, x_std=0.02, w_std=0.045),
+    # fold 16: four shards per launch, C = 20
+    "fold16_c20_d32": _cfg(hidden=512, n_heads=16, head_dim=32, ffn=704, seq=640, fold=16),
+}
+
+
+@pytest.mark.parametrize("case", sorted(GROUPED))
+def test_shards_per_launch(case):
+    """Every rank's layer share with the default grouped launches and with
+    one shard per launch (TSP_F_SHARD_LAUNCH), both against the oracle; the
+    grouped run with delayed and NaN-poisoned slot copies bit for bit equal
+    to the plain grouped run."""
+    from folded_tensor_sequence_rank_amd import tsp
+    cfg = GROUPED[case]
+    say(f"[gpu] shards per launch {case}: h={cfg.hidden} H={cfg.n_heads} Hkv={cfg.kv_heads} d={cfg.head_dim} "
+        f"S={cfg.seq} D={cfg.fold} B={cfg.batch}")
+    w = synth.gen_weights(cfg)
+    L = layer_dev(cfg, w)
+    pos = [O.zigzag_positions(cfg.seq, cfg.fold, r) for r in range(cfg.fold)]
+    xf = [synth.gen_x_rows(cfg, 0, cfg.seq, seq_index=b) for b in range(cfg.batch)]
+    xs = [to_dev(np.concatenate([x[p] for x in xf]), cfg) for p in pos]
+    kv = new_kv(cfg)
+    fill_kv(cfg, L, xs, kv)
+    T = cfg.local_tokens
+    for r in range(cfg.fold):
+        grouped = RankRun(cfg, r).layer(xs[r], L, kv)
+        single = RankRun(cfg, r, flags=tsp.TSP_F_SHARD_LAUNCH).layer(xs[r], L, kv)
+        stressed = RankRun(cfg, r, flags=tsp.TSP_F_DELAY_COPY | tsp.TSP_F_POISON_SLOTS).layer(xs[r], L, kv)
+        torch.cuda.synchronize()
+        assert torch.equal(grouped, stressed), f"rank {r}: delayed / poisoned grouped copies change the result"
+        for b in range(cfg.batch):
+            ref = O.layer_rows(xf[b], w, cfg.n_heads, cfg.eps, pos[r], cfg.rope_theta)
+            rows = slice(b * T, (b + 1) * T)
+            _check(cfg, f"rank {r} seq {b} grouped", f64(grouped)[rows], ref)
+            _check(cfg, f"rank {r} seq {b} one shard per launch", f64(single)[rows], ref)
+
+
 def test_7b_s16k_rank3_full():
     """The 7B shape at 16K context, fold 8, rank 3: every output row against
     the oracle, with the other ranks' K/V read in place and, through

@@ -26,18 +26,20 @@ def _case(cfg, r):
 
 
 def test_noalloc_matches_layer_shard_on_two_calls():
-    big = synth.get_config("7b_s16k").with_(seq=4096)          # 241 MiB of the 256 MiB scratch
+    # one shard per launch: 241 MiB of the 256 MiB scratch (two shards per
+    # launch, the default at this size, would need 329 MiB)
+    big = synth.get_config("7b_s16k").with_(seq=4096)
     small = synth.LayerConfig(name="small", hidden=512, n_heads=4, head_dim=128, ffn=688, seq=1600,
                               fold=2, batch=2, n_kv_heads=2, rope_theta=10000.0)
     cs = torch.cuda.Stream()
-    for cfg, r in ((big, 3), (small, 1)):
-        d = tsp.make_dims(cfg, r)
+    for cfg, r, flags in ((big, 3, tsp.TSP_F_SHARD_LAUNCH), (small, 1, 0)):
+        d = tsp.make_dims(cfg, r, flags)
         need = tsp.workspace_bytes(d, tsp.TSP_WS_LAYER)
         assert 0 < need <= tsp.NOALLOC_SCRATCH_BYTES
-        say(f"[gpu] no-alloc layer: h={cfg.hidden} S={cfg.seq} D={cfg.fold} B={cfg.batch} rank {r}, "
-            f"{need / 2**20:.1f} MiB of scratch")
+        say(f"[gpu] no-alloc layer: h={cfg.hidden} S={cfg.seq} D={cfg.fold} B={cfg.batch} rank {r} "
+            f"flags {flags}, {need / 2**20:.1f} MiB of scratch")
         L, x, kv = _case(cfg, r)
-        ref = RankRun(cfg, r).layer(x, L, kv)
+        ref = RankRun(cfg, r, flags).layer(x, L, kv)
         out = torch.full_like(x, float("nan"))
         tsp.tsp_layer_shard_noalloc(d, x, L.g1, L.w_attn, kv, L.g2, L.w_mlp, out, copy_stream=cs)
         again = torch.full_like(x, float("nan"))
@@ -50,7 +52,7 @@ def test_noalloc_matches_layer_shard_on_two_calls():
 
 
 def test_noalloc_refuses_shapes_past_the_scratch():
-    cfg = synth.get_config("7b_s16k")                            # 437 MiB
+    cfg = synth.get_config("7b_s16k")                            # over 400 MiB
     d = tsp.make_dims(cfg, 3)
     assert tsp.workspace_bytes(d, tsp.TSP_WS_LAYER) > tsp.NOALLOC_SCRATCH_BYTES
     x = torch.empty(cfg.local_tokens * cfg.hidden, dtype=torch.bfloat16, device="cuda")
