@@ -2635,8 +2635,10 @@ static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
 //    128x192 tiles (two per CU) when they fill at least 3/4 of the 512
 //    slots (8192 tokens), else 4-wave 128x128 when they fill half (the
 //    narrow N of grouped K/V), else 4-wave 64x64 (2048 tokens);
-//  * W1/W3 (two B operands): 128x64 (4 waves) when 128x192 leaves CUs idle,
-//    128x96 (4 waves) up to two rounds of 128x192, else the estimate.
+//  * W1/W3 (two B operands), up to two rounds of 128x192: 4-wave 128x96
+//    tiles when they fill 3/4 of the 512 slots (two shards per launch at
+//    2048 tokens: 0.104 ms against 0.123 for 128x64), else 4-wave 128x64
+//    (one shard at 2048 tokens); beyond that the estimate.
 // The estimate: rounds of 256 tiles x tile area / relative efficiency.
 template <int EPI>
 static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
@@ -2658,10 +2660,12 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
   };
   if constexpr (EPI == EPI_SWIGLU) {
     const int64_t t192 = tiles(128, 192);
-    if (t192 < 256) {
-      gemm_go<bf16, 128, 64, EPI, 4, 2>(a, vec, s);
-    } else if (t192 <= 512) {
-      gemm_go<bf16, 128, 96, EPI, 4, 4>(a, vec, s);
+    if (t192 <= 512) {
+      // 4-wave tiles, two per CU: 128x96 when they fill 3/4 of the 512 slots
+      if (tiles(128, 96) >= 384)
+        gemm_go<bf16, 128, 96, EPI, 4, 4>(a, vec, s);
+      else
+        gemm_go<bf16, 128, 64, EPI, 4, 2>(a, vec, s);
     } else {
       const Cand dual[] = {{256, 128, 1.0}, {128, 192, 0.8}};
       if (pick(dual, 2) == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
