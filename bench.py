@@ -32,7 +32,10 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "folded_tensor_sequence_rank_amd", "csrc", "tsp_kernels.hip")
+# The sources whose change voids the committed HBM counters: the kernels, and
+# the host code that decides the launches (tile choice, shards per launch).
+KERNEL_SRCS = [os.path.join(ROOT, "folded_tensor_sequence_rank_amd", "csrc", f)
+               for f in ("tsp_kernels.hip", "tsp_api.cpp")]
 
 
 def parse():
@@ -87,12 +90,16 @@ def bytes_per_launch(cfg):
 
 
 def kernel_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None once the kernel source has changed since the counters were taken."""
+    None once the kernel or launch source has changed since the counters were
+    taken."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):

@@ -194,26 +194,19 @@ AttnPlan plan_of(const Dims& d) {
   return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(d.Hd * d.B));
 }
 
-// Shards per launch in the forward halves (TSP_F_SHARD_LAUNCH).  When one
-// shard's projection, N columns over the B*T rows, has fewer than 256 tiles
-// of 256 x 192, P consecutive shards share one launch: P is the largest
-// divisor of G not above D/4, so the two weight slots (2P shards) hold at
-// most half of the layer's Q|K|V or W1|W3 shards, as the W_O and W2 group
-// buffers do, and a launch never spans two accumulation groups.
-int64_t group_shards(const Dims& d) {
+// Shards per launch in the forward halves: P consecutive shards share each
+// QKV, attention and W1/W3 launch (TSP_F_SHARD_LAUNCH: one).  P is the
+// largest divisor of G not above D/4, so the two weight slots (2P shards)
+// hold at most half of the layer's Q|K|V or W1|W3 shards, as the W_O and W2
+// group buffers do, and a launch never spans two accumulation groups.
+int64_t launch_shards(const Dims& d) {
+  if (d.flags & TSP_F_SHARD_LAUNCH) return 1;
   const int64_t G = acc_group(d);
   int64_t P = 1;
   for (int64_t p = 2; p <= G && p <= d.D / 4; p++)
     if (G % p == 0) P = p;
   return P;
 }
-int64_t launch_shards(const Dims& d, int64_t ncols) {
-  if (d.flags & TSP_F_SHARD_LAUNCH) return 1;
-  if (d.flags & TSP_F_GROUP_LAUNCH) return group_shards(d);
-  return ((d.BT + 255) / 256) * ((ncols + 191) / 192) < 256 ? group_shards(d) : 1;
-}
-int64_t attn_launch(const Dims& d) { return launch_shards(d, (int64_t)qkv_rows(d)); }
-int64_t mlp_launch(const Dims& d) { return launch_shards(d, d.Fs); }
 
 // Attention plan of a launch over np shards' heads.
 AttnPlan plan_for(const Dims& d, int64_t np) {
@@ -232,7 +225,7 @@ AttnWs attn_ws(const Dims& d, size_t base) {
   const size_t act = al((size_t)d.BT * d.h * d.es);
   w.xn = o; o += act;
   w.y = o; o += al((size_t)d.BT * d.h * 4);
-  const int64_t G = acc_group(d), P = attn_launch(d);
+  const int64_t G = acc_group(d), P = launch_shards(d);
   w.q = o; o += al((size_t)P * d.BT * d.hs * d.es);  // [P*Hd][B*T][d]
   w.o = o; o += al((size_t)d.BT * G * d.hs * d.es);  // [B*T][G*hs]
   for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al((size_t)P * qkv_rows(d) * d.h * d.es); }
@@ -249,7 +242,7 @@ AttnWs attn_ws(const Dims& d, size_t base) {
 MlpWs mlp_ws(const Dims& d, size_t base) {
   MlpWs w;
   size_t o = base;
-  const int64_t G = acc_group(d), P = mlp_launch(d);
+  const int64_t G = acc_group(d), P = launch_shards(d);
   w.xn = o; o += al((size_t)d.BT * d.h * d.es);
   w.y = o; o += al((size_t)d.BT * d.h * 4);
   w.gg = o; o += al((size_t)d.BT * G * d.Fs * d.es);  // [B*T][G*Fs]
@@ -484,7 +477,7 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
   const size_t es = d.es;
   const size_t qkvbytes = qkv_rows(d) * d.h * es;
   const size_t kvbytes = kv_block_elems(d) * es;
-  const int64_t G = acc_group(d), P = attn_launch(d);
+  const int64_t G = acc_group(d), P = launch_shards(d);
   TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x, g1, ws + L.xn, d.BT, (int)d.h, d.eps, c.s)));
   // Broadcast iterations j0 .. j0 + np - 1 (shards of ranks j0 ..) per launch.
   for (int64_t j0 = 0, li = 0; j0 < d.D; j0 += P, li++) {
@@ -583,7 +576,7 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
   char* ws = c.ws;
   const size_t es = d.es;
   const size_t wbytes = (size_t)d.Fs * d.h * es;  // one shard's W1 (or W3) block
-  const int64_t G = acc_group(d), P = mlp_launch(d);
+  const int64_t G = acc_group(d), P = launch_shards(d);
   TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.BT, (int)d.h, d.eps, c.s)));
   // Ring steps t0 .. t0 + np - 1 (shards (r + t) mod D) per launch.
   for (int64_t t0 = 0, li = 0; t0 < d.D; t0 += P, li++) {

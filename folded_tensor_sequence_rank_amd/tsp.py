@@ -27,7 +27,7 @@ TSP_WS_LAYER_BWD, TSP_WS_LAYER_BWD_FINISH = 7, 8
 TSP_F_DELAY_COPY, TSP_F_POISON_SLOTS, TSP_F_NO_OVERLAP, TSP_F_PROFILE = 1, 2, 4, 8
 TSP_F_RESCALE_TEST = 16
 TSP_F_KV_STREAM = 32
-TSP_F_SHARD_LAUNCH, TSP_F_GROUP_LAUNCH = 64, 128
+TSP_F_SHARD_LAUNCH = 64
 KERNELS = ["rmsnorm", "qkv", "attn", "merge", "oproj", "w13", "w2"]  # TSP_K_* order
 STATUS = {0: "TSP_OK", -1: "TSP_E_INVAL", -2: "TSP_E_SHAPE", -3: "TSP_E_ALIGN",
           -4: "TSP_E_WORKSPACE", -5: "TSP_E_DTYPE", -6: "TSP_E_HIP"}

@@ -169,17 +169,14 @@ enum {
    * 3: transfers pipelined behind the GEMMs).  Without it they are read in
    * place when C % 64 == 0.  Same results, bit for bit. */
   TSP_F_KV_STREAM = 32u,
-  /* Shards per launch.  When one shard's QKV projection (or W1/W3 projection)
-   * is too small to fill the GPU -- under 256 tiles of 256 x 192 -- P
-   * consecutive shards run as one QKV launch and one attention launch (one
-   * W1/W3 launch), once all P have arrived in a slot.  P is the largest
-   * divisor of the accumulation group G = max(1, min(4, D/2)) not above D/4
-   * (2 at D = 8), so the two slots hold at most half of the layer's shards.
-   * These flags force one shard per launch, or P, at any shape.  Results
-   * agree to rounding: the attention's work split depends on the heads per
-   * launch. */
-  TSP_F_SHARD_LAUNCH = 64u,
-  TSP_F_GROUP_LAUNCH = 128u
+  /* Shards per launch.  By default P consecutive shards run as one QKV
+   * launch and one attention launch (one W1/W3 launch) once all P have
+   * arrived in a slot: P is the largest divisor of the accumulation group
+   * G = max(1, min(4, D/2)) not above D/4 (2 at D = 8, 1 below D = 8), so the
+   * two slots hold at most half of the layer's shards.  This flag runs one
+   * shard per launch.  Results agree to rounding: the attention's work split
+   * depends on the heads per launch. */
+  TSP_F_SHARD_LAUNCH = 64u
 };
 
 /* Kernel classes reported by tsp_profile_read. */

@@ -147,32 +147,27 @@ def test_gqa_rope_dims_and_workspace():
 
 def test_shards_per_launch_workspace():
     """The forward halves run P = 2 shards of an accumulation group (G = 4 at
-    D = 8) per launch when one shard's projection has fewer than 256 tiles of
-    256 x 192 (7B: QKV 1536 columns, W1/W3 1376); the two weight slots, the
-    two K/V slots and the Q buffer then hold P shards each, 2P = D/2 shards
-    of the layer at most.  The flags force either choice."""
+    D = 8) per QKV, attention and W1/W3 launch; the two weight slots, the two
+    K/V slots and the Q buffer then hold P shards each, 2P = D/2 shards of the
+    layer at most.  TSP_F_SHARD_LAUNCH runs one shard per launch; below D = 8,
+    P = 1 anyway."""
     def ws(cfg, flags, which):
         d = tsp.make_dims(cfg, 3)
         d.flags |= flags
         return tsp.workspace_bytes(d, which)
-    S16 = C3.with_(seq=16384)
-    # 64K: 32 x 8 = 256 tiles per shard, one shard per launch by default
-    assert ws(C3, 0, tsp.TSP_WS_ATTN) == ws(C3, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
-    assert ws(C3, 0, tsp.TSP_WS_MLP) == ws(C3, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP)
-    # 16K: 8 x 8 = 64 tiles per shard, two shards per launch by default
-    assert ws(S16, 0, tsp.TSP_WS_ATTN) == ws(S16, tsp.TSP_F_GROUP_LAUNCH, tsp.TSP_WS_ATTN)
-    assert ws(S16, 0, tsp.TSP_WS_MLP) == ws(S16, tsp.TSP_F_GROUP_LAUNCH, tsp.TSP_WS_MLP)
-    T, h, hs, Fs, es = 2048, 4096, 512, 1376, 2
-    qkv = (hs + 2 * hs) * h * es            # one packed Q|K|V block
-    kvslot = 2 * 4 * 16384 * 128 * es       # one shard's K and V^T over the sequence
-    grown = 2 * qkv + 2 * kvslot + T * hs * es  # a second shard in each of 2 slots, and in Q
-    diff = ws(S16, 0, tsp.TSP_WS_ATTN) - ws(S16, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
-    assert grown <= diff <= grown + 16 * 1024 * 1024, (diff, grown)  # + split partials, alignment
-    assert ws(S16, 0, tsp.TSP_WS_MLP) - ws(S16, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP) == 2 * 2 * Fs * h * es
-    # fold 4: G = 2 and D/4 = 1, so one shard per launch at any shape
+    h, hs, Fs, es = 4096, 512, 1376, 2
+    qkv = (hs + 2 * hs) * h * es                # one packed Q|K|V block
+    for cfg in (C3, C3.with_(seq=16384)):
+        T, S = cfg.local_tokens, cfg.seq
+        kvslot = 2 * 4 * S * 128 * es           # one shard's K and V^T over the sequence
+        grown = 2 * qkv + 2 * kvslot + T * hs * es  # a second shard in each of 2 slots, and in Q
+        diff = ws(cfg, 0, tsp.TSP_WS_ATTN) - ws(cfg, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
+        assert grown - 16 * 1024 * 1024 <= diff <= grown + 16 * 1024 * 1024, (S, diff, grown)  # split partials
+        assert ws(cfg, 0, tsp.TSP_WS_MLP) - ws(cfg, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP) == 2 * 2 * Fs * h * es
+    # fold 4: G = 2 and D/4 = 1, so one shard per launch either way
     f4 = C3.with_(seq=16384, fold=4)
     assert ws(f4, 0, tsp.TSP_WS_ATTN) == ws(f4, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
-    assert ws(f4, tsp.TSP_F_GROUP_LAUNCH, tsp.TSP_WS_MLP) == ws(f4, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP)
+    assert ws(f4, 0, tsp.TSP_WS_MLP) == ws(f4, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP)
 
 
 def test_micro_batch_workspace():
