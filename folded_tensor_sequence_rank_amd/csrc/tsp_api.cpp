@@ -676,7 +676,8 @@ struct MlpBwdWs {
 // rows), V by rows [B*S][Hkd * d].
 int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 struct AttnBwdWs {
-  size_t o, lse, dl, qt, dot, kt, vr, op, ml, end;
+  size_t o, lse, dl, qt, dot, kt, vr, dqp, op, ml, end;
+  int dq_seg, dq_items;  // the dQ kernel's key segments (attn_bwd_dq_plan)
 };
 AttnBwdWs attn_bwd_ws(const Dims& d, size_t base = 0) {
   AttnBwdWs w;
@@ -688,6 +689,8 @@ AttnBwdWs attn_bwd_ws(const Dims& d, size_t base = 0) {
   w.dot = o; o += al((size_t)d.d * d.Hd * d.B * pad64(d.T) * d.es);
   w.kt = o; o += al((size_t)d.d * d.Hkd * d.B * pad64(d.S) * d.es);
   w.vr = o; o += al((size_t)d.d * d.Hkd * d.BS * d.es);
+  attn_bwd_dq_plan(d.T, d.C, (int)d.r, (int)d.D, d.Hd * d.B, &w.dq_seg, &w.dq_items);
+  w.dqp = o; o += al((size_t)d.Hd * d.B * w.dq_items * 128 * d.d * 4);  // 128-row query blocks
   const AttnPlan p = plan_of(d);
   const size_t nslot = p.split ? (size_t)d.Hd * d.B * p.nqt * p.maxseg * p.bq : 0;
   w.op = o; o += al(nslot * d.d * 4);
@@ -899,6 +902,9 @@ int attn_core_grads(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv, c
   b.Hkd = (int)d.Hkd;
   b.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.d));
   b.scale = (float)(1.0 / std::sqrt((double)d.d));
+  b.dQp = (float*)(w + L.dqp);
+  b.dq_seg = L.dq_seg;
+  b.dq_items = L.dq_items;
   b.Tp = pad64(d.T);
   b.Sp = pad64(d.S);
   b.Qt = w + L.qt;

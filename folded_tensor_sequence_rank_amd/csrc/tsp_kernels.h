@@ -153,6 +153,7 @@ struct AttnBwdArgs {
   const float* LSE;  // [Hd][B*T] log2 of each row's softmax normaliser (scaled scores)
   float* Dl;         // [Hd][B*T] rowsum(dO * O)
   float* dQ;         // [Hd][B*T][HD]
+  float* dQp;        // [Hd][B][dq_items][128][HD]: partial dQ of each (query block, key segment) item
   float* dK;         // [Hkd][B*S][HD]
   float* dV;         // [Hkd][B*S][HD]
   const void* Qt;    // [HD][Hd][B][Tp]: Q transposed, each sequence padded with zero rows to Tp
@@ -162,8 +163,14 @@ struct AttnBwdArgs {
   int64_t T, S, chunk, Tp, Sp;  // Tp, Sp: T and S rounded up to a multiple of 64
   int ldo, rank, fold, batch, grp, Hd, Hkd;
   float scale_log2, scale;
+  int dq_seg, dq_items;  // 64-key blocks per segment; items per (head, sequence)
 };
-// part 0: Dl; 1: dK and dV; 2: dQ.
+// The dQ kernel's work items: each 128-row query block's keys split into
+// segments of at most *seg 64-key blocks, so that the zigzag's long
+// second-chunk blocks do not leave half the CUs idle; *items per (head,
+// sequence).  heads = query heads x sequences of the launch.
+void attn_bwd_dq_plan(int64_t T, int64_t chunk, int rank, int fold, int64_t heads, int* seg, int* items);
+// part 0: Dl; 1: dK and dV; 2: dQ (the items, then their merge).
 hipError_t launch_attn_bwd(int head_dim, const AttnBwdArgs& a, int part, hipStream_t s);
 
 }  // namespace tsp

@@ -356,14 +356,15 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   const int bid = blockIdx.x;
   const int per = nt >> 3;
   const int t = bid < per * 8 ? (bid & 7) * per + (bid >> 3) : bid;
-  // For the QKV projection (and every GEMM under TSP_GEMM_GROUP) the tiles of
-  // that range go in groups of GM tile rows, column by column inside a
-  // group, so the tiles an XCD has in flight (32 of 8 waves, 64 of 4 waves)
-  // form a GM x 8 block: per k-step they read GM A slices and 8 B slices
-  // instead of two full tile rows' worth of B.  Measured in the layer at the
-  // 64K workload: QKV 4% faster; the O projection 3% slower, W2 1% faster,
-  // W1/W3 unchanged, so the others keep row order.
-  constexpr bool GROUPED = TSP_GEMM_GROUP != 0 || EPI == EPI_QKV;
+  // For the QKV and W1/W3 projections (and every GEMM under TSP_GEMM_GROUP)
+  // the tiles of that range go in groups of GM tile rows, column by column
+  // inside a group, so the tiles an XCD has in flight (32 of 8 waves, 64 of
+  // 4 waves) form a GM x 8 block: per k-step they read GM A slices and 8 B
+  // slices instead of two full tile rows' worth of B.  Measured in the layer
+  // with two shards per launch: W1/W3 1% faster at the 64K workload and 9% at
+  // 16K, QKV 4% faster at 64K; the O projection 3% slower, so the
+  // accumulating GEMMs keep row order.
+  constexpr bool GROUPED = TSP_GEMM_GROUP != 0 || EPI == EPI_QKV || EPI == EPI_SWIGLU;
   int m0, n0;
   if constexpr (GROUPED) {
     constexpr int GM = NW == 8 ? 4 : 8;
@@ -2155,8 +2156,27 @@ constexpr int kBK2 = 128;  // keys per work-group of the dK/dV kernel
 constexpr int kBQ2 = 128;  // query rows per work-group of the dQ kernel
 
 // Position of local row i of a rank's zigzag rows (chunks r and 2D-1-r).
-__device__ inline int64_t zz_pos(int64_t i, int64_t C, int r, int D) {
+__host__ __device__ inline int64_t zz_pos(int64_t i, int64_t C, int r, int D) {
   return i < C ? (int64_t)r * C + i : (2 * (int64_t)D - 1 - r) * C + (i - C);
+}
+
+// 64-key blocks that the rows of 128-row query block qb attend to.
+__host__ __device__ inline int dq_key_blocks(int64_t qb, int64_t T, int64_t C, int r, int D) {
+  const int64_t last = ((qb + 1) * kBQ2 < T ? (qb + 1) * kBQ2 : T) - 1;
+  return (int)((zz_pos(last, C, r, D) + kAB) / kAB);
+}
+
+void attn_bwd_dq_plan(int64_t T, int64_t chunk, int rank, int fold, int64_t heads, int* seg, int* items) {
+  const int64_t nqb = (T + kBQ2 - 1) / kBQ2;
+  int64_t total = 0;
+  for (int64_t qb = 0; qb < nqb; qb++) total += dq_key_blocks(qb, T, chunk, rank, fold);
+  // about two work-groups' worth of work per CU (four measured no faster and
+  // doubled the merge), and at least 16 key blocks (1024 keys) per item
+  const int64_t sg = std::max<int64_t>(16, (total * heads + 511) / 512);
+  int64_t n = 0;
+  for (int64_t qb = 0; qb < nqb; qb++) n += (dq_key_blocks(qb, T, chunk, rank, fold) + sg - 1) / sg;
+  *seg = (int)sg;
+  *items = (int)n;
 }
 
 // First local row of rank r whose position reaches p (T if none): positions
@@ -2385,13 +2405,22 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_kernel(AttnBwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int qh = w >> 1, kh = w & 1;
-  const int64_t q0 = (int64_t)blockIdx.x * kBQ2;
+  // item -> (query block, key segment): blocks in order, each split into
+  // ceil(nkb / dq_seg) segments of equal length
+  int64_t qb = 0;
+  int seg = blockIdx.x, nkbq = dq_key_blocks(0, a.T, a.chunk, a.rank, a.fold);
+  for (int ns = (nkbq + a.dq_seg - 1) / a.dq_seg; seg >= ns; ns = (nkbq + a.dq_seg - 1) / a.dq_seg) {
+    seg -= ns;
+    nkbq = dq_key_blocks(++qb, a.T, a.chunk, a.rank, a.fold);
+  }
+  const int nseg = (nkbq + a.dq_seg - 1) / a.dq_seg, slen = (nkbq + nseg - 1) / nseg;
+  const int kb_begin = seg * slen, kb_end = std::min(nkbq, kb_begin + slen);
+  const int64_t q0 = qb * kBQ2;
   const int64_t t = blockIdx.y;
   const int b = blockIdx.z;
   const int64_t hk = t / a.grp;
   const int64_t BS = (int64_t)a.batch * a.S;
   const int nq = (int)std::min<int64_t>(kBQ2, a.T - q0);
-  const int64_t kend = zz_pos(q0 + nq - 1, a.chunk, a.rank, a.fold) + 1;  // keys [0, kend)
   const uint32_t ldo = (uint32_t)a.ldo * 2;
   bf16x8 qf[KS], of[KS];  // second operands of S^T and dP^T: the wave's 32 queries of Q and dO
   {
@@ -2435,14 +2464,13 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; i++) dq[u][i] = 0.f;
   const int kr = 32 * kh + perm_rows(l32);  // the key row the lane feeds into S^T and dP^T
-  const int nkb = (int)((kend + kAB - 1) / kAB);
-  if (nkb > 0) issue(0, 0);
-  for (int kb = 0; kb < nkb; kb++) {
-    const int buf = kb & 1;
+  if (kb_begin < kb_end) issue((int64_t)kb_begin * kAB, 0);
+  for (int kb = kb_begin; kb < kb_end; kb++) {
+    const int buf = (kb - kb_begin) & 1;
     const int64_t k0 = (int64_t)kb * kAB;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // this block's tiles have landed, and no wave still reads the other buffer
-    if (kb + 1 < nkb) issue(k0 + kAB, buf ^ 1);
+    if (kb + 1 < kb_end) issue(k0 + kAB, buf ^ 1);
     const char* Ks = sm + buf * 3 * TB;
     const char* Vs = Ks + TB;
     const char* Kt = Ks + 2 * TB;
@@ -2488,10 +2516,36 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_kernel(AttnBwdArgs a) {
       for (int i = 0; i < 16; i++) {
         const int m = 32 * qh + 8 * (i >> 2) + 4 * h + (i & 3);
         if (m < nq)
-          a.dQ[((t * a.batch + b) * a.T + q0 + m) * HD + 32 * u + l32] =
-              (dq[u][i] + red[((qh * NKB + u) * 16 + i) * 64 + lane]) * a.scale;
+          a.dQp[(((t * a.batch + b) * a.dq_items + blockIdx.x) * kBQ2 + m) * HD + 32 * u + l32] =
+              dq[u][i] + red[((qh * NKB + u) * 16 + i) * 64 + lane];
       }
     }
+  }
+}
+
+// dQ of each row: the sum, in segment order, of its query block's item
+// partials, times 1/sqrt(d).  One work-group per (128-row query block, head
+// and sequence); each thread finds the block's items once.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_bwd_dq_merge_kernel(AttnBwdArgs a) {
+  const int64_t qb = blockIdx.x, tb = blockIdx.y;
+  int first = 0;
+  for (int64_t q = 0; q < qb; q++) first += (dq_key_blocks(q, a.T, a.chunk, a.rank, a.fold) + a.dq_seg - 1) / a.dq_seg;
+  const int nseg = (dq_key_blocks(qb, a.T, a.chunk, a.rank, a.fold) + a.dq_seg - 1) / a.dq_seg;
+  const int nq = (int)std::min<int64_t>(kBQ2, a.T - qb * kBQ2);
+  const float* src = a.dQp + (tb * a.dq_items + first) * kBQ2 * HD;
+  for (int e = threadIdx.x; e < nq * (HD / 4); e += 256) {
+    const int m = e / (HD / 4), c = 4 * (e % (HD / 4));
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sg = 0; sg < nseg; sg++) {
+      const float4 v = *(const float4*)(src + ((int64_t)sg * kBQ2 + m) * HD + c);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    *(float4*)(a.dQ + (tb * a.T + qb * kBQ2 + m) * HD + c) =
+        float4{acc.x * a.scale, acc.y * a.scale, acc.z * a.scale, acc.w * a.scale};
   }
 }
 
@@ -2860,7 +2914,8 @@ hipError_t attn_bwd_hd(const AttnBwdArgs& a, int part, hipStream_t s) {
   } else if (part == 1) {
     attn_bwd_dkdv_kernel<HD><<<dim3((unsigned)((a.S + kBK2 - 1) / kBK2), a.Hkd, a.batch), 512, 0, s>>>(a);
   } else {
-    attn_bwd_dq_kernel<HD><<<dim3((unsigned)((a.T + kBQ2 - 1) / kBQ2), a.Hd, a.batch), 512, 0, s>>>(a);
+    attn_bwd_dq_kernel<HD><<<dim3((unsigned)a.dq_items, a.Hd, a.batch), 512, 0, s>>>(a);
+    attn_bwd_dq_merge_kernel<HD><<<dim3((unsigned)((a.T + kBQ2 - 1) / kBQ2), a.Hd * a.batch), 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
