@@ -262,14 +262,31 @@ struct Events {
   hipEvent_t start, join, readyA[2], freeA[2], readyM[2], freeM[2], freeO[2], freeW[2];
 };
 constexpr int kMaxDev = 64;
-thread_local Events* g_ev[kMaxDev] = {};
+// One host thread's events for each device, destroyed when the thread ends.
+struct EventSets {
+  Events* ev[kMaxDev] = {};
+  ~EventSets() {
+    for (Events* e : ev) {
+      if (!e) continue;
+      hipEvent_t* all[] = {&e->start,    &e->join,     &e->readyA[0], &e->readyA[1],
+                           &e->freeA[0], &e->freeA[1], &e->readyM[0], &e->readyM[1],
+                           &e->freeM[0], &e->freeM[1], &e->freeO[0],  &e->freeO[1],
+                           &e->freeW[0], &e->freeW[1]};
+      for (hipEvent_t* p : all)
+        if (*p) (void)hipEventDestroy(*p);
+      delete e;
+    }
+  }
+};
+thread_local EventSets g_events;
+thread_local Events** const g_ev = g_events.ev;
 
 int get_events(Events** out) {
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   if (dev < 0 || dev >= kMaxDev) return fail(TSP_E_HIP, "device index %d unsupported", dev);
   if (!g_ev[dev]) {
-    Events* e = new Events;
+    Events* e = new Events();  // value-initialised: null handles until created
     hipEvent_t* all[] = {&e->start,    &e->join,     &e->readyA[0], &e->readyA[1],
                          &e->freeA[0], &e->freeA[1], &e->readyM[0], &e->readyM[1],
                          &e->freeM[0], &e->freeM[1], &e->freeO[0],  &e->freeO[1],
@@ -302,6 +319,13 @@ struct ProfState {
   std::vector<Pending> pending;
   double ms[TSP_K_COUNT] = {};
   int64_t n[TSP_K_COUNT] = {};
+  ~ProfState() {  // the thread's timing events, when it ends
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+    for (const Pending& p : pending) {
+      (void)hipEventDestroy(p.a);
+      (void)hipEventDestroy(p.b);
+    }
+  }
 };
 thread_local ProfState g_prof;
 

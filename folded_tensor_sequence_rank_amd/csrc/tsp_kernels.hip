@@ -2238,23 +2238,24 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(AttnBwdArgs a) {
 
 // One work-group per (128-key block, K/V head, sequence): dK and dV of those
 // keys, summed over the head's query heads and every query row of the rank
-// that attends to them.  Eight waves: wave (kh, qh) owns keys 32 kh.. of the
-// block, with K and V in registers, and queries 32 qh.. of each 64-row query
-// block; it sums dK and dV of its keys over its queries in registers, and
-// the two query halves are added once at the end.  Per block: Q, dO (rows)
-// and Q^T, dO^T (from Qt, dOt [HD][Hd][B][Tp]), with the rows' LSE and Dl.
+// that attends to them.  Four waves, one per SIMD: wave w owns keys 32 w..
+// of the block, with K and V in registers, and walks the 64-row query blocks
+// that reach them as two independent 32-row halves, so that the softmax of
+// one half can overlap the other half's MFMAs within the wave.  Per block:
+// Q, dO (rows) and Q^T, dO^T (from Qt, dOt [HD][Hd][B][Tp]), with the rows'
+// LSE and Dl.
 template <int HD>
-__global__ void __launch_bounds__(512) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
-  constexpr int RB = HD * 2;         // bytes of a row of a row-major tile
-  constexpr int TB = kAB * HD * 2;   // bytes of a 64 x HD tile, either layout
-  constexpr int NKB = HD / 32;       // 32-wide blocks of the head dimension
-  constexpr int KS = HD / 16;        // k steps of a product over the head dimension
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  constexpr int RB = HD * 2;        // bytes of a row of a row-major tile
+  constexpr int TB = kAB * HD * 2;  // bytes of a 64 x HD tile, either layout
+  constexpr int NKB = HD / 32;      // 32-wide blocks of the head dimension
+  constexpr int KS = HD / 16;       // k steps of a product over the head dimension
+  constexpr int NW = 4;
   static_assert(2 * kBK2 * RB <= 8 * TB, "K and V staging must fit in the loop's space");
   __shared__ __attribute__((aligned(1024))) char sm[2 * 4 * TB];  // two buffers of [Q | dO | Q^T | dO^T]
   __shared__ float lsd[2][2][kAB];                                // per buffer: the rows' LSE, Dl
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int kh = w >> 1, qh = w & 1;
   const int64_t k0 = (int64_t)blockIdx.x * kBK2;
   const int hk = blockIdx.y, b = blockIdx.z;
   const int64_t BS = (int64_t)a.batch * a.S;
@@ -2264,11 +2265,11 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     const bf16* kb = (const bf16*)a.K + ((int64_t)hk * BS + (int64_t)b * a.S + k0) * HD;
     const bf16* vb = (const bf16*)a.Vr + ((int64_t)b * a.S + k0) * a.Hkd * HD + (int64_t)hk * HD;
     const uint32_t ldv = (uint32_t)a.Hkd * RB;
-    dma_tile<kBK2, RB, 8>(make_rsrc(kb, (uint64_t)nkeys * RB), RB, sm, w, lane);
-    dma_tile<kBK2, RB, 8>(make_rsrc(vb, (uint64_t)(nkeys - 1) * ldv + RB), ldv, sm + kBK2 * RB, w, lane);
+    dma_tile<kBK2, RB, NW>(make_rsrc(kb, (uint64_t)nkeys * RB), RB, sm, w, lane);
+    dma_tile<kBK2, RB, NW>(make_rsrc(vb, (uint64_t)(nkeys - 1) * ldv + RB), ldv, sm + kBK2 * RB, w, lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int r = 32 * kh + l32;
+    const int r = 32 * w + l32;
 #pragma unroll
     for (int k = 0; k < KS; k++) {
       kf[k] = lds_chunk<RB>(sm, r, 2 * k + h);
@@ -2286,14 +2287,14 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     const int nq = (int)std::min<int64_t>(kAB, a.T - q0);
     char* base = sm + buf * 4 * TB;
     const int64_t row0 = (t * a.batch + b) * a.T + q0;
-    dma_tile<kAB, RB, 8>(make_rsrc((const bf16*)a.Q + row0 * HD, (uint64_t)nq * RB), RB, base, w, lane);
-    dma_tile<kAB, RB, 8>(make_rsrc((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD,
-                                   (uint64_t)(nq - 1) * ldo + RB),
-                         ldo, base + TB, w, lane);
+    dma_tile<kAB, RB, NW>(make_rsrc((const bf16*)a.Q + row0 * HD, (uint64_t)nq * RB), RB, base, w, lane);
+    dma_tile<kAB, RB, NW>(make_rsrc((const bf16*)a.dO + ((int64_t)b * a.T + q0) * a.ldo + t * HD,
+                                    (uint64_t)(nq - 1) * ldo + RB),
+                          ldo, base + TB, w, lane);
     const int64_t col = (t * a.batch + b) * a.Tp + q0;
     const uint64_t tbytes = (uint64_t)(HD - 1) * ldt + 128;
-    dma_tile<HD, 128, 8>(make_rsrc((const bf16*)a.Qt + col, tbytes), ldt, base + 2 * TB, w, lane);
-    dma_tile<HD, 128, 8>(make_rsrc((const bf16*)a.dOt + col, tbytes), ldt, base + 3 * TB, w, lane);
+    dma_tile<HD, 128, NW>(make_rsrc((const bf16*)a.Qt + col, tbytes), ldt, base + 2 * TB, w, lane);
+    dma_tile<HD, 128, NW>(make_rsrc((const bf16*)a.dOt + col, tbytes), ldt, base + 3 * TB, w, lane);
     if (w == 0) {
       buffer_to_lds4(make_rsrc(a.LSE + row0, (uint64_t)nq * 4), lsd[buf][0], (uint32_t)lane * 4);
       buffer_to_lds4(make_rsrc(a.Dl + row0, (uint64_t)nq * 4), lsd[buf][1], (uint32_t)lane * 4);
@@ -2305,9 +2306,8 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; i++) dk[u][i] = dv[u][i] = 0.f;
   // the lane's key (its column of S) is seen by local rows [qk, T)
-  const int64_t qk = first_row_at(k0 + 32 * kh + l32, a.chunk, a.rank, a.fold, a.T);
-  const int qr = 32 * qh + perm_rows(l32);  // the query row the lane feeds into S and dP
-  const int mb = 32 * qh + 8 * h;           // register i holds query block row mb + 16 (i / 8) + i % 8
+  const int64_t qk = first_row_at(k0 + 32 * w + l32, a.chunk, a.rank, a.fold, a.T);
+  const int qr = perm_rows(l32);  // the row of each 32-row half the lane feeds into S and dP
   if (total > 0) issue(0, 0);
   for (int it = 0; it < total; it++) {
     const int buf = it & 1;
@@ -2319,70 +2319,101 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     const char* dOs = Qs + TB;
     const char* Qt = Qs + 2 * TB;
     const char* dOt = Qs + 3 * TB;
-    f32x16 s, dp;
+    // P and dS as first operands: register i of half qh holds block row
+    // 32 qh + 8 h + 16 (i / 8) + i % 8, kept when that row is in [lo, hi)
+    const int lo = (int)std::min<int64_t>(std::max<int64_t>(qk - q0, 0), kAB) - 8 * h;
+    const int hi = (int)std::min<int64_t>(a.T - q0, kAB) - 8 * h;
+    // the rows' LSE and Dl, 16 of each per half
+    float4 lr[2][4], dr[2][4];
 #pragma unroll
-    for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
+    for (int qh = 0; qh < 2; qh++)
 #pragma unroll
-    for (int k = 0; k < KS; k++) {
-      s = MF<bf16>::mma(lds_chunk<RB>(Qs, qr, 2 * k + h), kf[k], s);
-      dp = MF<bf16>::mma(lds_chunk<RB>(dOs, qr, 2 * k + h), vf[k], dp);
-    }
-    // P and dS as first operands over the wave's 32 queries: register i holds
-    // block row mb + 16 (i / 8) + i % 8, kept when that row is in [lo, hi)
-    const int lo = (int)std::min<int64_t>(std::max<int64_t>(qk - q0, 0), kAB) - mb;
-    const int hi = (int)std::min<int64_t>(a.T - q0, kAB) - mb;
-    bf16x8 pa[2], da[2];
+      for (int j = 0; j < 4; j++) {
+        const int m = 32 * qh + 16 * (j >> 1) + 8 * h + 4 * (j & 1);
+        lr[qh][j] = *(const float4*)&lsd[buf][0][m];
+        dr[qh][j] = *(const float4*)&lsd[buf][1][m];
+      }
+    // MFMA steps: S and dP of half 0 (2 KS steps), of half 1 (2 KS, with
+    // half 0's softmax), dV and dK of half 0 (4 NKB, with half 1's softmax),
+    // of half 1 (4 NKB).  Step i reads the operand of step i + PD from LDS.
+    // Alternate steps feed different accumulators, so no MFMA waits on the
+    // one before.
+    constexpr int PD = 4, NA = 2 * KS, NB = 4 * NKB, NS = 2 * (NA + NB);
+    constexpr int EA = 16 / NA, EB = 16 / NB;  // softmax elements per step
+    static_assert(16 % NA == 0 && 16 % NB == 0, "softmax elements must spread evenly over the steps");
+    auto frag_at = [&](int i) -> bf16x8 {
+      if (i < 2 * NA) {
+        const int qh = i / NA, k = (i % NA) >> 1;
+        return lds_chunk<RB>((i & 1) ? dOs : Qs, 32 * qh + qr, 2 * k + h);
+      }
+      const int qh = (i - 2 * NA) / NB, j = (i - 2 * NA) % NB, s2 = j / (2 * NKB), u = (j % (2 * NKB)) >> 1;
+      return lds_chunk<128>((j & 1) ? Qt : dOt, 32 * u + l32, 4 * qh + 2 * s2 + h);
+    };
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; s2++) {
-      const float4* lp = (const float4*)&lsd[buf][0][mb + 16 * s2];
-      const float4* dq4 = (const float4*)&lsd[buf][1][mb + 16 * s2];
-      const float4 l0 = lp[0], l1 = lp[1], d0 = dq4[0], d1 = dq4[1];
-      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-      const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    for (int qh = 0; qh < 2; qh++)
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int i = 8 * s2 + j, c = 16 * s2 + j;
-        const float e = fast_exp2(s[i] * a.scale_log2 - lv[j]);
-        const float pr = (c >= lo && c < hi) ? e : 0.f;
-        pa[s2][j] = (bf16)pr;
-        da[s2][j] = (bf16)(pr * (dp[i] - dv8[j]));
+      for (int i = 0; i < 16; i++) s[qh][i] = dp[qh][i] = 0.f;
+    bf16x8 pa[2][2], da[2][2];
+    auto soft = [&](int qh, int i) {  // softmax element i of half qh
+      const float4 l4 = lr[qh][i >> 2], d4 = dr[qh][i >> 2];
+      const int e = i & 3;
+      const float lv = e == 0 ? l4.x : e == 1 ? l4.y : e == 2 ? l4.z : l4.w;
+      const float dl = e == 0 ? d4.x : e == 1 ? d4.y : e == 2 ? d4.z : d4.w;
+      const int c = 32 * qh + 16 * (i >> 3) + (i & 7);
+      const float ex = fast_exp2(s[qh][i] * a.scale_log2 - lv);
+      const float pr = (c >= lo && c < hi) ? ex : 0.f;
+      pa[qh][i >> 3][i & 7] = (bf16)pr;
+      da[qh][i >> 3][i & 7] = (bf16)(pr * (dp[qh][i] - dl));
+    };
+    bf16x8 ring[PD];
+#pragma unroll
+    for (int i = 0; i < PD; i++) ring[i] = frag_at(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qh = 0; qh < 2; qh++) {
+#pragma unroll
+      for (int j = 0; j < NA; j++) {
+        const int i = NA * qh + j;
+        const bf16x8 f = ring[i % PD];
+        ring[i % PD] = frag_at(i + PD);
+        if (j & 1)
+          dp[qh] = MF<bf16>::mma(f, vf[j >> 1], dp[qh]);
+        else
+          s[qh] = MF<bf16>::mma(f, kf[j >> 1], s[qh]);
+        if (qh == 1)
+#pragma unroll
+          for (int e = 0; e < EA; e++) soft(0, EA * j + e);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // dV += P^T dO and dK += dS^T Q for every 32-wide block of the head dimension
 #pragma unroll
-    for (int s2 = 0; s2 < 2; s2++) {
-      const int c = 4 * qh + 2 * s2 + h;  // the 8 queries' chunk in the transposed tiles
+    for (int qh = 0; qh < 2; qh++) {
 #pragma unroll
-      for (int u = 0; u < NKB; u++) {
-        dv[u] = MF<bf16>::mma(pa[s2], lds_chunk<128>(dOt, 32 * u + l32, c), dv[u]);
-        dk[u] = MF<bf16>::mma(da[s2], lds_chunk<128>(Qt, 32 * u + l32, c), dk[u]);
+      for (int j = 0; j < NB; j++) {
+        const int i = 2 * NA + NB * qh + j, s2 = j / (2 * NKB), u = (j % (2 * NKB)) >> 1;
+        const bf16x8 f = ring[i % PD];
+        if (i + PD < NS) ring[i % PD] = frag_at(i + PD);
+        if (j & 1)
+          dk[u] = MF<bf16>::mma(da[qh][s2], f, dk[u]);
+        else
+          dv[u] = MF<bf16>::mma(pa[qh][s2], f, dv[u]);
+        if (qh == 0)
+#pragma unroll
+          for (int e = 0; e < EB; e++) soft(1, EB * j + e);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
-  // The two query halves' sums meet in LDS; the qh = 0 waves store.
-  __syncthreads();
-  float* red = (float*)sm;  // [kh][dK | dV][NKB][16][64]
-  if (qh == 1) {
 #pragma unroll
-    for (int u = 0; u < NKB; u++)
+  for (int u = 0; u < NKB; u++) {
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        red[(((kh * 2 + 0) * NKB + u) * 16 + i) * 64 + lane] = dk[u][i];
-        red[(((kh * 2 + 1) * NKB + u) * 16 + i) * 64 + lane] = dv[u][i];
-      }
-  }
-  __syncthreads();
-  if (qh == 0) {
-#pragma unroll
-    for (int u = 0; u < NKB; u++) {
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int64_t kk = k0 + 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (kk < a.S) {
-          const int64_t off = ((int64_t)hk * BS + (int64_t)b * a.S + kk) * HD + 32 * u + l32;
-          a.dK[off] = (dk[u][i] + red[(((kh * 2 + 0) * NKB + u) * 16 + i) * 64 + lane]) * a.scale;
-          a.dV[off] = dv[u][i] + red[(((kh * 2 + 1) * NKB + u) * 16 + i) * 64 + lane];
-        }
+    for (int i = 0; i < 16; i++) {
+      const int64_t kk = k0 + 32 * w + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (kk < a.S) {
+        const int64_t off = ((int64_t)hk * BS + (int64_t)b * a.S + kk) * HD + 32 * u + l32;
+        a.dK[off] = dk[u][i] * a.scale;
+        a.dV[off] = dv[u][i];
       }
     }
   }
@@ -2912,7 +2943,7 @@ hipError_t attn_bwd_hd(const AttnBwdArgs& a, int part, hipStream_t s) {
     const int64_t items = (int64_t)a.Hd * a.batch * a.T;
     attn_bwd_delta_kernel<HD><<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a);
   } else if (part == 1) {
-    attn_bwd_dkdv_kernel<HD><<<dim3((unsigned)((a.S + kBK2 - 1) / kBK2), a.Hkd, a.batch), 512, 0, s>>>(a);
+    attn_bwd_dkdv_kernel<HD><<<dim3((unsigned)((a.S + kBK2 - 1) / kBK2), a.Hkd, a.batch), 256, 0, s>>>(a);
   } else {
     attn_bwd_dq_kernel<HD><<<dim3((unsigned)a.dq_items, a.Hd, a.batch), 512, 0, s>>>(a);
     attn_bwd_dq_merge_kernel<HD><<<dim3((unsigned)((a.T + kBQ2 - 1) / kBQ2), a.Hd * a.batch), 256, 0, s>>>(a);
