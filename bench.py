@@ -58,6 +58,9 @@ def parse():
                     help="time the attention core's backward for one head group instead")
     ap.add_argument("--layer-backward", action="store_true",
                     help="time the whole layer's backward of one rank (both parts) instead")
+    ap.add_argument("--recompute-attn", action="store_true",
+                    help="with --layer-backward: recompute each head group's forward attention in the "
+                         "backward instead of taking what tsp_attn_shard_save kept")
     ap.add_argument("--kv-stream", action="store_true",
                     help="headline with the other ranks' K/V copied through the side-stream slots "
                          "(TSP_F_KV_STREAM) instead of read in place; both are reported either way")
@@ -330,8 +333,10 @@ def layer_backward_bench(args):
     the forward's projections and MLP (data and weight gradients,
     2 * (8 T h^2 + 6 T h F) at one K/V head per query head) and 8 d per
     (query, visible key) pair and head (dP, dV, dQ, dK).  The recomputation
-    (forward attention, S and dP in the dQ kernel, the MLP's and QKV's
-    projections, the norms) is reported apart."""
+    (S and dP in the dQ kernel, the MLP's and QKV's projections, the norms,
+    and with --recompute-attn the forward attention) is reported apart.  By
+    default the forward is tsp_attn_shard_save, whose attention output and
+    softmax normalisers the backward takes."""
     import numpy as np
     import torch
 
@@ -354,7 +359,11 @@ def layer_backward_bench(args):
     fill_kv(cfg, L, xs, kv)
     x = xs[r]
     xs = None
-    x1 = RankRun(cfg, r).attn(x, L, kv)
+    saved = not args.recompute_attn
+    if saved:
+        x1, a_saved, lse_saved = RankRun(cfg, r).attn_save(x, L, kv)
+    else:
+        x1, a_saved, lse_saved = RankRun(cfg, r).attn(x, L, kv), None, None
     dout = to_dev(np.concatenate([synth.gen_rows(cfg, tsp.zigzag_positions(cfg.seq, D, r), layer=7, seq_index=b)
                                   for b in range(B)]), cfg)
     dims = tsp.make_dims(cfg, r)
@@ -374,7 +383,7 @@ def layer_backward_bench(args):
 
     def step():
         tsp.tsp_layer_shard_backward(dims, x, x1, L.g1, L.w_attn, kv, L.g2, L.w_mlp, dout, dx1, dg2, dw_mlp, dw_o,
-                                     dq, dkv, ws1)
+                                     dq, dkv, ws1, attn_saved=a_saved, lse_saved=lse_saved)
         tsp.tsp_layer_shard_backward_finish(dims, x, L.g1, L.w_attn, dx1, dq, dkv_own, dx, dg1, dw_qkv, ws2)
 
     for _ in range(args.warmup):
@@ -391,7 +400,7 @@ def layer_backward_bench(args):
     pairs = B * int((tsp.zigzag_positions(cfg.seq, D, r) + 1).sum())
     proj = 2 * BT * h * (h + 2 * Hkv * d) + 2 * BT * h * h + 6 * BT * h * cfg.ffn
     f_alg = 2 * proj + 8 * d * pairs * H
-    recompute = (4 * d * pairs * H          # forward attention for O and the log-sum-exp
+    recompute = ((0 if saved else 4 * d * pairs * H)  # forward attention for O and the log-sum-exp
                  + 4 * d * pairs * H        # S and dP again in the dQ kernel
                  + 4 * BT * h * cfg.ffn     # n2 W1 and n2 W3
                  + 2 * BT * h * (h + 2 * Hkv * d))  # Q and the rank's own K/V rows
@@ -402,7 +411,8 @@ def layer_backward_bench(args):
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "step_ms": {"median": round(per[len(per) // 2], 4), "min": round(per[0], 4), "max": round(per[-1], 4)},
         "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "rank": r, "batch": B, "local_tokens": BT},
+        "config": {"workload": cfg.name, "rank": r, "batch": B, "local_tokens": BT,
+                   "attention": "saved by the forward" if saved else "recomputed"},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "flops_per_step": f_alg, "recompute_flops_per_step": recompute,
         "executed_tflops": round((f_alg + recompute) / (ms * 1e-3) / 1e12, 2)}), flush=True)

@@ -468,12 +468,12 @@ int qkv_gemm(Ctx& c, const void* xn, const char* w, int col0, void* q, char* kvs
 
 // y (+)= a . w^T, or on the last group out = resid + y + a . w^T.
 // a [T][ld], w [h][ld]; only the first K columns take part.
-int acc_gemm(Ctx& c, const void* a, int64_t K, int64_t ld, const char* w, float* y, bool first,
+int acc_gemm(Ctx& c, const void* a, int64_t lda, int64_t K, int64_t ld, const char* w, float* y, bool first,
              bool last, const void* resid, void* out) {
   const Dims& d = *c.d;
   GemmArgs g = gemm_base();
   g.A = a;
-  g.lda = ld;
+  g.lda = lda;
   g.B = w;
   g.ldb = ld;
   g.M = (int)d.BT;
@@ -494,8 +494,11 @@ int acc_gemm(Ctx& c, const void* a, int64_t K, int64_t ld, const char* w, float*
   return TSP_OK;
 }
 
+// With save_a / save_lse, each head group's attention output goes to
+// save_a [B*T][h] (group j at columns j*hs) instead of the workspace, and
+// every row's log2 softmax normaliser to save_lse [H][B*T], for the backward.
 int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void* const* w_attn,
-              const void* kv, void* x1) {
+              const void* kv, void* x1, void* save_a = nullptr, float* save_lse = nullptr) {
   const Dims& d = *c.d;
   char* ws = c.ws;
   const size_t es = d.es;
@@ -560,14 +563,18 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
       a.kvh_per_shard = (int)d.Hkd;
       a.shard_stride = (int64_t)kv_block_elems(d);
     }
-    a.O = ws + L.o + gp * d.hs * es;  // these shards' columns of the group's [T][G*hs]
+    // these shards' columns of the group's [B*T][G*hs], or of save_a
+    char* const obase = save_a ? (char*)save_a + gi * G * d.hs * es : ws + L.o;
+    const int64_t ldA = save_a ? d.h : G * d.hs;
+    a.O = obase + gp * d.hs * es;
+    if (save_lse) a.LSE = save_lse + j0 * d.Hd * d.BT;
     a.Op = (float*)(ws + L.op);
     a.ML = (float*)(ws + L.ml);
     a.T = d.T;
     a.S = d.S;
     a.batch = (int)d.B;
     a.chunk = d.C;
-    a.ldo = (int)(G * d.hs);
+    a.ldo = (int)ldA;
     a.rank = (int)d.r;
     a.fold = (int)d.D;
     a.Hd = (int)(np * d.Hd);
@@ -584,7 +591,7 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     if (plan.split) TIMED(c, TSP_K_MERGE, HIP_TRY(launch_attention(d.dt, (int)d.d, a, plan, 1, c.s)));
     if (gp + np == G || j0 + np == d.D) {  // group complete: one O projection over its shards
       TIMED(c, TSP_K_OPROJ,
-            rc = acc_gemm(c, ws + L.o, (gp + np) * d.hs, G * d.hs, bo, (float*)(ws + L.y), gi == 0,
+            rc = acc_gemm(c, obase, ldA, (gp + np) * d.hs, G * d.hs, bo, (float*)(ws + L.y), gi == 0,
                           j0 + np == d.D, x, x1));
       if (rc) return rc;
       if (c.side) HIP_TRY(hipEventRecord(c.ev->freeO[gb], c.s));
@@ -656,7 +663,7 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
     int rc = 0;
     if (gp + np == G || t0 + np == d.D) {  // group complete: one W2 projection over its shards
       TIMED(c, TSP_K_W2,
-            rc = acc_gemm(c, ws + L.gg, (gp + np) * d.Fs, G * d.Fs, bw, (float*)(ws + L.y), gi == 0,
+            rc = acc_gemm(c, ws + L.gg, G * d.Fs, (gp + np) * d.Fs, G * d.Fs, bw, (float*)(ws + L.y), gi == 0,
                           t0 + np == d.D, x1, out));
       if (rc) return rc;
       if (c.side) HIP_TRY(hipEventRecord(c.ev->freeW[gb], c.s));
@@ -895,9 +902,10 @@ int attn_recompute(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv) {
 }
 
 // dq [Hd][B*T][d] and this rank's partial dk, dv [Hkd][B*S][d] (fp32) of the
-// group, given its recomputed O and log-sum-exp (in L) and dout [B*T][ldo].
-int attn_core_grads(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv, const void* dout, int ldo,
-                    float* dq, float* dk, float* dv) {
+// group, given its forward output o [B*T][ldo_fwd], the rows' log2 softmax
+// normalisers lse [Hd][B*T] and dout [B*T][ldo].
+int attn_core_grads(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv, const void* o, int ldo_fwd,
+                    const float* lse, const void* dout, int ldo, float* dq, float* dk, float* dv) {
   const Dims& d = *c.d;
   const hipStream_t s = c.s;
   char* w = c.ws;
@@ -907,9 +915,9 @@ int attn_core_grads(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv, c
   b.Q = q;
   b.K = kv;
   b.Vt = vt;
-  b.O = w + L.o;
+  b.O = o;
   b.dO = dout;
-  b.LSE = (const float*)(w + L.lse);
+  b.LSE = lse;
   b.Dl = (float*)(w + L.dl);
   b.dQ = dq;
   b.dK = dk;
@@ -918,6 +926,7 @@ int attn_core_grads(Ctx& c, const AttnBwdWs& L, const void* q, const void* kv, c
   b.S = d.S;
   b.chunk = d.C;
   b.ldo = ldo;
+  b.ldo_fwd = ldo_fwd;
   b.rank = (int)d.r;
   b.fold = (int)d.D;
   b.batch = (int)d.B;
@@ -1042,6 +1051,25 @@ int tsp_attn_shard(const tsp_dims* dims, const void* x, const void* g1, const vo
   return finish(c);
 }
 
+int tsp_attn_shard_save(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,
+                        const void* kv, void* x1, void* attn_out, float* lse, void* ws, size_t ws_bytes,
+                        void* stream, void* copy_stream) {
+  g_err.clear();
+  Dims d;
+  int rc = check_dims(dims, &d);
+  if (rc) return rc;
+  if (d.S == 0) return TSP_OK;
+  if ((rc = check_ptrs({x, g1, kv, x1, attn_out, lse, ws})) || (rc = check_shards(w_attn, d.D, "w_attn")))
+    return rc;
+  const AttnWs L = attn_ws(d, 0);
+  if (ws_bytes < L.end)
+    return fail(TSP_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.end);
+  Ctx c{&d, (char*)ws};
+  if ((rc = begin(c, (hipStream_t)stream, (hipStream_t)copy_stream, d.flags))) return rc;
+  if ((rc = attn_body(c, L, x, g1, w_attn, kv, x1, attn_out, lse))) return rc;
+  return finish(c);
+}
+
 int tsp_mlp_shard(const tsp_dims* dims, const void* x1, const void* g2, const void* const* w_mlp,
                   void* out, void* ws, size_t ws_bytes, void* stream, void* copy_stream) {
   g_err.clear();
@@ -1130,14 +1158,17 @@ int tsp_layer_shard_noalloc(const tsp_dims* dims, const void* x, const void* g1,
 
 int tsp_layer_shard_backward(const tsp_dims* dims, const void* x, const void* x1, const void* g1,
                              const void* const* w_attn, const void* kv, const void* g2, const void* const* w_mlp,
-                             const void* dout, void* dx1, float* dg2, float* const* dw_mlp, float* const* dw_o,
-                             float* dq, float* dkv, void* ws, size_t ws_bytes, void* stream) {
+                             const void* dout, const void* attn_saved, const float* lse_saved, void* dx1,
+                             float* dg2, float* const* dw_mlp, float* const* dw_o, float* dq, float* dkv, void* ws,
+                             size_t ws_bytes, void* stream) {
   g_err.clear();
   Dims d;
   int rc = check_dims(dims, &d);
   if (rc) return rc;
   if (d.S == 0) return TSP_OK;
   if ((rc = check_attn_bwd_dims(d))) return rc;
+  if (!attn_saved != !lse_saved)
+    return fail(TSP_E_INVAL, "attn_saved and lse_saved are given together or not at all");
   if ((rc = check_ptrs({x, x1, g1, kv, g2, dout, dx1, dg2, dq, dkv, ws})) ||
       (rc = check_shards(w_attn, d.D, "w_attn")) || (rc = check_shards(w_mlp, d.D, "w_mlp")) ||
       (rc = check_shards((const void* const*)dw_mlp, d.D, "dw_mlp")) ||
@@ -1164,7 +1195,17 @@ int tsp_layer_shard_backward(const tsp_dims* dims, const void* x, const void* x1
     // every other rank's rows copied from the gathered buffer
     if ((rc = copy_remote_kv(c, (const char*)kv + (size_t)j * kvbytes, w + L.slotkv, true))) return rc;
     if ((rc = qkv_gemm(c, w + L.n1, wj, 0, w + L.q, w + L.slotkv))) return rc;
-    if ((rc = attn_recompute(c, L.attn, w + L.q, w + L.slotkv))) return rc;
+    // the group's attention output and normalisers: the forward's, or recomputed
+    const void* oj = w + L.attn.o;
+    const float* lj = (const float*)(w + L.attn.lse);
+    int64_t ldoj = d.hs;
+    if (attn_saved) {
+      oj = (const char*)attn_saved + (size_t)j * d.hs * es;
+      lj = lse_saved + (size_t)j * d.Hd * d.BT;
+      ldoj = d.h;
+    } else if ((rc = attn_recompute(c, L.attn, w + L.q, w + L.slotkv))) {
+      return rc;
+    }
     // dA = dx1 W_O^T, and this rank's partial dW_O = dx1^T A (packed layout)
     HIP_TRY(launch_transpose(d.dt, wj + qkvbytes, w + L.wot, d.h, d.hs, d.hs, d.h, c.s));
     GemmArgs g = gemm_base();
@@ -1178,10 +1219,12 @@ int tsp_layer_shard_backward(const tsp_dims* dims, const void* x, const void* x1
     g.C = w + L.da;
     g.ldc = d.hs;
     HIP_TRY(launch_gemm(d.dt, EPI_STORE, g, c.s));
-    HIP_TRY(launch_transpose(d.dt, w + L.attn.o, w + L.ot, d.BT, d.hs, d.hs, d.BT, c.s));
+    HIP_TRY(launch_transpose(d.dt, oj, w + L.ot, d.BT, d.hs, ldoj, d.BT, c.s));
     if ((rc = plain_gemm(c, w + L.dx1t, d.BT, w + L.ot, d.BT, d.h, d.hs, d.BT, dw_o[j], d.hs, false))) return rc;
     // the attention core: dQ of the rank's rows, partial dK / dV of every position
-    if ((rc = attn_core_grads(c, L.attn, w + L.q, w + L.slotkv, w + L.da, (int)d.hs, dqj, dkj, dvj))) return rc;
+    if ((rc = attn_core_grads(c, L.attn, w + L.q, w + L.slotkv, oj, (int)ldoj, lj, w + L.da, (int)d.hs, dqj, dkj,
+                              dvj)))
+      return rc;
     if (l2c > 0.0) {  // gradients of the rotated Q and K, taken back through the rotation
       HIP_TRY(launch_rope_inverse(dqj, d.BT, (int)d.Hd, (int)d.d, 0, d.T, d.C, (int)d.r, (int)d.D, l2c, c.s));
       HIP_TRY(launch_rope_inverse(dkj, d.BS, (int)d.Hkd, (int)d.d, d.S, d.T, d.C, (int)d.r, (int)d.D, l2c, c.s));
@@ -1268,7 +1311,8 @@ int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, 
   Ctx c{&d, (char*)ws, (hipStream_t)stream, (hipStream_t)stream, false, nullptr, false};
   // forward recomputation: the group's output and each row's log-sum-exp
   if ((rc = attn_recompute(c, L, q, kv))) return rc;
-  return attn_core_grads(c, L, q, kv, dout, (int)d.hs, dq, dk, dv);
+  return attn_core_grads(c, L, q, kv, c.ws + L.o, (int)d.hs, (const float*)(c.ws + L.lse), dout, (int)d.hs, dq,
+                         dk, dv);
 }
 
 int tsp_kv_shard(const tsp_dims* dims, const void* x, const void* g1, const void* const* w_attn,

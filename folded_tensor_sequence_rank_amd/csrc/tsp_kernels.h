@@ -148,8 +148,8 @@ struct AttnBwdArgs {
   const void* Q;     // [Hd][B*T][HD] rotated queries
   const void* K;     // [Hkd][B*S][HD]
   const void* Vt;    // [Hkd][HD][B*S]
-  const void* O;     // [B*T][ldo] forward output, head t at columns t*HD
-  const void* dO;    // [B*T][ldo] its gradient
+  const void* O;     // [B*T][ldo_fwd] forward output, head t at columns t*HD
+  const void* dO;    // [B*T][ldo] its gradient, the same columns
   const float* LSE;  // [Hd][B*T] log2 of each row's softmax normaliser (scaled scores)
   float* Dl;         // [Hd][B*T] rowsum(dO * O)
   float* dQ;         // [Hd][B*T][HD]
@@ -161,7 +161,7 @@ struct AttnBwdArgs {
   const void* Kt;    // [HD][Hkd][B][Sp]: K transposed, each sequence padded with zero keys to Sp
   const void* Vr;    // [B*S][Hkd*HD]: V by rows
   int64_t T, S, chunk, Tp, Sp;  // Tp, Sp: T and S rounded up to a multiple of 64
-  int ldo, rank, fold, batch, grp, Hd, Hkd;
+  int ldo, ldo_fwd, rank, fold, batch, grp, Hd, Hkd;  // row pitches of dO and O
   float scale_log2, scale;
   int dq_seg, dq_items;  // 64-key blocks per segment; items per (head, sequence)
 };

@@ -2228,7 +2228,7 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(AttnBwdArgs a) {
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= (int64_t)a.Hd * BT) return;
   const int64_t t = item / BT, rowg = item % BT;
-  const bf16* o = (const bf16*)a.O + rowg * a.ldo + t * HD;
+  const bf16* o = (const bf16*)a.O + rowg * a.ldo_fwd + t * HD;
   const bf16* g = (const bf16*)a.dO + rowg * a.ldo + t * HD;
   float s = 0.f;
   for (int e = lane; e < HD; e += 64) s += (float)o[e] * (float)g[e];

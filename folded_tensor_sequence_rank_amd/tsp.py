@@ -74,14 +74,15 @@ def lib() -> ctypes.CDLL:
         L.tsp_zigzag_positions.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_int64)]
         L.tsp_attn_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _sz, _vp, _vp]
+        L.tsp_attn_shard_save.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_mlp_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_layer_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _sz, _vp, _vp]
         L.tsp_kv_shard.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _sz, _vp]
         L.tsp_layer_shard_noalloc.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _vp]
         L.tsp_mlp_shard_backward.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _pp, _vp, _sz, _vp]
         L.tsp_attn_core_backward.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
-        L.tsp_layer_shard_backward.argtypes = [D, _vp, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _vp, _pp,
-                                               _pp, _vp, _vp, _vp, _sz, _vp]
+        L.tsp_layer_shard_backward.argtypes = [D, _vp, _vp, _vp, _pp, _vp, _vp, _pp, _vp, _vp, _vp, _vp,
+                                               _vp, _pp, _pp, _vp, _vp, _vp, _sz, _vp]
         L.tsp_kv_grad_reduce.argtypes = [D, _pp, _vp, _vp]
         L.tsp_layer_shard_backward_finish.argtypes = [D, _vp, _vp, _pp, _vp, _vp, _vp, _vp, _vp, _pp, _vp,
                                                       _sz, _vp]
@@ -89,7 +90,7 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(ctypes.c_int32), _vp]
         L.tsp_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
-        for f in ("tsp_attn_shard", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
+        for f in ("tsp_attn_shard", "tsp_attn_shard_save", "tsp_mlp_shard", "tsp_layer_shard", "tsp_kv_shard",
                   "tsp_mlp_shard_backward", "tsp_attn_core_backward", "tsp_layer_shard_backward",
                   "tsp_kv_grad_reduce", "tsp_layer_shard_backward_finish",
                   "tsp_zigzag_positions", "tsp_profile_read", "tsp_clock_probe",
@@ -195,6 +196,26 @@ def tsp_attn_shard(dims, x, g1, w_attn, kv, x1, ws, stream=None, copy_stream=Non
                                 None if copy_stream is None else _stream(copy_stream)))
 
 
+def _saved_sizes(dims):
+    """Bytes of tsp_attn_shard_save's attn_out and lse."""
+    es = 2 if dims.dtype == TSP_BF16 else 4
+    BT = max(dims.batch, 1) * (dims.seq // dims.fold)
+    return BT * dims.hidden * es, dims.n_heads * BT * 4
+
+
+def tsp_attn_shard_save(dims, x, g1, w_attn, kv, x1, attn_out, lse, ws, stream=None, copy_stream=None):
+    """tsp_attn_shard that also keeps each head group's attention output
+    attn_out [B*T][h] and the rows' log2 softmax normalisers lse [H][B*T]
+    (fp32) for tsp_layer_shard_backward (include/tsp.h)."""
+    _check_sizes(dims, TSP_WS_ATTN, x=x, g1=g1, w_attn=w_attn, kv=kv, x1=x1)
+    na, nl = _saved_sizes(dims)
+    _need("attn_out", attn_out, na)
+    _need("lse", lse, nl)
+    _check(lib().tsp_attn_shard_save(ctypes.byref(dims), _ptr(x), _ptr(g1), _ptrs(w_attn), _ptr(kv),
+                                     _ptr(x1), _ptr(attn_out), _ptr(lse), _ptr(ws), _nbytes(ws),
+                                     _stream(stream), None if copy_stream is None else _stream(copy_stream)))
+
+
 def tsp_mlp_shard(dims, x1, g2, w_mlp, out, ws, stream=None, copy_stream=None):
     _check_sizes(dims, TSP_WS_MLP, x1=x1, g2=g2, w_mlp=w_mlp, out=out)
     _check(lib().tsp_mlp_shard(ctypes.byref(dims), _ptr(x1), _ptr(g2), _ptrs(w_mlp), _ptr(out),
@@ -285,23 +306,29 @@ def _bwd_sizes(dims):
 
 
 def tsp_layer_shard_backward(dims, x, x1, g1, w_attn, kv, g2, w_mlp, dout, dx1, dg2, dw_mlp, dw_o, dq, dkv,
-                             ws, stream=None):
+                             ws, stream=None, attn_saved=None, lse_saved=None):
     """Part 1 of the whole layer's backward (include/tsp.h): dx1, the partial
     dg2, dw_mlp and dw_o, the unrotated dq [H][B*T][d] and the partial dkv
-    [D][2][Hkv/D][B*S][d] (fp32)."""
+    [D][2][Hkv/D][B*S][d] (fp32).  attn_saved / lse_saved: the attn_out and
+    lse of tsp_attn_shard_save (the forward attention is then not
+    recomputed), or both None."""
     _check_sizes(dims, TSP_WS_LAYER_BWD, x=x, g1=g1, w_attn=w_attn, kv=kv, g2=g2, w_mlp=w_mlp, out=dout)
     _check_sizes(dims, TSP_WS_LAYER_BWD, x1=x1)
     _check_sizes(dims, TSP_WS_LAYER_BWD, x=dx1)
     n = _bwd_sizes(dims)
     for name, t in (("dq", dq), ("dkv", dkv), ("dg2", dg2)):
         _need(name, t, n[name] if name != "dg2" else n["gain"])
+    na, nl = _saved_sizes(dims)
+    _need("attn_saved", attn_saved, na)
+    _need("lse_saved", lse_saved, nl)
     for name, ts in (("dw_mlp", dw_mlp), ("dw_o", dw_o)):
         if len(ts) != dims.fold:
             raise ValueError(f"{name}: {len(ts)} shards for fold {dims.fold}")
         for i, t in enumerate(ts):
             _need(f"{name}[{i}]", t, n[name])
     _check(lib().tsp_layer_shard_backward(ctypes.byref(dims), _ptr(x), _ptr(x1), _ptr(g1), _ptrs(w_attn),
-                                          _ptr(kv), _ptr(g2), _ptrs(w_mlp), _ptr(dout), _ptr(dx1), _ptr(dg2),
+                                          _ptr(kv), _ptr(g2), _ptrs(w_mlp), _ptr(dout),
+                                          _ptr(attn_saved), _ptr(lse_saved), _ptr(dx1), _ptr(dg2),
                                           _ptrs(dw_mlp), _ptrs(dw_o), _ptr(dq), _ptr(dkv), _ptr(ws),
                                           _nbytes(ws), _stream(stream)))
 

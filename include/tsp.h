@@ -243,6 +243,22 @@ int tsp_attn_shard(const tsp_dims* dims, const void* x, const void* g1,
                    void* ws, size_t ws_bytes, void* stream, void* copy_stream);
 
 /*
+ * tsp_attn_shard for training: the same x1 (bit for bit), and it also keeps
+ * what the backward would otherwise recompute (FlashAttention's backward
+ * takes the forward output and the softmax statistics as inputs):
+ *   attn_out [B*T][h] dims->dtype: every head group's attention output, the
+ *            input of its O projection (shard j's heads at columns j*hs)
+ *   lse      [H][B*T] fp32: log2 of each row's softmax normaliser over the
+ *            scaled scores (head t = j*Hd + u of shard j at row block t)
+ * Both are overwritten; pass them to tsp_layer_shard_backward.
+ *   ws >= tsp_workspace_bytes(dims, TSP_WS_ATTN).
+ */
+int tsp_attn_shard_save(const tsp_dims* dims, const void* x, const void* g1,
+                        const void* const* w_attn, const void* kv, void* x1,
+                        void* attn_out, float* lse, void* ws, size_t ws_bytes,
+                        void* stream, void* copy_stream);
+
+/*
  * MLP half: out = x1 + sum_j (silu(n2 W1_j) * (n2 W3_j)) W2_j, n2 = RMSNorm(x1; g2).
  * Section 2, gated MLP layers: ring step t = 0..D-1 uses shard (r + t) mod D
  * (own shard first, read in place; the others are copied into a workspace
@@ -379,6 +395,8 @@ int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, 
  *   g1, w_attn, kv, g2, w_mlp   as the forward (kv: the gathered K/V; every
  *           other rank's rows are read, the rank's own are recomputed)
  *   dout    [B*T][h]   gradient of the layer output
+ *   attn_saved, lse_saved   the attn_out and lse of tsp_attn_shard_save on
+ *           the same inputs, or both NULL (TSP_E_INVAL if only one is given)
  * outputs (all overwritten):
  *   dx1     [B*T][h]   gradient of x1 (dout plus the MLP branch), dims->dtype
  *   dg2     [h] fp32   partial gradient of g2
@@ -393,12 +411,14 @@ int tsp_attn_core_backward(const tsp_dims* dims, const void* q, const void* kv, 
  *           keys before the rotation): this rank's partial K/V gradients,
  *           zero at positions none of its queries sees
  *   ws      >= tsp_workspace_bytes(dims, TSP_WS_LAYER_BWD)
- * The forward attention of each head group is recomputed (FlashAttention's
- * way), as are RMSNorm-1, Q and the rank's own K/V rows.
+ * Without attn_saved / lse_saved, the forward attention of each head group
+ * is recomputed (FlashAttention's way); RMSNorm-1, Q and the rank's own K/V
+ * rows are recomputed either way.
  */
 int tsp_layer_shard_backward(const tsp_dims* dims, const void* x, const void* x1, const void* g1,
                              const void* const* w_attn, const void* kv, const void* g2,
-                             const void* const* w_mlp, const void* dout, void* dx1, float* dg2,
+                             const void* const* w_mlp, const void* dout, const void* attn_saved,
+                             const float* lse_saved, void* dx1, float* dg2,
                              float* const* dw_mlp, float* const* dw_o, float* dq, float* dkv,
                              void* ws, size_t ws_bytes, void* stream);
 

@@ -88,6 +88,15 @@ class RankRun:
         tsp.tsp_attn_shard(self.dims, x, L.g1, L.w_attn, kv, x1, self.ws_a, copy_stream=self.cs)
         return x1
 
+    def attn_save(self, x, L: LayerDev, kv):
+        """tsp_attn_shard_save: x1, the attention output A [B*T][h] and the
+        rows' log2 softmax normalisers [H][B*T]."""
+        cfg = self.cfg
+        x1, a = torch.empty_like(x), torch.empty_like(x)
+        lse = torch.empty(cfg.n_heads * x.shape[0], dtype=torch.float32, device=DEV)
+        tsp.tsp_attn_shard_save(self.dims, x, L.g1, L.w_attn, kv, x1, a, lse, self.ws_a, copy_stream=self.cs)
+        return x1, a, lse
+
     def mlp(self, x1, L: LayerDev):
         out = torch.empty_like(x1)
         tsp.tsp_mlp_shard(self.dims, x1, L.g2, L.w_mlp, out, self.ws_m, copy_stream=self.cs)

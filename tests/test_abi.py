@@ -225,6 +225,21 @@ def test_attention_backward_rejects_unsupported_before_gpu():
         assert tsp.STATUS[rc] == want, (cfg.name, rc, L.tsp_last_error())
 
 
+def test_layer_backward_saved_inputs_come_in_pairs():
+    """attn_saved without lse_saved (or the reverse) is refused on the host,
+    before any pointer is read."""
+    L = tsp.lib()
+    cfg = synth.LayerConfig(name="b", hidden=256, n_heads=2, head_dim=128, ffn=512, seq=512, fold=2,
+                            ranks=(0,), layers=1, dtype="bf16")
+    dims = tsp.make_dims(cfg, 0)
+    ptrs = (ctypes.c_void_p * 2)(16, 16)
+    for a, l in ((16, None), (None, 16)):
+        rc = L.tsp_layer_shard_backward(ctypes.byref(dims), 16, 16, 16, ptrs, 16, 16, ptrs, 16, a, l, 16, 16, ptrs,
+                                        ptrs, 16, 16, 16, 1 << 40, None)
+        assert tsp.STATUS[rc] == "TSP_E_INVAL", (a, l, rc)
+        assert "together" in L.tsp_last_error().decode()
+
+
 @pytest.mark.parametrize("cfg,ok,what", [
     # bf16 7B shape at 128K, fold 8.  The widest activation operand is the W2
     # product's [B*T][G*Fs] (G = 4 shards of 1376 FFN columns): B*T*5504*2

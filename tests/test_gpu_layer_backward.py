@@ -8,6 +8,11 @@ All D ranks run on the one GPU: each runs its forward attention half (x1,
 which training keeps) and part 1; the exchange sums the D ranks' partial
 K/V gradients at each rank's positions; each rank then runs part 2.  Bar:
 relative Frobenius error <= 1e-2 per gradient tensor (bf16 workloads).
+
+Two modes: part 1 recomputes each head group's forward attention, or takes
+the attention output and softmax normalisers that tsp_attn_shard_save kept.
+The saved mode also checks that its x1 equals tsp_attn_shard's bit for bit
+and its attention output against the oracle's multi-head attention.
 """
 import numpy as np
 import pytest
@@ -42,6 +47,17 @@ CASES = {
 }
 
 
+_ORACLE = {}
+
+
+def _oracle_bwd(case, cfg, xf, w, gf, b):
+    """fold_schedule_backward of sequence b (both modes share it)."""
+    key = (case, b)
+    if key not in _ORACLE:
+        _ORACLE[key] = OB.fold_schedule_backward(xf[b], w, cfg.n_heads, cfg.eps, gf[b], cfg.fold, cfg.rope_theta)
+    return _ORACLE[key]
+
+
 def _ws(dims, which):
     return torch.empty(max(tsp.workspace_bytes(dims, which), 256), dtype=torch.uint8, device=DEV)
 
@@ -53,14 +69,15 @@ def _cmp(cfg, name, got, want, worst):
     assert np.isfinite(e) and e <= tol(cfg), f"{name}: rel {e:.3e}"
 
 
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_layer_backward_all_ranks(case):
+def test_layer_backward_all_ranks(case, saved):
     cfg = CASES[case]
     D, B, S, h, H, d = cfg.fold, cfg.batch, cfg.seq, cfg.hidden, cfg.n_heads, cfg.head_dim
     T, BT = cfg.local_tokens, cfg.batch * cfg.local_tokens
     hs, Fs = h // D, cfg.ffn // D
     ks = cfg.kv_heads * d // D
-    say(f"[gpu] layer backward {case}: h={h} H={H} Hkv={cfg.kv_heads} d={d} S={S} D={D} B={B} "
+    say(f"[gpu] layer backward {case} ({'saved attention' if saved else 'recomputed attention'}): h={h} H={H} Hkv={cfg.kv_heads} d={d} S={S} D={D} B={B} "
         f"theta={cfg.rope_theta}")
     w = synth.gen_weights(cfg)
     L = layer_dev(cfg, w)
@@ -73,16 +90,28 @@ def test_layer_backward_all_ranks(case):
     fill_kv(cfg, L, xs, kv)
     f32 = dict(dtype=torch.float32, device=DEV)
     outs = []
+    a_worst = 0.0
     for r in range(D):  # forward attention half, then part 1
         dims = tsp.make_dims(cfg, r)
-        x1 = RankRun(cfg, r).attn(xs[r], L, kv)
+        run = RankRun(cfg, r)
+        x1 = run.attn(xs[r], L, kv)
+        a_saved = lse = None
+        if saved:
+            x1s, a_saved, lse = run.attn_save(xs[r], L, kv)
+            assert torch.equal(x1s, x1), f"rank {r}: tsp_attn_shard_save's x1 differs from tsp_attn_shard's"
+            if B == 1:  # the kept attention output against the oracle's
+                n1 = O.rmsnorm(xf[0], w.g1, cfg.eps)
+                a_ref = O.multihead_causal(n1, pos[r], w, H, cfg.rope_theta)
+                e = rel_fro(f64(a_saved), a_ref)
+                a_worst = max(a_worst, e)
+                assert np.isfinite(e) and e <= tol(cfg), f"rank {r} saved attention output: rel {e:.3e}"
         o = dict(x1=x1, dx1=torch.empty_like(x1), dg2=torch.empty(h, **f32),
                  dw_mlp=[torch.empty(3 * Fs * h, **f32) for _ in range(D)],
                  dw_o=[torch.empty(h * hs, **f32) for _ in range(D)],
                  dq=torch.empty(H * BT * d, **f32), dkv=torch.full((2 * cfg.kv_heads * B * S * d,), float("nan"), **f32))
         tsp.tsp_layer_shard_backward(dims, xs[r], x1, L.g1, L.w_attn, kv, L.g2, L.w_mlp, gs[r], o["dx1"],
                                      o["dg2"], o["dw_mlp"], o["dw_o"], o["dq"], o["dkv"],
-                                     _ws(dims, tsp.TSP_WS_LAYER_BWD))
+                                     _ws(dims, tsp.TSP_WS_LAYER_BWD), attn_saved=a_saved, lse_saved=lse)
         outs.append(o)
     for r in range(D):  # the exchange, then part 2
         dims = tsp.make_dims(cfg, r)
@@ -98,7 +127,7 @@ def test_layer_backward_all_ranks(case):
     say("    GPU done; oracle running")
     worst = [0.0, ""]
     for b in range(B):
-        dx_ref, parts = OB.fold_schedule_backward(xf[b], w, H, cfg.eps, gf[b], D, cfg.rope_theta)
+        dx_ref, parts = _oracle_bwd(case, cfg, xf, w, gf, b)
         for r in range(D):
             o = outs[r]
             rows = slice(b * T, (b + 1) * T)
@@ -107,12 +136,12 @@ def test_layer_backward_all_ranks(case):
                 continue  # weight gradients sum over the sequences: checked below
             _check_weights(cfg, r, o, parts[r], worst)
     if B > 1:  # partial weight gradients of each rank sum over its sequences
-        refs = [OB.fold_schedule_backward(xf[b], w, H, cfg.eps, gf[b], D, cfg.rope_theta)[1] for b in range(B)]
+        refs = [_oracle_bwd(case, cfg, xf, w, gf, b)[1] for b in range(B)]
         for r in range(D):
             summed = OB.sum_partials([refs[b][r] for b in range(B)])
             _check_weights(cfg, r, outs[r], summed, worst)
     say(f"    {D} ranks: dx, dg1, dg2 and every shard's partial dW_Q/K/V/O/1/3/2 within {tol(cfg)}; "
-        f"worst rel {worst[0]:.3e} ({worst[1]})")
+        f"worst rel {worst[0]:.3e} ({worst[1]})" + (f"; saved A worst rel {a_worst:.3e}" if saved else ""))
 
 
 def _check_weights(cfg, r, o, p, worst):
