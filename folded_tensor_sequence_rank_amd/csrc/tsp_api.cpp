@@ -191,7 +191,7 @@ size_t kv_v_offset(const Dims& d) { return (size_t)d.Hkd * d.BS * d.d; }  // ele
 
 // The B sequences' items run side by side like extra heads.
 AttnPlan plan_of(const Dims& d) {
-  return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(d.Hd * d.B));
+  return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(d.Hd * d.B), attn_wide(d.dt, (int)d.d));
 }
 
 // Shards per launch in the forward halves: P consecutive shards share each
@@ -210,7 +210,7 @@ int64_t launch_shards(const Dims& d) {
 
 // Attention plan of a launch over np shards' heads.
 AttnPlan plan_for(const Dims& d, int64_t np) {
-  return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(np * d.Hd * d.B));
+  return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(np * d.Hd * d.B), attn_wide(d.dt, (int)d.d));
 }
 
 // Split-partial rows a launch over np shards needs.
@@ -579,6 +579,7 @@ int attn_body(Ctx& c, const AttnWs& L, const void* x, const void* g1, const void
     a.fold = (int)d.D;
     a.Hd = (int)(np * d.Hd);
     a.grp = (int)(d.H / d.Hkv);
+    a.bq = plan.bq;
     a.nqt = plan.nqt;
     a.lseg = plan.lseg;
     a.maxseg = plan.maxseg;
@@ -873,6 +874,7 @@ AttnArgs attn_args(const Dims& d, const AttnPlan& plan) {
   a.fold = (int)d.D;
   a.Hd = (int)d.Hd;
   a.grp = (int)(d.H / d.Hkv);
+  a.bq = plan.bq;
   a.nqt = plan.nqt;
   a.lseg = plan.lseg;
   a.maxseg = plan.maxseg;

@@ -64,8 +64,8 @@ struct AttnArgs {
   const void* Kg;
   const void* Vtg;
   void* O;         // [B*T][ldo]; head t writes columns [t*HD, (t+1)*HD)
-  float* Op;       // partial outputs of split items [Hd][B][nqt][maxseg][128][HD]
-  float* ML;       // partial (max, sum) [Hd][B][nqt][maxseg][128][2]
+  float* Op;       // partial outputs of split items [Hd][B][nqt][maxseg][bq][HD]
+  float* ML;       // partial (max, sum) [Hd][B][nqt][maxseg][bq][2]
   float* LSE;      // optional: per row log2 of its softmax normaliser, [Hd][B*T]
   int64_t T, S, chunk;
   int ldo, rank, fold, Hd;
@@ -76,7 +76,7 @@ struct AttnArgs {
   // blocks start shard_stride elements further on per shard.
   int kvh_per_shard;
   int64_t shard_stride;
-  int nqt, lseg, maxseg, nitems;
+  int bq, nqt, lseg, maxseg, nitems;  // bq: local query rows per tile (the plan's)
   float scale_log2;  // log2(e) / sqrt(HD)
   float sum_cap;     // largest 32-key block sum of exponentials before the reference max is raised
 };
@@ -90,7 +90,11 @@ struct AttnPlan {
   int nitems;  // work items per head
   bool split;  // any query tile has more than one split
 };
-AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int Hd);
+// wide: the 256-row query tiles of the bf16 128-dim kernel (one workgroup
+// per CU), else 128-row tiles (two per CU).
+AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int Hd, bool wide);
+// Whether attention of this dtype and head dim runs on 256-row query tiles.
+bool attn_wide(Dtype dt, int hd);
 
 hipError_t launch_rmsnorm(Dtype dt, const void* x, const void* g, void* y, int64_t rows, int h,
                           float eps, hipStream_t s);

@@ -957,6 +957,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 constexpr int kQB = 1;     // 32-query blocks per wave (two waves share a SIMD)
 constexpr int kBQ = 128 * kQB;  // local query rows per work item (4 waves)
+constexpr int kBQW = 256;       // the same for attn_pipe_kernel<8> (8 waves)
+#ifndef TSP_ATTN_WIDE
+#define TSP_ATTN_WIDE 1         // bf16 128-dim attention on 256-row tiles (0: 128-row tiles, 4 waves)
+#endif
 constexpr int kBKV = 64;   // keys per tile
 
 // Keys per K/V tile and LDS stages of attn_kernel: 64-key tiles, double
@@ -1000,8 +1004,9 @@ __device__ inline int kappa(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8
 
 
 
-__device__ __host__ inline int64_t qtile_kend(int64_t T, int qt, int64_t C, int rank, int fold) {
-  const int64_t last = (T < (int64_t)qt * kBQ + kBQ ? T : (int64_t)qt * kBQ + kBQ) - 1;
+// One past the causal end of query tile qt (bq local rows per tile).
+__device__ __host__ inline int64_t qtile_kend(int64_t T, int qt, int64_t C, int rank, int fold, int bq) {
+  const int64_t last = (T < (int64_t)qt * bq + bq ? T : (int64_t)qt * bq + bq) - 1;
   return zig(last, C, rank, fold) + 1;
 }
 
@@ -1014,7 +1019,7 @@ __device__ __attribute__((always_inline)) inline int first_tile_past(const AttnA
   int l = 0, h = a.nqt;  // smallest qt with kend(qt) > lo
   while (l < h) {
     const int mid = (l + h) >> 1;
-    if (qtile_kend(a.T, mid, a.chunk, a.rank, a.fold) > lo)
+    if (qtile_kend(a.T, mid, a.chunk, a.rank, a.fold, a.bq) > lo)
       h = mid;
     else
       l = mid + 1;
@@ -1056,7 +1061,7 @@ __device__ __attribute__((always_inline)) inline bool decode_item(const AttnArgs
     const int cnt = a.nqt - first_tile_past(a, (int64_t)seg * a.lseg);
     if (item < cnt) {
       qt = a.nqt - 1 - item;
-      kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold);
+      kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold, a.bq);
       nseg = (int)((kend + a.lseg - 1) / a.lseg);
       return true;
     }
@@ -1422,10 +1427,14 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined attention for bf16 with 128-dim heads.  Same work
-// items, tiles, LDS layouts, masking and softmax as attn_kernel (one wave per
-// 32 queries, 64-key tiles, two workgroups per CU), but each wave overlaps
-// its own MFMAs with its softmax instead of alternating between them:
+// Software-pipelined attention for bf16 with 128-dim heads.  Same tiles,
+// LDS layouts, masking and softmax as attn_kernel (one wave per 32 queries,
+// 64-key tiles), on NW waves per workgroup: NW = 8 (the default) takes
+// 256-row query tiles, one workgroup per CU, so each K/V tile brought into
+// LDS serves twice the rows of NW = 4 (128-row tiles, two workgroups per
+// CU) and the global-to-LDS loads per flop halve; both run two waves per
+// SIMD.  Each wave overlaps its own MFMAs with its softmax instead of
+// alternating between them:
 //   phase A of tile t:  S(t+1) = K(t+1) . Q^T      with the exponentials of
 //                                                  tile t's second 32 keys
 //   phase B of tile t:  O^T += V^T(t) . P^T(t)     with the exponentials of
@@ -1446,17 +1455,20 @@ __global__ void __launch_bounds__(256, (kQB == 1 ? AttnTile<T, HD>::WAVES : 1)) 
 #define TSP_ATTN_FOLD 1    // softmax scale and offset folded into the S products (below)
 #endif
 
-__global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) attn_pipe_kernel(AttnArgs a) {
   typedef bf16 T;
   typedef MF<bf16> M_;
   typedef bf16x8 frag;
-  static_assert(kQB == 1 && kBQ == 128, "one 32-query block per wave");
+  static_assert(kQB == 1 && (NW == 4 || NW == 8), "one 32-query block per wave");
+  constexpr int BQ = 32 * NW;  // local query rows per work item
   constexpr int HD = 128, ES = 2, V = 8, BKV = 64;
   constexpr int KROWB = HD * ES, KCH = KROWB / 16;   // K rows: 256 B
   constexpr int VROWB = BKV * ES, VCH = VROWB / 16;  // V^T rows: 128 B
   constexpr int KT = BKV * KROWB, VT = HD * VROWB;   // 16 KB per tile each
   constexpr int QK = HD / 16, DB = HD / 32, PK = BKV / 16;
-  constexpr int KJ = KT / 4096, VJ = VT / 4096;      // 1 KB loads per wave per tile
+  constexpr int KJ = KT / (NW * 1024), VJ = VT / (NW * 1024);  // 1 KB loads per wave per tile
+  static_assert(KJ + VJ <= 8, "spread loads: one per second MFMA of phase A");
   __shared__ __attribute__((aligned(16))) char smem[2 * KT + 2 * VT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1473,7 +1485,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   const int kbeg = seg * a.lseg;
   const int kfin = min(kend32, kbeg + a.lseg);
   const int T32 = (int)a.T, C32 = (int)a.chunk;
-  const int row0 = qt * kBQ + wave * 32;
+  const int row0 = qt * BQ + wave * 32;
   const bool qok = row0 + lr < T32;
   const int qpos = qok ? (int)zig(row0 + lr, C32, a.rank, a.fold) : -1;
   const bool wok = row0 < T32;
@@ -1500,14 +1512,14 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
   uint32_t koff[KJ], voff[VJ];
 #pragma unroll
   for (int j = 0; j < KJ; j++) {
-    const int b = (wave + 4 * j) * 1024 + 16 * lane;
+    const int b = (wave + NW * j) * 1024 + 16 * lane;
     const int r = b / KROWB, p = (b % KROWB) >> 4;
     krow[j] = r;
     koff[j] = (uint32_t)((r * HD + swz<KCH>(p, r) * V) * ES);
   }
 #pragma unroll
   for (int j = 0; j < VJ; j++) {
-    const int b = (wave + 4 * j) * 1024 + 16 * lane;
+    const int b = (wave + NW * j) * 1024 + 16 * lane;
     const int d = b / VROWB, p = (b % VROWB) >> 4;
     const int c = swz<VCH>(p, d);
     vkey[j] = c * V;
@@ -1524,11 +1536,11 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     if (k0 + BKV <= kend32) {
 #pragma unroll
       for (int j = 0; j < KJ; j++)
-        buffer_to_lds16(rK, sK0 + buf * KT + wofs + 4096 * j, koff[j], (uint32_t)(k0 * HD * ES));
+        buffer_to_lds16(rK, sK0 + buf * KT + wofs + NW * 1024 * j, koff[j], (uint32_t)(k0 * HD * ES));
     } else {
 #pragma unroll
       for (int j = 0; j < KJ; j++)
-        buffer_to_lds16(rK, sK0 + buf * KT + wofs + 4096 * j,
+        buffer_to_lds16(rK, sK0 + buf * KT + wofs + NW * 1024 * j,
                         k0 + krow[j] < kend32 ? koff[j] : kOOB, (uint32_t)(k0 * HD * ES));
     }
   };
@@ -1537,30 +1549,30 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
     if (k0 + BKV <= kend32) {
 #pragma unroll
       for (int j = 0; j < VJ; j++)
-        buffer_to_lds16(rV, sV0 + buf * VT + wofs + 4096 * j, voff[j], (uint32_t)(k0 * ES));
+        buffer_to_lds16(rV, sV0 + buf * VT + wofs + NW * 1024 * j, voff[j], (uint32_t)(k0 * ES));
     } else {
 #pragma unroll
       for (int j = 0; j < VJ; j++)
-        buffer_to_lds16(rV, sV0 + buf * VT + wofs + 4096 * j,
+        buffer_to_lds16(rV, sV0 + buf * VT + wofs + NW * 1024 * j,
                         k0 + vkey[j] < kend32 ? voff[j] : kOOB, (uint32_t)(k0 * ES));
     }
   };
   // One of the wave's KJ (VJ) loads of a K (V^T) tile.
   auto issueK1 = [&](int k0, int buf, int j) {
     const brsrc rK = make_rsrc(!split_src || own_tile(k0) ? Kh : Kgh, (uint64_t)a.S * HD * ES);
-    buffer_to_lds16(rK, sK0 + buf * KT + wofs + 4096 * j,
+    buffer_to_lds16(rK, sK0 + buf * KT + wofs + NW * 1024 * j,
                     k0 + BKV <= kend32 || k0 + krow[j] < kend32 ? koff[j] : kOOB, (uint32_t)(k0 * HD * ES));
   };
   auto issueV1 = [&](int k0, int buf, int j) {
     const brsrc rV = make_rsrc(!split_src || own_tile(k0) ? Vh : Vgh, (uint64_t)((HD - 1) * BS + a.S) * ES);
-    buffer_to_lds16(rV, sV0 + buf * VT + wofs + 4096 * j,
+    buffer_to_lds16(rV, sV0 + buf * VT + wofs + NW * 1024 * j,
                     k0 + BKV <= kend32 || k0 + vkey[j] < kend32 ? voff[j] : kOOB, (uint32_t)(k0 * ES));
   };
   auto fixupV = [&](int k0, int buf) {
     char* sV = sV0 + buf * VT;
     const int first = kend32 - k0;
     const int upto = min(BKV, (first + V - 1) / V * V);
-    for (int i = tid; i < HD * (upto - first); i += 256) {
+    for (int i = tid; i < HD * (upto - first); i += 64 * NW) {
       const int d = i / (upto - first), key = first + i % (upto - first);
       const int byte = key * ES;
       *(T*)(sV + d * VROWB + (swz<VCH>(byte >> 4, d) << 4) + (byte & 15)) = from_f<T>(0.f);
@@ -1775,12 +1787,11 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
           vq[i + PD - 16] = vfrag(vbuf, (i + PD - 16) >> 2, (i + PD - 16) & 3);
         s[i & 1] = M_::mma(f, qf[i >> 1], s[i & 1]);
         if (TSP_ATTN_SPREAD && (i & 1)) {
-          constexpr int KJ_ = KT / 4096;
-          const int jl = i >> 1;
-          if (jl < KJ_) {
+          const int jl = i >> 1;  // the wave's KJ K loads, then its VJ V^T loads
+          if (jl < KJ) {
             if (doK) issueK1(k0 + 2 * BKV, P, jl);
-          } else if (doV) {
-            issueV1(k0 + BKV, 1 - P, jl - KJ_);
+          } else if (jl < KJ + VJ && doV) {
+            issueV1(k0 + BKV, 1 - P, jl - KJ);
           }
         }
         pel(sh[i], nm, pf[2 + (i >> 3)], i & 7, ls, i < 4);
@@ -1848,8 +1859,12 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
       pf[1] = pn[1];
       sh = s[1];
     } else {
-      // this wave's last tile: the rest of its P, then its V^T product
+      // this wave's last tile: the rest of its P, then its V^T product.
+      // (The empty asm makes these exponentials differ from phase A's, which
+      // the compiler would otherwise compute once above the branch, out of
+      // phase A's MFMA block.)
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+v"(sh));
       exps(sh, nm, pf[2], pf[3], ls);
       float lsa = (ls[0] + ls[1]) + (ls[2] + ls[3]);
       if (__any(!(lsa <= kSumCap))) {
@@ -1879,7 +1894,7 @@ __global__ void __launch_bounds__(256, 2) attn_pipe_kernel(AttnArgs a) {
                     o[d][4 * q + 2] * inv, o[d][4 * q + 3] * inv);
     }
   } else {
-    const int64_t slot = ((((int64_t)head * nb + sb) * a.nqt + qt) * a.maxseg + seg) * kBQ + wave * 32 + lr;
+    const int64_t slot = ((((int64_t)head * nb + sb) * a.nqt + qt) * a.maxseg + seg) * BQ + wave * 32 + lr;
     float* op = a.Op + slot * HD;
 #pragma unroll
     for (int d = 0; d < DB; d++)
@@ -1907,17 +1922,17 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int64_t head = rid / BT, rowg = rid % BT;  // rowg = sb * T + row
   if (head >= a.Hd) return;
   const int64_t sb = rowg / a.T, row = rowg % a.T;
-  const int qt = (int)(row / kBQ);
-  const int64_t kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold);
+  const int qt = (int)(row / a.bq);
+  const int64_t kend = qtile_kend(a.T, qt, a.chunk, a.rank, a.fold, a.bq);
   const int nseg = (int)((kend + a.lseg - 1) / a.lseg);
   if (nseg == 1) return;
-  const int64_t base = (((head * nb + sb) * a.nqt + qt) * a.maxseg) * kBQ + (row % kBQ);
+  const int64_t base = (((head * nb + sb) * a.nqt + qt) * a.maxseg) * a.bq + (row % a.bq);
   float mx = -INFINITY;
-  for (int s = 0; s < nseg; s++) mx = fmaxf(mx, a.ML[2 * (base + s * kBQ)]);
+  for (int s = 0; s < nseg; s++) mx = fmaxf(mx, a.ML[2 * (base + s * a.bq)]);
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < nseg; s++) {
-    const int64_t slot = base + s * kBQ;
+    const int64_t slot = base + s * a.bq;
     const float ms = a.ML[2 * slot];
     const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - mx);
     L += w * a.ML[2 * slot + 1];
@@ -2625,25 +2640,28 @@ __global__ void clock_probe_kernel(uint64_t* __restrict__ out, int n, uint64_t i
 // schedule (items dispatched in order onto 256 CUs, each taking the first
 // free one; cost = keys + a fixed per-item overhead + a merge cost per split
 // item) finishes first.  Cached per shape.
-AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int Hd) {
+bool attn_wide(Dtype dt, int hd) { return TSP_ATTN_WIDE && dt == BF16 && hd == 128; }
+
+AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int Hd, bool wide) {
   AttnPlan p{};
-  p.bq = kBQ;
-  p.nqt = (int)((T + kBQ - 1) / kBQ);
+  p.bq = wide ? kBQW : kBQ;
+  p.nqt = (int)((T + p.bq - 1) / p.bq);
   if (T <= 0) return p;
-  struct Key { int64_t T, S, C; int r, D, Hd; };
+  struct Key { int64_t T, S, C; int r, D, Hd; bool wide; };
   struct Entry { Key k; AttnPlan p; };
   static thread_local std::vector<Entry> cache;
   for (const Entry& e : cache)
-    if (e.k.T == T && e.k.S == S && e.k.C == chunk && e.k.r == rank && e.k.D == fold && e.k.Hd == Hd)
+    if (e.k.T == T && e.k.S == S && e.k.C == chunk && e.k.r == rank && e.k.D == fold && e.k.Hd == Hd &&
+        e.k.wide == wide)
       return e.p;
   std::vector<int64_t> kend(p.nqt);
   int64_t kmax = 0;
   for (int qt = 0; qt < p.nqt; qt++) {
-    kend[qt] = qtile_kend(T, qt, chunk, rank, fold);
+    kend[qt] = qtile_kend(T, qt, chunk, rank, fold, p.bq);
     kmax = std::max(kmax, kend[qt]);
   }
   const int64_t kmax64 = (kmax + 63) / 64 * 64;
-  const int kCU = 256 * (kQB == 1 ? TSP_ATTN128_WAVES : 1);  // concurrent workgroups
+  const int kCU = wide ? 256 : 256 * (kQB == 1 ? TSP_ATTN128_WAVES : 1);  // concurrent workgroups
   const double overhead = 3 * kBKV, merge = 2 * kBKV;  // in key units
   double best = 1e300;
   int64_t best_l = kmax64;
@@ -2684,7 +2702,7 @@ AttnPlan attn_plan(int64_t T, int64_t S, int64_t chunk, int rank, int fold, int 
     p.nitems += ns;
   }
   p.split = p.maxseg > 1;
-  cache.push_back({{T, S, chunk, rank, fold, Hd}, p});
+  cache.push_back({{T, S, chunk, rank, fold, Hd, wide}, p});
   return p;
 }
 
@@ -2804,8 +2822,10 @@ hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
 template <typename T, int HD>
 static void attn_go(const AttnArgs& a, const AttnPlan& p, int part, hipStream_t s) {
   if (part == 0) {
-    if (sizeof(T) == 2 && HD == 128)
-      attn_pipe_kernel<<<p.nitems * a.Hd * batch_of(a), 256, 0, s>>>(a);
+    if (sizeof(T) == 2 && HD == 128 && p.bq == kBQW)
+      attn_pipe_kernel<8><<<p.nitems * a.Hd * batch_of(a), 512, 0, s>>>(a);
+    else if (sizeof(T) == 2 && HD == 128)
+      attn_pipe_kernel<4><<<p.nitems * a.Hd * batch_of(a), 256, 0, s>>>(a);
     else
       attn_kernel<T, HD><<<p.nitems * a.Hd * batch_of(a), 256, 0, s>>>(a);
   } else if (p.split) {
