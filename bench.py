@@ -7,7 +7,10 @@ projection accumulated in place), RMSNorm, D MLP shards (W1/W3 with SwiGLU,
 W2 accumulated in place), residuals, with the other ranks' shards and K/V
 rows streamed through the side-stream slots.  Inputs are resident in HBM
 before the timed region; the other ranks' K/V rows (the all-gather's
-payload) are produced beforehand with tsp_kv_shard and are not timed.
+payload) are produced beforehand with tsp_kv_shard and are not timed.  The
+call is captured once into a HIP graph and each step replays it (checked
+bit-identical to the eager call); the eager time of the same steps is
+reported beside it ("other_launch"), and --eager swaps the two.
 
 Default workload: the 7B shape (h 4096, 32 heads x 128, SwiGLU 11008) at
 S = 65536, fold D = 8, rank 3 (8192 local tokens in two zigzag chunks).
@@ -50,8 +53,8 @@ def parse():
                     help="local rows of the rank's second chunk the oracle computes")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
-                    help="time the headline steps only: no second K/V path, no clock-probe pass "
-                         "(for counter runs, which serialise every dispatch)")
+                    help="time the headline steps only, launched eagerly: no graph, no second K/V "
+                         "path, no clock-probe pass (for counter runs, which serialise every dispatch)")
     ap.add_argument("--mlp-backward", action="store_true",
                     help="time the MLP half's backward (tsp_mlp_shard_backward) instead of the layer")
     ap.add_argument("--attn-backward", action="store_true",
@@ -61,6 +64,9 @@ def parse():
     ap.add_argument("--recompute-attn", action="store_true",
                     help="with --layer-backward: recompute each head group's forward attention in the "
                          "backward instead of taking what tsp_attn_shard_save kept")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the layer call launched eagerly instead of replayed as a captured HIP "
+                         "graph (both are reported either way)")
     ap.add_argument("--kv-stream", action="store_true",
                     help="headline with the other ranks' K/V copied through the side-stream slots "
                          "(TSP_F_KV_STREAM) instead of read in place; both are reported either way")
@@ -484,11 +490,31 @@ def main():
         warm.append((time.perf_counter() - t0) * 1e3)
     est_ms = min(warm) if warm else 10.0  # a step's wall time, for sizing the clock probe
 
-    def timed(rr, probe=False):
+    # The layer call captured once into a HIP graph (its kernels, side-stream
+    # copies and the events ordering them) and replayed per step: the same
+    # launches without the host's per-launch cost between them.
+    graphs = {}
+
+    def capture(name):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            runs[name].layer(x, L, kv, out)
+        torch.cuda.synchronize()
+        return g
+
+    def timed(rr, probe=False, graph=None):
         """K steps bracketed by synchronisation, an event between steps; with
-        probe, the clock probe runs on a second stream over ~90% of them."""
+        probe, the clock probe runs on a second stream over ~90% of them.
+        With graph, each step replays it instead of calling rr.layer.  The W
+        warmup steps run right before, in the same launch mode, so that the
+        timed steps do not start on a GPU that idled through the set-up."""
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         samples, khz = None, 0
+        for _ in range(args.warmup):
+            if graph is not None:
+                graph.replay()
+            else:
+                rr.layer(x, L, kv, out)
         torch.cuda.synchronize()
         if probe:
             interval_us = 200
@@ -498,22 +524,42 @@ def main():
             khz = tsp.tsp_clock_probe(samples, n, interval_us, stream=ps)
         ev[0].record()
         for i in range(args.steps):
-            rr.layer(x, L, kv, out)
+            if graph is not None:
+                graph.replay()
+            else:
+                rr.layer(x, L, kv, out)
             ev[i + 1].record()
         torch.cuda.synchronize()
         per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
         return ev[0].elapsed_time(ev[-1]) / args.steps, per, (samples, khz)
 
+    # (counter runs, --headline-only, launch eagerly and time one mode only)
+    use_graph = not args.eager and not args.headline_only
+    if use_graph:
+        graphs[head] = capture(head)
+        # the replay writes what the eager call writes, bit for bit
+        runs[head].layer(x, L, kv, out)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        out.zero_()
+        graphs[head].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "graph replay differs from the eager call"
+        del ref
     with ClockSampler() as clk:
-        ms, step_times, _ = timed(runs[head])
+        ms, step_times, _ = timed(runs[head], graph=graphs.get(head))
     assert torch.isfinite(out).all(), "non-finite output"
+    # the other launch mode of the same steps, for comparison
+    ms_alt, per_alt = None, None
+    if not args.headline_only:
+        ms_alt, per_alt, _ = timed(runs[head], graph=None if use_graph else capture(head))
     # The effective clock, from a second pass of the same steps with the clock
     # probe beside them.  Not during the timed steps: the probe's wave holds a
     # slot on one CU, which keeps a full-register workgroup off that CU (a
     # GEMM launch of exactly two rounds of 256 tiles then needs a third).
     eff_clock, other, ms_other, per_other = None, None, None, None
     if not args.headline_only:
-        ms_probe, _, (samples, khz) = timed(runs[head], probe=True)
+        ms_probe, _, (samples, khz) = timed(runs[head], probe=True, graph=graphs.get(head))
         smp = samples.cpu().numpy().reshape(-1, 2)
         smp = smp[smp[:, 0] - smp[0, 0] <= ms_probe * args.steps * khz]  # inside the steps
         mhz = tsp.clock_mhz(smp, khz)
@@ -526,7 +572,9 @@ def main():
         other = "kv_stream" if head == "in_place" else "in_place"
         for _ in range(args.warmup):
             runs[other].layer(x, L, kv, out)
-        ms_other, per_other, _ = timed(runs[other])
+        if use_graph:
+            graphs[other] = capture(other)
+        ms_other, per_other, _ = timed(runs[other], graph=graphs.get(other))
 
     T = cfg.batch * cfg.local_tokens
     f_alg = sum(flops_per_step(cfg, r).values())
@@ -594,6 +642,10 @@ def main():
         "step_ms": step_stats(step_times),
         "kv_path": head,
         "kv_variant": variant,
+        "launch": "hip_graph" if use_graph else "eager",
+        "other_launch": None if ms_alt is None else {
+            "launch": "eager" if use_graph else "hip_graph", "ms_per_step": round(ms_alt, 4),
+            "value": round(f_alg / (ms_alt * 1e-3) / 1e12, 2), "step_ms": step_stats(per_alt)},
         "flops_per_step": f_alg,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -194,18 +194,15 @@ AttnPlan plan_of(const Dims& d) {
   return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(d.Hd * d.B), attn_wide(d.dt, (int)d.d));
 }
 
-// Shards per launch in the forward halves: P consecutive shards share each
-// QKV, attention and W1/W3 launch (TSP_F_SHARD_LAUNCH: one).  P is the
-// largest divisor of G not above D/4, so the two weight slots (2P shards)
-// hold at most half of the layer's Q|K|V or W1|W3 shards, as the W_O and W2
-// group buffers do, and a launch never spans two accumulation groups.
+// Shards per launch in the forward halves: the P = G shards of an
+// accumulation group share each QKV, attention and W1/W3 launch
+// (TSP_F_SHARD_LAUNCH: one).  Wider launches fill the CUs with larger GEMM
+// tiles and give attention more heads per launch (fewer split items); the
+// two weight slots then hold 2G shards' Q|K|V (W1|W3) blocks, all of them at
+// D = 8, a few hundred MB at the 7B shape.
 int64_t launch_shards(const Dims& d) {
   if (d.flags & TSP_F_SHARD_LAUNCH) return 1;
-  const int64_t G = acc_group(d);
-  int64_t P = 1;
-  for (int64_t p = 2; p <= G && p <= d.D / 4; p++)
-    if (G % p == 0) P = p;
-  return P;
+  return acc_group(d);
 }
 
 // Attention plan of a launch over np shards' heads.

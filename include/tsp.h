@@ -169,13 +169,12 @@ enum {
    * 3: transfers pipelined behind the GEMMs).  Without it they are read in
    * place when C % 64 == 0.  Same results, bit for bit. */
   TSP_F_KV_STREAM = 32u,
-  /* Shards per launch.  By default P consecutive shards run as one QKV
-   * launch and one attention launch (one W1/W3 launch) once all P have
-   * arrived in a slot: P is the largest divisor of the accumulation group
-   * G = max(1, min(4, D/2)) not above D/4 (2 at D = 8, 1 below D = 8), so the
-   * two slots hold at most half of the layer's shards.  This flag runs one
-   * shard per launch.  Results agree to rounding: the attention's work split
-   * depends on the heads per launch. */
+  /* Shards per launch.  By default the P = G shards of an accumulation group
+   * (G = max(1, min(4, D/2)): 4 at D = 8, 2 at D = 4) run as one QKV launch
+   * and one attention launch (one W1/W3 launch) once all of them have
+   * arrived in a slot, which takes two slots of G shards each.  This flag
+   * runs one shard per launch, in smaller slots.  Results agree to rounding:
+   * the attention's work split depends on the heads per launch. */
   TSP_F_SHARD_LAUNCH = 64u
 };
 

@@ -146,28 +146,27 @@ def test_gqa_rope_dims_and_workspace():
 
 
 def test_shards_per_launch_workspace():
-    """The forward halves run P = 2 shards of an accumulation group (G = 4 at
-    D = 8) per QKV, attention and W1/W3 launch; the two weight slots, the two
-    K/V slots and the Q buffer then hold P shards each, 2P = D/2 shards of the
-    layer at most.  TSP_F_SHARD_LAUNCH runs one shard per launch; below D = 8,
-    P = 1 anyway."""
+    """By default the G = min(4, D/2) shards of an accumulation group share
+    each QKV, attention and W1/W3 launch (4 at D = 8, 2 at D = 4); the two
+    weight slots, the two K/V slots and the Q buffer then hold G shards each.
+    TSP_F_SHARD_LAUNCH runs one shard per launch.  The attention's split
+    partials differ too: a launch over more heads splits less."""
     def ws(cfg, flags, which):
-        d = tsp.make_dims(cfg, 3)
+        d = tsp.make_dims(cfg, 3 % cfg.fold)
         d.flags |= flags
         return tsp.workspace_bytes(d, which)
-    h, hs, Fs, es = 4096, 512, 1376, 2
-    qkv = (hs + 2 * hs) * h * es                # one packed Q|K|V block
-    for cfg in (C3, C3.with_(seq=16384)):
-        T, S = cfg.local_tokens, cfg.seq
-        kvslot = 2 * 4 * S * 128 * es           # one shard's K and V^T over the sequence
-        grown = 2 * qkv + 2 * kvslot + T * hs * es  # a second shard in each of 2 slots, and in Q
+    h, es = 4096, 2
+    for cfg in (C3, C3.with_(seq=16384), C3.with_(seq=16384, fold=4)):
+        D, T, S = cfg.fold, cfg.local_tokens, cfg.seq
+        P = min(4, D // 2)
+        hs, Fs = h // D, 11008 // D
+        qkv = 3 * hs * h * es                   # one packed Q|K|V block
+        kvslot = 2 * (32 // D) * S * 128 * es   # one shard's K and V^T over the sequence
+        grown = (P - 1) * (2 * qkv + 2 * kvslot + T * hs * es)  # more shards in 2 slots each, and in Q
         diff = ws(cfg, 0, tsp.TSP_WS_ATTN) - ws(cfg, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
-        assert grown - 16 * 1024 * 1024 <= diff <= grown + 16 * 1024 * 1024, (S, diff, grown)  # split partials
-        assert ws(cfg, 0, tsp.TSP_WS_MLP) - ws(cfg, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP) == 2 * 2 * Fs * h * es
-    # fold 4: G = 2 and D/4 = 1, so one shard per launch either way
-    f4 = C3.with_(seq=16384, fold=4)
-    assert ws(f4, 0, tsp.TSP_WS_ATTN) == ws(f4, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
-    assert ws(f4, 0, tsp.TSP_WS_MLP) == ws(f4, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP)
+        assert grown - 128 * 2**20 <= diff <= grown + 32 * 2**20, (D, S, diff, grown)  # split partials
+        mlp = ws(cfg, 0, tsp.TSP_WS_MLP) - ws(cfg, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP)
+        assert mlp == (P - 1) * 2 * 2 * Fs * h * es, (D, mlp)
 
 
 def test_micro_batch_workspace():
