@@ -8,9 +8,8 @@ W2 accumulated in place), residuals, with the other ranks' shards and K/V
 rows streamed through the side-stream slots.  Inputs are resident in HBM
 before the timed region; the other ranks' K/V rows (the all-gather's
 payload) are produced beforehand with tsp_kv_shard and are not timed.  The
-call is captured once into a HIP graph and each step replays it (checked
-bit-identical to the eager call); the eager time of the same steps is
-reported beside it ("other_launch"), and --eager swaps the two.
+same steps replayed from a captured HIP graph are reported beside them
+("other_launch"); --graph swaps the two.
 
 Default workload: the 7B shape (h 4096, 32 heads x 128, SwiGLU 11008) at
 S = 65536, fold D = 8, rank 3 (8192 local tokens in two zigzag chunks).
@@ -64,9 +63,9 @@ def parse():
     ap.add_argument("--recompute-attn", action="store_true",
                     help="with --layer-backward: recompute each head group's forward attention in the "
                          "backward instead of taking what tsp_attn_shard_save kept")
-    ap.add_argument("--eager", action="store_true",
-                    help="time the layer call launched eagerly instead of replayed as a captured HIP "
-                         "graph (both are reported either way)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the layer call replayed as a captured HIP graph instead of launched "
+                         "eagerly (both are reported either way)")
     ap.add_argument("--kv-stream", action="store_true",
                     help="headline with the other ranks' K/V copied through the side-stream slots "
                          "(TSP_F_KV_STREAM) instead of read in place; both are reported either way")
@@ -496,10 +495,19 @@ def main():
     graphs = {}
 
     def capture(name):
+        """The call captured into a graph whose replay writes what the eager
+        call writes, bit for bit (checked)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             runs[name].layer(x, L, kv, out)
         torch.cuda.synchronize()
+        runs[name].layer(x, L, kv, out)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "graph replay differs from the eager call"
         return g
 
     def timed(rr, probe=False, graph=None):
@@ -534,18 +542,9 @@ def main():
         return ev[0].elapsed_time(ev[-1]) / args.steps, per, (samples, khz)
 
     # (counter runs, --headline-only, launch eagerly and time one mode only)
-    use_graph = not args.eager and not args.headline_only
+    use_graph = args.graph and not args.headline_only
     if use_graph:
         graphs[head] = capture(head)
-        # the replay writes what the eager call writes, bit for bit
-        runs[head].layer(x, L, kv, out)
-        torch.cuda.synchronize()
-        ref = out.clone()
-        out.zero_()
-        graphs[head].replay()
-        torch.cuda.synchronize()
-        assert torch.equal(out, ref), "graph replay differs from the eager call"
-        del ref
     with ClockSampler() as clk:
         ms, step_times, _ = timed(runs[head], graph=graphs.get(head))
     assert torch.isfinite(out).all(), "non-finite output"
