@@ -174,17 +174,30 @@ size_t qkv_rows(const Dims& d) { return (size_t)(d.hs + 2 * d.ks); }
 size_t attn_shard_elems(const Dims& d) { return (qkv_rows(d) + d.hs) * d.h; }
 size_t mlp_shard_elems(const Dims& d) { return 3 * (size_t)d.Fs * d.h; }
 
-// Accumulation groups.  The O projections (and W2 projections) of G
-// consecutive shards run as one GEMM with K = G*hs (G*Fs): the shards'
-// attention outputs (SwiGLU products) sit side by side, and each shard's W_O
-// (W2) block is copied next to the others' on the side stream.  That cuts the
-// fp32 accumulator's read-modify-write passes from D to D/G per half layer.
-// G <= D/2, so a rank never holds more than half of W_O or W2 at once.
+// Launch groups: the QKV, attention and W1/W3 launches of a forward half
+// each cover min(4, D/2) consecutive shards (one with TSP_F_SHARD_LAUNCH).
 #ifndef TSP_ACC_GROUP
 #define TSP_ACC_GROUP 4
 #endif
-int64_t acc_group(const Dims& d) {
+int64_t launch_group(const Dims& d) {
   return std::max<int64_t>(1, std::min<int64_t>(TSP_ACC_GROUP, d.D / 2));
+}
+
+// Accumulation groups.  The O projections (and W2 projections) of G
+// consecutive shards run as one GEMM with K = G*hs (G*Fs): the shards'
+// attention outputs (SwiGLU products) sit side by side, and each shard's W_O
+// (W2) block is copied next to the others' on the side stream.  By default
+// G = D: one O and one W2 projection per layer, K = h (F), which add the
+// residual in their epilogue, so no fp32 partial sum is written or read.  The
+// group buffers then hold all of W_O (W2), as many bytes as two half-layer
+// buffers.  With TSP_F_SHARD_LAUNCH, or when the layer's SwiGLU products
+// ([B*T][F]) would outgrow the kernels' 2^31-byte operand range, G =
+// min(4, D/2) (at most half of W_O or W2 held at once, D/G passes over an
+// fp32 accumulator).
+int64_t acc_group(const Dims& d) {
+  if (d.flags & TSP_F_SHARD_LAUNCH) return launch_group(d);
+  const uint64_t widest = (uint64_t)d.BT * (uint64_t)std::max<int64_t>(d.h, d.D * d.Fs) * d.es;
+  return widest <= (1ull << 31) ? d.D : launch_group(d);
 }
 size_t kv_block_elems(const Dims& d) { return 2 * (size_t)d.Hkd * d.BS * d.d; }
 size_t kv_v_offset(const Dims& d) { return (size_t)d.Hkd * d.BS * d.d; }  // elements before Vt_j
@@ -194,15 +207,14 @@ AttnPlan plan_of(const Dims& d) {
   return attn_plan(d.T, d.S, d.C, (int)d.r, (int)d.D, (int)(d.Hd * d.B), attn_wide(d.dt, (int)d.d));
 }
 
-// Shards per launch in the forward halves: the P = G shards of an
-// accumulation group share each QKV, attention and W1/W3 launch
-// (TSP_F_SHARD_LAUNCH: one).  Wider launches fill the CUs with larger GEMM
+// Shards per launch in the forward halves: the P shards of a launch group
+// share each QKV, attention and W1/W3 launch (TSP_F_SHARD_LAUNCH: one).  Wider launches fill the CUs with larger GEMM
 // tiles and give attention more heads per launch (fewer split items); the
 // two weight slots then hold 2G shards' Q|K|V (W1|W3) blocks, all of them at
 // D = 8, a few hundred MB at the 7B shape.
 int64_t launch_shards(const Dims& d) {
   if (d.flags & TSP_F_SHARD_LAUNCH) return 1;
-  return acc_group(d);
+  return launch_group(d);
 }
 
 // Attention plan of a launch over np shards' heads.
@@ -221,13 +233,18 @@ AttnWs attn_ws(const Dims& d, size_t base) {
   size_t o = base;
   const size_t act = al((size_t)d.BT * d.h * d.es);
   w.xn = o; o += act;
-  w.y = o; o += al((size_t)d.BT * d.h * 4);
   const int64_t G = acc_group(d), P = launch_shards(d);
+  const int ngroups = d.D > G ? 2 : 1;  // group buffers in use (double-buffered across groups)
+  w.y = o;
+  if (ngroups > 1) o += al((size_t)d.BT * d.h * 4);  // fp32 partial sum across groups
   w.q = o; o += al((size_t)P * d.BT * d.hs * d.es);  // [P*Hd][B*T][d]
   w.o = o; o += al((size_t)d.BT * G * d.hs * d.es);  // [B*T][G*hs]
   for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al((size_t)P * qkv_rows(d) * d.h * d.es); }
   for (int s = 0; s < 2; s++) { w.slotkv[s] = o; o += al((size_t)P * kv_block_elems(d) * d.es); }
-  for (int s = 0; s < 2; s++) { w.bo[s] = o; o += al((size_t)d.h * G * d.hs * d.es); }  // [h][G*hs]
+  for (int s = 0; s < 2; s++) {  // [h][G*hs]
+    w.bo[s] = o;
+    if (s < ngroups) o += al((size_t)d.h * G * d.hs * d.es);
+  }
   size_t nslot = split_rows(d, P);
   if (d.D % P) nslot = std::max(nslot, split_rows(d, d.D % P));  // the last, shorter launch
   w.op = o; o += al(nslot * d.d * 4);
@@ -240,12 +257,17 @@ MlpWs mlp_ws(const Dims& d, size_t base) {
   MlpWs w;
   size_t o = base;
   const int64_t G = acc_group(d), P = launch_shards(d);
+  const int ngroups = d.D > G ? 2 : 1;
   w.xn = o; o += al((size_t)d.BT * d.h * d.es);
-  w.y = o; o += al((size_t)d.BT * d.h * 4);
+  w.y = o;
+  if (ngroups > 1) o += al((size_t)d.BT * d.h * 4);
   w.gg = o; o += al((size_t)d.BT * G * d.Fs * d.es);  // [B*T][G*Fs]
   // [W1 of the launch's shards | their W3]
   for (int s = 0; s < 2; s++) { w.slotw[s] = o; o += al(2 * (size_t)P * d.Fs * d.h * d.es); }
-  for (int s = 0; s < 2; s++) { w.bw[s] = o; o += al((size_t)d.h * G * d.Fs * d.es); }  // [h][G*Fs]
+  for (int s = 0; s < 2; s++) {  // [h][G*Fs]
+    w.bw[s] = o;
+    if (s < ngroups) o += al((size_t)d.h * G * d.Fs * d.es);
+  }
   w.end = o;
   return w;
 }

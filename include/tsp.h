@@ -169,12 +169,18 @@ enum {
    * 3: transfers pipelined behind the GEMMs).  Without it they are read in
    * place when C % 64 == 0.  Same results, bit for bit. */
   TSP_F_KV_STREAM = 32u,
-  /* Shards per launch.  By default the P = G shards of an accumulation group
-   * (G = max(1, min(4, D/2)): 4 at D = 8, 2 at D = 4) run as one QKV launch
-   * and one attention launch (one W1/W3 launch) once all of them have
-   * arrived in a slot, which takes two slots of G shards each.  This flag
-   * runs one shard per launch, in smaller slots.  Results agree to rounding:
-   * the attention's work split depends on the heads per launch. */
+  /* Shards per launch and per O / W2 projection.  By default P = max(1,
+   * min(4, D/2)) consecutive shards (4 at D = 8, 2 at D = 4) run as one QKV
+   * launch and one attention launch (one W1/W3 launch) once all of them have
+   * arrived in a slot, which takes two slots of P shards each; and one O
+   * (W2) projection covers all D shards (K = h, K = F), adding the residual,
+   * with all of W_O (W2) copied into one group buffer -- unless the layer's
+   * SwiGLU products would exceed 2^31 bytes, when groups of P shards
+   * accumulate through an fp32 partial sum.  This flag runs one shard per
+   * launch in smaller slots and groups of P shards for the O / W2
+   * projections: the stream's smallest footprint.  Results agree to
+   * rounding: the attention's work split depends on the heads per launch,
+   * the projections' sums on the grouping. */
   TSP_F_SHARD_LAUNCH = 64u
 };
 

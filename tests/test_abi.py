@@ -146,27 +146,36 @@ def test_gqa_rope_dims_and_workspace():
 
 
 def test_shards_per_launch_workspace():
-    """By default the G = min(4, D/2) shards of an accumulation group share
-    each QKV, attention and W1/W3 launch (4 at D = 8, 2 at D = 4); the two
-    weight slots, the two K/V slots and the Q buffer then hold G shards each.
-    TSP_F_SHARD_LAUNCH runs one shard per launch.  The attention's split
-    partials differ too: a launch over more heads splits less."""
+    """By default the P = min(4, D/2) shards of a launch group share each QKV,
+    attention and W1/W3 launch, and one O (W2) projection covers all D shards:
+    its group buffers hold all of W_O (W2) and the attention outputs (SwiGLU
+    products) of the layer, and no fp32 partial sum exists.
+    TSP_F_SHARD_LAUNCH runs one shard per launch with accumulation groups of
+    P shards: two group buffers of half the columns, and the fp32 partial sum.
+    The attention's split partials differ too (a launch over more heads
+    splits less)."""
     def ws(cfg, flags, which):
         d = tsp.make_dims(cfg, 3 % cfg.fold)
         d.flags |= flags
         return tsp.workspace_bytes(d, which)
-    h, es = 4096, 2
+    h, F, es = 4096, 11008, 2
     for cfg in (C3, C3.with_(seq=16384), C3.with_(seq=16384, fold=4)):
         D, T, S = cfg.fold, cfg.local_tokens, cfg.seq
         P = min(4, D // 2)
-        hs, Fs = h // D, 11008 // D
+        hs, Fs = h // D, F // D
         qkv = 3 * hs * h * es                   # one packed Q|K|V block
         kvslot = 2 * (32 // D) * S * 128 * es   # one shard's K and V^T over the sequence
-        grown = (P - 1) * (2 * qkv + 2 * kvslot + T * hs * es)  # more shards in 2 slots each, and in Q
+        launch = (P - 1) * (2 * qkv + 2 * kvslot + T * hs * es)  # more shards in 2 slots each, and in Q
+        # accumulation: all D shards' columns in one group, against two groups of P shards' columns
+        # (D = 2P) and the [T][h] fp32 partial sum
+        acc_o = (T * h * es + h * h * es) - (T * P * hs * es + 2 * h * P * hs * es + 4 * T * h)
+        acc_m = (T * F * es + h * F * es) - (T * P * Fs * es + 2 * h * P * Fs * es + 4 * T * h)
         diff = ws(cfg, 0, tsp.TSP_WS_ATTN) - ws(cfg, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_ATTN)
-        assert grown - 128 * 2**20 <= diff <= grown + 32 * 2**20, (D, S, diff, grown)  # split partials
+        want = launch + acc_o
+        assert want - 128 * 2**20 <= diff <= want + 32 * 2**20, (D, S, diff, want)  # split partials
         mlp = ws(cfg, 0, tsp.TSP_WS_MLP) - ws(cfg, tsp.TSP_F_SHARD_LAUNCH, tsp.TSP_WS_MLP)
-        assert mlp == (P - 1) * 2 * 2 * Fs * h * es, (D, mlp)
+        want_m = (P - 1) * 2 * 2 * Fs * h * es + acc_m
+        assert abs(mlp - want_m) <= 4 * 256, (D, mlp, want_m)  # 256-byte alignment of each buffer
 
 
 def test_micro_batch_workspace():
