@@ -887,6 +887,51 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
           }
         }
       } else if constexpr (EPI == EPI_QKV) {
+        // the 256 x 256 instance is only launched with hd % 32 == 0 and
+        // carries the block path alone (the other one costs it registers)
+        constexpr bool BLOCK_ONLY = BM == 256 && BN == 256;
+        if (BLOCK_ONLY || g.hd % 32 == 0) {
+          // The block's 32 columns lie in one head of one part of one shard
+          // (hs, ks and the shard width are multiples of hd): split the
+          // block's first column once, from a wave-uniform value, and step
+          // through the block by offsets.
+          int c = __builtin_amdgcn_readfirstlane(n0 + wn * WN + j * 32 + g.col0);
+          T* qb = (T*)g.Q;
+          T* kb = (T*)g.Kd;
+          T* vb = (T*)g.Vt;
+          if (g.shard_cols > 0) {
+            const int u = c / g.shard_cols;
+            c -= u * g.shard_cols;
+            qb += u * g.q_stride;
+            kb += u * g.kv_stride;
+            vb += u * g.kv_stride;
+          }
+          const int part = c < g.hs ? 0 : (c < g.hs + g.ks ? 1 : 2);
+          const int rem = part == 0 ? c : c - g.hs - (part - 1) * g.ks;
+          const int head = rem / g.hd;
+          const int e0 = rem - head * g.hd;
+          T* const qrow = qb + ((int64_t)head * qrows + m) * g.hd + e0;
+          T* const krow = kb + ((int64_t)head * krows + pos) * g.hd + e0;
+          T* const vcol = vb + ((int64_t)head * g.hd + e0) * krows + pos;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            if (!ok[q]) continue;
+            const int eo = 8 * q + 4 * lg;  // the chunk's first column within the block
+            float o4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+            if (part < 2 && g.rope_l2 > 0.0) rope_pairs(o4, e0 + eo, spos, g.rope_l2 / g.hd);
+            if (part == 0) {
+              store4<T>(qrow + eo, o4[0], o4[1], o4[2], o4[3]);
+            } else if (part == 1) {
+              store4<T>(krow + eo, o4[0], o4[1], o4[2], o4[3]);
+            } else {
+              T* pv = vcol + (int64_t)eo * krows;
+#pragma unroll
+              for (int t = 0; t < 4; t++) pv[(int64_t)t * krows] = from_f<T>(o4[t]);
+            }
+          }
+          continue;
+        }
+        if constexpr (!BLOCK_ONLY) {
 #pragma unroll
         for (int q = 0; q < 4; q++) {
           if (!ok[q]) continue;
@@ -918,6 +963,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int t = 0; t < 4; t++) pv[(int64_t)t * krows] = from_f<T>(o4[t]);
           }
+        }
         }
       }
     }
@@ -2778,7 +2824,11 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
     if (tiles(256, 256) >= 256) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
     else gemm_go<bf16, 128, 128, EPI, 4, 2>(a, vec, s);
   } else {
-    if (tiles(256, 192) > 256) {
+    if (tiles(256, 192) > 256 && a.hd % 32 == 0) {
+      // more than one round of tiles: 256 x 256 (the head dim a multiple of
+      // 32, so every 32-column block of the epilogue lies in one head)
+      gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
+    } else if (tiles(256, 192) > 256) {
       gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
     } else if (tiles(128, 192) >= 384) {
       // one round of 4-wave 128x192 tiles, two per CU, filling >= 3/4 of them
