@@ -2368,6 +2368,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     for (int i = 0; i < 16; i++) dk[u][i] = dv[u][i] = 0.f;
   // the lane's key (its column of S) is seen by local rows [qk, T)
   const int64_t qk = first_row_at(k0 + 32 * w + l32, a.chunk, a.rank, a.fold, a.T);
+  // rows from here on see all of the wave's keys (first_row_at grows with the key)
+  const int64_t qk_all = first_row_at(k0 + 32 * w + 31, a.chunk, a.rank, a.fold, a.T);
   const int qr = perm_rows(l32);  // the row of each 32-row half the lane feeds into S and dP
   if (total > 0) issue(0, 0);
   for (int it = 0; it < total; it++) {
@@ -2399,6 +2401,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     // of half 1 (4 NKB).  Step i reads the operand of step i + PD from LDS.
     // Alternate steps feed different accumulators, so no MFMA waits on the
     // one before.
+    // A block whose 64 rows all lie in [qk_all, T) needs no mask.  The
+    // softmax below forms P and dS unmasked; on the other blocks each half's
+    // entries outside [lo, hi) are zeroed in the packed bf16 operands just
+    // before the dV / dK products read them (they may hold inf or NaN for
+    // rows past T, which the select drops).
+    const bool full = q0 >= qk_all && q0 + kAB <= a.T;
     constexpr int PD = 4, NA = 2 * KS, NB = 4 * NKB, NS = 2 * (NA + NB);
     constexpr int EA = 16 / NA, EB = 16 / NB;  // softmax elements per step
     static_assert(16 % NA == 0 && 16 % NB == 0, "softmax elements must spread evenly over the steps");
@@ -2410,11 +2418,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
       const int qh = (i - 2 * NA) / NB, j = (i - 2 * NA) % NB, s2 = j / (2 * NKB), u = (j % (2 * NKB)) >> 1;
       return lds_chunk<128>((j & 1) ? Qt : dOt, 32 * u + l32, 4 * qh + 2 * s2 + h);
     };
+    // (each half's first S and dP products start from a zero accumulator)
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qh = 0; qh < 2; qh++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) s[qh][i] = dp[qh][i] = 0.f;
     bf16x8 pa[2][2], da[2][2];
     auto soft = [&](int qh, int i) {  // softmax element i of half qh
       const float4 l4 = lr[qh][i >> 2], d4 = dr[qh][i >> 2];
@@ -2422,10 +2427,19 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
       const float lv = e == 0 ? l4.x : e == 1 ? l4.y : e == 2 ? l4.z : l4.w;
       const float dl = e == 0 ? d4.x : e == 1 ? d4.y : e == 2 ? d4.z : d4.w;
       const int c = 32 * qh + 16 * (i >> 3) + (i & 7);
-      const float ex = fast_exp2(s[qh][i] * a.scale_log2 - lv);
-      const float pr = (c >= lo && c < hi) ? ex : 0.f;
+      (void)c;
+      const float pr = fast_exp2(s[qh][i] * a.scale_log2 - lv);
       pa[qh][i >> 3][i & 7] = (bf16)pr;
       da[qh][i >> 3][i & 7] = (bf16)(pr * (dp[qh][i] - dl));
+    };
+    auto mask_half = [&](int qh) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int c = 32 * qh + 16 * (i >> 3) + (i & 7);
+        const bool keep = c >= lo && c < hi;
+        pa[qh][i >> 3][i & 7] = keep ? pa[qh][i >> 3][i & 7] : (bf16)0.f;
+        da[qh][i >> 3][i & 7] = keep ? da[qh][i >> 3][i & 7] : (bf16)0.f;
+      }
     };
     bf16x8 ring[PD];
 #pragma unroll
@@ -2439,9 +2453,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
         const bf16x8 f = ring[i % PD];
         ring[i % PD] = frag_at(i + PD);
         if (j & 1)
-          dp[qh] = MF<bf16>::mma(f, vf[j >> 1], dp[qh]);
+          dp[qh] = MF<bf16>::mma(f, vf[j >> 1], j < 2 ? f32x16{0} : dp[qh]);
         else
-          s[qh] = MF<bf16>::mma(f, kf[j >> 1], s[qh]);
+          s[qh] = MF<bf16>::mma(f, kf[j >> 1], j < 2 ? f32x16{0} : s[qh]);
         if (qh == 1)
 #pragma unroll
           for (int e = 0; e < EA; e++) soft(0, EA * j + e);
@@ -2450,6 +2464,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     }
 #pragma unroll
     for (int qh = 0; qh < 2; qh++) {
+      if (!full) {  // this half's P and dS are complete: drop the rows its keys do not see
+        mask_half(qh);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int j = 0; j < NB; j++) {
         const int i = 2 * NA + NB * qh + j, s2 = j / (2 * NKB), u = (j % (2 * NKB)) >> 1;
@@ -2556,6 +2574,9 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; i++) dq[u][i] = 0.f;
   const int kr = 32 * kh + perm_rows(l32);  // the key row the lane feeds into S^T and dP^T
+  // the wave's smallest query position (positions grow with the row), or -1
+  // when some of its 32 rows lie past the block's last row
+  const int64_t qpos_w = 32 * qh + 31 < nq ? zz_pos(q0 + 32 * qh, a.chunk, a.rank, a.fold) : -1;
   if (kb_begin < kb_end) issue((int64_t)kb_begin * kAB, 0);
   for (int kb = kb_begin; kb < kb_end; kb++) {
     const int buf = (kb - kb_begin) & 1;
@@ -2566,24 +2587,30 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_kernel(AttnBwdArgs a) {
     const char* Ks = sm + buf * 3 * TB;
     const char* Vs = Ks + TB;
     const char* Kt = Ks + 2 * TB;
-    f32x16 s, dp;
-#pragma unroll
-    for (int i = 0; i < 16; i++) s[i] = dp[i] = 0.f;
+    f32x16 s, dp;  // (the first products start from a zero accumulator)
 #pragma unroll
     for (int k = 0; k < KS; k++) {
-      s = MF<bf16>::mma(lds_chunk<RB>(Ks, kr, 2 * k + h), qf[k], s);
-      dp = MF<bf16>::mma(lds_chunk<RB>(Vs, kr, 2 * k + h), of[k], dp);
+      s = MF<bf16>::mma(lds_chunk<RB>(Ks, kr, 2 * k + h), qf[k], k == 0 ? f32x16{0} : s);
+      dp = MF<bf16>::mma(lds_chunk<RB>(Vs, kr, 2 * k + h), of[k], k == 0 ? f32x16{0} : dp);
     }
     // dS as the first operand over the wave's 32 keys: register i holds key
-    // k0 + 32 kh + 8 h + 16 (i / 8) + i % 8, kept while that key <= qpos
-    const int lim = (int)std::max<int64_t>(std::min<int64_t>(qpos - k0 - 32 * kh - 8 * h, kAB), -1);
+    // k0 + 32 kh + 8 h + 16 (i / 8) + i % 8, kept while that key <= qpos.
+    // Formed unmasked; when some of the wave's rows do not see all its keys
+    // the entries past them are zeroed afterwards (they may hold inf or NaN,
+    // which the select drops).
     bf16x8 da[2];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const int c = 16 * (i >> 3) + (i & 7);
       const float e = fast_exp2(s[i] * a.scale_log2 - lq);
-      const float pr = c <= lim ? e : 0.f;
-      da[i >> 3][i & 7] = (bf16)(pr * (dp[i] - dlq));
+      da[i >> 3][i & 7] = (bf16)(e * (dp[i] - dlq));
+    }
+    if (!(qpos_w >= k0 + 32 * kh + 31)) {
+      const int lim = (int)std::max<int64_t>(std::min<int64_t>(qpos - k0 - 32 * kh - 8 * h, kAB), -1);
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int c = 16 * (i >> 3) + (i & 7);
+        da[i >> 3][i & 7] = c <= lim ? da[i >> 3][i & 7] : (bf16)0.f;
+      }
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; s2++) {
