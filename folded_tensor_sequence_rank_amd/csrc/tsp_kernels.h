@@ -14,7 +14,10 @@ enum Epi {
   EPI_RESID = 2,  // C = R + (beta ? Y : 0) + acc         (residual add, output dtype)
   EPI_QKV = 3,    // scatter columns to Q / K / Vt at zigzag positions
   EPI_SWIGLU = 4,  // C = silu(A.B1^T) * (A.B3^T)          (two B operands)
-  EPI_STORE = 5    // C = acc                               (output dtype)
+  EPI_STORE = 5,   // C = acc                               (output dtype)
+  // EPI_QKV with the rotary embedding (rope_l2 > 0): launch_gemm picks it for
+  // EPI_QKV calls that rotate, so the plain instance carries no fp64 angle code
+  EPI_QKV_ROPE = 6
 };
 
 struct GemmArgs {

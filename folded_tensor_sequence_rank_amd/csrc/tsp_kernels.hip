@@ -320,6 +320,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   typedef MF<T> M_;
   typedef typename M_::frag frag;
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
+  constexpr bool QKVE = EPI == EPI_QKV || EPI == EPI_QKV_ROPE;  // the Q/K/V scatter epilogue
+  constexpr bool ROPE = EPI == EPI_QKV_ROPE;                    // ... with the rotary embedding
   constexpr int ES = sizeof(T);
   constexpr int V = 16 / ES;
   constexpr int BK = 128 / ES;  // elements per 128-byte LDS row
@@ -364,7 +366,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   // with two shards per launch: W1/W3 1% faster at the 64K workload and 9% at
   // 16K, QKV 4% faster at 64K; the O projection 3% slower, so the
   // accumulating GEMMs keep row order.
-  constexpr bool GROUPED = TSP_GEMM_GROUP != 0 || EPI == EPI_QKV || EPI == EPI_SWIGLU;
+  constexpr bool GROUPED = TSP_GEMM_GROUP != 0 || QKVE || EPI == EPI_SWIGLU;
   int m0, n0;
   if constexpr (GROUPED) {
     constexpr int GM = NW == 8 ? 4 : 8;
@@ -762,7 +764,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
     if (m >= g.M) continue;
     int64_t pos = m, spos = m;
     int64_t qrows = g.T, krows = g.S;  // Q rows and K/V positions per head
-    if constexpr (EPI == EPI_QKV) {
+    if constexpr (QKVE) {
       // local row m = b*T + i of sequence b sits at position zigzag(i) of its
       // sequence, key row b*S + zigzag(i)
       const int nbt = g.batch > 0 ? g.batch : 1;
@@ -886,7 +888,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
               if (n + e < g.N) pc[e] = from_f<T>(s[e]);
           }
         }
-      } else if constexpr (EPI == EPI_QKV) {
+      } else if constexpr (QKVE) {
         // the 256 x 256 instance is only launched with hd % 32 == 0 and
         // carries the block path alone (the other one costs it registers)
         constexpr bool BLOCK_ONLY = BM == 256 && BN == 256;
@@ -918,7 +920,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
             if (!ok[q]) continue;
             const int eo = 8 * q + 4 * lg;  // the chunk's first column within the block
             float o4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-            if (part < 2 && g.rope_l2 > 0.0) rope_pairs(o4, e0 + eo, spos, g.rope_l2 / g.hd);
+            if constexpr (ROPE)
+              if (part < 2) rope_pairs(o4, e0 + eo, spos, g.rope_l2 / g.hd);
             if (part == 0) {
               store4<T>(qrow + eo, o4[0], o4[1], o4[2], o4[3]);
             } else if (part == 1) {
@@ -953,7 +956,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
           const int head = rem / g.hd;
           const int e = rem - head * g.hd;
           float o4[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-          if (part < 2 && g.rope_l2 > 0.0) rope_pairs(o4, e, spos, g.rope_l2 / g.hd);
+          if constexpr (ROPE)
+            if (part < 2) rope_pairs(o4, e, spos, g.rope_l2 / g.hd);
           if (part == 0) {
             store4<T>(qb + ((int64_t)head * qrows + m) * g.hd + e, o4[0], o4[1], o4[2], o4[3]);
           } else if (part == 1) {
@@ -2880,7 +2884,13 @@ hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
     switch (epi) {
       case EPI_ACC: gemm_bf16<EPI_ACC>(a, vec, s); break;
       case EPI_RESID: gemm_bf16<EPI_RESID>(a, vec, s); break;
-      case EPI_QKV: gemm_bf16<EPI_QKV>(a, vec, s); break;
+      case EPI_QKV:
+        if (a.rope_l2 > 0.0)
+          gemm_bf16<EPI_QKV_ROPE>(a, vec, s);
+        else
+          gemm_bf16<EPI_QKV>(a, vec, s);
+        break;
+      case EPI_QKV_ROPE: gemm_bf16<EPI_QKV_ROPE>(a, vec, s); break;
       case EPI_SWIGLU: gemm_bf16<EPI_SWIGLU>(a, vec, s); break;
       case EPI_STORE: gemm_bf16<EPI_STORE>(a, vec, s); break;
     }
@@ -2888,7 +2898,13 @@ hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
     switch (epi) {
       case EPI_ACC: gemm_go<float, 64, 64, EPI_ACC>(a, vec, s); break;
       case EPI_RESID: gemm_go<float, 64, 64, EPI_RESID>(a, vec, s); break;
-      case EPI_QKV: gemm_go<float, 64, 64, EPI_QKV>(a, vec, s); break;
+      case EPI_QKV:
+        if (a.rope_l2 > 0.0)
+          gemm_go<float, 64, 64, EPI_QKV_ROPE>(a, vec, s);
+        else
+          gemm_go<float, 64, 64, EPI_QKV>(a, vec, s);
+        break;
+      case EPI_QKV_ROPE: gemm_go<float, 64, 64, EPI_QKV_ROPE>(a, vec, s); break;
       case EPI_SWIGLU: gemm_go<float, 64, 64, EPI_SWIGLU>(a, vec, s); break;
       case EPI_STORE: gemm_go<float, 64, 64, EPI_STORE>(a, vec, s); break;
     }
