@@ -629,6 +629,18 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
   const size_t wbytes = (size_t)d.Fs * d.h * es;  // one shard's W1 (or W3) block
   const int64_t G = acc_group(d), P = launch_shards(d);
   TIMED(c, TSP_K_RMSNORM, HIP_TRY(launch_rmsnorm(d.dt, x1, g2, ws + L.xn, d.BT, (int)d.h, d.eps, c.s)));
+  // Two consecutive launch groups of one accumulation group share one W1/W3
+  // launch (their slots as the two weight blocks of the SwiGLU GEMM): the
+  // second group's shards are in by then at the measured shapes, and one
+  // launch over both fills the CUs' last round of tiles once, not twice.
+#ifndef TSP_W13_PAIR
+#define TSP_W13_PAIR 1
+#endif
+  struct Pending {
+    const char* b;
+    int64_t n, gp;
+    int s;
+  } pend = {nullptr, 0, 0, -1};
   // Ring steps t0 .. t0 + np - 1 (shards (r + t) mod D) per launch.
   for (int64_t t0 = 0, li = 0; t0 < d.D; t0 += P, li++) {
     const int64_t np = std::min<int64_t>(P, d.D - t0);
@@ -668,6 +680,10 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
       HIP_TRY(hipStreamWaitEvent(c.s, c.ev->readyM[s], 0));
     }
     // ---- compute stream
+    if (TSP_W13_PAIR && P > 1 && pend.s < 0 && gp + np < G && t0 + np < d.D) {
+      pend = {w, np, gp, s};  // W1/W3 runs with the next launch group's
+      continue;
+    }
     GemmArgs g = gemm_base();
     g.A = ws + L.xn;
     g.lda = d.h;
@@ -679,6 +695,15 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
     g.K = (int)d.h;
     g.C = ws + L.gg + gp * d.Fs * es;  // these shards' columns of the group's [T][G*Fs]
     g.ldc = G * d.Fs;
+    if (pend.s >= 0) {  // the previous launch group's shards first (columns just before these)
+      g.B_2 = g.B;
+      g.B3_2 = g.B3;
+      g.B = pend.b;
+      g.B3 = pend.b + pend.n * wbytes;
+      g.n_split = (int)(pend.n * d.Fs);
+      g.N += g.n_split;
+      g.C = ws + L.gg + pend.gp * d.Fs * es;
+    }
     TIMED(c, TSP_K_W13, HIP_TRY(launch_gemm(d.dt, EPI_SWIGLU, g, c.s)));
     int rc = 0;
     if (gp + np == G || t0 + np == d.D) {  // group complete: one W2 projection over its shards
@@ -688,7 +713,11 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
       if (rc) return rc;
       if (c.side) HIP_TRY(hipEventRecord(c.ev->freeW[gb], c.s));
     }
-    if (c.side) HIP_TRY(hipEventRecord(c.ev->freeM[s], c.s));
+    if (c.side) {
+      HIP_TRY(hipEventRecord(c.ev->freeM[s], c.s));
+      if (pend.s >= 0) HIP_TRY(hipEventRecord(c.ev->freeM[pend.s], c.s));
+    }
+    pend.s = -1;
   }
   return TSP_OK;
 }

@@ -24,6 +24,12 @@ struct GemmArgs {
   const void* A;
   const void* B;
   const void* B3;  // second B operand (EPI_SWIGLU)
+  // EPI_SWIGLU over two weight blocks: output columns from n_split on take
+  // their W1 / W3 rows from B_2 / B3_2 (row c - n_split) instead of B / B3
+  // (n_split = 0: one block).
+  const void* B_2;
+  const void* B3_2;
+  int n_split;
   int64_t lda, ldb;
   int M, N, K;
   void* C;

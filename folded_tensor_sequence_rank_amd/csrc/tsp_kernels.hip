@@ -383,6 +383,19 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
   const T* A = (const T*)g.A;
   const T* B = (const T*)g.B;
   const T* B3 = (const T*)g.B3;
+  // B rows of this tile's columns: n0 - nb (W1/W3 over two weight blocks; the
+  // launcher puts the split on a tile boundary), out of nbr rows
+  int nb = 0, nbr = g.N;
+  if (DUAL && g.n_split > 0) {
+    if (n0 >= g.n_split) {
+      B = (const T*)g.B_2;
+      B3 = (const T*)g.B3_2;
+      nb = g.n_split;
+      nbr = g.N - g.n_split;
+    } else {
+      nbr = g.n_split;
+    }
+  }
   const int nk = (g.K + BK - 1) / BK;
 
   f32x16 acc[MB][NB];
@@ -457,8 +470,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
     // physical chunk l%8 of row RR*i + 8w + l/8, i.e. logical chunk
     // (l%8) ^ (row%8).
     const brsrc rA = make_rsrc(A, (uint64_t)g.M * g.lda * ES);
-    const brsrc rB = make_rsrc(B, (uint64_t)g.N * g.ldb * ES);
-    const brsrc rB3 = make_rsrc(DUAL ? B3 : B, (uint64_t)g.N * g.ldb * ES);
+    const brsrc rB = make_rsrc(B, (uint64_t)nbr * g.ldb * ES);
+    const brsrc rB3 = make_rsrc(DUAL ? B3 : B, (uint64_t)nbr * g.ldb * ES);
     const int lrow = 8 * wave + (lane >> 3);
     // logical chunk of this lane's physical chunk lane%8 (round offsets RR*i
     // are multiples of 16 rows, so the swizzle term depends on lrow only)
@@ -472,8 +485,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < BC; i++) {
       const int rr = RR * i + lrow;
-      const int gn = n0 + (DUAL && rr >= BN ? rr - BN : rr);
-      offB[i] = gn < g.N ? (uint32_t)(((int64_t)gn * g.ldb + lc * V) * ES) : kOOB;
+      const int gn = n0 - nb + (DUAL && rr >= BN ? rr - BN : rr);
+      offB[i] = gn < nbr ? (uint32_t)(((int64_t)gn * g.ldb + lc * V) * ES) : kOOB;
     }
     auto issue = [&](int kt, int buf) {
       const int k0 = kt * BK;
@@ -666,8 +679,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs g) {
           src = B3;
           rr = row - BN;
         }
-        const int gn = n0 + rr;
-        rb[i] = load_chunk<T, false>(src, gn < g.N, gn, g.ldb, k0 + c * V, g.K);
+        const int gn = n0 - nb + rr;
+        rb[i] = load_chunk<T, false>(src, gn < nbr, gn, g.ldb, k0 + c * V, g.K);
       }
     };
     auto sstore = [&](int buf) {
@@ -2820,36 +2833,30 @@ static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
 //    2048 tokens: 0.104 ms against 0.123 for 128x64), else 4-wave 128x64
 //    (one shard at 2048 tokens); beyond that the estimate.
 // The estimate: rounds of 256 tiles x tile area / relative efficiency.
+//
+// The bf16 W1/W3 tile for M x N, named by its width: 96 (4-wave 128x96), 64
+// (4-wave 128x64), 128 (8-wave 256x128) or 192 (8-wave 128x192).
+static int swiglu_tile_n(int M, int N) {
+  auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (tiles(128, 192) <= 512)  // 4-wave tiles, two per CU: 128x96 when they fill 3/4 of the 512 slots
+    return tiles(128, 96) >= 384 ? 96 : 64;
+  // rounds of 256 tiles x tile area / relative efficiency (128x192: 0.8)
+  const double t128 = (double)((tiles(256, 128) + 255) / 256) * 256 * 128;
+  const double t192 = (double)((tiles(128, 192) + 255) / 256) * 128 * 192 / 0.8;
+  return t192 < t128 * 0.999 ? 192 : 128;
+}
+
 template <int EPI>
 static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
   auto tiles = [&](int bm, int bn) {
     return (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
   };
-  struct Cand { int bm, bn; double eff; };
-  auto pick = [&](const Cand* cs, int nc) {
-    int best = 0;
-    double bt = 1e300;
-    for (int c = 0; c < nc; c++) {
-      const double t = (double)((tiles(cs[c].bm, cs[c].bn) + 255) / 256) * cs[c].bm * cs[c].bn / cs[c].eff;
-      if (t < bt * 0.999) {
-        bt = t;
-        best = c;
-      }
-    }
-    return best;
-  };
   if constexpr (EPI == EPI_SWIGLU) {
-    const int64_t t192 = tiles(128, 192);
-    if (t192 <= 512) {
-      // 4-wave tiles, two per CU: 128x96 when they fill 3/4 of the 512 slots
-      if (tiles(128, 96) >= 384)
-        gemm_go<bf16, 128, 96, EPI, 4, 4>(a, vec, s);
-      else
-        gemm_go<bf16, 128, 64, EPI, 4, 2>(a, vec, s);
-    } else {
-      const Cand dual[] = {{256, 128, 1.0}, {128, 192, 0.8}};
-      if (pick(dual, 2) == 0) gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s);
-      else gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s);
+    switch (swiglu_tile_n(a.M, a.N)) {
+      case 96: gemm_go<bf16, 128, 96, EPI, 4, 4>(a, vec, s); break;
+      case 64: gemm_go<bf16, 128, 64, EPI, 4, 2>(a, vec, s); break;
+      case 128: gemm_go<bf16, 256, 128, EPI, 8>(a, vec, s); break;
+      default: gemm_go<bf16, 128, 192, EPI, 8, 4>(a, vec, s); break;
     }
   } else if constexpr (EPI == EPI_ACC || EPI == EPI_RESID || EPI == EPI_STORE) {
     if (tiles(256, 256) >= 256) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
@@ -2877,9 +2884,28 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 hipError_t launch_gemm(Dtype dt, Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.n_split != 0) {
+    if (epi != EPI_SWIGLU || a.n_split < 0 || a.n_split >= a.N || !a.B_2 || !a.B3_2) return hipErrorInvalidValue;
+    // one launch when the split falls on a tile boundary, else the two
+    // blocks as two launches
+    const int bn = dt == BF16 ? swiglu_tile_n(a.M, a.N) : 64;
+    if (a.n_split % bn != 0) {
+      GemmArgs p = a;
+      p.n_split = 0;
+      p.N = a.n_split;
+      hipError_t e = launch_gemm(dt, epi, p, s);
+      if (e != hipSuccess) return e;
+      p.B = a.B_2;
+      p.B3 = a.B3_2;
+      p.N = a.N - a.n_split;
+      p.C = (char*)a.C + (size_t)a.n_split * (dt == BF16 ? 2 : 4);
+      return launch_gemm(dt, epi, p, s);
+    }
+  }
   const int V = dt == BF16 ? 8 : 4;
   const bool vec = a.K % V == 0 && a.lda % V == 0 && a.ldb % V == 0 && aligned16(a.A) &&
-                   aligned16(a.B) && (a.B3 == nullptr || aligned16(a.B3));
+                   aligned16(a.B) && (a.B3 == nullptr || aligned16(a.B3)) &&
+                   (a.n_split == 0 || (aligned16(a.B_2) && aligned16(a.B3_2)));
   if (dt == BF16) {
     switch (epi) {
       case EPI_ACC: gemm_bf16<EPI_ACC>(a, vec, s); break;
