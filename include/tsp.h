@@ -171,8 +171,9 @@ enum {
   TSP_F_KV_STREAM = 32u,
   /* Shards per launch and per O / W2 projection.  By default P = max(1,
    * min(4, D/2)) consecutive shards (4 at D = 8, 2 at D = 4) run as one QKV
-   * launch and one attention launch (one W1/W3 launch) once all of them have
-   * arrived in a slot, which takes two slots of P shards each; and one O
+   * launch and one attention launch once all of them have arrived in a slot,
+   * which takes two slots of P shards each; the W1/W3 projection of two such
+   * groups runs as one launch over both slots; and one O
    * (W2) projection covers all D shards (K = h, K = F), adding the residual,
    * with all of W_O (W2) copied into one group buffer -- unless the layer's
    * SwiGLU products would exceed 2^31 bytes, when groups of P shards
@@ -187,12 +188,12 @@ enum {
 /* Kernel classes reported by tsp_profile_read. */
 enum {
   TSP_K_RMSNORM = 0, /* RMSNorm of the rank's tokens */
-  TSP_K_QKV = 1,     /* QKV projection of one attention shard (+ K/V scatter) */
-  TSP_K_ATTN = 2,    /* zigzag causal flash attention of one head group */
+  TSP_K_QKV = 1,     /* QKV projection of a launch's attention shards (+ K/V scatter) */
+  TSP_K_ATTN = 2,    /* zigzag causal flash attention of a launch's head groups */
   TSP_K_MERGE = 3,   /* merge of split attention work items */
-  TSP_K_OPROJ = 4,   /* O projection of one shard, accumulated in fp32 */
-  TSP_K_W13 = 5,     /* W1/W3 projection of one MLP shard with the SwiGLU product */
-  TSP_K_W2 = 6,      /* W2 projection of one MLP shard, accumulated in fp32 */
+  TSP_K_OPROJ = 4,   /* O projection of a group of shards (all of them by default), + residual */
+  TSP_K_W13 = 5,     /* W1/W3 projection of a launch's MLP shards with the SwiGLU product */
+  TSP_K_W2 = 6,      /* W2 projection of a group of shards (all of them by default), + residual */
   TSP_K_COUNT = 7
 };
 
