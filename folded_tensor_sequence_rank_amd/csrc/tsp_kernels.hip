@@ -2059,6 +2059,64 @@ __global__ void __launch_bounds__(256) transpose_pad_kernel(const T* __restrict_
   }
 }
 
+// Both forms for bf16 with 16-byte global accesses: a 64 x 64 tile per
+// work-group, read as 16-byte chunks of input rows (8 elements) and written as
+// 16-byte chunks of output rows gathered from the tile's columns.  Output row
+// c, column zs z + r holds input row r, column c of matrix z (at in + (z /
+// zdiv) s1 + (z % zdiv) s0); rows R <= r < Rw are written as zeros.  The
+// tile's rows are 132 bytes apart, so the eight rows one gather reads at a
+// time fall on eight different groups of four banks.  Needs 16-byte aligned
+// in and out, and ldi, ldo, s1, s0, zs multiples of 8 elements.
+__global__ void __launch_bounds__(256) transpose16_kernel(const bf16* __restrict__ in, bf16* __restrict__ out,
+                                                          int64_t R, int64_t Rw, int64_t C, int64_t ldi,
+                                                          int64_t ldo, int64_t zdiv, int64_t s1, int64_t s0,
+                                                          int64_t zs) {
+  constexpr int P = 66;  // tile row pitch in elements (132 bytes)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * P];
+  const int64_t z = blockIdx.z;
+  const uint16_t* src = (const uint16_t*)in + (z / zdiv) * s1 + (z % zdiv) * s0;
+  uint16_t* dst = (uint16_t*)out + z * zs;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int q = t + 256 * u, rr = q >> 3, cc = (q & 7) * 8;
+    const int64_t r = r0 + rr, c = c0 + cc;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (r < R) {
+      if (c + 8 <= C) {
+        v = *(const uint4*)(src + r * ldi + c);
+      } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int k = 0; k < 8 && c + k < C; k++) w[k >> 1] |= (uint32_t)src[r * ldi + c + k] << (16 * (k & 1));
+        v = uint4{w[0], w[1], w[2], w[3]};
+      }
+    }
+    uint32_t* row = (uint32_t*)(tile + rr * P + cc);
+    row[0] = v.x;
+    row[1] = v.y;
+    row[2] = v.z;
+    row[3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int q = t + 256 * u, oc = q >> 3, orr = (q & 7) * 8;
+    const int64_t c = c0 + oc, r = r0 + orr;
+    if (c >= C || r >= Rw) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+      w[k] = (uint32_t)tile[(orr + 2 * k) * P + oc] | ((uint32_t)tile[(orr + 2 * k + 1) * P + oc] << 16);
+    uint16_t* o = dst + c * ldo + r;
+    if (r + 8 <= Rw) {
+      *(uint4*)o = uint4{w[0], w[1], w[2], w[3]};
+    } else {
+      for (int k = 0; r + k < Rw; k++) o[k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+}
+
 // SwiGLU backward per element, a = n W1 and b = n W3 given in fp32 side by
 // side ([rows][2F]: a in columns [0, F), b in [F, 2F)) and dg = dout W2^T in
 // fp32 [rows][F]: da = dg b silu'(a), db = dg silu(a) into
@@ -2984,9 +3042,22 @@ hipError_t launch_fill32(void* p, uint32_t pattern, size_t bytes, hipStream_t s)
   return hipGetLastError();
 }
 
+// The 16-byte bf16 transpose when its alignment conditions hold and the grid
+// fits; false: use the element-wise kernels.
+static bool transpose16(Dtype dt, const void* in, void* out, int64_t R, int64_t Rw, int64_t C, int64_t ldi,
+                        int64_t ldo, int64_t Z, int64_t zdiv, int64_t s1, int64_t s0, int64_t zs, hipStream_t s) {
+  if (dt != BF16 || !aligned16(in) || !aligned16(out) || ((ldi | ldo | s1 | s0 | zs) & 7) != 0) return false;
+  const int64_t gx = (Rw + 63) / 64, gy = (C + 63) / 64;
+  if (gx > 0x7fffffff || gy > 65535 || Z > 65535) return false;
+  transpose16_kernel<<<dim3((unsigned)gx, (unsigned)gy, (unsigned)Z), 256, 0, s>>>(
+      (const bf16*)in, (bf16*)out, R, Rw, C, ldi, ldo, zdiv, s1, s0, zs);
+  return true;
+}
+
 hipError_t launch_transpose(Dtype dt, const void* in, void* out, int64_t R, int64_t C, int64_t ldi,
                             int64_t ldo, hipStream_t s) {
   if (R <= 0 || C <= 0) return hipSuccess;
+  if (transpose16(dt, in, out, R, R, C, ldi, ldo, 1, 1, 0, 0, 0, s)) return hipGetLastError();
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
   if (dt == BF16)
     transpose_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)in, (bf16*)out, R, C, ldi, ldo);
@@ -3000,6 +3071,7 @@ hipError_t launch_transpose_pad(Dtype dt, const void* in, void* out, int64_t R, 
                                 hipStream_t s) {
   if (Rp <= 0 || C <= 0 || Z <= 0) return hipSuccess;
   if (Rp % 64 != 0 || Rp < R || zdiv <= 0 || Z > 65535 || (C + 63) / 64 > 65535) return hipErrorInvalidValue;
+  if (transpose16(dt, in, out, R, Rp, C, ldi, ldo, Z, zdiv, s1, s0, Rp, s)) return hipGetLastError();
   const dim3 grid((unsigned)(Rp / 64), (unsigned)((C + 63) / 64), (unsigned)Z);
   if (dt == BF16)
     transpose_pad_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)in, (bf16*)out, R, Rp, C, ldi, ldo, zdiv, s1, s0);
