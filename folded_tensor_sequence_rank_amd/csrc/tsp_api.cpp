@@ -850,8 +850,10 @@ int mlp_bwd_body(Ctx& c, const MlpBwdWs& L, const void* x1, const void* g2, cons
     if ((rc = plain_gemm(c, ws + L.dot, T, ws + L.gmt, T, h, F, T, dw_mlp[j] + 2 * F * h, F, false)))
       return rc;
   }
-  HIP_TRY(launch_rmsnorm_bwd(d.dt, x1, g2, dn, dout, dx1, (float*)(ws + L.rs), dg2, T, (int)h, d.eps,
-                             c.s));
+  // the gain's partial sums go to n2t, free once the last shard's GEMMs have read it
+  // (T h es bytes hold ceil(T / 64) h floats for every T >= 2)
+  HIP_TRY(launch_rmsnorm_bwd(d.dt, x1, g2, dn, dout, dx1, (float*)(ws + L.rs), dg2, (float*)(ws + L.n2t), T,
+                             (int)h, d.eps, c.s));
   return TSP_OK;
 }
 
@@ -1343,7 +1345,9 @@ int tsp_layer_shard_backward_finish(const tsp_dims* dims, const void* x, const v
     if ((rc = plain_gemm(c, w + L.gt, d.BT, w + L.n1t, d.BT, N, d.h, d.BT, dw_qkv[j], d.h, false))) return rc;
   }
   HIP_TRY(launch_fill32(dg1, 0u, (size_t)d.h * 4, c.s));
-  HIP_TRY(launch_rmsnorm_bwd(d.dt, x, g1, dn, dx1, dx, (float*)(w + L.rs), dg1, d.BT, (int)d.h, d.eps, c.s));
+  // the gain's partial sums go to n1t, free once the last shard's GEMMs have read it
+  HIP_TRY(launch_rmsnorm_bwd(d.dt, x, g1, dn, dx1, dx, (float*)(w + L.rs), dg1, (float*)(w + L.n1t), d.BT, (int)d.h,
+                             d.eps, c.s));
   return TSP_OK;
 }
 

@@ -129,10 +129,13 @@ hipError_t launch_transpose_pad(Dtype dt, const void* in, void* out, int64_t R, 
 // ab: [rows][2F] fp32, a = n W1 then b = n W3; dg: [rows][F] fp32.
 hipError_t launch_swiglu_bwd(Dtype dt, const float* ab, const float* dg, void* dab, void* g, int64_t rows,
                              int64_t F, hipStream_t s);
-// dx = res + RMSNorm'(x)^T dn; dgain += the gain's gradient (not zeroed here).
+// dx = res + RMSNorm'(x)^T dn; dgain += the gain's gradient (not zeroed here),
+// summed in a fixed order through partial (gain_partial_floats(rows, h)
+// floats of scratch).
 hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const float* dn, const void* res,
-                              void* dx, float* rs, float* dgain, int64_t rows, int h, float eps,
+                              void* dx, float* rs, float* dgain, float* partial, int64_t rows, int h, float eps,
                               hipStream_t s);
+int64_t gain_partial_floats(int64_t rows, int h);
 
 // Rotations undone: every 4-dim group of v (fp32, rows of hd values, `rows`
 // rows per head, `heads` heads) turned back by its row's position.  Row m of

@@ -2173,18 +2173,32 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const T* __restrict__ 
   if (lane == 0) rs[row] = r;
 }
 
-// Gain gradient: dgain[c] += sum over rows of dn[row][c] x[row][c] rs[row].
-// Each thread sums a run of 256 rows of one column, then adds it atomically.
+// Gain gradient, dgain[c] += sum over rows of dn[row][c] x[row][c] rs[row],
+// in two passes with a fixed summation order (no atomics, so the result is
+// the same on every run).  First pass: partial[b][c] = the sum over rows
+// [kGainRows b, kGainRows (b + 1)), one thread per column.
+constexpr int kGainRows = 64;
 template <typename T>
 __global__ void __launch_bounds__(256) gain_grad_kernel(const T* __restrict__ x, const float* __restrict__ dn,
-                                                        const float* __restrict__ rs, float* __restrict__ dgain,
+                                                        const float* __restrict__ rs, float* __restrict__ partial,
                                                         int64_t rows, int h) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= h) return;
-  const int64_t r0 = (int64_t)blockIdx.y * 256, r1 = r0 + 256 < rows ? r0 + 256 : rows;
+  const int64_t r0 = (int64_t)blockIdx.y * kGainRows;
+  const int64_t r1 = r0 + kGainRows < rows ? r0 + kGainRows : rows;
   float acc = 0.f;
   for (int64_t r = r0; r < r1; r++) acc += dn[r * h + c] * to_f(x[r * h + c]) * rs[r];
-  atomicAdd(dgain + c, acc);
+  partial[(int64_t)blockIdx.y * h + c] = acc;
+}
+
+// Second pass: dgain[c] += the nb partial sums of column c, in block order.
+__global__ void __launch_bounds__(256) gain_sum_kernel(const float* __restrict__ partial, float* __restrict__ dgain,
+                                                       int64_t nb, int h) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= h) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < nb; b++) s += partial[b * h + c];
+  dgain[c] += s;
 }
 
 // ---------------------------------------------------------------------------
@@ -2287,6 +2301,9 @@ __global__ void __launch_bounds__(256) qkv_grad_pack_kernel(const float* __restr
 // per sequence to a multiple of 64 rows with zeros, so that those tiles are
 // always whole.
 // ---------------------------------------------------------------------------
+#ifndef TSP_BWD_DIST
+#define TSP_BWD_DIST 4  // dK/dV kernel: LDS fragment reads in flight ahead of the MFMAs
+#endif
 constexpr int kAB = 64;    // rows of a query or key block
 constexpr int kBK2 = 128;  // keys per work-group of the dK/dV kernel
 constexpr int kBQ2 = 128;  // query rows per work-group of the dQ kernel
@@ -2482,7 +2499,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     // before the dV / dK products read them (they may hold inf or NaN for
     // rows past T, which the select drops).
     const bool full = q0 >= qk_all && q0 + kAB <= a.T;
-    constexpr int PD = 4, NA = 2 * KS, NB = 4 * NKB, NS = 2 * (NA + NB);
+    constexpr int PD = TSP_BWD_DIST, NA = 2 * KS, NB = 4 * NKB, NS = 2 * (NA + NB);
     constexpr int EA = 16 / NA, EB = 16 / NB;  // softmax elements per step
     static_assert(16 % NA == 0 && 16 % NB == 0, "softmax elements must spread evenly over the steps");
     auto frag_at = [&](int i) -> bf16x8 {
@@ -3093,20 +3110,25 @@ hipError_t launch_swiglu_bwd(Dtype dt, const float* ab, const float* dg, void* d
   return hipGetLastError();
 }
 
+int64_t gain_partial_floats(int64_t rows, int h) { return (rows + kGainRows - 1) / kGainRows * (int64_t)h; }
+
 hipError_t launch_rmsnorm_bwd(Dtype dt, const void* x, const void* g, const float* dn, const void* res,
-                              void* dx, float* rs, float* dgain, int64_t rows, int h, float eps,
+                              void* dx, float* rs, float* dgain, float* partial, int64_t rows, int h, float eps,
                               hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const dim3 rg((unsigned)((rows + 3) / 4)), cg((unsigned)((h + 255) / 256), (unsigned)((rows + 255) / 256));
+  const int64_t nb = (rows + kGainRows - 1) / kGainRows;
+  if (nb > 65535) return hipErrorInvalidValue;
+  const dim3 rg((unsigned)((rows + 3) / 4)), cg((unsigned)((h + 255) / 256), (unsigned)nb);
   if (dt == BF16) {
     rmsnorm_bwd_kernel<bf16><<<rg, 256, 0, s>>>((const bf16*)x, (const bf16*)g, dn, (const bf16*)res,
                                                (bf16*)dx, rs, rows, h, eps);
-    gain_grad_kernel<bf16><<<cg, 256, 0, s>>>((const bf16*)x, dn, rs, dgain, rows, h);
+    gain_grad_kernel<bf16><<<cg, 256, 0, s>>>((const bf16*)x, dn, rs, partial, rows, h);
   } else {
     rmsnorm_bwd_kernel<float><<<rg, 256, 0, s>>>((const float*)x, (const float*)g, dn, (const float*)res,
                                                 (float*)dx, rs, rows, h, eps);
-    gain_grad_kernel<float><<<cg, 256, 0, s>>>((const float*)x, dn, rs, dgain, rows, h);
+    gain_grad_kernel<float><<<cg, 256, 0, s>>>((const float*)x, dn, rs, partial, rows, h);
   }
+  gain_sum_kernel<<<dim3((unsigned)((h + 255) / 256)), 256, 0, s>>>(partial, dgain, nb, h);
   return hipGetLastError();
 }
 

@@ -76,3 +76,11 @@ def test_mlp_backward(case):
     # rounding, as for the forward blocks
     _delta_check(cfg, "dx1", f64(dx1), dout + dxn, dout, dout)
     _check(cfg, "dg2 (partial)", f64(dg2), dg)
+    # the path sums in a fixed order (no atomics): a second call on the same
+    # inputs gives the same bits
+    dx1b, dg2b = torch.empty_like(dx1), torch.full_like(dg2, float("nan"))
+    dwb = [torch.full_like(t, float("nan")) for t in dw]
+    tsp.tsp_mlp_shard_backward(dims, x1_d, L.g2, L.w_mlp, dout_d, dx1b, dg2b, dwb, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1b, dx1) and torch.equal(dg2b, dg2), "second call differs"
+    assert all(torch.equal(a_, b_) for a_, b_ in zip(dwb, dw)), "second call's weight gradients differ"
