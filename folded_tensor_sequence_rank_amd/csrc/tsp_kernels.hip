@@ -2908,6 +2908,9 @@ static void gemm_go(const GemmArgs& a, bool vec, hipStream_t s) {
 //    2048 tokens: 0.104 ms against 0.123 for 128x64), else 4-wave 128x64
 //    (one shard at 2048 tokens); beyond that the estimate.
 // The estimate: rounds of 256 tiles x tile area / relative efficiency.
+#ifndef TSP_ACC_SMALL
+#define TSP_ACC_SMALL 1
+#endif
 //
 // The bf16 W1/W3 tile for M x N, named by its width: 96 (4-wave 128x96), 64
 // (4-wave 128x64), 128 (8-wave 256x128) or 192 (8-wave 128x192).
@@ -2935,7 +2938,8 @@ static void gemm_bf16(const GemmArgs& a, bool vec, hipStream_t s) {
     }
   } else if constexpr (EPI == EPI_ACC || EPI == EPI_RESID || EPI == EPI_STORE) {
     if (tiles(256, 256) >= 256) gemm_go<bf16, 256, 256, EPI, 8>(a, vec, s);
-    else gemm_go<bf16, 128, 128, EPI, 4, 2>(a, vec, s);
+    else if (tiles(128, 128) >= 256 || !TSP_ACC_SMALL) gemm_go<bf16, 128, 128, EPI, 4, 2>(a, vec, s);
+    else gemm_go<bf16, 64, 64, EPI, 4, 2>(a, vec, s);  // small outputs (a shard's dW_O): fill the CUs
   } else {
     if (tiles(256, 192) > 256 && a.hd % 32 == 0) {
       // more than one round of tiles: 256 x 256 (the head dim a multiple of
