@@ -174,10 +174,14 @@ size_t qkv_rows(const Dims& d) { return (size_t)(d.hs + 2 * d.ks); }
 size_t attn_shard_elems(const Dims& d) { return (qkv_rows(d) + d.hs) * d.h; }
 size_t mlp_shard_elems(const Dims& d) { return 3 * (size_t)d.Fs * d.h; }
 
-// Launch groups: the QKV, attention and W1/W3 launches of a forward half
-// each cover min(4, D/2) consecutive shards (one with TSP_F_SHARD_LAUNCH).
+// Launch groups: the QKV and attention launches of a forward half each cover
+// min(4, D/2) consecutive shards (one with TSP_F_SHARD_LAUNCH); the W1/W3
+// launch covers two such groups when they share an accumulation group.
 #ifndef TSP_ACC_GROUP
 #define TSP_ACC_GROUP 4
+#endif
+#ifndef TSP_W13_PAIR
+#define TSP_W13_PAIR 1  // W1/W3 of two launch groups in one launch (mlp_body)
 #endif
 int64_t launch_group(const Dims& d) {
   return std::max<int64_t>(1, std::min<int64_t>(TSP_ACC_GROUP, d.D / 2));
@@ -633,9 +637,6 @@ int mlp_body(Ctx& c, const MlpWs& L, const void* x1, const void* g2, const void*
   // launch (their slots as the two weight blocks of the SwiGLU GEMM): the
   // second group's shards are in by then at the measured shapes, and one
   // launch over both fills the CUs' last round of tiles once, not twice.
-#ifndef TSP_W13_PAIR
-#define TSP_W13_PAIR 1
-#endif
   struct Pending {
     const char* b;
     int64_t n, gp;
