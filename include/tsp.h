@@ -293,7 +293,8 @@ int tsp_layer_shard(const tsp_dims* dims, const void* x, const void* g1,
  * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, kernels and results (bit for bit) as tsp_layer_shard; the
  * workspace is instead a static device array of TSP_NOALLOC_SCRATCH_BYTES
- * (256 MiB: the 7B-shape layer share fits up to S = 4096 at D = 8) that the
+ * (256 MiB: the 7B-shape layer share fits up to S = 4096 at D = 8 with
+ * TSP_F_SHARD_LAUNCH) that the
  * library holds on every GPU it runs on until the process ends.
  *   - Returns TSP_E_WORKSPACE, before anything is enqueued, when the dims
  *     need more than that (tsp_workspace_bytes(dims, TSP_WS_LAYER) tells).

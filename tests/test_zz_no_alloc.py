@@ -26,8 +26,8 @@ def _case(cfg, r):
 
 
 def test_noalloc_matches_layer_shard_on_two_calls():
-    # one shard per launch: 241 MiB of the 256 MiB scratch (two shards per
-    # launch, the default at this size, would need 329 MiB)
+    # one shard per launch: 241 MiB of the 256 MiB scratch (the default
+    # launch grouping would need 495 MiB at this size)
     big = synth.get_config("7b_s16k").with_(seq=4096)
     small = synth.LayerConfig(name="small", hidden=512, n_heads=4, head_dim=128, ffn=688, seq=1600,
                               fold=2, batch=2, n_kv_heads=2, rope_theta=10000.0)
