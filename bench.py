@@ -423,6 +423,30 @@ def layer_backward_bench(args):
         "executed_tflops": round((f_alg + recompute) / (ms * 1e-3) / 1e12, 2)}), flush=True)
 
 
+def hbm_copy_rate(mib=1024, reps=5):
+    """A device-to-device copy of `mib` MiB (the runtime's copy kernel) timed
+    with HIP events: bytes read plus bytes written per second, the measured
+    counterpart of the 8 TB/s HBM figure against which the HBM-bound kernels'
+    GB/s read."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"bytes_per_copy_read_and_written": 2 * n, "ms": round(ms, 4),
+            "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1), "peak_gbs": 8000.0}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -458,6 +482,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    hbm = None if args.headline_only else hbm_copy_rate()
     t_setup = time.perf_counter()
     w = synth.gen_weights(cfg)
     L = layer_dev(cfg, w)
@@ -651,6 +676,7 @@ def main():
         "kernels": kernels,
         "effective_clock_mhz": eff_clock,
         "gpu_clock_configured": clk.summary(),
+        "hbm_copy": hbm,
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(line), flush=True)
