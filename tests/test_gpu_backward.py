@@ -84,3 +84,53 @@ def test_mlp_backward(case):
     torch.cuda.synchronize()
     assert torch.equal(dx1b, dx1) and torch.equal(dg2b, dg2), "second call differs"
     assert all(torch.equal(a_, b_) for a_, b_ in zip(dwb, dw)), "second call's weight gradients differ"
+
+
+def test_mlp_backward_7b_s64k_rank3():
+    """The MLP half's backward at the full 64K shape the layer-backward
+    benchmark times (7B, S = 65536, fold 8, rank 3, 8192 rows).  A row's
+    dx1 depends on that row alone, so it is checked on sampled rows; an
+    intermediate column f's weight gradients (row f of a shard's dW1 / dW3,
+    column f of its dW2) need that column's activations over all rows only,
+    so they are checked on four sampled columns of every shard."""
+    cfg = synth.get_config("7b_s64k")
+    r, D, h, F = cfg.ranks[0], cfg.fold, cfg.hidden, cfg.ffn
+    Fs = F // D
+    say(f"[gpu] MLP backward 7b_s64k: h={h} F={F} S={cfg.seq} D={D} rank {r}")
+    w = synth.gen_weights(cfg)
+    L = layer_dev(cfg, w)
+    pos = O.zigzag_positions(cfg.seq, D, r)
+    x1_d = to_dev(synth.gen_rows(cfg, pos), cfg)
+    dout_d = to_dev(synth.gen_rows(cfg, pos, layer=7), cfg)
+    dims = tsp.make_dims(cfg, r)
+    ws = torch.empty(tsp.workspace_bytes(dims, tsp.TSP_WS_MLP_BWD), dtype=torch.uint8, device=DEV)
+    dx1 = torch.empty_like(x1_d)
+    dg2 = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    dw = [torch.full((3 * Fs * h,), float("nan"), dtype=torch.float32, device=DEV) for _ in range(D)]
+    tsp.tsp_mlp_shard_backward(dims, x1_d, L.g2, L.w_mlp, dout_d, dx1, dg2, dw, ws)
+    torch.cuda.synchronize()
+    say("    GPU done; oracle running")
+    x1, dout = f64(x1_d), f64(dout_d)  # the values the GPU received
+    T = x1.shape[0]
+    g2 = np.asarray(w.g2, np.float64)
+    rng = np.random.default_rng(77)
+    # both chunks' edges and interior rows
+    rows = np.unique(np.concatenate([[0, 1, T // 2 - 1, T // 2, T - 1], rng.integers(0, T, 43)]))
+    n2r = O.rmsnorm(x1[rows], g2, cfg.eps)
+    dn2r = B.swiglu_backward(n2r, w.w1, w.w3, w.w2, dout[rows])[0]
+    dxn, _ = B.rmsnorm_backward(x1[rows], g2, cfg.eps, dn2r)
+    _delta_check(cfg, f"dx1 on {rows.size} rows", f64(dx1)[rows], dout[rows] + dxn, dout[rows], dout[rows])
+    # four intermediate columns of every shard: its first, its last, two inside
+    local = [np.unique(np.concatenate([[0, Fs - 1], rng.integers(1, Fs - 1, 2)])) for _ in range(D)]
+    cols = np.concatenate([j * Fs + local[j] for j in range(D)])
+    n2 = O.rmsnorm(x1, g2, cfg.eps)
+    _, ew1, ew3, ew2 = B.swiglu_backward(n2, w.w1[:, cols], w.w3[:, cols], w.w2[cols, :], dout)
+    at = 0
+    for j in range(D):
+        k = local[j].size
+        got = f64(dw[j])
+        _check(cfg, f"shard {j} dW1 rows {[int(v) for v in local[j]]}", got[:Fs * h].reshape(Fs, h)[local[j]],
+               ew1[:, at:at + k].T)
+        _check(cfg, f"shard {j} dW3 rows", got[Fs * h:2 * Fs * h].reshape(Fs, h)[local[j]], ew3[:, at:at + k].T)
+        _check(cfg, f"shard {j} dW2 columns", got[2 * Fs * h:].reshape(h, Fs)[:, local[j]], ew2[at:at + k].T)
+        at += k
